@@ -1,0 +1,399 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one part of the oracle to a closed form, a hand-worked example,
+a library routine (torch SDPA in float64 on the CPU) on a special case, a brute
+force enumeration, or an invariant of the method as the pages state it
+("Efficient Edge-aware Attention Network for Graph Generation", full-text
+summary and abstract). Chosen so that a dropped term, a wrong sign, a wrong
+index or a transposed operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from edge_aware_graph_amd import workloads as W
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_batch(seed=0, B=3, n=10, d=16, de=8, dy=4, H=2, bias_scale=0.3, n_real=None):
+    dims = W.LayerDims(B=B, n=n, d=d, de=de, dy=dy, H=H, dh=d // H, dtype="fp32")
+    b = W.make_batch("tiny", seed=seed, bias_scale=bias_scale, dims=dims)
+    if n_real is not None:
+        b["mask"][:] = 0
+        for g, k in enumerate(n_real):
+            b["mask"][g, :k] = 1
+        pair = (b["mask"][:, :, None] & b["mask"][:, None, :]).astype(bool)
+        b["X"][b["mask"] == 0] = 0
+        b["E"][~pair] = 0
+    # make the FiLM terms large enough to matter
+    for k in ("w_emul", "w_eadd", "w_ymul", "w_yadd"):
+        b[k] = (b[k] * 3.0).astype(np.float32)
+    return b
+
+
+def t64(a):
+    return torch.tensor(np.asarray(a), dtype=torch.float64)
+
+
+def real_pairs(mask):
+    m = mask.astype(bool)
+    return m[:, :, None] & m[:, None, :]
+
+
+def sdpa_reference(batch, H, scale=None, add_bias=None, q_scale=None, k_scale=None):
+    """torch SDPA (float64, CPU) on the masked batch.
+
+    add_bias [B,H,n,n] is an additive float bias; q_scale/k_scale [B,H,n]
+    rescale query/key rows. Returns O [B,n,d] and A [B,H,n,n]; A is obtained
+    from the same library call with the identity as the value matrix.
+    """
+    X = t64(batch["X"])
+    B, n, d = X.shape
+    dh = d // H
+    q = F.linear(X, t64(batch["w_q"]), t64(batch["b_q"])).view(B, n, H, dh).transpose(1, 2)
+    k = F.linear(X, t64(batch["w_k"]), t64(batch["b_k"])).view(B, n, H, dh).transpose(1, 2)
+    v = F.linear(X, t64(batch["w_v"]), t64(batch["b_v"])).view(B, n, H, dh).transpose(1, 2)
+    if q_scale is not None:
+        q = q * t64(q_scale)[..., None]
+    if k_scale is not None:
+        k = k * t64(k_scale)[..., None]
+    pm = torch.tensor(real_pairs(batch["mask"]))[:, None, :, :].expand(B, H, n, n)
+    bias = torch.zeros(B, H, n, n, dtype=torch.float64)
+    if add_bias is not None:
+        bias = bias + t64(add_bias)
+    bias = bias.masked_fill(~pm, float("-inf"))
+    eye = torch.eye(n, dtype=torch.float64).expand(B, H, n, n).contiguous()
+    outs, amaps = [], []
+    for h in range(H):
+        sc = None if scale is None else float(np.asarray(scale).reshape(-1)[h] if np.ndim(scale) else scale)
+        outs.append(F.scaled_dot_product_attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1],
+                                                   attn_mask=bias[:, h:h + 1], scale=sc))
+        amaps.append(F.scaled_dot_product_attention(q[:, h:h + 1], k[:, h:h + 1], eye[:, h:h + 1],
+                                                    attn_mask=bias[:, h:h + 1], scale=sc))
+    o = torch.cat(outs, 1).transpose(1, 2).reshape(B, n, d)
+    a = torch.cat(amaps, 1)
+    return o.numpy(), a.numpy()
+
+
+def real_rows(mask):
+    return mask.astype(bool)
+
+
+def zero_film(batch):
+    b = dict(batch)
+    for k in ("w_emul", "w_eadd", "w_ymul", "w_yadd"):
+        b[k] = np.zeros_like(batch[k])
+    for k in ("b_emul", "b_eadd", "b_ymul", "b_yadd"):
+        b[k] = np.zeros_like(batch[k])
+    return b
+
+
+def check_vs_sdpa(out, ref_o, ref_a, mask, tol=1e-12):
+    rr = real_rows(mask)
+    pm = real_pairs(mask)
+    H = out["A"].shape[1]
+    assert np.abs(out["O"][rr] - ref_o[rr]).max() < tol
+    A_real = np.where(pm[:, None], out["A"], 0.0)
+    ref_real = np.where(pm[:, None], ref_a, 0.0)
+    rows = np.broadcast_to(rr[:, None, :, None], out["A"].shape)
+    assert np.abs(A_real - ref_real)[rows].max() < tol
+    assert np.all(out["A"][~np.broadcast_to(pm[:, None], out["A"].shape)] == 0.0)
+
+
+# ------------------------------------------------------------------ pins
+
+def test_hand_worked_example():
+    """Closed form worked by hand for a 3-node graph (tests/golden)."""
+    with open(os.path.join(GOLDEN, "hand_worked_example.json")) as f:
+        g = json.load(f)
+    inp = {k: np.array(v, dtype=np.float32) for k, v in g["inputs"].items()}
+    inp["mask"] = np.array(g["inputs"]["mask"], dtype=np.uint8)
+    out = O.forward(inp, H=g["dims"]["H"])
+    env = {"exp": math.exp, "inf": math.inf, "__builtins__": {}}
+    for key in ("U", "A", "O", "Ep"):
+        exp_vals = np.vectorize(lambda s: float(eval(s, env)))(np.array(g["expected"][key], dtype=object))
+        got = out[key]
+        assert got.shape == exp_vals.shape, key
+        fin = np.isfinite(exp_vals)
+        assert np.all(got[~fin] == exp_vals[~fin]), key
+        assert np.allclose(got[fin], exp_vals[fin], rtol=1e-13, atol=1e-14), (key, got, exp_vals)
+
+
+def test_rows_sum_to_one_and_masked_zero():
+    """Normalized coefficients: each real row sums to 1; masked entries are +0.0."""
+    b = small_batch(seed=1, n_real=[10, 7, 3])
+    out = O.forward(b, H=2)
+    pm = real_pairs(b["mask"])
+    rr = real_rows(b["mask"])
+    s = out["A"].sum(-1)  # [B,H,n]
+    assert np.abs(s.transpose(0, 2, 1)[rr] - 1).max() < 1e-13
+    masked = ~np.broadcast_to(pm[:, None], out["A"].shape)
+    assert np.all(out["A"][masked] == 0) and not np.any(np.signbit(out["A"][masked]))
+    em = ~np.broadcast_to(pm[..., None], out["Ep"].shape)
+    assert np.all(out["Ep"][em] == 0) and not np.any(np.signbit(out["Ep"][em]))
+    assert np.all(out["O"][~rr] == 0) and not np.any(np.signbit(out["O"][~rr]))
+
+
+def test_vi_identity_block_equals_A():
+    """A*[V|I]: the last n columns are A bitwise, the first dh are the aggregation."""
+    b = small_batch(seed=2, n_real=[10, 6, 8])
+    out = O.forward(b, H=2)
+    Vall = O.project(b, "v", H=2)
+    dh = 8
+    for g in range(3):
+        for i in range(10):
+            vi = O.vi_product(out["A"][g, :, i, :], Vall[g], dh)
+            assert np.array_equal(vi[:, dh:], out["A"][g, :, i, :])
+            assert np.array_equal(vi[:, :dh].reshape(-1), out["O"][g, i])
+
+
+def test_zero_film_is_masked_sdpa():
+    """Zero FiLM weights and biases: the layer is plain masked SDPA (library)."""
+    b = zero_film(small_batch(seed=3, n_real=[10, 5, 9]))
+    out = O.forward(b, H=2)
+    ref_o, ref_a = sdpa_reference(b, H=2)
+    check_vs_sdpa(out, ref_o, ref_a, b["mask"])
+
+
+def test_edge_beta_is_additive_bias():
+    """gamma_e = gamma_y = 1: beta_e acts as SDPA's additive float mask."""
+    b = small_batch(seed=4, n_real=[10, 8, 4])
+    for k in ("w_emul", "b_emul", "w_ymul", "b_ymul"):
+        b[k] = np.zeros_like(b[k])
+    beta_e = F.linear(t64(b["E"]), t64(b["w_eadd"]), t64(b["b_eadd"])).permute(0, 3, 1, 2).numpy()
+    out = O.forward(b, H=2)
+    ref_o, ref_a = sdpa_reference(b, H=2, add_bias=beta_e)
+    check_vs_sdpa(out, ref_o, ref_a, b["mask"])
+
+
+def test_global_gamma_scales_score_and_edge_beta():
+    """Constant gamma_y per head multiplies both the scaled score and beta_e."""
+    b = small_batch(seed=5, n_real=[10, 9, 6])
+    for k in ("w_emul", "b_emul", "w_ymul"):
+        b[k] = np.zeros_like(b[k])
+    c = np.array([0.5, 2.5], dtype=np.float32)
+    b["b_ymul"] = (c - 1.0).astype(np.float32)
+    beta_e = F.linear(t64(b["E"]), t64(b["w_eadd"]), t64(b["b_eadd"])).permute(0, 3, 1, 2).numpy()
+    out = O.forward(b, H=2)
+    dh = 8
+    c64 = c.astype(np.float64)
+    ref_o, ref_a = sdpa_reference(b, H=2, scale=c64 / math.sqrt(dh),
+                                  add_bias=beta_e * c64[None, :, None, None])
+    check_vs_sdpa(out, ref_o, ref_a, b["mask"])
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_edge_gamma_multiplies_score(axis):
+    """E depending only on i (or only on j) makes gamma_e a per-query (per-key) scale.
+
+    Catches an E_ij / E_ji transposition: the two cases give different answers.
+    """
+    b = small_batch(seed=6, n_real=[10, 7, 10])
+    for k in ("w_eadd", "b_eadd", "w_ymul", "b_ymul"):
+        b[k] = np.zeros_like(b[k])
+    rng = np.random.default_rng(60)
+    Bn, n, de = 3, 10, 8
+    vec = rng.standard_normal((Bn, n, de)).astype(np.float32) * 0.5
+    E = vec[:, :, None, :] if axis == "row" else vec[:, None, :, :]
+    E = np.broadcast_to(E, (Bn, n, n, de)).copy()
+    E[~real_pairs(b["mask"])] = 0
+    b["E"] = E
+    g = 1.0 + F.linear(t64(vec), t64(b["w_emul"]), t64(b["b_emul"])).permute(0, 2, 1).numpy()  # [B,H,n]
+    out = O.forward(b, H=2)
+    if axis == "row":
+        ref_o, ref_a = sdpa_reference(b, H=2, q_scale=g)
+    else:
+        ref_o, ref_a = sdpa_reference(b, H=2, k_scale=g)
+    check_vs_sdpa(out, ref_o, ref_a, b["mask"])
+
+
+def test_global_beta_is_softmax_invariant():
+    """beta_y adds a per-(graph, head) constant to whole rows: A, O, E' unchanged."""
+    b = small_batch(seed=7, n_real=[10, 6, 9])
+    o1 = O.forward(b, H=2)
+    b2 = dict(b)
+    b2["w_yadd"] = (b["w_yadd"] * -4.0 + 1.0).astype(np.float32)
+    b2["b_yadd"] = (b["b_yadd"] + 3.0).astype(np.float32)
+    o2 = O.forward(b2, H=2)
+    for k in ("A", "O", "Ep"):
+        assert np.abs(o1[k] - o2[k]).max() < 1e-12
+    fin = np.isfinite(o1["U"])
+    assert np.abs(o1["U"][fin] - o2["U"][fin]).max() > 0.1
+
+
+def test_edge_update_is_linear_map_of_A():
+    """E' - E on real pairs equals torch Linear(H -> de) applied to A's head vector."""
+    b = small_batch(seed=8, n_real=[10, 8, 5])
+    out = O.forward(b, H=2)
+    a_edge = t64(out["A"]).permute(0, 2, 3, 1)  # [B,n,n,H]
+    ref = (t64(b["E"]) + F.linear(a_edge, t64(b["w_e"]), t64(b["b_e"]))).numpy()
+    pm = real_pairs(b["mask"])
+    assert np.abs(out["Ep"][pm] - ref[pm]).max() < 1e-13
+
+
+def test_single_real_node_closed_form():
+    """One real node: A = [1], O = V_0, E'_00 = E_00 + W_e 1 + b_e."""
+    b = small_batch(seed=9, B=1, n=6, n_real=[1])
+    out = O.forward(b, H=2)
+    v0 = F.linear(t64(b["X"][0, 0]), t64(b["w_v"]), t64(b["b_v"])).numpy()
+    assert np.all(out["A"][0, :, 0, 0] == 1.0)
+    assert np.abs(out["O"][0, 0] - v0).max() < 1e-14
+    e00 = b["E"][0, 0, 0].astype(np.float64) + b["w_e"].astype(np.float64).sum(1) + b["b_e"]
+    assert np.abs(out["Ep"][0, 0, 0] - e00).max() < 1e-14
+
+
+def test_uniform_attention_closed_form():
+    """Q = K = 0 and E constant over pairs: A = 1/n_b exactly (n_b power of 2)."""
+    b = small_batch(seed=10, B=2, n=12, n_real=[8, 4])
+    b["X"][:] = 0
+    for k in ("b_q", "b_k"):
+        b[k] = np.zeros_like(b[k])
+    pm = real_pairs(b["mask"])
+    e = np.random.default_rng(1).standard_normal(8).astype(np.float32)
+    b["E"][:] = 0
+    b["E"][pm] = e
+    out = O.forward(b, H=2)
+    for g, nb in enumerate([8, 4]):
+        assert np.all(out["A"][g, :, :nb, :nb] == 1.0 / nb)
+
+
+def test_mask_enumeration_matches_induced_subgraph():
+    """All 2^12 node subsets of a 12-node graph: padded+masked == unpadded subgraph, bitwise."""
+    n = 12
+    base = small_batch(seed=11, B=1, n=n, d=8, de=4, dy=4, H=2, n_real=[n])
+    subsets = np.arange(1 << n)
+    Bn = len(subsets)
+    mask = ((subsets[:, None] >> np.arange(n)[None, :]) & 1).astype(np.uint8)
+    big = dict(base)
+    big["X"] = np.repeat(base["X"], Bn, 0) * mask[:, :, None]
+    pm = mask[:, :, None].astype(bool) & mask[:, None, :].astype(bool)
+    big["E"] = np.where(pm[..., None], np.repeat(base["E"], Bn, 0), 0).astype(np.float32)
+    big["y"] = np.repeat(base["y"], Bn, 0)
+    big["mask"] = mask
+    out = O.forward(big, H=2)
+    rng = np.random.default_rng(0)
+    check = rng.choice(Bn, size=512, replace=False)
+    check = np.union1d(check, [0, 1, Bn - 1, 0b101010101010])
+    for s in check:
+        idx = np.flatnonzero(mask[s])
+        assert np.all(out["A"][s][:, ~mask[s].astype(bool)] == 0)
+        assert np.all(out["O"][s][~mask[s].astype(bool)] == 0)
+        if len(idx) == 0:
+            assert np.all(out["A"][s] == 0) and np.all(out["Ep"][s] == 0)
+            continue
+        sub = dict(base)
+        sub["X"] = base["X"][:, idx]
+        sub["E"] = base["E"][:, idx][:, :, idx]
+        sub["mask"] = np.ones((1, len(idx)), dtype=np.uint8)
+        ref = O.forward(sub, H=2)
+        assert np.array_equal(out["O"][s][idx], ref["O"][0])
+        assert np.array_equal(out["A"][s][:, idx][:, :, idx], ref["A"][0])
+        assert np.array_equal(out["Ep"][s][idx][:, idx], ref["Ep"][0])
+
+
+def test_permutation_equivariance():
+    """Relabelling the real nodes relabels O, A and E' the same way."""
+    b = small_batch(seed=12, B=2, n=10, n_real=[10, 10])
+    out = O.forward(b, H=2)
+    perm = np.random.default_rng(3).permutation(10)
+    bp = dict(b)
+    bp["X"] = b["X"][:, perm]
+    bp["E"] = b["E"][:, perm][:, :, perm]
+    outp = O.forward(bp, H=2)
+    assert np.abs(outp["O"] - out["O"][:, perm]).max() < 1e-12
+    assert np.abs(outp["A"] - out["A"][:, :, perm][:, :, :, perm]).max() < 1e-12
+    assert np.abs(outp["Ep"] - out["Ep"][:, perm][:, :, perm]).max() < 1e-12
+
+
+def test_zero_update_weights_keep_E_and_linearity():
+    """W_e = 0, b_e = 0 gives E' = E bitwise; E' - E is linear in W_e."""
+    b = small_batch(seed=13, n_real=[10, 7, 2])
+    pm = real_pairs(b["mask"])
+    b0 = dict(b, w_e=np.zeros_like(b["w_e"]), b_e=np.zeros_like(b["b_e"]))
+    out0 = O.forward(b0, H=2)
+    assert np.array_equal(out0["Ep"][pm], b["E"][pm].astype(np.float64))
+    rng = np.random.default_rng(5)
+    # dyadic weights so that w1 + w2 is exact in float32
+    w1 = (rng.integers(-16, 17, size=b["w_e"].shape) / 8.0).astype(np.float32)
+    w2 = (rng.integers(-16, 17, size=b["w_e"].shape) / 8.0).astype(np.float32)
+    d = {}
+    for name, w in (("1", w1), ("2", w2), ("12", w1 + w2)):
+        d[name] = O.forward(dict(b0, w_e=w), H=2)["Ep"] - b["E"]
+    assert np.abs((d["1"] + d["2"] - d["12"])[pm]).max() < 1e-12
+
+
+def test_nan_padding_does_not_leak():
+    """NaN/Inf in padded X rows and E pairs leave every real output bitwise unchanged."""
+    b = small_batch(seed=14, n_real=[10, 6, 3])
+    ref = O.forward(b, H=2)
+    p = dict(b)
+    pm = real_pairs(b["mask"])
+    X = b["X"].copy()
+    X[b["mask"] == 0] = np.nan
+    E = b["E"].copy()
+    E[~pm] = np.inf
+    E[~pm, 0] = np.nan
+    p["X"], p["E"] = X, E
+    out = O.forward(p, H=2)
+    for k in ("O", "A", "Ep", "U", "lse"):
+        assert np.array_equal(out[k], ref[k]), k
+    assert not np.isnan(out["O"]).any() and not np.isnan(out["A"]).any() and not np.isnan(out["Ep"]).any()
+
+
+def test_bf16_round_matches_torch():
+    """The oracle's bfloat16 rounding equals torch's float32 -> bfloat16 conversion (RNE)."""
+    rng = np.random.default_rng(15)
+    bits = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, size=4000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    special = np.array([0x00000000, 0x80000000, 0x3F808000, 0x3F818000, 0x7F7FFFFF, 0x7F7F8000,
+                        0x00000001, 0x00008000, 0x00018000, 0x007FFFFF, 0x3F800001, 0xBF7FFFFF],
+                       dtype=np.uint32)
+    vals = np.concatenate([bits, ties, special]).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    ref = torch.from_numpy(vals.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([O.bf16_round(float(v)) for v in vals])
+    assert np.array_equal(got, ref)
+    assert math.isnan(O.bf16_round(float("nan")))
+    assert O.bf16_round(float("inf")) == float("inf")
+
+
+def test_bf16_rounding_points_zero_film():
+    """bf16 mode, zero FiLM: Q/K/V rounded after projection, A rounded, O = bf16(A) bf16(V)."""
+    b = zero_film(small_batch(seed=16, n_real=[10, 9, 5]))
+    for k in ("X", "E", "y", "w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_e", "b_e"):
+        b[k] = W.bf16_round_array(b[k])
+    out = O.forward(b, H=2, bf16=True)
+    X = t64(b["X"])
+    B, n, d = X.shape
+    H, dh = 2, 8
+
+    def proj(w, bias):
+        p = F.linear(X, t64(b[w]), t64(b[bias]))
+        return p.to(torch.bfloat16).to(torch.float64).view(B, n, H, dh).transpose(1, 2)
+
+    q, k, v = proj("w_q", "b_q"), proj("w_k", "b_k"), proj("w_v", "b_v")
+    qo = O.project(b, "q", H=2, bf16=True)
+    q_ref = q.transpose(1, 2).reshape(B, n, d).numpy() * b["mask"][:, :, None]
+    assert np.array_equal(qo, q_ref)
+    pm = torch.tensor(real_pairs(b["mask"]))[:, None].expand(B, H, n, n)
+    bias = torch.zeros(B, H, n, n, dtype=torch.float64).masked_fill(~pm, float("-inf"))
+    eye = torch.eye(n, dtype=torch.float64).expand(B, H, n, n).contiguous()
+    a = F.scaled_dot_product_attention(q, k, eye, attn_mask=bias)
+    a = torch.nan_to_num(a, nan=0.0).to(torch.bfloat16).to(torch.float64)
+    o = torch.matmul(a, v).transpose(1, 2).reshape(B, n, d).numpy()
+    rr = real_rows(b["mask"])
+    a = a.numpy()
+    rows = np.broadcast_to(rr[:, None, :, None], a.shape)
+    diff = np.abs(out["A"] - a)[rows]
+    # identical up to a rare one-ulp flip where the two float64 softmaxes straddle a tie
+    assert (diff > 0).mean() < 1e-3 and diff.max() <= 2 ** -8
+    o_ref = np.einsum("bhij,bhjt->bhit", out["A"], v.numpy()).transpose(0, 2, 1, 3).reshape(B, n, d)
+    assert np.abs(out["O"][rr] - o_ref[rr]).max() < 1e-12
+    assert np.abs(out["O"][rr] - o[rr]).max() < 4e-3
