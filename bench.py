@@ -1,0 +1,244 @@
+"""Benchmark of one edge-aware attention layer forward (node + edge outputs) on
+one MI355X.
+
+A step is one whole layer call (``edge_attn_layer``: Q/K/V projection, scores
+with head-wise FiLM, masked softmax, A and O, residual edge update) over one
+synthetic batch already resident in HBM. Steps rotate over enough distinct
+input/output buffer sets that the working set exceeds the 256 MB Infinity
+Cache, so every step streams from HBM.
+
+Prints one JSON line: graphs/s (value), edge-tokens/s, the dominant kernel's
+roofline record (algorithmic bytes over its HIP-event-timed average
+duration), and the CPU oracle timed on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+INFINITY_CACHE_BYTES = 256 << 20
+KERNEL_SOURCE = os.path.join(ROOT, "edge_aware_graph_amd", "csrc", "ea_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="planar", choices=["planar", "tree", "sbm", "large", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hot", action="store_true", help="also time back-to-back calls on one buffer set")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool) -> float:
+    """Bytes one launch of `kernel` must move (inputs read once, outputs written once).
+
+    Per edge token (b, i, j): E read (real pairs only), E' written (whole
+    padded layout), A written (single pass). Per node row: O written, the
+    per-head Q, K, V read from the workspace. Per graph: lse for two-pass.
+    """
+    s = 2 if dims.dtype == "bf16" else 4
+    B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
+    tokens = B * n * n
+    real_tokens = float(np.sum(n_real.astype(np.float64) ** 2))
+    rows = B * n
+    e_read = real_tokens * de * s
+    e_write = tokens * de * s
+    a_io = tokens * H * s
+    o_write = rows * d * s
+    qkv = 3 * rows * d * s
+    lse = B * H * n * 4
+    if kernel == "attn_kernel(fused)":
+        return e_read + e_write + a_io + o_write + qkv
+    if kernel == "attn_kernel":
+        return e_read + o_write + qkv + (lse if two_pass else a_io)
+    if kernel == "update_kernel":
+        return e_read + e_write + ((2 * rows * d * s + lse) if two_pass else a_io)
+    if kernel == "qkv_kernel":
+        return rows * d * s + 3 * d * d * s + qkv
+    raise ValueError(kernel)
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel.split("(")[0], workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(batch, dims, budget_s: float = 12.0):
+    """The oracle (as it stands) on whole graphs of the same batch, host cores."""
+    from oracle import oracle as OR
+    threads = OR.num_threads()
+    # a first graph to size the sample
+    t0 = time.perf_counter()
+    OR.forward({k: (v[:1] if k in ("X", "E", "y", "mask", "adj", "n_real") else v) for k, v in batch.items()},
+               dims.H, bf16=(dims.dtype == "bf16"))
+    per_graph = max(time.perf_counter() - t0, 1e-4)
+    g = int(max(1, min(dims.B, budget_s / per_graph)))
+    sub = {k: (v[:g] if k in ("X", "E", "y", "mask", "adj", "n_real") else v) for k, v in batch.items()}
+    t0 = time.perf_counter()
+    OR.forward(sub, dims.H, bf16=(dims.dtype == "bf16"))
+    dt = time.perf_counter() - t0
+    return {"value": g / dt, "unit": "graphs/s", "cores": threads, "kind": "oracle",
+            "sample": "the first %d of the %d graphs of the timed batch, every query row, all outputs "
+                      "(float64 C loops, OpenMP over rows); graphs/s scales directly" % (g, dims.B)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the layer's batch dimension shards across GPUs "
+              "with no communication, so a multi-GPU figure is the one-GPU figure times N; "
+              "use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from edge_aware_graph_amd import workloads as W
+    from edge_aware_graph_amd.layer import EdgeAttention
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.workload]
+    dims = cfg.dims
+    print("[bench] workload %s: %s" % (cfg.name, cfg.description), file=sys.stderr, flush=True)
+    batch = W.make_batch(cfg.name, bias_scale=0.0)
+    n_real = batch["n_real"]
+    dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+
+    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype)
+    two_pass = layer.two_pass
+    weights = {k: torch.from_numpy(batch[k]).to(dev, dt) for k in batch if k.startswith(("w_", "b_"))}
+    # biases are all zero in the timed configuration: pass NULL
+    for k in list(weights):
+        if k.startswith("b_"):
+            weights.pop(k)
+
+    X0 = torch.from_numpy(batch["X"]).to(dev, dt)
+    E0 = torch.from_numpy(batch["E"]).to(dev, dt)
+    y0 = torch.from_numpy(batch["y"]).to(dev, dt)
+    m0 = torch.from_numpy(batch["mask"]).to(dev)
+    B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
+    es = 2 if dims.dtype == "bf16" else 4
+    set_bytes = (2 * B * n * n * de + B * n * d * 2 + (0 if two_pass else B * H * n * n)) * es + layer.workspace_bytes
+    nsets = int(max(1, min(16, -(-2 * INFINITY_CACHE_BYTES // set_bytes))))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(
+            X=X0.clone(), E=E0.clone(), y=y0.clone(), mask=m0.clone(),
+            O=torch.empty(B, n, d, dtype=dt, device=dev),
+            A=None if two_pass else torch.empty(B, H, n, n, dtype=dt, device=dev),
+            Eo=torch.empty(B, n, n, de, dtype=dt, device=dev),
+            ws=torch.empty(layer.workspace_bytes, dtype=torch.uint8, device=dev)))
+    print("[bench] %d buffer sets of %.1f MiB (two_pass=%s)" % (nsets, set_bytes / 2**20, two_pass),
+          file=sys.stderr, flush=True)
+
+    def step(k):
+        s = sets[k % nsets]
+        layer.layer(weights, s["X"], s["E"], s["y"], s["mask"], s["O"], s["A"], s["Eo"], s["ws"])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # timed region: exactly K steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    graphs_per_s = B / (ms_per_step * 1e-3)
+    print("[bench] timed %d steps: %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+
+    # per-kernel durations from HIP events on the launch stream, same step sequence
+    layer.profile_begin()
+    for k in range(args.steps):
+        step(k)
+    prof = layer.profile_end()
+    kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    avg_s = kernels[dominant]["avg_us"] * 1e-6
+    alg = algorithmic_bytes(dominant, dims, n_real, two_pass)
+    achieved = alg / avg_s / 1e9
+    for name in kernels:
+        b = algorithmic_bytes(name, dims, n_real, two_pass)
+        kernels[name]["alg_bytes"] = b
+        kernels[name]["alg_GBps"] = b / (kernels[name]["avg_us"] * 1e-6) / 1e9
+    traffic = traffic_from_profiles(dominant, cfg.name)
+
+    out = {
+        "metric": "graphs/s per fused layer forward (edge-aware attention + residual edge update)",
+        "value": graphs_per_s,
+        "unit": "graphs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded %s graphs, random Xavier weights)" % cfg.structure,
+        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "dy": dims.dy, "H": H,
+                   "dh": dims.dh, "structure": cfg.structure, "two_pass": two_pass,
+                   "edge_tokens_per_step": B * n * n, "real_edge_tokens_per_step": int(np.sum(n_real ** 2)),
+                   "buffer_sets": nsets},
+        "edge_tokens_per_s": B * n * n / (ms_per_step * 1e-3),
+        "layer_alg_GBps": sum(algorithmic_bytes(k, dims, n_real, two_pass) for k in kernels) / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": alg, "avg_launch_us": kernels[dominant]["avg_us"]},
+        "kernels": kernels,
+    }
+
+    if args.hot:
+        s = sets[0]
+        for _ in range(args.warmup):
+            layer.layer(weights, s["X"], s["E"], s["y"], s["mask"], s["O"], s["A"], s["Eo"], s["ws"])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.layer(weights, s["X"], s["E"], s["y"], s["mask"], s["O"], s["A"], s["Eo"], s["ws"])
+        torch.cuda.synchronize()
+        out["hot_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # plain copy of known size (for scaling rocprofv3 byte counters)
+    cp_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    out["copy_calibration_bytes"] = 256 << 20
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(batch, dims)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,366 @@
+// C ABI of the edge-aware attention layer: argument validation, workspace
+// plan, mode choice (one pass or the two-pass scheme for large graphs) and
+// kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/edge_attn.h"
+#include "ea_internal.h"
+
+struct ea_ctx {
+  ea_desc d;
+  int NP;          // n rounded up to a multiple of 16
+  int two_pass;
+  int forward_done;
+  size_t esz;      // element size of desc.dtype
+  size_t off_q, off_k, off_v, off_lse, ws_bytes;
+  // kernel timing window
+  int prof_on;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<int> ev_kernel;  // kernel id of each recorded pair
+  size_t ev_used;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ea_status fail(ea_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+ea_status check_ptr(const void* p, const char* name, size_t align, bool required) {
+  if (!p) return required ? fail(EA_E_NULLPTR, "%s is NULL", name) : EA_OK;
+  if (!aligned(p, align)) return fail(EA_E_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return EA_OK;
+}
+
+#define EA_TRY(x)                 \
+  do {                            \
+    ea_status s_ = (x);           \
+    if (s_ != EA_OK) return s_;   \
+  } while (0)
+
+ea_status check_attn_params(const ea_attn_params* p) {
+  if (!p) return fail(EA_E_NULLPTR, "attention parameters are NULL");
+  EA_TRY(check_ptr(p->w_q, "w_q", 16, true));
+  EA_TRY(check_ptr(p->w_k, "w_k", 16, true));
+  EA_TRY(check_ptr(p->w_v, "w_v", 16, true));
+  EA_TRY(check_ptr(p->w_emul, "w_emul", 16, true));
+  EA_TRY(check_ptr(p->w_eadd, "w_eadd", 16, true));
+  EA_TRY(check_ptr(p->w_ymul, "w_ymul", 4, true));
+  EA_TRY(check_ptr(p->w_yadd, "w_yadd", 4, true));
+  EA_TRY(check_ptr(p->b_q, "b_q", 4, false));
+  EA_TRY(check_ptr(p->b_k, "b_k", 4, false));
+  EA_TRY(check_ptr(p->b_v, "b_v", 4, false));
+  EA_TRY(check_ptr(p->b_emul, "b_emul", 4, false));
+  EA_TRY(check_ptr(p->b_eadd, "b_eadd", 4, false));
+  EA_TRY(check_ptr(p->b_ymul, "b_ymul", 4, false));
+  EA_TRY(check_ptr(p->b_yadd, "b_yadd", 4, false));
+  return EA_OK;
+}
+
+ea_status check_ws(const ea_ctx* c, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(EA_E_WORKSPACE, "workspace is NULL (%zu bytes required)", c->ws_bytes);
+  if (!aligned(ws, 256)) return fail(EA_E_ALIGN, "workspace is not 256-byte aligned");
+  if (ws_bytes < c->ws_bytes)
+    return fail(EA_E_WORKSPACE, "workspace has %zu bytes, %zu required", ws_bytes, c->ws_bytes);
+  return EA_OK;
+}
+
+ea::LayerArgs make_args(const ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                        const void* X, const void* E, const void* y, const uint8_t* mask,
+                        void* ws) {
+  ea::LayerArgs a;
+  memset(&a, 0, sizeof(a));
+  a.X = X; a.E = E; a.y = y; a.mask = mask;
+  if (p) {
+    a.w_q = p->w_q; a.w_k = p->w_k; a.w_v = p->w_v;
+    a.b_q = p->b_q; a.b_k = p->b_k; a.b_v = p->b_v;
+    a.w_emul = p->w_emul; a.w_eadd = p->w_eadd; a.b_emul = p->b_emul; a.b_eadd = p->b_eadd;
+    a.w_ymul = p->w_ymul; a.w_yadd = p->w_yadd; a.b_ymul = p->b_ymul; a.b_yadd = p->b_yadd;
+  }
+  if (u) { a.w_e = u->w_e; a.b_e = u->b_e; }
+  char* base = static_cast<char*>(ws);
+  a.Qw = base + c->off_q;
+  a.Kw = base + c->off_k;
+  a.Vt = base + c->off_v;
+  a.lse = reinterpret_cast<float*>(base + c->off_lse);
+  a.B = c->d.B; a.n = c->d.n; a.NP = c->NP; a.dy = c->d.dy;
+  a.scale = (float)(1.0 / sqrt((double)c->d.dh));
+  return a;
+}
+
+// Launch with optional event timing around it.
+template <typename F>
+ea_status timed(ea_ctx* c, int kernel, hipStream_t s, F&& launch) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (c->prof_on && c->ev_used + 2 <= c->ev_pool.size()) {
+    e0 = c->ev_pool[c->ev_used];
+    e1 = c->ev_pool[c->ev_used + 1];
+    c->ev_kernel.push_back(kernel);
+    c->ev_used += 2;
+    if (hipEventRecord(e0, s) != hipSuccess) return fail(EA_E_HIP, "hipEventRecord failed");
+  }
+  hipError_t err = launch();
+  if (err != hipSuccess)
+    return fail(EA_E_HIP, "%s launch failed: %s", ea_kernel_name(kernel), hipGetErrorString(err));
+  if (e1 && hipEventRecord(e1, s) != hipSuccess) return fail(EA_E_HIP, "hipEventRecord failed");
+  return EA_OK;
+}
+
+ea_status run_qkv(ea_ctx* c, const ea::LayerArgs& a, hipStream_t s) {
+  return timed(c, EA_K_QKV, s, [&] { return ea::launch_qkv(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, s); });
+}
+
+ea_status check_io(const ea_ctx* c, const void* X, const void* E, const void* y,
+                   const uint8_t* mask, bool needX) {
+  if (needX) EA_TRY(check_ptr(X, "X", 16, true));
+  EA_TRY(check_ptr(E, "E", 16, true));
+  EA_TRY(check_ptr(y, "y", 4, true));
+  if (!mask) return fail(EA_E_NULLPTR, "node_mask is NULL");
+  (void)c;
+  return EA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ea_status_str(ea_status s) {
+  switch (s) {
+    case EA_OK: return "ok";
+    case EA_E_NULLPTR: return "null pointer";
+    case EA_E_SHAPE: return "bad shape";
+    case EA_E_UNSUPPORTED: return "unsupported configuration";
+    case EA_E_ALIGN: return "misaligned pointer";
+    case EA_E_WORKSPACE: return "workspace too small";
+    case EA_E_STATE: return "call order violated";
+    case EA_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* ea_last_error(void) { return g_err; }
+
+const char* ea_kernel_name(int k) {
+  switch (k) {
+    case EA_K_QKV: return "qkv_kernel";
+    case EA_K_ATTN: return "attn_kernel";
+    case EA_K_UPDATE: return "update_kernel";
+    case EA_K_FUSED: return "attn_kernel(fused)";
+  }
+  return "?";
+}
+
+ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
+  g_err[0] = 0;
+  if (!desc || !out) return fail(EA_E_NULLPTR, "desc or out is NULL");
+  *out = nullptr;
+  const ea_desc& d = *desc;
+  if (d.B < 1 || d.n < 1 || d.d < 1 || d.de < 1 || d.dy < 1 || d.H < 1 || d.dh < 1)
+    return fail(EA_E_SHAPE, "all sizes must be >= 1 (B=%d n=%d d=%d de=%d dy=%d H=%d dh=%d)",
+                d.B, d.n, d.d, d.de, d.dy, d.H, d.dh);
+  if ((long long)d.H * d.dh != d.d) return fail(EA_E_SHAPE, "d (%d) != H*dh (%d*%d)", d.d, d.H, d.dh);
+  if (d.B > 65535) return fail(EA_E_SHAPE, "B (%d) exceeds 65535", d.B);
+  if (d.n > (1 << 20)) return fail(EA_E_SHAPE, "n (%d) exceeds 2^20", d.n);
+  if (d.dtype != EA_FP32 && d.dtype != EA_BF16) return fail(EA_E_UNSUPPORTED, "dtype %d", d.dtype);
+  if (d.flags & ~EA_FORCE_TWO_PASS) return fail(EA_E_UNSUPPORTED, "unknown flags 0x%x", d.flags);
+  if (!ea::shape_supported(d.dtype, d.H, d.dh, d.de))
+    return fail(EA_E_UNSUPPORTED, "(H, dh, de) = (%d, %d, %d) is not built; supported: (4,16,16), (8,32,64)",
+                d.H, d.dh, d.de);
+  ea_ctx* c = new (std::nothrow) ea_ctx();
+  if (!c) return fail(EA_E_SHAPE, "out of host memory");
+  c->d = d;
+  c->NP = (d.n + 15) / 16 * 16;
+  c->two_pass = (d.flags & EA_FORCE_TWO_PASS) || d.n > EA_SINGLE_PASS_MAX_N;
+  c->forward_done = 0;
+  c->esz = d.dtype == EA_BF16 ? 2 : 4;
+  const size_t qkv = round256((size_t)d.B * d.H * c->NP * d.dh * c->esz);
+  c->off_q = 0;
+  c->off_k = qkv;
+  c->off_v = 2 * qkv;
+  c->off_lse = 3 * qkv;
+  c->ws_bytes = 3 * qkv + round256((size_t)d.B * d.H * c->NP * sizeof(float));
+  c->prof_on = 0;
+  c->ev_used = 0;
+  *out = c;
+  return EA_OK;
+}
+
+void ea_ctx_destroy(ea_ctx* c) {
+  if (!c) return;
+  for (hipEvent_t e : c->ev_pool) hipEventDestroy(e);
+  delete c;
+}
+
+size_t ea_workspace_bytes(const ea_ctx* c) { return c ? c->ws_bytes : 0; }
+
+int ea_is_two_pass(const ea_ctx* c) { return c ? c->two_pass : -1; }
+
+ea_status edge_attn_forward(ea_ctx* c, const ea_attn_params* p, const void* X, const void* E,
+                            const void* y, const uint8_t* mask, void* O, void* A, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  EA_TRY(check_attn_params(p));
+  EA_TRY(check_io(c, X, E, y, mask, true));
+  EA_TRY(check_ptr(O, "O", 16, true));
+  if (c->two_pass) {
+    if (A) return fail(EA_E_UNSUPPORTED, "A is not produced in two-pass mode; pass NULL");
+  } else {
+    EA_TRY(check_ptr(A, "A", 16, true));
+  }
+  EA_TRY(check_ws(c, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ea::LayerArgs a = make_args(c, p, nullptr, X, E, y, mask, ws);
+  a.O = O;
+  a.A = A;
+  c->forward_done = 0;
+  EA_TRY(run_qkv(c, a, s));
+  const int mode = c->two_pass ? ea::kOnline : ea::kSingle;
+  EA_TRY(timed(c, EA_K_ATTN, s, [&] { return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, mode, s); }));
+  c->forward_done = 1;
+  return EA_OK;
+}
+
+ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                      const void* E, const void* y, const uint8_t* mask, const void* A,
+                      void* E_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
+  EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
+  EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
+  EA_TRY(check_ptr(E_out, "E_out", 16, true));
+  EA_TRY(check_ptr(E, "E", 16, true));
+  if (!mask) return fail(EA_E_NULLPTR, "node_mask is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->two_pass) {
+    EA_TRY(check_attn_params(p));
+    EA_TRY(check_ptr(y, "y", 4, true));
+    EA_TRY(check_ws(c, ws, ws_bytes));
+    if (!c->forward_done)
+      return fail(EA_E_STATE, "two-pass edge_update needs a preceding edge_attn_forward on this context");
+    ea::LayerArgs a = make_args(c, p, u, nullptr, E, y, mask, ws);
+    a.E_out = E_out;
+    return timed(c, EA_K_UPDATE, s, [&] {
+      return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kRecompute, s);
+    });
+  }
+  EA_TRY(check_ptr(A, "A", 16, true));
+  ea::LayerArgs a = make_args(c, nullptr, u, nullptr, E, y, mask, ws ? ws : E_out);
+  a.A = const_cast<void*>(A);
+  a.E_out = E_out;
+  return timed(c, EA_K_UPDATE, s, [&] {
+    return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kReadA, s);
+  });
+}
+
+ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                          const void* X, const void* E, const void* y, const uint8_t* mask,
+                          void* O, void* A, void* E_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  if (c->two_pass) {
+    // Validate everything before the first launch.
+    if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
+    EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
+    EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
+    EA_TRY(check_ptr(E_out, "E_out", 16, true));
+    EA_TRY(edge_attn_forward(c, p, X, E, y, mask, O, A, ws, ws_bytes, stream));
+    return edge_update(c, p, u, E, y, mask, nullptr, E_out, ws, ws_bytes, stream);
+  }
+  EA_TRY(check_attn_params(p));
+  EA_TRY(check_io(c, X, E, y, mask, true));
+  EA_TRY(check_ptr(O, "O", 16, true));
+  EA_TRY(check_ptr(A, "A", 16, true));
+  if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
+  EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
+  EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
+  EA_TRY(check_ptr(E_out, "E_out", 16, true));
+  EA_TRY(check_ws(c, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ea::LayerArgs a = make_args(c, p, u, X, E, y, mask, ws);
+  a.O = O;
+  a.A = A;
+  a.E_out = E_out;
+  c->forward_done = 0;
+  EA_TRY(run_qkv(c, a, s));
+  EA_TRY(timed(c, EA_K_FUSED, s, [&] {
+    return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kFused, s);
+  }));
+  c->forward_done = 1;
+  return EA_OK;
+}
+
+ea_status ea_debug_logits(ea_ctx* c, const ea_attn_params* p, const void* X, const void* E,
+                          const void* y, const uint8_t* mask, float* U, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  EA_TRY(check_attn_params(p));
+  EA_TRY(check_io(c, X, E, y, mask, true));
+  EA_TRY(check_ptr(U, "U", 16, true));
+  EA_TRY(check_ws(c, ws, ws_bytes));
+  if (c->NP > 4 * 64) return fail(EA_E_UNSUPPORTED, "logit export is limited to n <= 256");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ea::LayerArgs a = make_args(c, p, nullptr, X, E, y, mask, ws);
+  a.U = U;
+  EA_TRY(run_qkv(c, a, s));
+  return timed(c, EA_K_ATTN, s, [&] {
+    return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kLogits, s);
+  });
+}
+
+ea_status ea_profile_begin(ea_ctx* c) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  const size_t want = 2 * 4096;
+  while (c->ev_pool.size() < want) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return fail(EA_E_HIP, "hipEventCreate failed");
+    c->ev_pool.push_back(e);
+  }
+  c->ev_kernel.clear();
+  c->ev_used = 0;
+  c->prof_on = 1;
+  return EA_OK;
+}
+
+ea_status ea_profile_end(ea_ctx* c, double* total_ms, int64_t* launches) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  if (!total_ms || !launches) return fail(EA_E_NULLPTR, "output arrays are NULL");
+  for (int k = 0; k < EA_NUM_KERNELS; ++k) { total_ms[k] = 0.0; launches[k] = 0; }
+  c->prof_on = 0;
+  if (c->ev_used && hipEventSynchronize(c->ev_pool[c->ev_used - 1]) != hipSuccess)
+    return fail(EA_E_HIP, "hipEventSynchronize failed");
+  for (size_t k = 0; k < c->ev_kernel.size(); ++k) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->ev_pool[2 * k], c->ev_pool[2 * k + 1]) != hipSuccess)
+      return fail(EA_E_HIP, "hipEventElapsedTime failed");
+    total_ms[c->ev_kernel[k]] += ms;
+    launches[c->ev_kernel[k]] += 1;
+  }
+  c->ev_kernel.clear();
+  c->ev_used = 0;
+  return EA_OK;
+}
+
+}  // extern "C"

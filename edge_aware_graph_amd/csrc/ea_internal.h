@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ea {
+
+// Kernel modes of the attention kernel.
+enum AttnMode : int {
+  kSingle = 0,  // one pass over full rows: writes O and A
+  kFused = 1,   // kSingle plus the residual edge update: writes O, A and E'
+  kOnline = 2,  // two-pass pass 1: online softmax, writes O and softmax statistics
+  kLogits = 3,  // stage export: writes the masked logits u
+};
+// Kernel modes of the edge-update kernel.
+enum UpdateMode : int {
+  kReadA = 0,      // single pass: A comes from the forward's output
+  kRecompute = 1,  // two-pass pass 2: A = exp(u - lse) recomputed per tile
+};
+
+struct LayerArgs {
+  // inputs
+  const void* X;
+  const void* E;
+  const void* y;
+  const uint8_t* mask;
+  const void *w_q, *w_k, *w_v, *b_q, *b_k, *b_v;
+  const void *w_emul, *w_eadd, *b_emul, *b_eadd;
+  const void *w_ymul, *w_yadd, *b_ymul, *b_yadd;
+  const void *w_e, *b_e;
+  // workspace
+  void* Qw;    // [B, H, NP, dh]
+  void* Kw;    // [B, H, NP, dh]
+  void* Vt;    // [B, H, dh, NP]
+  float* lse;  // [B, H, NP]
+  // outputs
+  void* O;
+  void* A;       // attention map (kSingle/kFused) or the map to read (kReadA)
+  void* E_out;
+  float* U;      // logits (kLogits)
+  // sizes
+  int B, n, NP, dy;
+  float scale;   // 1/sqrt(dh)
+};
+
+// Launchers; each returns the hipError_t of its launch. `dtype` 0 = fp32, 1 = bf16.
+hipError_t launch_qkv(const LayerArgs& a, int dtype, int H, int dh, int de, hipStream_t s);
+hipError_t launch_attn(const LayerArgs& a, int dtype, int H, int dh, int de, int mode,
+                       hipStream_t s);
+hipError_t launch_update(const LayerArgs& a, int dtype, int H, int dh, int de, int mode,
+                         hipStream_t s);
+// Whether (dtype, H, dh, de) is instantiated.
+bool shape_supported(int dtype, int H, int dh, int de);
+
+}  // namespace ea

@@ -1,0 +1,178 @@
+/*
+ * edge_attn.h — C ABI of the MI355X (gfx950) edge-aware attention layer.
+ *
+ * The layer is the edge-aware attention layer of "Efficient Edge-aware
+ * Attention Network for Graph Generation" (ai-frontier-tracker digest,
+ * full-text summary; the kongchang.com explainer, "Design Strategy of the
+ * Edge-aware Attention Layer"). On a dense padded batch of B graphs with n
+ * node slots it computes, per graph b, query row i, key j and head h:
+ *
+ *   Q, K, V      = X W_{q,k,v}^T + b_{q,k,v}, split into H heads of dh (c = h*dh + t)
+ *   s            = q_i . k_j / sqrt(dh)                     (scaled dot product)
+ *   gamma_e      = 1 + E_ij W_emul^T + b_emul,  beta_e = E_ij W_eadd^T + b_eadd
+ *   gamma_y      = 1 + y W_ymul^T + b_ymul,     beta_y = y W_yadd^T + b_yadd
+ *   u            = (s * gamma_e + beta_e) * gamma_y + beta_y  (head-wise FiLM)
+ *   u            = -inf unless mask_i and mask_j              (graph mask)
+ *   A            = softmax_j(u)   (a row with no real key gives A = 0)
+ *   O_i          = sum_j A_ij V_j, heads merged to [d]        (A [V | I] gives O and A)
+ *   E'_ij        = E_ij + W_e A_ij + b_e on real pairs, +0.0 elsewhere
+ *                                                             (residual edge update)
+ *
+ * Graphs whose edge tensor is too large for one pass use the two-pass scheme
+ * the same page names: pass 1 computes softmax statistics and O, pass 2
+ * recomputes the scores and applies the edge update.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are contiguous, row-major, in device memory of the current
+ *    HIP device, of element type desc.dtype (float32, or bfloat16 stored as
+ *    uint16) unless stated otherwise. Weights use the nn.Linear [out, in]
+ *    layout. X, E, O, A, E_out, every weight matrix and the workspace must be
+ *    16-byte aligned (the workspace 256-byte aligned).
+ *  - The caller owns every buffer and the stream; the library allocates no
+ *    device memory and keeps no device state between calls. Calls are
+ *    asynchronous on `stream` (a hipStream_t; NULL is the default stream).
+ *  - Every argument is validated before anything is enqueued. On error the
+ *    call returns a status, enqueues nothing, and ea_last_error() describes
+ *    the problem. A kernel launch failure returns EA_E_HIP. Faults inside a
+ *    kernel surface at the caller's next synchronization.
+ *  - Padded entries (mask 0) of X and E may hold any bits, NaN/Inf included;
+ *    no output depends on them. Masked outputs are written as +0.0.
+ *  - bfloat16 mode rounds Q, K, V to bfloat16 after their projection and
+ *    rounds A to bfloat16 before it is stored, multiplied with V and used in
+ *    the edge update; all other arithmetic accumulates in float32.
+ */
+#ifndef EDGE_ATTN_H
+#define EDGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EA_OK = 0,
+  EA_E_NULLPTR = 1,     /* a required pointer is NULL                         */
+  EA_E_SHAPE = 2,       /* inconsistent or out-of-range sizes                 */
+  EA_E_UNSUPPORTED = 3, /* valid but not built: (H, dh, de) combination, dtype */
+  EA_E_ALIGN = 4,       /* a pointer breaks the alignment rule                */
+  EA_E_WORKSPACE = 5,   /* workspace missing or smaller than required         */
+  EA_E_STATE = 6,       /* call order violated (two-pass update before forward) */
+  EA_E_HIP = 7          /* a HIP runtime call or kernel launch failed         */
+} ea_status;
+
+typedef enum { EA_FP32 = 0, EA_BF16 = 1 } ea_dtype;
+
+/* desc.flags */
+#define EA_FORCE_TWO_PASS 0x1u /* use the two-pass scheme even when one pass fits */
+
+/* Largest n handled in one pass (full rows on chip); larger n is two-pass. */
+#define EA_SINGLE_PASS_MAX_N 256
+
+typedef struct {
+  int32_t B;     /* graphs in the batch, >= 1                        */
+  int32_t n;     /* node slots per graph (padded), >= 1              */
+  int32_t d;     /* node feature width, d = H * dh                   */
+  int32_t de;    /* edge feature width                               */
+  int32_t dy;    /* global feature width, >= 1                       */
+  int32_t H;     /* heads                                            */
+  int32_t dh;    /* head width                                       */
+  int32_t dtype; /* ea_dtype                                         */
+  uint32_t flags;
+} ea_desc;
+
+/* Supported shapes: (H, dh, de) in {(4, 16, 16), (8, 32, 64)}; any B, n, dy. */
+
+typedef struct {
+  const void *w_q, *w_k, *w_v;            /* [d, d]                       */
+  const void *b_q, *b_k, *b_v;            /* [d] or NULL (= 0)            */
+  const void *w_emul, *w_eadd;            /* [H, de]  edge FiLM gamma/beta */
+  const void *b_emul, *b_eadd;            /* [H] or NULL                  */
+  const void *w_ymul, *w_yadd;            /* [H, dy]  global FiLM         */
+  const void *b_ymul, *b_yadd;            /* [H] or NULL                  */
+} ea_attn_params;
+
+typedef struct {
+  const void *w_e; /* [de, H] residual edge-update map      */
+  const void *b_e; /* [de] or NULL                          */
+} ea_update_params;
+
+typedef struct ea_ctx ea_ctx; /* opaque, host memory only */
+
+/* Validate desc and create a host-side context (mode, workspace plan). */
+ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out);
+void ea_ctx_destroy(ea_ctx* ctx);
+
+/* Workspace bytes the context needs (Q, K, V^T per head, softmax statistics). */
+size_t ea_workspace_bytes(const ea_ctx* ctx);
+
+/* 1 when the context runs the two-pass scheme, else 0 (-1 for NULL). */
+int ea_is_two_pass(const ea_ctx* ctx);
+
+/*
+ * Attention forward: node output O [B, n, d] and, in single-pass mode, the
+ * attention map A [B, H, n, n] (j contiguous). In two-pass mode A must be
+ * NULL; the softmax statistics stay in the workspace for edge_update.
+ * X [B, n, d], E [B, n, n, de], y [B, dy], node_mask [B, n] uint8 (nonzero =
+ * real node; any pattern is allowed).
+ */
+ea_status edge_attn_forward(ea_ctx* ctx, const ea_attn_params* p,
+                            const void* X, const void* E, const void* y,
+                            const uint8_t* node_mask, void* O, void* A,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Residual edge update E_out = E + W_e A + b_e on real pairs (+0.0 elsewhere),
+ * E_out [B, n, n, de] (may alias E). Single-pass: A is the map written by
+ * edge_attn_forward (required; p may be NULL). Two-pass: A is ignored and
+ * recomputed from E, p and the statistics a previous edge_attn_forward on
+ * this context left in ws (same ws, same stream, inputs unchanged);
+ * otherwise EA_E_STATE.
+ */
+ea_status edge_update(ea_ctx* ctx, const ea_attn_params* p, const ea_update_params* u,
+                      const void* E, const void* y, const uint8_t* node_mask,
+                      const void* A, void* E_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole layer in one call: the same outputs as edge_attn_forward followed
+ * by edge_update. Single-pass mode runs attention and the edge update in one
+ * fused kernel; two-pass mode runs both passes. A as in edge_attn_forward.
+ * E_out may alias E.
+ */
+ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_params* u,
+                          const void* X, const void* E, const void* y,
+                          const uint8_t* node_mask, void* O, void* A, void* E_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+const char* ea_status_str(ea_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* ea_last_error(void);
+
+/*
+ * Stage export for parity tests: the masked logits u [B, H, n, n] (float32,
+ * -inf at masked pairs), computed by the same score stage as the layer.
+ */
+ea_status ea_debug_logits(ea_ctx* ctx, const ea_attn_params* p,
+                          const void* X, const void* E, const void* y,
+                          const uint8_t* node_mask, float* U,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing with HIP events recorded on the launch stream around every
+ * kernel the context launches while enabled. ea_profile_begin starts a
+ * window (at most 4096 launches are recorded); ea_profile_end waits for the
+ * last event and returns, per kernel id, the summed milliseconds and the
+ * launch count (arrays of EA_NUM_KERNELS entries).
+ */
+enum { EA_K_QKV = 0, EA_K_ATTN = 1, EA_K_UPDATE = 2, EA_K_FUSED = 3, EA_NUM_KERNELS = 4 };
+ea_status ea_profile_begin(ea_ctx* ctx);
+ea_status ea_profile_end(ea_ctx* ctx, double* total_ms, int64_t* launches);
+const char* ea_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EDGE_ATTN_H */

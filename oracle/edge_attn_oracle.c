@@ -44,6 +44,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 typedef struct {
   int32_t B, n, d, de, dy, H, dh;
@@ -266,4 +269,13 @@ void eao_vi_product(const eao_dims* dm, const double* A_row /*[H][n]*/, const do
       out[(size_t)h * w + col] = acc;
     }
   }
+}
+
+/* Threads the row loop uses (1 without OpenMP). */
+int eao_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

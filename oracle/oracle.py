@@ -67,6 +67,8 @@ def _load():
         lib.eao_project.argtypes = [ctypes.POINTER(_Dims), _f32p, _u8p, _f32p, _f32p, _f64p]
         lib.eao_vi_product.restype = None
         lib.eao_vi_product.argtypes = [ctypes.POINTER(_Dims), _f64p, _f64p, _f64p]
+        lib.eao_num_threads.restype = ctypes.c_int
+        lib.eao_num_threads.argtypes = []
         lib.eao_bf16_round.restype = ctypes.c_double
         lib.eao_bf16_round.argtypes = [ctypes.c_double]
         _lib = lib
@@ -175,3 +177,8 @@ def vi_product(A_row: np.ndarray, V: np.ndarray, dh: int) -> np.ndarray:
 def bf16_round(x: float) -> float:
     """The oracle's own round-to-nearest-even bfloat16 routine."""
     return float(_load().eao_bf16_round(float(x)))
+
+
+def num_threads() -> int:
+    """Threads the oracle's row loop runs on."""
+    return int(_load().eao_num_threads())

@@ -1,0 +1,168 @@
+"""C-ABI boundary on the CPU: the library loads, exports what include/edge_attn.h
+declares, and rejects bad arguments before anything is enqueued.
+
+No call here reaches a kernel launch: every call is built to fail validation,
+so fake (never dereferenced) pointer values are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from edge_aware_graph_amd import layer as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "edge_attn.h")
+
+FAKE = 0x10000  # 64 KiB: 256-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ea_\w+|edge_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def make_desc(B=2, n=12, d=64, de=16, dy=16, H=4, dh=16, dtype=L.EA_FP32, flags=0):
+    return L.Desc(B, n, d, de, dy, H, dh, dtype, flags)
+
+
+def create(lib, desc):
+    ctx = ctypes.c_void_p()
+    st = lib.ea_ctx_create(ctypes.byref(desc), ctypes.byref(ctx))
+    return st, ctx
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), L.EA_E_SHAPE), (dict(n=0), L.EA_E_SHAPE), (dict(dy=0), L.EA_E_SHAPE),
+    (dict(d=60), L.EA_E_SHAPE), (dict(B=70000), L.EA_E_SHAPE),
+    (dict(dtype=7), L.EA_E_UNSUPPORTED), (dict(flags=0x10), L.EA_E_UNSUPPORTED),
+    (dict(H=2, dh=32), L.EA_E_UNSUPPORTED), (dict(de=32), L.EA_E_UNSUPPORTED),
+    (dict(), L.EA_OK), (dict(d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_BF16), L.EA_OK),
+])
+def test_ctx_create_validation(lib, kw, status):
+    st, ctx = create(lib, make_desc(**kw))
+    assert st == status, lib.ea_last_error()
+    if st == L.EA_OK:
+        assert ctx.value
+        lib.ea_ctx_destroy(ctx)
+    else:
+        assert not ctx.value and lib.ea_last_error()
+
+
+def test_null_desc(lib):
+    ctx = ctypes.c_void_p()
+    assert lib.ea_ctx_create(None, ctypes.byref(ctx)) == L.EA_E_NULLPTR
+
+
+def test_mode_and_workspace_plan(lib):
+    for n, flags, two in ((256, 0, 0), (257, 0, 1), (12, L.EA_FORCE_TWO_PASS, 1), (1024, 0, 1)):
+        st, ctx = create(lib, make_desc(B=3, n=n, d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_BF16, flags=flags))
+        assert st == L.EA_OK
+        assert lib.ea_is_two_pass(ctx) == two
+        NP = (n + 15) // 16 * 16
+        qkv = -(-3 * 8 * NP * 32 * 2 // 256) * 256
+        lse = -(-3 * 8 * NP * 4 // 256) * 256
+        assert lib.ea_workspace_bytes(ctx) == 3 * qkv + lse
+        lib.ea_ctx_destroy(ctx)
+    assert lib.ea_is_two_pass(None) == -1
+    assert lib.ea_workspace_bytes(None) == 0
+
+
+def attn_params(**over):
+    vals = {k: FAKE for k in L.ATTN_PARAM_NAMES if k.startswith("w_")}
+    vals.update(over)
+    return L.AttnParams(*[vals.get(k) for k in L.ATTN_PARAM_NAMES])
+
+
+def fwd(lib, ctx, p=None, X=FAKE, E=FAKE, y=FAKE, mask=FAKE, O=FAKE, A=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    p = attn_params() if p is None else p
+    return lib.edge_attn_forward(ctx, ctypes.byref(p), X, E, y, mask, O, A, ws, ws_bytes, None)
+
+
+@pytest.fixture
+def ctx1(lib):
+    st, ctx = create(lib, make_desc())
+    assert st == L.EA_OK
+    yield ctx
+    lib.ea_ctx_destroy(ctx)
+
+
+@pytest.fixture
+def ctx2(lib):
+    st, ctx = create(lib, make_desc(n=300))
+    assert st == L.EA_OK and lib.ea_is_two_pass(ctx) == 1
+    yield ctx
+    lib.ea_ctx_destroy(ctx)
+
+
+def test_forward_argument_errors(lib, ctx1):
+    assert fwd(lib, None) == L.EA_E_NULLPTR
+    assert fwd(lib, ctx1, X=None) == L.EA_E_NULLPTR
+    assert b"X" in lib.ea_last_error()
+    assert fwd(lib, ctx1, E=MISALIGNED) == L.EA_E_ALIGN
+    assert fwd(lib, ctx1, O=None) == L.EA_E_NULLPTR
+    assert fwd(lib, ctx1, A=None) == L.EA_E_NULLPTR
+    assert fwd(lib, ctx1, mask=None) == L.EA_E_NULLPTR
+    assert fwd(lib, ctx1, p=attn_params(w_q=None)) == L.EA_E_NULLPTR
+    assert fwd(lib, ctx1, p=attn_params(w_emul=MISALIGNED)) == L.EA_E_ALIGN
+    assert fwd(lib, ctx1, ws=None) == L.EA_E_WORKSPACE
+    assert fwd(lib, ctx1, ws=FAKE + 16) == L.EA_E_ALIGN
+    assert fwd(lib, ctx1, ws_bytes=lib.ea_workspace_bytes(ctx1) - 1) == L.EA_E_WORKSPACE
+    assert lib.edge_attn_forward(ctx1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == L.EA_E_NULLPTR
+
+
+def test_two_pass_rules(lib, ctx2):
+    # two-pass forward produces no A
+    assert fwd(lib, ctx2) == L.EA_E_UNSUPPORTED
+    # update before any forward on this context
+    p = attn_params()
+    u = L.UpdateParams(FAKE, None)
+    st = lib.edge_update(ctx2, ctypes.byref(p), ctypes.byref(u), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None)
+    assert st == L.EA_E_STATE
+    assert b"edge_attn_forward" in lib.ea_last_error()
+
+
+def test_update_and_layer_argument_errors(lib, ctx1):
+    p = attn_params()
+    u = L.UpdateParams(FAKE, None)
+    upd = lambda **k: lib.edge_update(ctx1, ctypes.byref(p), k.get("u", ctypes.byref(u)), k.get("E", FAKE), FAKE, k.get("mask", FAKE),
+                                      k.get("A", FAKE), k.get("Eo", FAKE), FAKE, 1 << 40, None)
+    assert upd(u=None) == L.EA_E_NULLPTR
+    assert upd(A=None) == L.EA_E_NULLPTR
+    assert upd(Eo=MISALIGNED) == L.EA_E_ALIGN
+    assert upd(mask=None) == L.EA_E_NULLPTR
+    bad_u = L.UpdateParams(None, None)
+    assert upd(u=ctypes.byref(bad_u)) == L.EA_E_NULLPTR
+    layer = lambda **k: lib.edge_attn_layer(ctx1, ctypes.byref(p), k.get("u", ctypes.byref(u)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, k.get("Eo", FAKE), FAKE, k.get("wsb", 1 << 40), None)
+    assert layer(u=None) == L.EA_E_NULLPTR
+    assert layer(Eo=None) == L.EA_E_NULLPTR
+    assert layer(wsb=0) == L.EA_E_WORKSPACE
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.ea_status_str(s)
+    assert lib.ea_status_str(99) == b"unknown status"
+    assert lib.ea_kernel_name(0) == b"qkv_kernel"
+
+
+def test_binding_raises_on_bad_shape():
+    with pytest.raises(L.EaError) as e:
+        L.EdgeAttention(1, 4, 64, 16, 16, 4, 8, "fp32")
+    assert e.value.status == L.EA_E_SHAPE
