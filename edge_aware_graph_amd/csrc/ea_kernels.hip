@@ -160,69 +160,197 @@ __device__ __forceinline__ float wave_sum_lg(float v) {
   return v + __shfl_xor(v, 32);
 }
 
+
+// Lane-group block transpose in registers. Lane group p (lanes 16p..16p+15)
+// holds in R[x] the block (p, x); afterwards it holds in R[x] the block
+// (x, p). Two rounds of swaps: v_permlane32_swap exchanges lane groups
+// {0,1} <-> {2,3} (bit 1 of the group), v_permlane16_swap exchanges 0 <-> 1
+// and 2 <-> 3 (bit 0). NE is the number of 32-bit elements per block.
+template <int NE>
+__device__ __forceinline__ void lane_group_transpose(float (&R)[4][NE]) {
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    float s[2][2];  // s[x0][bit1 of the source block's second coordinate]
+#pragma unroll
+    for (int x0 = 0; x0 < 2; ++x0) {
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(R[x0][e]), __float_as_uint(R[x0 ^ 2][e]),
+                                                      false, false);
+      s[x0][0] = __uint_as_float(p[0]);
+      s[x0][1] = __uint_as_float(p[1]);
+    }
+#pragma unroll
+    for (int b1 = 0; b1 < 2; ++b1) {
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[0][b1]), __float_as_uint(s[1][b1]),
+                                                      false, false);
+      R[2 * b1][e] = __uint_as_float(p[0]);
+      R[2 * b1 + 1][e] = __uint_as_float(p[1]);
+    }
+  }
+}
+
+// Global FiLM coefficients of graph b into gy_s[0..2H): gamma_y = 1 + ..., then
+// beta_y. All threads of the block take part (16 lanes per coefficient);
+// the caller synchronizes before reading gy_s.
+template <typename T, int H>
+__device__ __forceinline__ void global_film(const LayerArgs& a, int b, float* gy_s) {
+  const int o = threadIdx.x >> 4, part = threadIdx.x & 15;
+  float acc = 0.f;
+  if (o < 2 * H) {
+    const int h = o % H;
+    const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)h * a.dy;
+    const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
+    for (int c = part; c < a.dy; c += 16) acc += Num<T>::ld(yb + c) * Num<T>::ld(Wy + c);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 8);
+  if (o < 2 * H && part == 0) {
+    const float bias = ld_or0<T>(o < H ? a.b_ymul : a.b_yadd, o % H);
+    gy_s[o] = o < H ? 1.f + (bias + acc) : bias + acc;
+  }
+}
+
 // ------------------------------------------------------------------ QKV
 
 // Q | K | V = X W^T + b for rows (b, i) of the padded batch; rows of padded
 // nodes and the slots i in [n, NP) are written as zeros. Q, K: [B, H, NP, DH];
-// V transposed: [B, H, DH, NP]. Grid: (ceil(B*NP/64), 3*D/64), 4 waves of 16 rows.
+// V transposed: [B, H, DH, NP]. One block computes a 64-row x 64-feature tile:
+// X and W chunks are staged in LDS with coalesced 16-byte loads, each wave
+// computes 32 x 32 with MFMA, and the tile leaves through LDS so that every
+// global store writes 16 contiguous bytes.
 template <typename T, int D, int DH>
 __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   constexpr int H = D / DH;
-  constexpr int Qk = D / 4;                    // contraction quarter per lane group
-  constexpr int CQ = sizeof(T) == 2 ? 8 : 4;   // elements per 16-byte step
+  constexpr int KC = D < 128 ? D : 128;          // contraction chunk staged in LDS
+  constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+  constexpr int CPR = KC / EPC;                  // chunks per staged row
+  constexpr int PITCH = KC + 16 / (int)sizeof(T);  // padded LDS row pitch (elements)
+  constexpr int OPITCH = 64 + 4;                 // output tile pitch (floats)
+  static_assert(2 * 64 * PITCH * (int)sizeof(T) >= 64 * OPITCH * 4, "output tile fits");
+  __shared__ __align__(16) T lds[2 * 64 * PITCH];
+  T* xs = lds;
+  T* wsm = lds + 64 * PITCH;
+
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int NP = a.NP, n = a.n;
   const long rows = (long)a.B * NP;
-  const long m0 = (long)blockIdx.x * 64 + w * 16;
+  const long m0 = (long)blockIdx.x * 64;
   const int f0 = blockIdx.y * 64;
   const int which = f0 / D, fl0 = f0 % D;
   const T* W = static_cast<const T*>(which == 0 ? a.w_q : which == 1 ? a.w_k : a.w_v);
   const void* bias = which == 0 ? a.b_q : which == 1 ? a.b_k : a.b_v;
+  const int wm = w & 1, wn = w >> 1;  // this wave's 32 x 32 quadrant
 
-  const long m = m0 + li;
-  bool valid = false;
-  const T* xrow = static_cast<const T*>(a.X);
-  if (m < rows) {
-    const int b = (int)(m / NP), i = (int)(m % NP);
-    if (i < n && a.mask[(size_t)b * n + i]) {
-      valid = true;
-      xrow += ((size_t)b * n + i) * D;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kc = 0; kc < D; kc += KC) {
+    for (int idx = tid; idx < 64 * CPR; idx += kThreads) {
+      const int row = idx / CPR, ch = idx % CPR;
+      const long m = m0 + row;
+      u32x4 xv = {0u, 0u, 0u, 0u};
+      if (m < rows) {
+        const int b = (int)(m / NP), i = (int)(m % NP);
+        if (i < n && a.mask[(size_t)b * n + i])
+          xv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.X) + ((size_t)b * n + i) * D + kc + ch * EPC);
+      }
+      *reinterpret_cast<u32x4*>(xs + row * PITCH + ch * EPC) = xv;
+      *reinterpret_cast<u32x4*>(wsm + row * PITCH + ch * EPC) =
+          *reinterpret_cast<const u32x4*>(W + (size_t)(fl0 + row) * D + kc + ch * EPC);
     }
-  }
-  f32x4 acc[4];
+    __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KC / (4 * EPC); ++ks) {
+      // lane group lg takes elements [ks*4*EPC + lg*EPC, +EPC) of the chunk
+      Frag<T, EPC> af[2], bfr[2];
 #pragma unroll
-  for (int s = 0; s < Qk / CQ; ++s) {
-    Frag<T, CQ> xa;
-    if (valid) xa.load(xrow + lg * Qk + s * CQ); else xa.zero();
+      for (int t = 0; t < 2; ++t) {
+        af[t].load(xs + (wm * 32 + t * 16 + li) * PITCH + ks * 4 * EPC + lg * EPC);
+        bfr[t].load(wsm + (wn * 32 + t * 16 + li) * PITCH + ks * 4 * EPC + lg * EPC);
+      }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      Frag<T, CQ> wb;
-      wb.load(W + (size_t)(fl0 + nt * 16 + li) * D + lg * Qk + s * CQ);
-      acc[nt] = mma(acc[nt], xa, wb);
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma(acc[mt][nt], af[mt], bfr[nt]);
     }
+    __syncthreads();
   }
+
+  // epilogue: bias, padding rows to zero, tile through LDS as floats
+  float* os = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int fl = fl0 + nt * 16 + li, h = fl / DH, t = fl % DH;
-    const float bv = ld_or0<T>(bias, fl);
+  for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const long mr = m0 + 4 * lg + r;
-      if (mr >= rows) continue;
-      const int b = (int)(mr / NP), i = (int)(mr % NP);
-      const bool ok = i < n && a.mask[(size_t)b * n + i];
-      const float v = ok ? acc[nt][r] + bv : 0.f;
-      if (which == 2)
-        Num<T>::st(static_cast<T*>(a.Vt) + (((size_t)b * H + h) * DH + t) * NP + i, v);
-      else
-        Num<T>::st(static_cast<T*>(which == 0 ? a.Qw : a.Kw) + (((size_t)b * H + h) * NP + i) * DH + t, v);
+      const int row = wm * 32 + mt * 16 + 4 * lg + r;
+      const long m = m0 + row;
+      bool ok = false;
+      if (m < rows) {
+        const int b = (int)(m / NP), i = (int)(m % NP);
+        ok = i < n && a.mask[(size_t)b * n + i];
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int col = wn * 32 + nt * 16 + li;
+        os[row * OPITCH + col] = ok ? acc[mt][nt][r] + ld_or0<T>(bias, fl0 + col) : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // 8 consecutive elements per thread and store
+  for (int idx = tid; idx < 64 * 8; idx += kThreads) {
+    if (which < 2) {
+      const int row = idx >> 3, c8 = (idx & 7) * 8;  // 8 features of one row
+      const long m = m0 + row;
+      if (m >= rows) continue;
+      const int b = (int)(m / NP), i = (int)(m % NP);
+      const int f = fl0 + c8, h = f / DH, t = f % DH;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = os[row * OPITCH + c8 + k];
+      Frag<T, 8> o;
+      o.set(v);
+      o.store(static_cast<T*>(which == 0 ? a.Qw : a.Kw) + (((size_t)b * H + h) * NP + i) * DH + t);
+    } else {
+      const int col = idx >> 3, r8 = (idx & 7) * 8;  // 8 consecutive rows of one feature
+      const long m = m0 + r8;
+      if (m >= rows) continue;
+      const int b = (int)(m / NP), i = (int)(m % NP);
+      const int f = fl0 + col, h = f / DH, t = f % DH;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = os[(r8 + k) * OPITCH + col];
+      Frag<T, 8> o;
+      o.set(v);
+      o.store(static_cast<T*>(a.Vt) + (((size_t)b * H + h) * DH + t) * NP + i);
     }
   }
 }
 
 // ------------------------------------------------------------------ score stage
+
+// E fragments of one 16 x 16 (query, key) tile: lane (li, lg) holds channels
+// [lg*DE/4, (lg+1)*DE/4) of edge (i0 + li, j0 + jj) for jj = 0..15. Masked
+// pairs are not read (zeros).
+template <typename T, int DE>
+struct ETile {
+  Frag<T, DE / 4> f[16];
+  __device__ __forceinline__ void load(const T* E, int b, int n, int i, bool mi, const uint8_t* mask_b, int j0,
+                                       int lg) {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = j0 + jj;
+      if (mi && j < n && mask_b[j])
+        f[jj].load(E + (((size_t)b * n + i) * n + j) * DE + lg * (DE / 4));
+      else
+        f[jj].zero();
+    }
+  }
+};
 
 // Per-lane state of one (graph b, 16-query block) for the score stage.
 template <typename T, int H, int DH, int DE>
@@ -238,9 +366,9 @@ struct Scorer {
   float bmul[H], badd[H];
   float gy[2 * H];     // gamma_y (1 + ...) then beta_y, for graph b
 
-  // Must be called by every thread of the block (contains a barrier).
-  __device__ __forceinline__ void init(const LayerArgs& a, int b_, int i0, float* gy_s) {
-    const int tid = threadIdx.x, l = tid & 63;
+  // Per-lane constants; no memory beyond registers. Call before any load.
+  __device__ __forceinline__ void setup(const LayerArgs& a, int b_, int i0) {
+    const int l = threadIdx.x & 63;
     li = l & 15; lg = l >> 4;
     b = b_; n = a.n; NP = a.NP; JT = a.NP / 16; i = i0 + li;
     mask_b = a.mask + (size_t)b * n;
@@ -248,16 +376,10 @@ struct Scorer {
     E = static_cast<const T*>(a.E);
     Kw = static_cast<const T*>(a.Kw);
     scale = a.scale;
-    // global FiLM of graph b: one thread per coefficient
-    if (tid < 2 * H) {
-      const int o = tid, h = o % H;
-      const bool mul = o < H;
-      const T* Wy = static_cast<const T*>(mul ? a.w_ymul : a.w_yadd) + (size_t)h * a.dy;
-      const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
-      float acc = ld_or0<T>(mul ? a.b_ymul : a.b_yadd, h);
-      for (int c = 0; c < a.dy; ++c) acc += Num<T>::ld(yb + c) * Num<T>::ld(Wy + c);
-      gy_s[o] = mul ? 1.f + acc : acc;
-    }
+  }
+  // Weights, queries and the global FiLM (every thread of the block; one barrier).
+  __device__ __forceinline__ void init(const LayerArgs& a, float* gy_s) {
+    global_film<T, H>(a, b, gy_s);
     const T* Qw = static_cast<const T*>(a.Qw);
 #pragma unroll
     for (int h = 0; h < H; ++h) qf[h].load(Qw + (((size_t)b * H + h) * NP + i) * DH + lg * (DH / 4));
@@ -277,36 +399,21 @@ struct Scorer {
     for (int o = 0; o < 2 * H; ++o) gy[o] = gy_s[o];
   }
 
-  // Masked logits u[h][r] of query i for key j = 16*jt + 4*lg + r. Every
-  // thread of the block must call this the same number of times (barriers);
-  // a tile jt >= JT yields -inf. fs: this wave's 16*16*16-float scratch.
-  __device__ __forceinline__ void logits(int jt, float (&u)[H][4], float* fs) const {
+  // Masked logits u[h][r] of query i for key j = 16*jt + 4*lg + r from the
+  // tile's E fragments; a tile jt >= JT yields -inf. No LDS, no barrier.
+  __device__ __forceinline__ void logits(int jt, const ETile<T, DE>& et, float (&u)[H][4]) const {
     const int j0 = 16 * jt;
     const bool tile = jt < JT;
-    // edge FiLM for the 16 keys of the tile; MFMA column = query row
+    // edge FiLM: MFMA column = query row, rows = (gamma, beta) x head
+    float R[4][16];  // R[x][4*r' + r]: key 4*x + r', film row 4*lg + r
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const int j = j0 + jj;
-      Frag<T, DE / 4> ef;
-      if (mi && j < n && mask_b[j])
-        ef.load(E + (((size_t)b * n + i) * n + j) * DE + lg * (DE / 4));
-      else
-        ef.zero();
-      const f32x4 F = mma(f32x4{0.f, 0.f, 0.f, 0.f}, wf, ef);
-      *reinterpret_cast<f32x4*>(fs + (jj * 16 + li) * 16 + 4 * lg) = F;
-    }
-    __syncthreads();
-    float gam[H][4], bet[H][4];
+      const f32x4 F = mma(f32x4{0.f, 0.f, 0.f, 0.f}, wf, et.f[jj]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float* src = fs + ((4 * lg + r) * 16 + li) * 16;
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        gam[h][r] = 1.f + (src[h] + bmul[h]);
-        bet[h][r] = src[H + h] + badd[h];
-      }
+      for (int r = 0; r < 4; ++r) R[jj >> 2][4 * (jj & 3) + r] = F[r];
     }
-    __syncthreads();
+    // now R[x][4*r' + r]: key 4*lg + r', film row 4*x + r
+    lane_group_transpose<16>(R);
     bool real[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -321,7 +428,9 @@ struct Scorer {
       const f32x4 s = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kf, qf[h]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = ((s[r] * scale) * gam[h][r] + bet[h][r]) * gy[h] + gy[H + h];
+        const float gam = 1.f + (R[h >> 2][4 * r + (h & 3)] + bmul[h]);
+        const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)] + badd[h];
+        const float v = ((s[r] * scale) * gam + bet) * gy[h] + gy[H + h];
         u[h][r] = real[r] ? v : kNegInf;
       }
     }
@@ -330,9 +439,11 @@ struct Scorer {
 
 // ------------------------------------------------------------------ edge update
 
-// Residual edge update of one 16x16 (query, key) tile from the attention map
-// staged in LDS as [key jj][query li][head]. MFMA per key j and 16-channel
-// chunk: E'^T (channels x queries) = W_e (channels x heads) A^T + E^T + b_e.
+// Residual edge update of one 16 x 16 (query, key) tile. Per key j and
+// 16-channel chunk: E'^T (channels x queries) = W_e (channels x heads) A^T
+// + E^T + b_e, with A given as this lane's values for keys 4*lg + r and all
+// heads; they are regrouped in registers so that lane group lg supplies heads
+// [lg*QH, (lg+1)*QH) for every key.
 template <typename T, int H, int DE>
 struct Updater {
   static constexpr int QH = sizeof(T) == 2 ? 4 : H / 4;  // heads per lane group
@@ -355,19 +466,39 @@ struct Updater {
     for (int k = 0; k < DE / 4; ++k) be[k] = ld_or0<T>(a.b_e, lg * (DE / 4) + k);
   }
 
-  __device__ __forceinline__ void tile(const T* E, T* Eout, int b, int n, int i, bool mi,
-                                       const uint8_t* mask_b, int j0, int li, int lg,
-                                       const T* stage) const {
-#pragma unroll 4
+  // KEEP: et holds the tile's E fragments; otherwise E is read here.
+  template <bool KEEP>
+  __device__ __forceinline__ void tile(const ETile<T, DE>& et, const T* E, T* Eout, int b, int n, int i,
+                                       bool mi, const uint8_t* mask_b, int j0, int lg,
+                                       const float (&A)[H][4]) const {
+    float R[4][4 * QH];  // R[x][r'*QH + q]: key 4*lg + r', head x*QH + q
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int rp = 0; rp < 4; ++rp)
+#pragma unroll
+        for (int q = 0; q < QH; ++q) {
+          const int h = x * QH + q;
+          R[x][rp * QH + q] = h < H ? A[h][rp] : 0.f;
+        }
+    // now R[x][r'*QH + q]: key 4*x + r', head lg*QH + q
+    lane_group_transpose<4 * QH>(R);
+#pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       const int j = j0 + jj;
       const bool inb = i < n && j < n;
       const bool real = mi && j < n && mask_b[j];
       Frag<T, QH> af;
-      if (has_heads) af.load(stage + (jj * 16 + li) * H + lg * QH); else af.zero();
+      af.set(&R[jj >> 2][(jj & 3) * QH]);
       const size_t off = (((size_t)b * n + i) * n + j) * DE + lg * (DE / 4);
       Frag<T, DE / 4> ef;
-      if (real) ef.load(E + off); else ef.zero();
+      if constexpr (KEEP) {
+        ef = et.f[jj];
+      } else if (real) {
+        ef.load(E + off);
+      } else {
+        ef.zero();
+      }
       float out[DE / 4];
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
@@ -386,64 +517,159 @@ struct Updater {
   }
 };
 
-// Stage this lane's A values (keys 4*lg + r, all heads) as [key][query][head].
-template <typename T, int H>
-__device__ __forceinline__ void stage_A(T* sw, const float (&A)[H][4], int li, int lg) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float hv[H];
-#pragma unroll
-    for (int h = 0; h < H; ++h) hv[h] = A[h][r];
-    Frag<T, H> f;
-    f.set(hv);
-    f.store(sw + ((4 * lg + r) * 16 + li) * H);
-  }
-}
-
 // Cross-wave reduction of the per-wave O^T partials and the store of O rows.
 template <typename T, int H, int DH>
 __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, const f32x4 (&oacc)[H][DH / 16],
                                                int b, int i0, int w, int li, int lg) {
   constexpr int D = H * DH;
-  __syncthreads();
+  constexpr int P = 17;  // padded pitch of a 16-query row
 #pragma unroll
   for (int h = 0; h < H; ++h)
 #pragma unroll
     for (int tc = 0; tc < DH / 16; ++tc)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) os[((w * D) + h * DH + tc * 16 + 4 * lg + r) * 16 + li] = oacc[h][tc][r];
+      for (int r = 0; r < 4; ++r) os[((w * D) + h * DH + tc * 16 + 4 * lg + r) * P + li] = oacc[h][tc][r];
   __syncthreads();
   const uint8_t* mask_b = a.mask + (size_t)b * a.n;
-  for (int idx = threadIdx.x; idx < 16 * D; idx += kThreads) {
-    const int il = idx / D, c = idx % D, ii = i0 + il;
+  for (int idx = threadIdx.x; idx < 16 * D / 4; idx += kThreads) {
+    const int il = idx / (D / 4), c = (idx % (D / 4)) * 4, ii = i0 + il;
     if (ii >= a.n) continue;
-    float v = 0.f;
+    float v[4];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) v += os[(ww * D + c) * 16 + il];
-    if (!mask_b[ii]) v = 0.f;
-    Num<T>::st(static_cast<T*>(a.O) + ((size_t)b * a.n + ii) * D + c, v);
+    for (int k = 0; k < 4; ++k) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) s += os[(ww * D + c + k) * P + il];
+      v[k] = mask_b[ii] ? s : 0.f;
+    }
+    Frag<T, 4> o;
+    o.set(v);
+    o.store(static_cast<T*>(a.O) + ((size_t)b * a.n + ii) * D + c);
   }
 }
 
 // ------------------------------------------------------------------ attention
 
+// Single-pass tail shared by kSingle and kFused: masked softmax over the full
+// row (lane groups by DPP-free shuffles, waves through LDS), A rounded to the
+// storage type and stored, O^T += V^T A^T on MFMA, the residual edge update
+// (kFused) and the cross-wave O reduction. et: the tile's E fragments when
+// they were kept in registers, else nullptr (E is read again).
+template <typename T, int H, int DH, int DE, int MAXT, int MODE, bool KEEP_E>
+__device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H, DH, DE>& sc,
+                                          float (&u)[MAXT][H][4], f32x4 (&oacc)[H][DH / 16], float* os_s,
+                                          float (&red_s)[2][kWaves][H][16], const ETile<T, DE>& et) {
+  const int w = threadIdx.x >> 6, li = sc.li, lg = sc.lg;
+  const int b = sc.b, n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, i0 = i - li;
+  const T* Vt = static_cast<const T*>(a.Vt);
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float m = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, u[tt][h][r]);
+    m = wave_max_lg(m);
+    if (lg == 0) red_s[0][w][h][li] = m;
+  }
+  __syncthreads();
+  float inv[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_s[0][ww][h][li]);
+    float s = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = (u[tt][h][r] == kNegInf) ? 0.f : __expf(u[tt][h][r] - M);
+        u[tt][h][r] = p;
+        s += p;
+      }
+    s = wave_sum_lg(s);
+    if (lg == 0) red_s[1][w][h][li] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) L += red_s[1][ww][h][li];
+    inv[h] = (L > 0.f) ? 1.f / L : 0.f;
+  }
+  T* Ag = static_cast<T*>(a.A);
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) {
+    const int jt = w + kWaves * tt, j0 = 16 * jt;
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[tt][h][r] = Num<T>::rnd(u[tt][h][r] * inv[h]);
+    if (jt < JT) {
+      if (i < n) {
+        const int jb = j0 + 4 * lg;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          T* row = Ag + (((size_t)b * H + h) * n + i) * n;
+          if ((n & 3) == 0 && jb + 3 < n) {
+            Frag<T, 4> f;
+            f.set(u[tt][h]);
+            f.store(row + jb);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (jb + r < n) Num<T>::st(row + jb + r, u[tt][h][r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        Frag<T, 4> af;
+        af.set(u[tt][h]);
+#pragma unroll
+        for (int tc = 0; tc < DH / 16; ++tc) {
+          Frag<T, 4> vf;
+          vf.load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + j0 + 4 * lg);
+          oacc[h][tc] = mma(oacc[h][tc], vf, af);
+        }
+      }
+    }
+  }
+  if constexpr (MODE == kFused) {
+    Updater<T, H, DE> up;
+    up.init(a, li, lg);
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt) {
+      const int jt = w + kWaves * tt;
+      if (jt < JT)
+        up.template tile<KEEP_E>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, sc.mask_b, 16 * jt, lg,
+                                 u[tt]);
+    }
+  }
+  reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg);
+}
+
+
 // One block per (graph b = blockIdx.y, 16-query block blockIdx.x); wave w
 // owns key tiles w, w+4, ... . kSingle/kFused/kLogits keep the MAXT logit
 // tiles of a wave in registers (n <= 64*MAXT); kOnline streams any n.
+// With one tile per wave and bfloat16 data the fused mode keeps the tile's E
+// fragments in registers from the scores to the edge update (E read once).
 template <typename T, int H, int DH, int DE, int MAXT, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
   constexpr int D = H * DH;
+  constexpr bool kKeepE = MODE == kFused && MAXT == 1 && sizeof(T) == 2;
   static_assert(D <= 256 && 2 * H <= 16, "shape");
-  __shared__ __align__(16) float scratch[kWaves * 16 * 16 * 16];  // FiLM transpose, then O reduction
+  __shared__ __align__(16) float os_s[kWaves * D * 17];  // O^T partials of each wave
   __shared__ float red_s[2][kWaves][H][16];
   __shared__ float gy_s[2 * H];
-  __shared__ __align__(16) T stage_s[MODE == kFused ? kWaves * 16 * 16 * H : 8];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, i0 = blockIdx.x * 16;
   Scorer<T, H, DH, DE> sc;
-  sc.init(a, b, i0, gy_s);
-  float* fs = scratch + w * 4096;
+  sc.setup(a, b, i0);
   const int JT = sc.JT, n = a.n, NP = a.NP, i = sc.i;
   const T* Vt = static_cast<const T*>(a.Vt);
 
@@ -454,38 +680,37 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
     for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (MODE == kOnline) {
+    sc.init(a, gy_s);
     float m_run[H], l_run[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
-    const int NT = (JT + kWaves - 1) / kWaves;
-    for (int tt = 0; tt < NT; ++tt) {
-      const int jt = w + kWaves * tt;
+    for (int jt = w; jt < JT; jt += kWaves) {
+      const int j0 = 16 * jt;
+      ETile<T, DE> et;
+      et.load(sc.E, b, n, i, sc.mi, sc.mask_b, j0, lg);
       float u[H][4];
-      sc.logits(jt, u, fs);
-      if (jt < JT) {
-        const int j0 = 16 * jt;
+      sc.logits(jt, et, u);
 #pragma unroll
-        for (int h = 0; h < H; ++h) {
-          const float tm = wave_max_lg(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
-          const float mnew = fmaxf(m_run[h], tm);
-          const float alpha = (mnew == kNegInf) ? 1.f : __expf(m_run[h] - mnew);
-          float p[4], ps = 0.f;
+      for (int h = 0; h < H; ++h) {
+        const float tm = wave_max_lg(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
+        const float mnew = fmaxf(m_run[h], tm);
+        const float alpha = (mnew == kNegInf) ? 1.f : __expf(m_run[h] - mnew);
+        float p[4], ps = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[r] = (u[h][r] == kNegInf) ? 0.f : __expf(u[h][r] - mnew);
-            ps += p[r];
-          }
-          l_run[h] = l_run[h] * alpha + ps;
-          m_run[h] = mnew;
-          Frag<T, 4> af;
-          af.set(p);
+        for (int r = 0; r < 4; ++r) {
+          p[r] = (u[h][r] == kNegInf) ? 0.f : __expf(u[h][r] - mnew);
+          ps += p[r];
+        }
+        l_run[h] = l_run[h] * alpha + ps;
+        m_run[h] = mnew;
+        Frag<T, 4> af;
+        af.set(p);
 #pragma unroll
-          for (int tc = 0; tc < DH / 16; ++tc) {
-            Frag<T, 4> vf;
-            vf.load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + j0 + 4 * lg);
-            oacc[h][tc] *= alpha;
-            oacc[h][tc] = mma(oacc[h][tc], vf, af);
-          }
+        for (int tc = 0; tc < DH / 16; ++tc) {
+          Frag<T, 4> vf;
+          vf.load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + j0 + 4 * lg);
+          oacc[h][tc] *= alpha;
+          oacc[h][tc] = mma(oacc[h][tc], vf, af);
         }
       }
     }
@@ -512,113 +737,60 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
       for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] *= f;
       if (w == 0 && lg == 0) a.lse[((size_t)b * H + h) * NP + i] = (L > 0.f) ? M + __logf(L) : kNegInf;
     }
-    reduce_store_O<T, H, DH>(a, scratch, oacc, b, i0, w, li, lg);
+    reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg);
   } else {
     float u[MAXT][H][4];
-#pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) sc.logits(w + kWaves * tt, u[tt], fs);
-
-    if constexpr (MODE == kLogits) {
-      if (i < n) {
-#pragma unroll
-        for (int tt = 0; tt < MAXT; ++tt)
+    if constexpr (MAXT == 1) {
+      // issue the tile's E loads before anything else
+      ETile<T, DE> et;
+      et.load(sc.E, b, n, i, sc.mi, sc.mask_b, 16 * w, lg);
+      sc.init(a, gy_s);
+      sc.logits(w, et, u[0]);
+      if constexpr (kKeepE) {
+        // softmax, A, A V and the edge update below use `et` directly
+        static_assert(MODE == kFused, "");
+      }
+      // fallthrough to the common code with the fragments still live
+      if constexpr (MODE == kLogits) {
+        if (i < n) {
 #pragma unroll
           for (int h = 0; h < H; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int j = 16 * (w + kWaves * tt) + 4 * lg + r;
-              if (j < n) a.U[(((size_t)b * H + h) * n + i) * n + j] = u[tt][h][r];
+              const int j = 16 * w + 4 * lg + r;
+              if (j < n) a.U[(((size_t)b * H + h) * n + i) * n + j] = u[0][h][r];
             }
+        }
+        return;
+      } else {
+        // single-tile fast path continues in attn_rest
+        attn_rest<T, H, DH, DE, 1, MODE, kKeepE>(a, sc, u, oacc, os_s, red_s, et);
       }
-      return;
     } else {
-      // masked softmax over the full row: max, then sum, across lane groups and waves
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        float m = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < MAXT; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) m = fmaxf(m, u[tt][h][r]);
-        m = wave_max_lg(m);
-        if (lg == 0) red_s[0][w][h][li] = m;
-      }
-      __syncthreads();
-      float inv[H];
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        float M = kNegInf;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_s[0][ww][h][li]);
-        float s = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < MAXT; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = (u[tt][h][r] == kNegInf) ? 0.f : __expf(u[tt][h][r] - M);
-            u[tt][h][r] = p;
-            s += p;
-          }
-        s = wave_sum_lg(s);
-        if (lg == 0) red_s[1][w][h][li] = s;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        float L = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) L += red_s[1][ww][h][li];
-        inv[h] = (L > 0.f) ? 1.f / L : 0.f;
-      }
-      // A (rounded to the storage type), its store, and O^T += V^T A^T
-      T* Ag = static_cast<T*>(a.A);
+      sc.init(a, gy_s);
 #pragma unroll
       for (int tt = 0; tt < MAXT; ++tt) {
-        const int jt = w + kWaves * tt, j0 = 16 * jt;
+        ETile<T, DE> et;
+        et.load(sc.E, b, n, i, sc.mi, sc.mask_b, 16 * (w + kWaves * tt), lg);
+        sc.logits(w + kWaves * tt, et, u[tt]);
+      }
+      if constexpr (MODE == kLogits) {
+        if (i < n) {
 #pragma unroll
-        for (int h = 0; h < H; ++h)
+          for (int tt = 0; tt < MAXT; ++tt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) u[tt][h][r] = Num<T>::rnd(u[tt][h][r] * inv[h]);
-        if (jt < JT) {
-          if (i < n) {
-#pragma unroll
-            for (int h = 0; h < H; ++h) {
-              T* row = Ag + (((size_t)b * H + h) * n + i) * n;
+            for (int h = 0; h < H; ++h)
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const int j = j0 + 4 * lg + r;
-                if (j < n) Num<T>::st(row + j, u[tt][h][r]);
+                const int j = 16 * (w + kWaves * tt) + 4 * lg + r;
+                if (j < n) a.U[(((size_t)b * H + h) * n + i) * n + j] = u[tt][h][r];
               }
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < H; ++h) {
-            Frag<T, 4> af;
-            af.set(u[tt][h]);
-#pragma unroll
-            for (int tc = 0; tc < DH / 16; ++tc) {
-              Frag<T, 4> vf;
-              vf.load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + j0 + 4 * lg);
-              oacc[h][tc] = mma(oacc[h][tc], vf, af);
-            }
-          }
         }
+        return;
+      } else {
+        ETile<T, DE> unused;
+        attn_rest<T, H, DH, DE, MAXT, MODE, false>(a, sc, u, oacc, os_s, red_s, unused);
       }
-      if constexpr (MODE == kFused) {
-        Updater<T, H, DE> up;
-        up.init(a, li, lg);
-        T* sw = stage_s + w * 16 * 16 * H;
-#pragma unroll
-        for (int tt = 0; tt < MAXT; ++tt) {
-          const int jt = w + kWaves * tt;
-          stage_A<T, H>(sw, u[tt], li, lg);
-          __syncthreads();
-          if (jt < JT)
-            up.tile(sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, sc.mask_b, 16 * jt, li, lg, sw);
-          __syncthreads();
-        }
-      }
-      reduce_store_O<T, H, DH>(a, scratch, oacc, b, i0, w, li, lg);
     }
   }
 }
@@ -627,24 +799,27 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
 
 // Grid (NP/16 query blocks, B, ceil(NP/64)); wave w of block z takes key tile
 // 4*z + w. kReadA reads A from the forward's output; kRecompute re-runs the
-// score stage and takes A = exp(u - lse) from pass 1's statistics.
+// score stage and takes A = exp(u - lse) from pass 1's statistics. The E
+// fragments of the tile are read once (bfloat16) and serve both stages.
 template <typename T, int H, int DH, int DE, int MODE>
 __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
-  __shared__ __align__(16) float scratch[MODE == kRecompute ? kWaves * 16 * 16 * 16 : 4];
   __shared__ float gy_s[2 * H];
-  __shared__ __align__(16) T stage_s[kWaves * 16 * 16 * H];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, i0 = blockIdx.x * 16, i = i0 + li;
   const int n = a.n, NP = a.NP, JT = NP / 16;
   const int jt = blockIdx.z * kWaves + w, j0 = 16 * jt;
   const uint8_t* mask_b = a.mask + (size_t)b * n;
   const bool mi = i < n && mask_b[i];
+  constexpr bool kKeepE = sizeof(T) == 2;
   float A[H][4];
+  ETile<T, DE> et;
   if constexpr (MODE == kRecompute) {
     Scorer<T, H, DH, DE> sc;
-    sc.init(a, b, i0, gy_s);
+    sc.setup(a, b, i0);
+    et.load(sc.E, b, n, i, mi, mask_b, j0, lg);
+    sc.init(a, gy_s);
     float u[H][4];
-    sc.logits(jt, u, scratch + w * 4096);
+    sc.logits(jt, et, u);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const float L = a.lse[((size_t)b * H + h) * NP + i];
@@ -653,6 +828,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
         A[h][r] = (u[h][r] == kNegInf || L == kNegInf) ? 0.f : Num<T>::rnd(__expf(u[h][r] - L));
     }
   } else {
+    if (kKeepE) et.load(static_cast<const T*>(a.E), b, n, i, mi, mask_b, j0, lg);
     const T* Ag = static_cast<const T*>(a.A);
 #pragma unroll
     for (int h = 0; h < H; ++h)
@@ -664,11 +840,9 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   }
   Updater<T, H, DE> up;
   up.init(a, li, lg);
-  T* sw = stage_s + w * 16 * 16 * H;
-  stage_A<T, H>(sw, A, li, lg);
-  __syncthreads();
   if (jt < JT)
-    up.tile(static_cast<const T*>(a.E), static_cast<T*>(a.E_out), b, n, i, mi, mask_b, j0, li, lg, sw);
+    up.template tile<kKeepE>(et, static_cast<const T*>(a.E), static_cast<T*>(a.E_out), b, n, i, mi, mask_b, j0,
+                             lg, A);
 }
 
 // ------------------------------------------------------------------ dispatch
