@@ -20,7 +20,7 @@ struct ea_ctx {
   int two_pass;
   int forward_done;
   size_t esz;      // element size of desc.dtype
-  size_t off_q, off_k, off_v, off_lse, ws_bytes;
+  size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
   // kernel timing window
   int prof_on;
   std::vector<hipEvent_t> ev_pool;
@@ -101,6 +101,7 @@ ea::LayerArgs make_args(const ea_ctx* c, const ea_attn_params* p, const ea_updat
   a.Kw = base + c->off_k;
   a.Vt = base + c->off_v;
   a.lse = reinterpret_cast<float*>(base + c->off_lse);
+  a.gy = reinterpret_cast<float*>(base + c->off_gy);
   a.B = c->d.B; a.n = c->d.n; a.NP = c->NP; a.dy = c->d.dy;
   a.scale = (float)(1.0 / sqrt((double)c->d.dh));
   return a;
@@ -196,7 +197,8 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->off_k = qkv;
   c->off_v = 2 * qkv;
   c->off_lse = 3 * qkv;
-  c->ws_bytes = 3 * qkv + round256((size_t)d.B * d.H * c->NP * sizeof(float));
+  c->off_gy = c->off_lse + round256((size_t)d.B * d.H * c->NP * sizeof(float));
+  c->ws_bytes = c->off_gy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->prof_on = 0;
   c->ev_used = 0;
   *out = c;

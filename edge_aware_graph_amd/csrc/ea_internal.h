@@ -34,6 +34,7 @@ struct LayerArgs {
   void* Kw;    // [B, H, NP, dh]
   void* Vt;    // [B, H, dh, NP]
   float* lse;  // [B, H, NP]
+  float* gy;   // [B, 2H]: gamma_y (1 + ...) then beta_y per graph
   // outputs
   void* O;
   void* A;       // attention map (kSingle/kFused) or the map to read (kReadA)

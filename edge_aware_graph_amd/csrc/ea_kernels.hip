@@ -151,15 +151,44 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float, Q>& a, const F
   return acc;
 }
 
-__device__ __forceinline__ float wave_max_lg(float v) {  // max over the 4 lane groups of a column
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// Max / sum over the 4 lane groups of a column (lanes li, li+16, li+32,
+// li+48); every lane receives the same bits. Swapping a register with itself
+// through v_permlane32_swap / v_permlane16_swap yields both halves in each
+// lane, so the combine order is identical in all four lanes.
+__device__ __forceinline__ float lg_max(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
-__device__ __forceinline__ float wave_sum_lg(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ float lg_sum(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Bit jj set when key j0 + jj is a real node, from the mask byte this lane
+// loaded for key j0 + li (identical in all lanes).
+__device__ __forceinline__ uint32_t key_bits(uint32_t mask_byte) {
+  return (uint32_t)(__ballot(mask_byte != 0u) & 0xffffull);
+}
+
+// Logical (16-query block, graph) of this block. Consecutive block ids go to
+// the 8 XCDs in turn; regrouping them keeps all query blocks of a graph on one
+// XCD, whose L2 then serves the graph's K and V to all of them.
+__device__ __forceinline__ void xcd_block(int& ib, int& b) {
+  const int IB = gridDim.x, NB = gridDim.x * gridDim.y;
+  const int L = blockIdx.y * gridDim.x + blockIdx.x;
+  if ((NB & 7) == 0) {
+    const int u = (L & 7) * (NB >> 3) + (L >> 3);
+    ib = u % IB;
+    b = u / IB;
+  } else {
+    ib = blockIdx.x;
+    b = blockIdx.y;
+  }
+}
 
 // Lane-group block transpose in registers. Lane group p (lanes 16p..16p+15)
 // holds in R[x] the block (p, x); afterwards it holds in R[x] the block
@@ -185,29 +214,6 @@ __device__ __forceinline__ void lane_group_transpose(float (&R)[4][NE]) {
       R[2 * b1][e] = __uint_as_float(p[0]);
       R[2 * b1 + 1][e] = __uint_as_float(p[1]);
     }
-  }
-}
-
-// Global FiLM coefficients of graph b into gy_s[0..2H): gamma_y = 1 + ..., then
-// beta_y. All threads of the block take part (16 lanes per coefficient);
-// the caller synchronizes before reading gy_s.
-template <typename T, int H>
-__device__ __forceinline__ void global_film(const LayerArgs& a, int b, float* gy_s) {
-  const int o = threadIdx.x >> 4, part = threadIdx.x & 15;
-  float acc = 0.f;
-  if (o < 2 * H) {
-    const int h = o % H;
-    const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)h * a.dy;
-    const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
-    for (int c = part; c < a.dy; c += 16) acc += Num<T>::ld(yb + c) * Num<T>::ld(Wy + c);
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  acc += __shfl_xor(acc, 8);
-  if (o < 2 * H && part == 0) {
-    const float bias = ld_or0<T>(o < H ? a.b_ymul : a.b_yadd, o % H);
-    gy_s[o] = o < H ? 1.f + (bias + acc) : bias + acc;
   }
 }
 
@@ -241,6 +247,29 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   const T* W = static_cast<const T*>(which == 0 ? a.w_q : which == 1 ? a.w_k : a.w_v);
   const void* bias = which == 0 ? a.b_q : which == 1 ? a.b_k : a.b_v;
   const int wm = w & 1, wn = w >> 1;  // this wave's 32 x 32 quadrant
+
+  if (blockIdx.y == 0) {
+    // global FiLM of the graphs whose slot 0 lies in this row block: 16 lanes
+    // per coefficient (2H <= 16), reduced across the lanes
+    const int o = tid >> 4, part = tid & 15;
+    for (long m = (m0 + NP - 1) / NP * NP; m < m0 + 64 && m < rows; m += NP) {
+      const int b = (int)(m / NP);
+      float acc = 0.f;
+      if (o < 2 * H) {
+        const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)(o % H) * a.dy;
+        const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
+        for (int c = part; c < a.dy; c += 16) acc += Num<T>::ld(yb + c) * Num<T>::ld(Wy + c);
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      acc += __shfl_xor(acc, 8);
+      if (o < 2 * H && part == 0) {
+        const float bias = ld_or0<T>(o < H ? a.b_ymul : a.b_yadd, o % H);
+        a.gy[(size_t)b * 2 * H + o] = o < H ? 1.f + (bias + acc) : bias + acc;
+      }
+    }
+  }
 
   f32x4 acc[2][2];
 #pragma unroll
@@ -334,18 +363,17 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 // ------------------------------------------------------------------ score stage
 
 // E fragments of one 16 x 16 (query, key) tile: lane (li, lg) holds channels
-// [lg*DE/4, (lg+1)*DE/4) of edge (i0 + li, j0 + jj) for jj = 0..15. Masked
-// pairs are not read (zeros).
+// [lg*DE/4, (lg+1)*DE/4) of edge (i0 + li, j0 + jj) for jj = 0..15. Pairs
+// that are not real (query or key masked, or past n) are not read: zeros.
 template <typename T, int DE>
 struct ETile {
   Frag<T, DE / 4> f[16];
-  __device__ __forceinline__ void load(const T* E, int b, int n, int i, bool mi, const uint8_t* mask_b, int j0,
-                                       int lg) {
+  __device__ __forceinline__ void load(const T* E, int b, int n, int i, bool mi, int j0, int lg, uint32_t bits) {
+    const T* row = E + ((size_t)b * n + i) * n * DE + lg * (DE / 4);
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const int j = j0 + jj;
-      if (mi && j < n && mask_b[j])
-        f[jj].load(E + (((size_t)b * n + i) * n + j) * DE + lg * (DE / 4));
+      if (mi && ((bits >> jj) & 1u))
+        f[jj].load(row + (size_t)(j0 + jj) * DE);
       else
         f[jj].zero();
     }
@@ -360,26 +388,31 @@ struct Scorer {
   const uint8_t* mask_b;
   const T* E;
   const T* Kw;
+  const T* Vt;
   float scale;
   Frag<T, DH / 4> qf[H];
   Frag<T, DE / 4> wf;  // edge-FiLM weights, row li: gamma of head li, then beta of head li-H
-  float bmul[H], badd[H];
-  float gy[2 * H];     // gamma_y (1 + ...) then beta_y, for graph b
+  f32x4 fc;            // FiLM accumulator start: 1 + b_emul (gamma rows), b_eadd (beta rows)
+  float gy[2 * H];     // gamma_y then beta_y of graph b
 
-  // Per-lane constants; no memory beyond registers. Call before any load.
+  // Per-lane constants; no loads.
   __device__ __forceinline__ void setup(const LayerArgs& a, int b_, int i0) {
     const int l = threadIdx.x & 63;
     li = l & 15; lg = l >> 4;
     b = b_; n = a.n; NP = a.NP; JT = a.NP / 16; i = i0 + li;
     mask_b = a.mask + (size_t)b * n;
-    mi = i < n && mask_b[i];
     E = static_cast<const T*>(a.E);
     Kw = static_cast<const T*>(a.Kw);
+    Vt = static_cast<const T*>(a.Vt);
     scale = a.scale;
   }
-  // Weights, queries and the global FiLM (every thread of the block; one barrier).
-  __device__ __forceinline__ void init(const LayerArgs& a, float* gy_s) {
-    global_film<T, H>(a, b, gy_s);
+  __device__ __forceinline__ uint32_t query_mask_byte() const { return i < n ? mask_b[i] : 0u; }
+  __device__ __forceinline__ uint32_t key_mask_byte(int jt) const {
+    const int j = 16 * jt + li;
+    return j < n ? mask_b[j] : 0u;
+  }
+  // Queries, FiLM weights and biases, global FiLM coefficients.
+  __device__ __forceinline__ void load_weights(const LayerArgs& a) {
     const T* Qw = static_cast<const T*>(a.Qw);
 #pragma unroll
     for (int h = 0; h < H; ++h) qf[h].load(Qw + (((size_t)b * H + h) * NP + i) * DH + lg * (DH / 4));
@@ -390,48 +423,53 @@ struct Scorer {
     else
       wf.zero();
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      bmul[h] = ld_or0<T>(a.b_emul, h);
-      badd[h] = ld_or0<T>(a.b_eadd, h);
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lg + r;
+      fc[r] = row < H ? 1.f + ld_or0<T>(a.b_emul, row) : row < 2 * H ? ld_or0<T>(a.b_eadd, row - H) : 0.f;
     }
-    __syncthreads();
 #pragma unroll
-    for (int o = 0; o < 2 * H; ++o) gy[o] = gy_s[o];
+    for (int o = 0; o < 2 * H; ++o) gy[o] = a.gy[(size_t)b * 2 * H + o];
+  }
+  __device__ __forceinline__ void load_k(int jt, Frag<T, DH / 4> (&kf)[H]) const {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      if (jt < JT) kf[h].load(Kw + (((size_t)b * H + h) * NP + 16 * jt + li) * DH + lg * (DH / 4));
+      else kf[h].zero();
+    }
+  }
+  __device__ __forceinline__ void load_v(int jt, Frag<T, 4> (&vf)[H][DH / 16]) const {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int tc = 0; tc < DH / 16; ++tc) {
+        if (jt < JT) vf[h][tc].load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + 16 * jt + 4 * lg);
+        else vf[h][tc].zero();
+      }
   }
 
   // Masked logits u[h][r] of query i for key j = 16*jt + 4*lg + r from the
-  // tile's E fragments; a tile jt >= JT yields -inf. No LDS, no barrier.
-  __device__ __forceinline__ void logits(int jt, const ETile<T, DE>& et, float (&u)[H][4]) const {
-    const int j0 = 16 * jt;
-    const bool tile = jt < JT;
+  // tile's E fragments and K fragments; bits: real keys of the tile.
+  __device__ __forceinline__ void logits(const ETile<T, DE>& et, const Frag<T, DH / 4> (&kf)[H], uint32_t bits,
+                                         float (&u)[H][4]) const {
     // edge FiLM: MFMA column = query row, rows = (gamma, beta) x head
     float R[4][16];  // R[x][4*r' + r]: key 4*x + r', film row 4*lg + r
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const f32x4 F = mma(f32x4{0.f, 0.f, 0.f, 0.f}, wf, et.f[jj]);
+      const f32x4 F = mma(fc, wf, et.f[jj]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) R[jj >> 2][4 * (jj & 3) + r] = F[r];
     }
     // now R[x][4*r' + r]: key 4*lg + r', film row 4*x + r
     lane_group_transpose<16>(R);
-    bool real[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j0 + 4 * lg + r;
-      real[r] = mi && j < n && mask_b[j];
-    }
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      Frag<T, DH / 4> kf;
-      if (tile) kf.load(Kw + (((size_t)b * H + h) * NP + j0 + li) * DH + lg * (DH / 4));
-      else kf.zero();
-      const f32x4 s = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kf, qf[h]);
+      const f32x4 s = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kf[h], qf[h]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float gam = 1.f + (R[h >> 2][4 * r + (h & 3)] + bmul[h]);
-        const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)] + badd[h];
+        const float gam = R[h >> 2][4 * r + (h & 3)];
+        const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)];
         const float v = ((s[r] * scale) * gam + bet) * gy[h] + gy[H + h];
-        u[h][r] = real[r] ? v : kNegInf;
+        u[h][r] = (mi && ((bits >> (4 * lg + r)) & 1u)) ? v : kNegInf;
       }
     }
   }
@@ -441,35 +479,49 @@ struct Scorer {
 
 // Residual edge update of one 16 x 16 (query, key) tile. Per key j and
 // 16-channel chunk: E'^T (channels x queries) = W_e (channels x heads) A^T
-// + E^T + b_e, with A given as this lane's values for keys 4*lg + r and all
+// + E^T (+ b_e), with A given as this lane's values for keys 4*lg + r and all
 // heads; they are regrouped in registers so that lane group lg supplies heads
-// [lg*QH, (lg+1)*QH) for every key.
+// [lg*QH, (lg+1)*QH) for every key. In bfloat16 mode the contraction has 16
+// slots for H <= 12 heads; slot H carries 1 against b_e, so the bias costs
+// no VALU work.
 template <typename T, int H, int DE>
 struct Updater {
-  static constexpr int QH = sizeof(T) == 2 ? 4 : H / 4;  // heads per lane group
+  static constexpr bool kBF = sizeof(T) == 2;
+  static constexpr int QH = kBF ? 4 : H / 4;  // heads per lane group
   static constexpr int NCH = DE / 16;
   Frag<T, QH> wef[NCH];
-  float be[DE / 4];
+  float be[kBF ? 1 : DE / 4];
   bool has_heads;
 
   __device__ __forceinline__ void init(const LayerArgs& a, int li, int lg) {
     const T* We = static_cast<const T*>(a.w_e);
-    has_heads = lg * QH < H;
+    has_heads = lg * QH < H || (kBF && lg * QH == H && a.b_e);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       // MFMA row li of chunk ch is channel (li/4)*(DE/4) + 4*ch + li%4, so that
       // output rows 4*lg + r land on this lane group's channel quarter.
       const int c = (li >> 2) * (DE / 4) + 4 * ch + (li & 3);
-      if (has_heads) wef[ch].load(We + (size_t)c * H + lg * QH); else wef[ch].zero();
+      if (lg * QH < H) {
+        wef[ch].load(We + (size_t)c * H + lg * QH);
+      } else if (kBF && lg * QH == H && a.b_e) {
+        float v[QH] = {};
+        v[0] = Num<T>::ld(static_cast<const T*>(a.b_e) + c);
+        wef[ch].set(v);
+      } else {
+        wef[ch].zero();
+      }
     }
+    if constexpr (!kBF) {
 #pragma unroll
-    for (int k = 0; k < DE / 4; ++k) be[k] = ld_or0<T>(a.b_e, lg * (DE / 4) + k);
+      for (int k = 0; k < DE / 4; ++k) be[k] = ld_or0<T>(a.b_e, lg * (DE / 4) + k);
+    }
   }
 
   // KEEP: et holds the tile's E fragments; otherwise E is read here.
+  // bits: real keys of the tile; full: every pair of the tile is real.
   template <bool KEEP>
   __device__ __forceinline__ void tile(const ETile<T, DE>& et, const T* E, T* Eout, int b, int n, int i,
-                                       bool mi, const uint8_t* mask_b, int j0, int lg,
+                                       bool mi, int j0, int lg, uint32_t bits, bool full,
                                        const float (&A)[H][4]) const {
     float R[4][4 * QH];  // R[x][r'*QH + q]: key 4*lg + r', head x*QH + q
 #pragma unroll
@@ -479,40 +531,48 @@ struct Updater {
 #pragma unroll
         for (int q = 0; q < QH; ++q) {
           const int h = x * QH + q;
-          R[x][rp * QH + q] = h < H ? A[h][rp] : 0.f;
+          R[x][rp * QH + q] = h < H ? A[h][rp] : (kBF && h == H) ? 1.f : 0.f;
         }
     // now R[x][r'*QH + q]: key 4*x + r', head lg*QH + q
     lane_group_transpose<4 * QH>(R);
+    const size_t rowoff = ((size_t)b * n + i) * n * DE + lg * (DE / 4);
+    if (full) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int j = j0 + jj;
-      const bool inb = i < n && j < n;
-      const bool real = mi && j < n && mask_b[j];
-      Frag<T, QH> af;
-      af.set(&R[jj >> 2][(jj & 3) * QH]);
-      const size_t off = (((size_t)b * n + i) * n + j) * DE + lg * (DE / 4);
-      Frag<T, DE / 4> ef;
-      if constexpr (KEEP) {
-        ef = et.f[jj];
-      } else if (real) {
-        ef.load(E + off);
-      } else {
-        ef.zero();
-      }
-      float out[DE / 4];
+      for (int jj = 0; jj < 16; ++jj) step<KEEP, true>(et, E, Eout, rowoff + (size_t)(j0 + jj) * DE, true, true, R, jj);
+    } else {
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        f32x4 c = {ef.get(4 * ch) + be[4 * ch], ef.get(4 * ch + 1) + be[4 * ch + 1],
-                   ef.get(4 * ch + 2) + be[4 * ch + 2], ef.get(4 * ch + 3) + be[4 * ch + 3]};
-        c = mma(c, wef[ch], af);
+      for (int jj = 0; jj < 16; ++jj) {
+        const int j = j0 + jj;
+        step<KEEP, false>(et, E, Eout, rowoff + (size_t)j * DE, i < n && j < n, mi && ((bits >> jj) & 1u), R, jj);
+      }
+    }
+  }
+
+  template <bool KEEP, bool FULL>
+  __device__ __forceinline__ void step(const ETile<T, DE>& et, const T* E, T* Eout, size_t off, bool inb,
+                                       bool real, const float (&R)[4][4 * QH], int jj) const {
+    Frag<T, QH> af;
+    if (has_heads) af.set(&R[jj >> 2][(jj & 3) * QH]); else af.zero();
+    Frag<T, DE / 4> ef;
+    if constexpr (KEEP) {
+      ef = et.f[jj];
+    } else {
+      if (real) ef.load(E + off); else ef.zero();
+    }
+    float out[DE / 4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[4 * ch + r] = real ? c[r] : 0.f;
-      }
-      if (inb) {
-        Frag<T, DE / 4> of;
-        of.set(out);
-        of.store(Eout + off);
-      }
+    for (int ch = 0; ch < NCH; ++ch) {
+      f32x4 c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[r] = ef.get(4 * ch + r) + (kBF ? 0.f : be[kBF ? 0 : 4 * ch + r]);
+      c = mma(c, wef[ch], af);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[4 * ch + r] = (FULL || real) ? c[r] : 0.f;
+    }
+    if (FULL || inb) {
+      Frag<T, DE / 4> of;
+      of.set(out);
+      of.store(Eout + off);
     }
   }
 };
@@ -548,20 +608,30 @@ __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, co
   }
 }
 
+// Whether all 16 queries of the block and all 16 keys of the tile are real.
+__device__ __forceinline__ bool tile_full(bool mi, uint32_t bits) {
+  return bits == 0xffffu && (__ballot(mi) & 0xffffull) == 0xffffull;
+}
+
 // ------------------------------------------------------------------ attention
 
 // Single-pass tail shared by kSingle and kFused: masked softmax over the full
-// row (lane groups by DPP-free shuffles, waves through LDS), A rounded to the
+// row (lane groups by register swaps, waves through LDS), A rounded to the
 // storage type and stored, O^T += V^T A^T on MFMA, the residual edge update
-// (kFused) and the cross-wave O reduction. et: the tile's E fragments when
-// they were kept in registers, else nullptr (E is read again).
+// (kFused) and the cross-wave O reduction. With KEEP_E the tile's E fragments
+// were kept in registers (E read once); otherwise the update reads E again.
 template <typename T, int H, int DH, int DE, int MAXT, int MODE, bool KEEP_E>
 __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H, DH, DE>& sc,
-                                          float (&u)[MAXT][H][4], f32x4 (&oacc)[H][DH / 16], float* os_s,
+                                          float (&u)[MAXT][H][4], const uint32_t (&bits)[MAXT],
+                                          const Frag<T, 4> (&vf)[MAXT][H][DH / 16], float* os_s,
                                           float (&red_s)[2][kWaves][H][16], const ETile<T, DE>& et) {
   const int w = threadIdx.x >> 6, li = sc.li, lg = sc.lg;
-  const int b = sc.b, n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, i0 = i - li;
-  const T* Vt = static_cast<const T*>(a.Vt);
+  const int b = sc.b, n = a.n, JT = sc.JT, i = sc.i, i0 = i - li;
+  f32x4 oacc[H][DH / 16];
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     float m = kNegInf;
@@ -569,7 +639,7 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
     for (int tt = 0; tt < MAXT; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) m = fmaxf(m, u[tt][h][r]);
-    m = wave_max_lg(m);
+    m = lg_max(m);
     if (lg == 0) red_s[0][w][h][li] = m;
   }
   __syncthreads();
@@ -588,7 +658,7 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
         u[tt][h][r] = p;
         s += p;
       }
-    s = wave_sum_lg(s);
+    s = lg_sum(s);
     if (lg == 0) red_s[1][w][h][li] = s;
   }
   __syncthreads();
@@ -629,11 +699,7 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
         Frag<T, 4> af;
         af.set(u[tt][h]);
 #pragma unroll
-        for (int tc = 0; tc < DH / 16; ++tc) {
-          Frag<T, 4> vf;
-          vf.load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + j0 + 4 * lg);
-          oacc[h][tc] = mma(oacc[h][tc], vf, af);
-        }
+        for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = mma(oacc[h][tc], vf[tt][h][tc], af);
       }
     }
   }
@@ -643,20 +709,22 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
 #pragma unroll
     for (int tt = 0; tt < MAXT; ++tt) {
       const int jt = w + kWaves * tt;
+      const bool full = tile_full(sc.mi, bits[tt]);
       if (jt < JT)
-        up.template tile<KEEP_E>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, sc.mask_b, 16 * jt, lg,
+        up.template tile<KEEP_E>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, 16 * jt, lg, bits[tt], full,
                                  u[tt]);
     }
   }
   reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg);
 }
 
-
-// One block per (graph b = blockIdx.y, 16-query block blockIdx.x); wave w
-// owns key tiles w, w+4, ... . kSingle/kFused/kLogits keep the MAXT logit
-// tiles of a wave in registers (n <= 64*MAXT); kOnline streams any n.
-// With one tile per wave and bfloat16 data the fused mode keeps the tile's E
-// fragments in registers from the scores to the edge update (E read once).
+// One block per (graph, 16-query block); wave w owns key tiles w, w+4, ... .
+// kSingle/kFused/kLogits keep the MAXT logit tiles of a wave in registers
+// (n <= 64*MAXT); kOnline streams any n. Loads are issued in the order they
+// are consumed so that a wait never covers the E stream early: mask bytes,
+// then queries, weights, K and V fragments, then the E tile. With one tile per
+// wave and bfloat16 data the fused mode keeps the E fragments in registers
+// from the scores to the edge update (E read once).
 template <typename T, int H, int DH, int DE, int MAXT, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
   constexpr int D = H * DH;
@@ -664,35 +732,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
   static_assert(D <= 256 && 2 * H <= 16, "shape");
   __shared__ __align__(16) float os_s[kWaves * D * 17];  // O^T partials of each wave
   __shared__ float red_s[2][kWaves][H][16];
-  __shared__ float gy_s[2 * H];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int b = blockIdx.y, i0 = blockIdx.x * 16;
+  int ib, b;
+  xcd_block(ib, b);
+  const int i0 = ib * 16;
   Scorer<T, H, DH, DE> sc;
   sc.setup(a, b, i0);
   const int JT = sc.JT, n = a.n, NP = a.NP, i = sc.i;
-  const T* Vt = static_cast<const T*>(a.Vt);
-
-  f32x4 oacc[H][DH / 16];
-#pragma unroll
-  for (int h = 0; h < H; ++h)
-#pragma unroll
-    for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (MODE == kOnline) {
-    sc.init(a, gy_s);
+    const uint32_t mq = sc.query_mask_byte();
+    uint32_t mk = sc.key_mask_byte(w);
+    sc.load_weights(a);
+    sc.mi = mq != 0u;
+    f32x4 oacc[H][DH / 16];
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run[H], l_run[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
     for (int jt = w; jt < JT; jt += kWaves) {
-      const int j0 = 16 * jt;
+      const uint32_t bits = key_bits(mk);
+      Frag<T, DH / 4> kf[H];
+      sc.load_k(jt, kf);
+      Frag<T, 4> vf[H][DH / 16];
+      sc.load_v(jt, vf);
       ETile<T, DE> et;
-      et.load(sc.E, b, n, i, sc.mi, sc.mask_b, j0, lg);
+      et.load(sc.E, b, n, i, sc.mi, 16 * jt, lg, bits);
+      mk = sc.key_mask_byte(jt + kWaves);  // next tile's mask, behind this tile's loads
       float u[H][4];
-      sc.logits(jt, et, u);
+      sc.logits(et, kf, bits, u);
 #pragma unroll
       for (int h = 0; h < H; ++h) {
-        const float tm = wave_max_lg(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
+        const float tm = lg_max(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
         const float mnew = fmaxf(m_run[h], tm);
         const float alpha = (mnew == kNegInf) ? 1.f : __expf(m_run[h] - mnew);
         float p[4], ps = 0.f;
@@ -707,17 +782,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
         af.set(p);
 #pragma unroll
         for (int tc = 0; tc < DH / 16; ++tc) {
-          Frag<T, 4> vf;
-          vf.load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + j0 + 4 * lg);
           oacc[h][tc] *= alpha;
-          oacc[h][tc] = mma(oacc[h][tc], vf, af);
+          oacc[h][tc] = mma(oacc[h][tc], vf[h][tc], af);
         }
       }
     }
     // combine lane groups, then waves
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const float lsum = wave_sum_lg(l_run[h]);
+      const float lsum = lg_sum(l_run[h]);
       if (lg == 0) { red_s[0][w][h][li] = m_run[h]; red_s[1][w][h][li] = lsum; }
     }
     __syncthreads();
@@ -740,56 +813,50 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
     reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg);
   } else {
     float u[MAXT][H][4];
+    uint32_t mk[MAXT], bits[MAXT];
+    const uint32_t mq = sc.query_mask_byte();
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt) mk[tt] = sc.key_mask_byte(w + kWaves * tt);
+    sc.load_weights(a);
+    Frag<T, DH / 4> kf[MAXT][H];
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt) sc.load_k(w + kWaves * tt, kf[tt]);
+    sc.mi = mq != 0u;
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt) bits[tt] = key_bits(mk[tt]);
+    Frag<T, 4> vf[MAXT][H][DH / 16];
     if constexpr (MAXT == 1) {
-      // issue the tile's E loads before anything else
       ETile<T, DE> et;
-      et.load(sc.E, b, n, i, sc.mi, sc.mask_b, 16 * w, lg);
-      sc.init(a, gy_s);
-      sc.logits(w, et, u[0]);
-      if constexpr (kKeepE) {
-        // softmax, A, A V and the edge update below use `et` directly
-        static_assert(MODE == kFused, "");
+      et.load(sc.E, b, n, i, sc.mi, 16 * w, lg, bits[0]);
+      if constexpr (MODE != kLogits) sc.load_v(w, vf[0]);
+      sc.logits(et, kf[0], bits[0], u[0]);
+      if constexpr (MODE != kLogits)
+        attn_rest<T, H, DH, DE, 1, MODE, kKeepE>(a, sc, u, bits, vf, os_s, red_s, et);
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < MAXT; ++tt) {
+        ETile<T, DE> et;
+        et.load(sc.E, b, n, i, sc.mi, 16 * (w + kWaves * tt), lg, bits[tt]);
+        sc.logits(et, kf[tt], bits[tt], u[tt]);
       }
-      // fallthrough to the common code with the fragments still live
-      if constexpr (MODE == kLogits) {
-        if (i < n) {
+      if constexpr (MODE != kLogits) {
+#pragma unroll
+        for (int tt = 0; tt < MAXT; ++tt) sc.load_v(w + kWaves * tt, vf[tt]);
+        ETile<T, DE> unused;
+        attn_rest<T, H, DH, DE, MAXT, MODE, false>(a, sc, u, bits, vf, os_s, red_s, unused);
+      }
+    }
+    if constexpr (MODE == kLogits) {
+      if (i < n) {
+#pragma unroll
+        for (int tt = 0; tt < MAXT; ++tt)
 #pragma unroll
           for (int h = 0; h < H; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int j = 16 * w + 4 * lg + r;
-              if (j < n) a.U[(((size_t)b * H + h) * n + i) * n + j] = u[0][h][r];
+              const int j = 16 * (w + kWaves * tt) + 4 * lg + r;
+              if (j < n) a.U[(((size_t)b * H + h) * n + i) * n + j] = u[tt][h][r];
             }
-        }
-        return;
-      } else {
-        // single-tile fast path continues in attn_rest
-        attn_rest<T, H, DH, DE, 1, MODE, kKeepE>(a, sc, u, oacc, os_s, red_s, et);
-      }
-    } else {
-      sc.init(a, gy_s);
-#pragma unroll
-      for (int tt = 0; tt < MAXT; ++tt) {
-        ETile<T, DE> et;
-        et.load(sc.E, b, n, i, sc.mi, sc.mask_b, 16 * (w + kWaves * tt), lg);
-        sc.logits(w + kWaves * tt, et, u[tt]);
-      }
-      if constexpr (MODE == kLogits) {
-        if (i < n) {
-#pragma unroll
-          for (int tt = 0; tt < MAXT; ++tt)
-#pragma unroll
-            for (int h = 0; h < H; ++h)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int j = 16 * (w + kWaves * tt) + 4 * lg + r;
-                if (j < n) a.U[(((size_t)b * H + h) * n + i) * n + j] = u[tt][h][r];
-              }
-        }
-        return;
-      } else {
-        ETile<T, DE> unused;
-        attn_rest<T, H, DH, DE, MAXT, MODE, false>(a, sc, u, oacc, os_s, red_s, unused);
       }
     }
   }
@@ -803,46 +870,60 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
 // fragments of the tile are read once (bfloat16) and serve both stages.
 template <typename T, int H, int DH, int DE, int MODE>
 __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
-  __shared__ float gy_s[2 * H];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, i0 = blockIdx.x * 16, i = i0 + li;
   const int n = a.n, NP = a.NP, JT = NP / 16;
   const int jt = blockIdx.z * kWaves + w, j0 = 16 * jt;
-  const uint8_t* mask_b = a.mask + (size_t)b * n;
-  const bool mi = i < n && mask_b[i];
   constexpr bool kKeepE = sizeof(T) == 2;
+  Scorer<T, H, DH, DE> sc;
+  sc.setup(a, b, i0);
+  const uint32_t mq = sc.query_mask_byte();
+  const uint32_t mk = sc.key_mask_byte(jt);
   float A[H][4];
   ETile<T, DE> et;
+  uint32_t bits;
   if constexpr (MODE == kRecompute) {
-    Scorer<T, H, DH, DE> sc;
-    sc.setup(a, b, i0);
-    et.load(sc.E, b, n, i, mi, mask_b, j0, lg);
-    sc.init(a, gy_s);
+    sc.load_weights(a);
+    Frag<T, DH / 4> kf[H];
+    sc.load_k(jt, kf);
+    float L[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)b * H + h) * NP + i];
+    sc.mi = mq != 0u;
+    bits = key_bits(mk);
+    et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
     float u[H][4];
-    sc.logits(jt, et, u);
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      const float L = a.lse[((size_t)b * H + h) * NP + i];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        A[h][r] = (u[h][r] == kNegInf || L == kNegInf) ? 0.f : Num<T>::rnd(__expf(u[h][r] - L));
-    }
-  } else {
-    if (kKeepE) et.load(static_cast<const T*>(a.E), b, n, i, mi, mask_b, j0, lg);
-    const T* Ag = static_cast<const T*>(a.A);
+    sc.logits(et, kf, bits, u);
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * lg + r;
-        A[h][r] = (jt < JT && i < n && j < n) ? Num<T>::ld(Ag + (((size_t)b * H + h) * n + i) * n + j) : 0.f;
+      for (int r = 0; r < 4; ++r)
+        A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : Num<T>::rnd(__expf(u[h][r] - L[h]));
+  } else {
+    const T* Ag = static_cast<const T*>(a.A);
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const T* row = Ag + (((size_t)b * H + h) * n + i) * n + j0 + 4 * lg;
+      if (jt < JT && i < n && (n & 3) == 0 && j0 + 4 * lg + 3 < n) {
+        Frag<T, 4> f;
+        f.load(row);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A[h][r] = f.get(r);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          A[h][r] = (jt < JT && i < n && j0 + 4 * lg + r < n) ? Num<T>::ld(row + r) : 0.f;
       }
+    }
+    sc.mi = mq != 0u;
+    bits = key_bits(mk);
+    if (kKeepE) et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
   }
   Updater<T, H, DE> up;
   up.init(a, li, lg);
+  const bool full = tile_full(sc.mi, bits);
   if (jt < JT)
-    up.template tile<kKeepE>(et, static_cast<const T*>(a.E), static_cast<T*>(a.E_out), b, n, i, mi, mask_b, j0,
-                             lg, A);
+    up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, A);
 }
 
 // ------------------------------------------------------------------ dispatch

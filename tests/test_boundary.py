@@ -77,7 +77,8 @@ def test_mode_and_workspace_plan(lib):
         NP = (n + 15) // 16 * 16
         qkv = -(-3 * 8 * NP * 32 * 2 // 256) * 256
         lse = -(-3 * 8 * NP * 4 // 256) * 256
-        assert lib.ea_workspace_bytes(ctx) == 3 * qkv + lse
+        gy = -(-3 * 2 * 8 * 4 // 256) * 256
+        assert lib.ea_workspace_bytes(ctx) == 3 * qkv + lse + gy
         lib.ea_ctx_destroy(ctx)
     assert lib.ea_is_two_pass(None) == -1
     assert lib.ea_workspace_bytes(None) == 0
