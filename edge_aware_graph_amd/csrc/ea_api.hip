@@ -11,7 +11,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/edge_attn.h"
+#include "edge_attn.h"
 #include "ea_internal.h"
 
 struct ea_ctx {
@@ -180,6 +180,8 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   if ((long long)d.H * d.dh != d.d) return fail(EA_E_SHAPE, "d (%d) != H*dh (%d*%d)", d.d, d.H, d.dh);
   if (d.B > 65535) return fail(EA_E_SHAPE, "B (%d) exceeds 65535", d.B);
   if (d.n > (1 << 20)) return fail(EA_E_SHAPE, "n (%d) exceeds 2^20", d.n);
+  if ((long long)d.B * ((d.n + 15) / 16 * 16) >= (1ll << 31))
+    return fail(EA_E_SHAPE, "B * n (padded to 16) must stay below 2^31");
   if (d.dtype != EA_FP32 && d.dtype != EA_BF16) return fail(EA_E_UNSUPPORTED, "dtype %d", d.dtype);
   if (d.flags & ~EA_FORCE_TWO_PASS) return fail(EA_E_UNSUPPORTED, "unknown flags 0x%x", d.flags);
   if (!ea::shape_supported(d.dtype, d.H, d.dh, d.de))
@@ -207,7 +209,7 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
 
 void ea_ctx_destroy(ea_ctx* c) {
   if (!c) return;
-  for (hipEvent_t e : c->ev_pool) hipEventDestroy(e);
+  for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   delete c;
 }
 

@@ -229,6 +229,7 @@ template <typename T, int D, int DH>
 __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   constexpr int H = D / DH;
   constexpr int KC = D < 128 ? D : 128;          // contraction chunk staged in LDS
+  constexpr int NKC = D / KC;                    // chunks, all loaded before the first is used
   constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
   constexpr int CPR = KC / EPC;                  // chunks per staged row
   constexpr int PITCH = KC + 16 / (int)sizeof(T);  // padded LDS row pitch (elements)
@@ -239,26 +240,32 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   T* wsm = lds + 64 * PITCH;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int NP = a.NP, n = a.n;
-  const long rows = (long)a.B * NP;
-  const long m0 = (long)blockIdx.x * 64;
+  const uint32_t NP = a.NP, n = a.n;
+  const uint32_t rows = (uint32_t)a.B * NP;  // < 2^31 (checked at context creation)
+  const uint32_t m0 = blockIdx.x * 64u;
   const int f0 = blockIdx.y * 64;
-  const int which = f0 / D, fl0 = f0 % D;
-  const T* W = static_cast<const T*>(which == 0 ? a.w_q : which == 1 ? a.w_k : a.w_v);
-  const void* bias = which == 0 ? a.b_q : which == 1 ? a.b_k : a.b_v;
-  const int wm = w & 1, wn = w >> 1;  // this wave's 32 x 32 quadrant
-
-  if (blockIdx.y == 0) {
-    // global FiLM of the graphs whose slot 0 lies in this row block: 16 lanes
-    // per coefficient (2H <= 16), reduced across the lanes
+  if (f0 >= 3 * D) {
+    // extra column of blocks: global FiLM of the graphs whose slot 0 lies in
+    // this row block; 16 lanes per coefficient (2H <= 16), loads batched
     const int o = tid >> 4, part = tid & 15;
-    for (long m = (m0 + NP - 1) / NP * NP; m < m0 + 64 && m < rows; m += NP) {
-      const int b = (int)(m / NP);
+    const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)(o % H) * a.dy;
+    for (uint32_t m = (m0 + NP - 1) / NP * NP; m < m0 + 64 && m < rows; m += NP) {
+      const uint32_t b = m / NP;
+      const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
       float acc = 0.f;
       if (o < 2 * H) {
-        const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)(o % H) * a.dy;
-        const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
-        for (int c = part; c < a.dy; c += 16) acc += Num<T>::ld(yb + c) * Num<T>::ld(Wy + c);
+        constexpr int kBatch = 8;
+        for (int c0 = 0; c0 < a.dy; c0 += 16 * kBatch) {
+          float yv[kBatch], wv[kBatch];
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            const int c = c0 + part + 16 * k;
+            yv[k] = c < a.dy ? Num<T>::ld(yb + c) : 0.f;
+            wv[k] = c < a.dy ? Num<T>::ld(Wy + c) : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) acc += yv[k] * wv[k];
+        }
       }
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
@@ -269,7 +276,12 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
         a.gy[(size_t)b * 2 * H + o] = o < H ? 1.f + (bias + acc) : bias + acc;
       }
     }
+    return;
   }
+  const int which = f0 / D, fl0 = f0 % D;
+  const T* W = static_cast<const T*>(which == 0 ? a.w_q : which == 1 ? a.w_k : a.w_v);
+  const void* bias = which == 0 ? a.b_q : which == 1 ? a.b_k : a.b_v;
+  const int wm = w & 1, wn = w >> 1;  // this wave's 32 x 32 quadrant
 
   f32x4 acc[2][2];
 #pragma unroll
@@ -277,19 +289,59 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < D; kc += KC) {
-    for (int idx = tid; idx < 64 * CPR; idx += kThreads) {
-      const int row = idx / CPR, ch = idx % CPR;
-      const long m = m0 + row;
-      u32x4 xv = {0u, 0u, 0u, 0u};
-      if (m < rows) {
-        const int b = (int)(m / NP), i = (int)(m % NP);
-        if (i < n && a.mask[(size_t)b * n + i])
-          xv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.X) + ((size_t)b * n + i) * D + kc + ch * EPC);
-      }
-      *reinterpret_cast<u32x4*>(xs + row * PITCH + ch * EPC) = xv;
-      *reinterpret_cast<u32x4*>(wsm + row * PITCH + ch * EPC) =
-          *reinterpret_cast<const u32x4*>(W + (size_t)(fl0 + row) * D + kc + ch * EPC);
+  // Rows (b, i) of the tile without a division per row: NP >= 16, so a row
+  // offset below 64 crosses at most four graph boundaries.
+  const uint32_t b0 = m0 / NP, i00 = m0 - b0 * NP;
+  auto split = [&](uint32_t off, uint32_t& b, uint32_t& i) {
+    b = b0;
+    i = i00 + off;
+    while (i >= NP) { i -= NP; ++b; }
+  };
+  // The rows this thread stages: X rows are read whenever they exist (i < n)
+  // and zeroed afterwards for padded nodes, so no load waits on the mask.
+  constexpr int RPT = 64 * CPR / kThreads;  // staged chunks per thread and matrix
+  static_assert((64 * CPR) % kThreads == 0, "staging split");
+  const T* xsrc[RPT];
+  const uint8_t* xmask[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int row = (tid + k * kThreads) / CPR;
+    uint32_t b, i;
+    split(row, b, i);
+    const bool exists = m0 + row < rows && i < n;
+    xsrc[k] = exists ? static_cast<const T*>(a.X) + ((size_t)b * n + i) * D : nullptr;
+    xmask[k] = exists ? a.mask + (size_t)b * n + i : nullptr;
+  }
+  u32x4 xv[NKC][RPT], wv[NKC][RPT];
+#pragma unroll
+  for (int q = 0; q < NKC; ++q)
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int idx = tid + k * kThreads, row = idx / CPR, ch = idx % CPR;
+      xv[q][k] = xsrc[k] ? *reinterpret_cast<const u32x4*>(xsrc[k] + q * KC + ch * EPC) : u32x4{0u, 0u, 0u, 0u};
+      wv[q][k] = *reinterpret_cast<const u32x4*>(W + (size_t)(fl0 + row) * D + q * KC + ch * EPC);
+    }
+  // mask bytes after the X and W loads, so waiting for them costs nothing extra
+  bool xok[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) xok[k] = xmask[k] && *xmask[k];
+  bool rok[2][4];  // output rows of this lane that belong to real nodes
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = wm * 32 + mt * 16 + 4 * lg + r;
+      uint32_t b, i;
+      split(off, b, i);
+      rok[mt][r] = m0 + off < rows && i < n && a.mask[(size_t)b * n + i];
+    }
+#pragma unroll
+  for (int q = 0; q < NKC; ++q) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int idx = tid + k * kThreads, row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<u32x4*>(xs + row * PITCH + ch * EPC) = xok[k] ? xv[q][k] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(wsm + row * PITCH + ch * EPC) = wv[q][k];
     }
     __syncthreads();
 #pragma unroll
@@ -316,12 +368,7 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = wm * 32 + mt * 16 + 4 * lg + r;
-      const long m = m0 + row;
-      bool ok = false;
-      if (m < rows) {
-        const int b = (int)(m / NP), i = (int)(m % NP);
-        ok = i < n && a.mask[(size_t)b * n + i];
-      }
+      const bool ok = rok[mt][r];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int col = wn * 32 + nt * 16 + li;
@@ -334,9 +381,9 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   for (int idx = tid; idx < 64 * 8; idx += kThreads) {
     if (which < 2) {
       const int row = idx >> 3, c8 = (idx & 7) * 8;  // 8 features of one row
-      const long m = m0 + row;
-      if (m >= rows) continue;
-      const int b = (int)(m / NP), i = (int)(m % NP);
+      if (m0 + row >= rows) continue;
+      uint32_t b, i;
+      split(row, b, i);
       const int f = fl0 + c8, h = f / DH, t = f % DH;
       float v[8];
 #pragma unroll
@@ -346,9 +393,9 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
       o.store(static_cast<T*>(which == 0 ? a.Qw : a.Kw) + (((size_t)b * H + h) * NP + i) * DH + t);
     } else {
       const int col = idx >> 3, r8 = (idx & 7) * 8;  // 8 consecutive rows of one feature
-      const long m = m0 + r8;
-      if (m >= rows) continue;
-      const int b = (int)(m / NP), i = (int)(m % NP);
+      if (m0 + r8 >= rows) continue;
+      uint32_t b, i;
+      split(r8, b, i);
       const int f = fl0 + col, h = f / DH, t = f % DH;
       float v[8];
 #pragma unroll
@@ -972,7 +1019,8 @@ hipError_t update_shape(const LayerArgs& a, int mode, hipStream_t s) {
 template <typename T, int D, int DH>
 hipError_t qkv_shape(const LayerArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.NP;
-  const dim3 grid((unsigned)((rows + 63) / 64), 3 * D / 64);
+  // one extra column of blocks computes the global FiLM coefficients
+  const dim3 grid((unsigned)((rows + 63) / 64), 3 * D / 64 + 1);  // rows < 2^31
   hipLaunchKernelGGL((qkv_kernel<T, D, DH>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -173,6 +173,23 @@ class EdgeAttention:
             self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask),
             _ptr(O), _ptr(A), _ptr(E_out), _ptr(ws), self._ws_len(ws), _stream(stream)))
 
+    def bind_layer(self, w, X, E, y, mask, O, A, E_out, ws, stream=None):
+        """Marshal the arguments of one layer call once; returns a callable
+        that launches it (on `stream`, else the current stream at bind time)."""
+        p = self.attn_params(w)
+        u = self.update_params(w)
+        args = (self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask),
+                _ptr(O), _ptr(A), _ptr(E_out), _ptr(ws), self._ws_len(ws), _stream(stream))
+        fn, lib = self.lib.edge_attn_layer, self.lib
+        keep = (p, u, w, X, E, y, mask, O, A, E_out, ws)  # keep the tensors alive
+
+        def call():
+            st = fn(*args)
+            if st != EA_OK:
+                _check(lib, st)
+        call.keep = keep
+        return call
+
     def debug_logits(self, w, X, E, y, mask, U, ws, stream=None):
         p = self.attn_params(w)
         _check(self.lib, self.lib.ea_debug_logits(
