@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -20,16 +21,39 @@ FLAGS = [
 ]
 
 
+def scratch_users(remarks: str):
+    """Kernels whose resource-usage remarks report scratch (private) memory."""
+    users, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
+
+
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile every HIP source into the shared library (always rebuilds)."""
+    """Compile every HIP source into the shared library (always rebuilds).
+
+    Every kernel must run without scratch memory: register spills are a
+    performance cliff here, and spill code has been seen to reload a
+    spilled fragment incompletely. The build fails if any kernel spills.
+    """
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra) + SOURCES + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage"] + list(extra) + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building %s" % LIB)
+    spills = scratch_users(res.stderr)
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("kernels use scratch memory: %s" % ", ".join("%s (%d B/lane)" % s for s in spills))
     os.replace(tmp, LIB)
     return LIB
 

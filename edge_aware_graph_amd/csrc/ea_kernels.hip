@@ -62,9 +62,28 @@ struct Num<bf16_t> {
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = (bf16_t)(pack_bf2(v, 0.f) & 0xffffu); }
 };
 
+// 256 zero bytes in device memory. Lanes whose element does not exist, and
+// absent optional parameters, load from here instead of skipping the load: a
+// load under a divergent condition makes the compiler wait for it, and for
+// every load and store issued before it, right where the branches join,
+// which would serialize the small loads of a kernel behind one another.
+// Not declared const: it stays in the global address space like the
+// parameter vectors, so a select between the two is still a global load.
+// Nothing writes it.
+__device__ __align__(16) uint32_t kZeros[64] = {};
+
+template <typename T>
+__device__ __forceinline__ const T* zeros() { return reinterpret_cast<const T*>(kZeros); }
+
+// Address of element k of the optional vector p when ok holds, else of a zero.
+template <typename T>
+__device__ __forceinline__ const T* elem_or_zero(const void* p, size_t k, bool ok) {
+  return (p != nullptr && ok) ? static_cast<const T*>(p) + k : zeros<T>();
+}
+
 template <typename T>
 __device__ __forceinline__ float ld_or0(const void* p, size_t k) {
-  return p ? Num<T>::ld(static_cast<const T*>(p) + k) : 0.f;
+  return Num<T>::ld(elem_or_zero<T>(p, k, true));
 }
 
 // Q consecutive elements of type T held by one lane, packed in dwords.
@@ -260,8 +279,10 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
             const int c = c0 + part + 16 * k;
-            yv[k] = c < a.dy ? Num<T>::ld(yb + c) : 0.f;
-            wv[k] = c < a.dy ? Num<T>::ld(Wy + c) : 0.f;
+            const float yl = Num<T>::ld(yb + (c < a.dy ? c : 0));
+            const float wl = Num<T>::ld(Wy + (c < a.dy ? c : 0));
+            yv[k] = c < a.dy ? yl : 0.f;
+            wv[k] = c < a.dy ? wl : 0.f;
           }
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) acc += yv[k] * wv[k];
@@ -301,16 +322,22 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   // and zeroed afterwards for padded nodes, so no load waits on the mask.
   constexpr int RPT = 64 * CPR / kThreads;  // staged chunks per thread and matrix
   static_assert((64 * CPR) % kThreads == 0, "staging split");
+  float bcol[2];  // bias of this lane's output columns
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) bcol[nt] = ld_or0<T>(bias, fl0 + wn * 32 + nt * 16 + li);
+  // Slots without a node read node 0 (a valid address) and are zeroed.
   const T* xsrc[RPT];
   const uint8_t* xmask[RPT];
+  bool xexists[RPT];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     const int row = (tid + k * kThreads) / CPR;
     uint32_t b, i;
     split(row, b, i);
-    const bool exists = m0 + row < rows && i < n;
-    xsrc[k] = exists ? static_cast<const T*>(a.X) + ((size_t)b * n + i) * D : nullptr;
-    xmask[k] = exists ? a.mask + (size_t)b * n + i : nullptr;
+    xexists[k] = m0 + row < rows && i < n;
+    const size_t node = xexists[k] ? (size_t)b * n + i : 0;
+    xsrc[k] = static_cast<const T*>(a.X) + node * D;
+    xmask[k] = a.mask + node;
   }
   u32x4 xv[NKC][RPT], wv[NKC][RPT];
 #pragma unroll
@@ -318,13 +345,16 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int idx = tid + k * kThreads, row = idx / CPR, ch = idx % CPR;
-      xv[q][k] = xsrc[k] ? *reinterpret_cast<const u32x4*>(xsrc[k] + q * KC + ch * EPC) : u32x4{0u, 0u, 0u, 0u};
+      xv[q][k] = *reinterpret_cast<const u32x4*>(xsrc[k] + q * KC + ch * EPC);
       wv[q][k] = *reinterpret_cast<const u32x4*>(W + (size_t)(fl0 + row) * D + q * KC + ch * EPC);
     }
   // mask bytes after the X and W loads, so waiting for them costs nothing extra
   bool xok[RPT];
 #pragma unroll
-  for (int k = 0; k < RPT; ++k) xok[k] = xmask[k] && *xmask[k];
+  for (int k = 0; k < RPT; ++k) {
+    const uint8_t mv = *xmask[k];
+    xok[k] = xexists[k] && mv != 0;
+  }
   bool rok[2][4];  // output rows of this lane that belong to real nodes
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -333,8 +363,11 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
       const uint32_t off = wm * 32 + mt * 16 + 4 * lg + r;
       uint32_t b, i;
       split(off, b, i);
-      rok[mt][r] = m0 + off < rows && i < n && a.mask[(size_t)b * n + i];
+      const bool exists = m0 + off < rows && i < n;
+      const uint8_t mv = a.mask[exists ? (size_t)b * n + i : 0];
+      rok[mt][r] = exists && mv != 0;
     }
+
 #pragma unroll
   for (int q = 0; q < NKC; ++q) {
 #pragma unroll
@@ -372,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int col = wn * 32 + nt * 16 + li;
-        os[row * OPITCH + col] = ok ? acc[mt][nt][r] + ld_or0<T>(bias, fl0 + col) : 0.f;
+        os[row * OPITCH + col] = ok ? acc[mt][nt][r] + bcol[nt] : 0.f;
       }
     }
   }
@@ -415,6 +448,18 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
 template <typename T, int DE>
 struct ETile {
   Frag<T, DE / 4> f[16];
+  // Every pair, masked or not, with no mask bytes needed and no condition on
+  // any load; pairs outside the n x n layout read the nearest pair inside it.
+  // Values of pairs that are not real are discarded by the selects of the
+  // score stage and of the edge update.
+  __device__ __forceinline__ void load_all(const T* E, int b, int n, int i, int j0, int lg) {
+    const T* row = E + ((size_t)b * n + (i < n ? i : n - 1)) * n * DE + lg * (DE / 4);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = j0 + jj < n ? j0 + jj : n - 1;
+      f[jj].load(row + (size_t)j * DE);
+    }
+  }
   __device__ __forceinline__ void load(const T* E, int b, int n, int i, bool mi, int j0, int lg, uint32_t bits) {
     const T* row = E + ((size_t)b * n + i) * n * DE + lg * (DE / 4);
 #pragma unroll
@@ -432,6 +477,7 @@ template <typename T, int H, int DH, int DE>
 struct Scorer {
   int b, n, NP, JT, i, li, lg;
   bool mi;
+  bool mi_any;  // some query of the block is real
   const uint8_t* mask_b;
   const T* E;
   const T* Kw;
@@ -439,7 +485,7 @@ struct Scorer {
   float scale;
   Frag<T, DH / 4> qf[H];
   Frag<T, DE / 4> wf;  // edge-FiLM weights, row li: gamma of head li, then beta of head li-H
-  f32x4 fc;            // FiLM accumulator start: 1 + b_emul (gamma rows), b_eadd (beta rows)
+  Frag<T, 4> fb;       // FiLM biases of rows 4*lg .. 4*lg+3 (b_emul or b_eadd, or zeros)
   float gy[2 * H];     // gamma_y then beta_y of graph b
 
   // Per-lane constants; no loads.
@@ -453,61 +499,129 @@ struct Scorer {
     Vt = static_cast<const T*>(a.Vt);
     scale = a.scale;
   }
-  __device__ __forceinline__ uint32_t query_mask_byte() const { return i < n ? mask_b[i] : 0u; }
+  // Mask bytes; slots past n read node n-1 and count as masked.
+  __device__ __forceinline__ uint32_t query_mask_byte() const {
+    const uint32_t v = mask_b[i < n ? i : n - 1];
+    return i < n ? v : 0u;
+  }
   __device__ __forceinline__ uint32_t key_mask_byte(int jt) const {
     const int j = 16 * jt + li;
-    return j < n ? mask_b[j] : 0u;
+    const uint32_t v = mask_b[j < n ? j : n - 1];
+    return j < n ? v : 0u;
   }
   // Queries, FiLM weights and biases, global FiLM coefficients.
   __device__ __forceinline__ void load_weights(const LayerArgs& a) {
     const T* Qw = static_cast<const T*>(a.Qw);
 #pragma unroll
     for (int h = 0; h < H; ++h) qf[h].load(Qw + (((size_t)b * H + h) * NP + i) * DH + lg * (DH / 4));
-    if (li < H)
-      wf.load(static_cast<const T*>(a.w_emul) + (size_t)li * DE + lg * (DE / 4));
-    else if (li < 2 * H)
-      wf.load(static_cast<const T*>(a.w_eadd) + (size_t)(li - H) * DE + lg * (DE / 4));
-    else
-      wf.zero();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * lg + r;
-      fc[r] = row < H ? 1.f + ld_or0<T>(a.b_emul, row) : row < 2 * H ? ld_or0<T>(a.b_eadd, row - H) : 0.f;
-    }
+    const T* wrow = li < H ? static_cast<const T*>(a.w_emul) + (size_t)li * DE
+                  : static_cast<const T*>(a.w_eadd) + (size_t)(li - H) * DE;
+    wf.load(li < 2 * H ? wrow + lg * (DE / 4) : zeros<T>());
+    // FiLM rows 4*lg .. 4*lg+3 are all gamma rows or all beta rows (4 | H)
+    static_assert(H % 4 == 0, "heads");
+    const int r0 = 4 * lg;
+    fb.load(r0 < H ? elem_or_zero<T>(a.b_emul, r0, true) : elem_or_zero<T>(a.b_eadd, r0 - H, r0 < 2 * H));
 #pragma unroll
     for (int o = 0; o < 2 * H; ++o) gy[o] = a.gy[(size_t)b * 2 * H + o];
   }
+  // K and V fragments of key tile jt. A tile past the padded size reads tile
+  // JT-1 instead: its keys are masked (all logits -inf, all A exactly 0), and
+  // workspace K and V values are finite, so they add nothing.
   __device__ __forceinline__ void load_k(int jt, Frag<T, DH / 4> (&kf)[H]) const {
+    const int jc = jt < JT ? jt : JT - 1;
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      if (jt < JT) kf[h].load(Kw + (((size_t)b * H + h) * NP + 16 * jt + li) * DH + lg * (DH / 4));
-      else kf[h].zero();
-    }
+    for (int h = 0; h < H; ++h) kf[h].load(Kw + (((size_t)b * H + h) * NP + 16 * jc + li) * DH + lg * (DH / 4));
   }
   __device__ __forceinline__ void load_v(int jt, Frag<T, 4> (&vf)[H][DH / 16]) const {
+    const int jc = jt < JT ? jt : JT - 1;
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
-      for (int tc = 0; tc < DH / 16; ++tc) {
-        if (jt < JT) vf[h][tc].load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + 16 * jt + 4 * lg);
-        else vf[h][tc].zero();
-      }
+      for (int tc = 0; tc < DH / 16; ++tc)
+        vf[h][tc].load(Vt + (((size_t)b * H + h) * DH + tc * 16 + li) * NP + 16 * jc + 4 * lg);
   }
 
   // Masked logits u[h][r] of query i for key j = 16*jt + 4*lg + r from the
   // tile's E fragments and K fragments; bits: real keys of the tile.
+  // SKIP_EMPTY: a tile without real keys returns early (a branch that lets
+  // the compiler sink the loads it guards behind the mask bytes).
+  template <bool SKIP_EMPTY = true>
   __device__ __forceinline__ void logits(const ETile<T, DE>& et, const Frag<T, DH / 4> (&kf)[H], uint32_t bits,
                                          float (&u)[H][4]) const {
-    // edge FiLM: MFMA column = query row, rows = (gamma, beta) x head
+    if (SKIP_EMPTY && bits == 0u) {
+      no_keys(u);
+      return;
+    }
+    const f32x4 fc = film_start();
     float R[4][16];  // R[x][4*r' + r]: key 4*x + r', film row 4*lg + r
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const f32x4 F = mma(fc, wf, et.f[jj]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) R[jj >> 2][4 * (jj & 3) + r] = F[r];
+    for (int jj = 0; jj < 16; ++jj) film(et.f[jj], fc, R, jj);
+    scores(R, kf, bits, u);
+  }
+
+  // The same for float32 data, whose E tile would not fit in registers next
+  // to the rest: the fragments of key tile j0 are read here in groups of 2
+  // keys, the next group in flight while the current one is used.
+  __device__ __forceinline__ void logits_streamed(int j0, const Frag<T, DH / 4> (&kf)[H], uint32_t bits,
+                                                  float (&u)[H][4]) const {
+    constexpr int G = 2, NG = 16 / G;
+    if (bits == 0u) {
+      no_keys(u);
+      return;
     }
+    const T* row = E + ((size_t)b * n + i) * n * DE + lg * (DE / 4);
+    const f32x4 fc = film_start();
+    float R[4][16];
+    Frag<T, DE / 4> eg[2][G];
+    auto load_group = [&](Frag<T, DE / 4>(&f)[G], int g) {
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        const int jj = G * g + q;
+        if (mi && ((bits >> jj) & 1u)) f[q].load(row + (size_t)(j0 + jj) * DE);
+        else f[q].zero();
+      }
+    };
+    load_group(eg[0], 0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) load_group(eg[(g + 1) & 1], g + 1);
+      __builtin_amdgcn_sched_barrier(0);  // no more than two groups live
+#pragma unroll
+      for (int q = 0; q < G; ++q) film(eg[g & 1][q], fc, R, G * g + q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    scores(R, kf, bits, u);
+  }
+
+ private:
+  __device__ __forceinline__ static void no_keys(float (&u)[H][4]) {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[h][r] = kNegInf;
+  }
+  // Edge FiLM on MFMA: column = query row, rows = (gamma, beta) x head; the
+  // accumulator starts at 1 + b_emul (gamma rows) or b_eadd (beta rows).
+  __device__ __forceinline__ f32x4 film_start() const {
+    f32x4 fc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fc[r] = (4 * lg < H ? 1.f : 0.f) + fb.get(r);
+    return fc;
+  }
+  __device__ __forceinline__ void film(const Frag<T, DE / 4>& e, const f32x4& fc, float (&R)[4][16], int jj) const {
+    const f32x4 F = mma(fc, wf, e);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) R[jj >> 2][4 * (jj & 3) + r] = F[r];
+  }
+  // From the FiLM rows of the 16 keys to the masked logits.
+  __device__ __forceinline__ void scores(float (&R)[4][16], const Frag<T, DH / 4> (&kf)[H], uint32_t bits,
+                                         float (&u)[H][4]) const {
     // now R[x][4*r' + r]: key 4*lg + r', film row 4*x + r
     lane_group_transpose<16>(R);
+    // real pairs of this lane (bit r: key 4*lg + r), as plain bit tests: a
+    // short-circuit condition here becomes divergent branches around the
+    // whole logit array
+    const uint32_t okb = (bits >> (4 * lg)) & (mi ? 0xfu : 0u);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const f32x4 s = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kf[h], qf[h]);
@@ -516,11 +630,23 @@ struct Scorer {
         const float gam = R[h >> 2][4 * r + (h & 3)];
         const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)];
         const float v = ((s[r] * scale) * gam + bet) * gy[h] + gy[H + h];
-        u[h][r] = (mi && ((bits >> (4 * lg + r)) & 1u)) ? v : kNegInf;
+        u[h][r] = ((okb >> r) & 1u) ? v : kNegInf;
       }
     }
   }
 };
+
+// +0.0 into the edge outputs of one 16 x 16 tile (pairs inside the n x n layout).
+template <typename T, int DE>
+__device__ __forceinline__ void zero_edge_tile(T* Eout, int b, int n, int i, int j0, int lg) {
+  if (i >= n) return;
+  T* row = Eout + ((size_t)b * n + i) * n * DE + lg * (DE / 4);
+  Frag<T, DE / 4> z;
+  z.zero();
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj)
+    if (j0 + jj < n) z.store(row + (size_t)(j0 + jj) * DE);
+}
 
 // ------------------------------------------------------------------ edge update
 
@@ -529,17 +655,22 @@ struct Scorer {
 // + E^T (+ b_e), with A given as this lane's values for keys 4*lg + r and all
 // heads; they are regrouped in registers so that lane group lg supplies heads
 // [lg*QH, (lg+1)*QH) for every key. In bfloat16 mode the contraction has 16
-// slots for H <= 12 heads; slot H carries 1 against b_e, so the bias costs
-// no VALU work.
+// slots for H <= 12 heads; slot H carries 1 against b_e, and E^T enters
+// through a second MFMA against the identity (exact: products by 1 and sums
+// with zeros), straight from its packed fragment, so the update spends no
+// VALU work on E.
 template <typename T, int H, int DE>
 struct Updater {
   static constexpr bool kBF = sizeof(T) == 2;
   static constexpr int QH = kBF ? 4 : H / 4;  // heads per lane group
   static constexpr int NCH = DE / 16;
   Frag<T, QH> wef[NCH];
-  float be[kBF ? 1 : DE / 4];
-  bool has_heads;
+  Frag<T, 4> eye;                    // identity rows li, slots 4*lg .. 4*lg+3 (bfloat16)
+  T bl[kBF ? NCH : 1];               // raw b_e values of the bias lane group (bfloat16)
+  Frag<T, kBF ? 4 : DE / 4> bfr;     // raw b_e of this lane's channels (fp32)
+  bool has_heads, bias_lane;
 
+  // Issues the loads only; finish() builds the operands once they are needed.
   __device__ __forceinline__ void init(const LayerArgs& a, int li, int lg) {
     const T* We = static_cast<const T*>(a.w_e);
     has_heads = lg * QH < H || (kBF && lg * QH == H && a.b_e);
@@ -548,19 +679,25 @@ struct Updater {
       // MFMA row li of chunk ch is channel (li/4)*(DE/4) + 4*ch + li%4, so that
       // output rows 4*lg + r land on this lane group's channel quarter.
       const int c = (li >> 2) * (DE / 4) + 4 * ch + (li & 3);
-      if (lg * QH < H) {
-        wef[ch].load(We + (size_t)c * H + lg * QH);
-      } else if (kBF && lg * QH == H && a.b_e) {
-        float v[QH] = {};
-        v[0] = Num<T>::ld(static_cast<const T*>(a.b_e) + c);
-        wef[ch].set(v);
-      } else {
-        wef[ch].zero();
-      }
+      wef[ch].load(lg * QH < H ? We + (size_t)c * H + lg * QH : zeros<T>());
+      // lane group H / QH: b_e goes in slot 0, against the constant-1 head slot
+      if constexpr (kBF) bl[ch] = *elem_or_zero<T>(a.b_e, c, lg * QH == H);
     }
-    if constexpr (!kBF) {
+    bias_lane = kBF && lg * QH == H;
+    if constexpr (kBF) {
+      constexpr uint32_t kOne = 0x3f80u;  // bfloat16 1.0
+      const int q = li - 4 * lg;         // slot of the diagonal in this lane, if any
+      eye.w[0] = (q == 0 ? kOne : 0u) | (q == 1 ? kOne << 16 : 0u);
+      eye.w[1] = (q == 2 ? kOne : 0u) | (q == 3 ? kOne << 16 : 0u);
+    } else {
+      bfr.load(elem_or_zero<T>(a.b_e, lg * (DE / 4), true));
+    }
+  }
+  __device__ __forceinline__ void finish() {
+    if constexpr (kBF) {
 #pragma unroll
-      for (int k = 0; k < DE / 4; ++k) be[k] = ld_or0<T>(a.b_e, lg * (DE / 4) + k);
+      for (int ch = 0; ch < NCH; ++ch)  // slot 0 is the low half of dword 0
+        wef[ch].w[0] = bias_lane ? (uint32_t)bl[ch] : wef[ch].w[0];
     }
   }
 
@@ -583,35 +720,77 @@ struct Updater {
     // now R[x][r'*QH + q]: key 4*x + r', head lg*QH + q
     lane_group_transpose<4 * QH>(R);
     const size_t rowoff = ((size_t)b * n + i) * n * DE + lg * (DE / 4);
-    if (full) {
+    if (bits == 0u) {  // no real pair in the tile (uniform): zeros only
+      zero_edge_tile<T, DE>(Eout, b, n, i, j0, lg);
+      return;
+    }
+    const uint32_t okj = mi ? bits : 0u;  // bit jj: pair (i, j0 + jj) is real
+    const bool iin = i < n;
+    if constexpr (KEEP) {
+      if (full) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) step<KEEP, true>(et, E, Eout, rowoff + (size_t)(j0 + jj) * DE, true, true, R, jj);
-    } else {
+        for (int jj = 0; jj < 16; ++jj) step<true>(et.f[jj], Eout, rowoff + (size_t)(j0 + jj) * DE, true, true, R, jj);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          step<false>(et.f[jj], Eout, rowoff + (size_t)(j0 + jj) * DE, iin & (j0 + jj < n), (okj >> jj) & 1u, R, jj);
+      }
+    } else if constexpr (kBF) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        const int j = j0 + jj;
-        step<KEEP, false>(et, E, Eout, rowoff + (size_t)j * DE, i < n && j < n, mi && ((bits >> jj) & 1u), R, jj);
+        const size_t off = rowoff + (size_t)(j0 + jj) * DE;
+        const bool real = (okj >> jj) & 1u;
+        Frag<T, DE / 4> ef;
+        if (real) ef.load(E + off); else ef.zero();
+        step<false>(ef, Eout, off, iin & (j0 + jj < n), real, R, jj);
+      }
+    } else {
+      // float32: E read in groups of 4 keys, the next group in flight (the
+      // whole tile would not fit in registers next to the rest)
+      Frag<T, DE / 4> eg[2][4];
+      auto load_group = [&](Frag<T, DE / 4>(&f)[4], int g) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jj = 4 * g + q;
+          if ((okj >> jj) & 1u) f[q].load(E + rowoff + (size_t)(j0 + jj) * DE);
+          else f[q].zero();
+        }
+      };
+      load_group(eg[0], 0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g < 3) load_group(eg[(g + 1) & 1], g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jj = 4 * g + q;
+          step<false>(eg[g & 1][q], Eout, rowoff + (size_t)(j0 + jj) * DE, iin & (j0 + jj < n), (okj >> jj) & 1u, R, jj);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  template <bool KEEP, bool FULL>
-  __device__ __forceinline__ void step(const ETile<T, DE>& et, const T* E, T* Eout, size_t off, bool inb,
-                                       bool real, const float (&R)[4][4 * QH], int jj) const {
+  // One key of the tile: ef holds this lane's E channels of pair (i, j).
+  template <bool FULL>
+  __device__ __forceinline__ void step(const Frag<T, DE / 4>& ef, T* Eout, size_t off, bool inb, bool real,
+                                       const float (&R)[4][4 * QH], int jj) const {
     Frag<T, QH> af;
     if (has_heads) af.set(&R[jj >> 2][(jj & 3) * QH]); else af.zero();
-    Frag<T, DE / 4> ef;
-    if constexpr (KEEP) {
-      ef = et.f[jj];
-    } else {
-      if (real) ef.load(E + off); else ef.zero();
-    }
     float out[DE / 4];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       f32x4 c;
+      if constexpr (kBF) {
+        // channels 4*ch .. 4*ch+3 of this lane's quarter are dwords 2*ch, 2*ch+1
+        Frag<T, 4> e4;
+        e4.w[0] = ef.w[2 * ch];
+        e4.w[1] = ef.w[2 * ch + 1];
+        c = mma(f32x4{0.f, 0.f, 0.f, 0.f}, eye, e4);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) c[r] = ef.get(4 * ch + r) + (kBF ? 0.f : be[kBF ? 0 : 4 * ch + r]);
+        for (int r = 0; r < 4; ++r) c[r] = ef.get(4 * ch + r) + bfr.get(4 * ch + r);
+      }
       c = mma(c, wef[ch], af);
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[4 * ch + r] = (FULL || real) ? c[r] : 0.f;
@@ -627,7 +806,7 @@ struct Updater {
 // Cross-wave reduction of the per-wave O^T partials and the store of O rows.
 template <typename T, int H, int DH>
 __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, const f32x4 (&oacc)[H][DH / 16],
-                                               int b, int i0, int w, int li, int lg) {
+                                               int b, int i0, int w, int li, int lg, uint32_t qbits) {
   constexpr int D = H * DH;
   constexpr int P = 17;  // padded pitch of a 16-query row
 #pragma unroll
@@ -637,7 +816,6 @@ __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, co
 #pragma unroll
       for (int r = 0; r < 4; ++r) os[((w * D) + h * DH + tc * 16 + 4 * lg + r) * P + li] = oacc[h][tc][r];
   __syncthreads();
-  const uint8_t* mask_b = a.mask + (size_t)b * a.n;
   for (int idx = threadIdx.x; idx < 16 * D / 4; idx += kThreads) {
     const int il = idx / (D / 4), c = (idx % (D / 4)) * 4, ii = i0 + il;
     if (ii >= a.n) continue;
@@ -647,7 +825,7 @@ __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, co
       float s = 0.f;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) s += os[(ww * D + c + k) * P + il];
-      v[k] = mask_b[ii] ? s : 0.f;
+      v[k] = ((qbits >> il) & 1u) ? s : 0.f;
     }
     Frag<T, 4> o;
     o.set(v);
@@ -670,8 +848,9 @@ __device__ __forceinline__ bool tile_full(bool mi, uint32_t bits) {
 template <typename T, int H, int DH, int DE, int MAXT, int MODE, bool KEEP_E>
 __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H, DH, DE>& sc,
                                           float (&u)[MAXT][H][4], const uint32_t (&bits)[MAXT],
-                                          const Frag<T, 4> (&vf)[MAXT][H][DH / 16], float* os_s,
-                                          float (&red_s)[2][kWaves][H][16], const ETile<T, DE>& et) {
+                                          Frag<T, 4> (&vf)[H][DH / 16], float* os_s,
+                                          float (&red_s)[2][kWaves][H][16], const ETile<T, DE>& et,
+                                          Updater<T, H, DE>& up) {
   const int w = threadIdx.x >> 6, li = sc.li, lg = sc.lg;
   const int b = sc.b, n = a.n, JT = sc.JT, i = sc.i, i0 = i - li;
   f32x4 oacc[H][DH / 16];
@@ -741,18 +920,18 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
           }
         }
       }
+      if constexpr (MAXT > 1) sc.load_v(jt, vf);  // with one tile, loaded by the caller
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         Frag<T, 4> af;
         af.set(u[tt][h]);
 #pragma unroll
-        for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = mma(oacc[h][tc], vf[tt][h][tc], af);
+        for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = mma(oacc[h][tc], vf[h][tc], af);
       }
     }
   }
   if constexpr (MODE == kFused) {
-    Updater<T, H, DE> up;
-    up.init(a, li, lg);
+    up.finish();
 #pragma unroll
     for (int tt = 0; tt < MAXT; ++tt) {
       const int jt = w + kWaves * tt;
@@ -762,7 +941,7 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
                                  u[tt]);
     }
   }
-  reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg);
+  reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg, (uint32_t)(__ballot(sc.mi) & 0xffffull));
 }
 
 // One block per (graph, 16-query block); wave w owns key tiles w, w+4, ... .
@@ -793,6 +972,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
     uint32_t mk = sc.key_mask_byte(w);
     sc.load_weights(a);
     sc.mi = mq != 0u;
+    sc.mi_any = (__ballot(sc.mi) & 0xffffull) != 0ull;
     f32x4 oacc[H][DH / 16];
 #pragma unroll
     for (int h = 0; h < H; ++h)
@@ -803,15 +983,26 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
     for (int h = 0; h < H; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
     for (int jt = w; jt < JT; jt += kWaves) {
       const uint32_t bits = key_bits(mk);
+      if (bits == 0u || !sc.mi_any) {  // tile without real pairs: the running statistics do not change
+        mk = sc.key_mask_byte(jt + kWaves);
+        continue;
+      }
       Frag<T, DH / 4> kf[H];
       sc.load_k(jt, kf);
       Frag<T, 4> vf[H][DH / 16];
-      sc.load_v(jt, vf);
-      ETile<T, DE> et;
-      et.load(sc.E, b, n, i, sc.mi, 16 * jt, lg, bits);
-      mk = sc.key_mask_byte(jt + kWaves);  // next tile's mask, behind this tile's loads
       float u[H][4];
-      sc.logits(et, kf, bits, u);
+      if constexpr (sizeof(T) == 2) {
+        sc.load_v(jt, vf);
+        ETile<T, DE> et;
+        et.load(sc.E, b, n, i, sc.mi, 16 * jt, lg, bits);
+        mk = sc.key_mask_byte(jt + kWaves);  // next tile's mask, behind this tile's loads
+        sc.logits(et, kf, bits, u);
+      } else {
+        // float32: V after the scores, so that it is not live next to them
+        mk = sc.key_mask_byte(jt + kWaves);
+        sc.logits_streamed(16 * jt, kf, bits, u);
+        sc.load_v(jt, vf);
+      }
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         const float tm = lg_max(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
@@ -857,40 +1048,83 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
       for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] *= f;
       if (w == 0 && lg == 0) a.lse[((size_t)b * H + h) * NP + i] = (L > 0.f) ? M + __logf(L) : kNegInf;
     }
-    reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg);
+    reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg, (uint32_t)(__ballot(sc.mi) & 0xffffull));
   } else {
     float u[MAXT][H][4];
     uint32_t mk[MAXT], bits[MAXT];
+    // Issue order: mask bytes, then every small load, then the E stream; no
+    // load waits on another, so the E stream leaves at once.
     const uint32_t mq = sc.query_mask_byte();
 #pragma unroll
     for (int tt = 0; tt < MAXT; ++tt) mk[tt] = sc.key_mask_byte(w + kWaves * tt);
     sc.load_weights(a);
-    Frag<T, DH / 4> kf[MAXT][H];
-#pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) sc.load_k(w + kWaves * tt, kf[tt]);
-    sc.mi = mq != 0u;
-#pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) bits[tt] = key_bits(mk[tt]);
-    Frag<T, 4> vf[MAXT][H][DH / 16];
+    // K and V of the wave's tile are loaded here with one tile per wave;
+    // with several, each tile's K is loaded with its E and its V right
+    // before its A V product (bounded register use)
+    Frag<T, DH / 4> kf[H];
+    Frag<T, 4> vf[H][DH / 16];
     if constexpr (MAXT == 1) {
+      sc.load_k(w, kf);
+      if constexpr (MODE != kLogits) sc.load_v(w, vf);
+    }
+    Updater<T, H, DE> up;
+    if constexpr (MODE == kFused) up.init(a, li, lg);
+    if constexpr (MAXT == 1 && sizeof(T) == 2) {
+      // one tile per wave: every in-bounds pair is read, so the loads need
+      // no mask bytes (masked values are discarded by the selects)
       ETile<T, DE> et;
-      et.load(sc.E, b, n, i, sc.mi, 16 * w, lg, bits[0]);
-      if constexpr (MODE != kLogits) sc.load_v(w, vf[0]);
-      sc.logits(et, kf[0], bits[0], u[0]);
+      et.load_all(sc.E, b, n, i, 16 * w, lg);
+      __builtin_amdgcn_sched_barrier(0);  // nothing that waits on a load moves above the E stream
+      sc.mi = mq != 0u;
+      bits[0] = key_bits(mk[0]);
+      sc.template logits<false>(et, kf, bits[0], u[0]);
       if constexpr (MODE != kLogits)
-        attn_rest<T, H, DH, DE, 1, MODE, kKeepE>(a, sc, u, bits, vf, os_s, red_s, et);
+        attn_rest<T, H, DH, DE, 1, MODE, kKeepE>(a, sc, u, bits, vf, os_s, red_s, et, up);
     } else {
+      sc.mi = mq != 0u;
+#pragma unroll
+      for (int tt = 0; tt < MAXT; ++tt) bits[tt] = key_bits(mk[tt]);
+      if constexpr (MODE != kLogits) {
+        if ((__ballot(sc.mi) & 0xffffull) == 0ull) {
+          // no real query in the block (uniform): A, O and E' rows are all +0.0
+          T* Ag = static_cast<T*>(a.A);
+#pragma unroll
+          for (int tt = 0; tt < MAXT; ++tt) {
+            const int jt = w + kWaves * tt, jb = 16 * jt + 4 * lg;
+            if (jt >= JT || i >= n) continue;
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+              T* row = Ag + (((size_t)b * H + h) * n + i) * n;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (jb + r < n) Num<T>::st(row + jb + r, 0.f);
+            }
+            if constexpr (MODE == kFused) zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, 16 * jt, lg);
+          }
+          for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+            const int il = idx / (D / 4), c = (idx % (D / 4)) * 4;
+            if (i0 + il >= n) continue;
+            Frag<T, 4> z;
+            z.zero();
+            z.store(static_cast<T*>(a.O) + ((size_t)b * n + i0 + il) * D + c);
+          }
+          return;
+        }
+      }
 #pragma unroll
       for (int tt = 0; tt < MAXT; ++tt) {
-        ETile<T, DE> et;
-        et.load(sc.E, b, n, i, sc.mi, 16 * (w + kWaves * tt), lg, bits[tt]);
-        sc.logits(et, kf[tt], bits[tt], u[tt]);
+        if constexpr (MAXT > 1) sc.load_k(w + kWaves * tt, kf);
+        if constexpr (sizeof(T) == 2) {
+          ETile<T, DE> et;
+          et.load(sc.E, b, n, i, sc.mi, 16 * (w + kWaves * tt), lg, bits[tt]);
+          sc.logits(et, kf, bits[tt], u[tt]);
+        } else {
+          sc.logits_streamed(16 * (w + kWaves * tt), kf, bits[tt], u[tt]);
+        }
       }
       if constexpr (MODE != kLogits) {
-#pragma unroll
-        for (int tt = 0; tt < MAXT; ++tt) sc.load_v(w + kWaves * tt, vf[tt]);
         ETile<T, DE> unused;
-        attn_rest<T, H, DH, DE, MAXT, MODE, false>(a, sc, u, bits, vf, os_s, red_s, unused);
+        attn_rest<T, H, DH, DE, MAXT, MODE, false>(a, sc, u, bits, vf, os_s, red_s, unused, up);
       }
     }
     if constexpr (MODE == kLogits) {
@@ -924,50 +1158,72 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   constexpr bool kKeepE = sizeof(T) == 2;
   Scorer<T, H, DH, DE> sc;
   sc.setup(a, b, i0);
+  // Issue order: mask bytes and every small load (none conditional), then
+  // the tile test, then the E stream.
   const uint32_t mq = sc.query_mask_byte();
   const uint32_t mk = sc.key_mask_byte(jt);
+  Updater<T, H, DE> up;
+  up.init(a, li, lg);
   float A[H][4];
-  ETile<T, DE> et;
-  uint32_t bits;
+  Frag<T, DH / 4> kf[H];
+  float L[H];
   if constexpr (MODE == kRecompute) {
     sc.load_weights(a);
-    Frag<T, DH / 4> kf[H];
     sc.load_k(jt, kf);
-    float L[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)b * H + h) * NP + i];
-    sc.mi = mq != 0u;
-    bits = key_bits(mk);
-    et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
+  } else {
+    // entries outside the n x n map read entry (0, 0) of the head and are zeroed
+    const T* Ag = static_cast<const T*>(a.A);
+    const int jb = j0 + 4 * lg;
+    if ((n & 3) == 0) {  // uniform: 4 consecutive keys in or out together
+      const bool ok = jt < JT && i < n && jb < n;
+      Frag<T, 4> f[H];
+#pragma unroll
+      for (int h = 0; h < H; ++h) f[h].load(Ag + ((size_t)b * H + h) * n * n + (ok ? (size_t)i * n + jb : 0));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A[h][r] = ok ? f[h].get(r) : 0.f;
+    } else {
+      T raw[H][4];
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = jt < JT && i < n && jb + r < n;
+          raw[h][r] = Ag[((size_t)b * H + h) * n * n + (ok ? (size_t)i * n + jb + r : 0)];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = jt < JT && i < n && jb + r < n;
+          A[h][r] = ok ? Num<T>::ld(&raw[h][r]) : 0.f;
+        }
+    }
+  }
+  sc.mi = mq != 0u;
+  const uint32_t bits = key_bits(mk);
+  if ((__ballot(sc.mi) & 0xffffull) == 0ull || bits == 0u) {  // no real pair in the tile (uniform): zeros only
+    if (jt < JT) zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, j0, lg);
+    return;
+  }
+  ETile<T, DE> et;
+  if constexpr (kKeepE) et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
+  if constexpr (MODE == kRecompute) {
     float u[H][4];
-    sc.logits(et, kf, bits, u);
+    if constexpr (kKeepE) sc.logits(et, kf, bits, u);
+    else sc.logits_streamed(j0, kf, bits, u);
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : Num<T>::rnd(__expf(u[h][r] - L[h]));
-  } else {
-    const T* Ag = static_cast<const T*>(a.A);
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      const T* row = Ag + (((size_t)b * H + h) * n + i) * n + j0 + 4 * lg;
-      if (jt < JT && i < n && (n & 3) == 0 && j0 + 4 * lg + 3 < n) {
-        Frag<T, 4> f;
-        f.load(row);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) A[h][r] = f.get(r);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          A[h][r] = (jt < JT && i < n && j0 + 4 * lg + r < n) ? Num<T>::ld(row + r) : 0.f;
-      }
-    }
-    sc.mi = mq != 0u;
-    bits = key_bits(mk);
-    if (kKeepE) et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
   }
-  Updater<T, H, DE> up;
-  up.init(a, li, lg);
+  up.finish();
   const bool full = tile_full(sc.mi, bits);
   if (jt < JT)
     up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, A);
