@@ -511,9 +511,11 @@ struct Scorer {
   }
   // Queries, FiLM weights and biases, global FiLM coefficients.
   __device__ __forceinline__ void load_weights(const LayerArgs& a) {
-    const T* Qw = static_cast<const T*>(a.Qw);
-#pragma unroll
-    for (int h = 0; h < H; ++h) qf[h].load(Qw + (((size_t)b * H + h) * NP + i) * DH + lg * (DH / 4));
+    load_film(a);
+    load_queries(a);
+  }
+  // Edge-FiLM weights and biases (all the score stage needs besides E).
+  __device__ __forceinline__ void load_film(const LayerArgs& a) {
     const T* wrow = li < H ? static_cast<const T*>(a.w_emul) + (size_t)li * DE
                   : static_cast<const T*>(a.w_eadd) + (size_t)(li - H) * DE;
     wf.load(li < 2 * H ? wrow + lg * (DE / 4) : zeros<T>());
@@ -521,9 +523,16 @@ struct Scorer {
     static_assert(H % 4 == 0, "heads");
     const int r0 = 4 * lg;
     fb.load(r0 < H ? elem_or_zero<T>(a.b_emul, r0, true) : elem_or_zero<T>(a.b_eadd, r0 - H, r0 < 2 * H));
+  }
+  // Query fragments and the graph's global FiLM coefficients.
+  __device__ __forceinline__ void load_queries(const LayerArgs& a) {
+    const T* Qw = static_cast<const T*>(a.Qw);
+#pragma unroll
+    for (int h = 0; h < H; ++h) qf[h].load(Qw + (((size_t)b * H + h) * NP + i) * DH + lg * (DH / 4));
 #pragma unroll
     for (int o = 0; o < 2 * H; ++o) gy[o] = a.gy[(size_t)b * 2 * H + o];
   }
+
   // K and V fragments of key tile jt. A tile past the padded size reads tile
   // JT-1 instead: its keys are masked (all logits -inf, all A exactly 0), and
   // workspace K and V values are finite, so they add nothing.
@@ -803,30 +812,34 @@ struct Updater {
   }
 };
 
+// Row pitch (floats) of the O partials in LDS: 4 floats of padding put the
+// 16-byte writes of 8 consecutive query rows on distinct banks.
+template <int D>
+constexpr int kOPitch = D + 4;
+
 // Cross-wave reduction of the per-wave O^T partials and the store of O rows.
+// Lane (li, lg) holds O[i0 + li][h*DH + 16*tc + 4*lg + r] in oacc[h][tc][r]:
+// 4 consecutive channels, written to LDS as one 16-byte row piece.
 template <typename T, int H, int DH>
 __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, const f32x4 (&oacc)[H][DH / 16],
                                                int b, int i0, int w, int li, int lg, uint32_t qbits) {
-  constexpr int D = H * DH;
-  constexpr int P = 17;  // padded pitch of a 16-query row
+  constexpr int D = H * DH, OP = kOPitch<D>;
 #pragma unroll
   for (int h = 0; h < H; ++h)
 #pragma unroll
     for (int tc = 0; tc < DH / 16; ++tc)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) os[((w * D) + h * DH + tc * 16 + 4 * lg + r) * P + li] = oacc[h][tc][r];
+      *reinterpret_cast<f32x4*>(os + (w * 16 + li) * OP + h * DH + tc * 16 + 4 * lg) = oacc[h][tc];
   __syncthreads();
   for (int idx = threadIdx.x; idx < 16 * D / 4; idx += kThreads) {
     const int il = idx / (D / 4), c = (idx % (D / 4)) * 4, ii = i0 + il;
     if (ii >= a.n) continue;
+    f32x4 s = *reinterpret_cast<const f32x4*>(os + il * OP + c);
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) s += *reinterpret_cast<const f32x4*>(os + (ww * 16 + il) * OP + c);
+    const bool real = (qbits >> il) & 1u;
     float v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float s = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) s += os[(ww * D + c + k) * P + il];
-      v[k] = ((qbits >> il) & 1u) ? s : 0.f;
-    }
+    for (int k = 0; k < 4; ++k) v[k] = real ? s[k] : 0.f;
     Frag<T, 4> o;
     o.set(v);
     o.store(static_cast<T*>(a.O) + ((size_t)b * a.n + ii) * D + c);
@@ -956,7 +969,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
   constexpr int D = H * DH;
   constexpr bool kKeepE = MODE == kFused && MAXT == 1 && sizeof(T) == 2;
   static_assert(D <= 256 && 2 * H <= 16, "shape");
-  __shared__ __align__(16) float os_s[kWaves * D * 17];  // O^T partials of each wave
+  __shared__ __align__(16) float os_s[kWaves * 16 * kOPitch<D>];  // O partials of each wave
   __shared__ float red_s[2][kWaves][H][16];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
