@@ -30,6 +30,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -673,6 +674,7 @@ struct Updater {
   static constexpr bool kBF = sizeof(T) == 2;
   static constexpr int QH = kBF ? 4 : H / 4;  // heads per lane group
   static constexpr int NCH = DE / 16;
+  static constexpr int RW = kBF ? 8 : 4 * QH;  // 32-bit words per key group of the head operand
   Frag<T, QH> wef[NCH];
   Frag<T, 4> eye;                    // identity rows li, slots 4*lg .. 4*lg+3 (bfloat16)
   T bl[kBF ? NCH : 1];               // raw b_e values of the bias lane group (bfloat16)
@@ -712,22 +714,42 @@ struct Updater {
 
   // KEEP: et holds the tile's E fragments; otherwise E is read here.
   // bits: real keys of the tile; full: every pair of the tile is real.
+  // A: this lane's attention values in the storage type, keys 4*lg .. 4*lg+3
+  // of each head (the layout of the A store and of the A V operand).
   template <bool KEEP>
   __device__ __forceinline__ void tile(const ETile<T, DE>& et, const T* E, T* Eout, int b, int n, int i,
                                        bool mi, int j0, int lg, uint32_t bits, bool full,
-                                       const float (&A)[H][4]) const {
-    float R[4][4 * QH];  // R[x][r'*QH + q]: key 4*lg + r', head x*QH + q
+                                       const Frag<T, 4> (&A)[H]) const {
+    float R[4][RW];
+    if constexpr (kBF) {
+      // R[x][2*r' + q2]: packed bfloat16 pair (head 4x + 2q2, head 4x + 2q2 + 1)
+      // of key 4*lg + r'; slot H holds 1 (against b_e), the rest 0
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int rp = 0; rp < 4; ++rp)
+        for (int rp = 0; rp < 4; ++rp)
 #pragma unroll
-        for (int q = 0; q < QH; ++q) {
-          const int h = x * QH + q;
-          R[x][rp * QH + q] = h < H ? A[h][rp] : (kBF && h == H) ? 1.f : 0.f;
-        }
-    // now R[x][r'*QH + q]: key 4*x + r', head lg*QH + q
-    lane_group_transpose<4 * QH>(R);
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int h0 = 4 * x + 2 * q2;
+            uint32_t v = h0 == H ? 0x3f80u : 0u;  // bfloat16 1.0 in the low half
+            if (h0 < H)  // H is even: key r' of heads h0 and h0 + 1, taken from their key pairs
+              v = __builtin_amdgcn_perm(A[h0 + 1].w[rp >> 1], A[h0].w[rp >> 1], (rp & 1) ? 0x07060302u : 0x05040100u);
+            R[x][2 * rp + q2] = __uint_as_float(v);
+          }
+    } else {
+      // R[x][r'*QH + q]: key 4*lg + r', head x*QH + q
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int rp = 0; rp < 4; ++rp)
+#pragma unroll
+          for (int q = 0; q < QH; ++q) {
+            const int h = x * QH + q;
+            R[x][rp * QH + q] = h < H ? A[h].get(rp) : 0.f;
+          }
+    }
+    // now block x of lane group lg: key 4*x + r', heads lg*QH .. (lg+1)*QH - 1
+    lane_group_transpose<RW>(R);
     const size_t rowoff = ((size_t)b * n + i) * n * DE + lg * (DE / 4);
     if (bits == 0u) {  // no real pair in the tile (uniform): zeros only
       zero_edge_tile<T, DE>(Eout, b, n, i, j0, lg);
@@ -783,9 +805,14 @@ struct Updater {
   // One key of the tile: ef holds this lane's E channels of pair (i, j).
   template <bool FULL>
   __device__ __forceinline__ void step(const Frag<T, DE / 4>& ef, T* Eout, size_t off, bool inb, bool real,
-                                       const float (&R)[4][4 * QH], int jj) const {
+                                       const float (&R)[4][RW], int jj) const {
     Frag<T, QH> af;
-    if (has_heads) af.set(&R[jj >> 2][(jj & 3) * QH]); else af.zero();
+    if constexpr (kBF) {
+      af.w[0] = has_heads ? __float_as_uint(R[jj >> 2][2 * (jj & 3)]) : 0u;
+      af.w[1] = has_heads ? __float_as_uint(R[jj >> 2][2 * (jj & 3) + 1]) : 0u;
+    } else {
+      if (has_heads) af.set(&R[jj >> 2][(jj & 3) * QH]); else af.zero();
+    }
     float out[DE / 4];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
@@ -866,6 +893,9 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
                                           Updater<T, H, DE>& up) {
   const int w = threadIdx.x >> 6, li = sc.li, lg = sc.lg;
   const int b = sc.b, n = a.n, JT = sc.JT, i = sc.i, i0 = i - li;
+  // several tiles: the first tile's V now (no wait in the softmax covers it),
+  // each next one right after the previous A V, ahead of that tile's A stores
+  if constexpr (MAXT > 1) sc.load_v(w, vf);
   f32x4 oacc[H][DH / 16];
 #pragma unroll
   for (int h = 0; h < H; ++h)
@@ -888,12 +918,15 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
     float M = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_s[0][ww][h][li]);
+    // exp(u - M) as 2^(u log2 e - M log2 e): one FMA and one v_exp_f32; masked
+    // logits (-inf) give exactly 0, and a row without real keys takes M = 0
+    const float mb = (M == kNegInf) ? 0.f : M * kLog2e;
     float s = 0.f;
 #pragma unroll
     for (int tt = 0; tt < MAXT; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = (u[tt][h][r] == kNegInf) ? 0.f : __expf(u[tt][h][r] - M);
+        const float p = __builtin_amdgcn_exp2f(fmaf(u[tt][h][r], kLog2e, -mb));
         u[tt][h][r] = p;
         s += p;
       }
@@ -906,42 +939,47 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
     float L = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) L += red_s[1][ww][h][li];
-    inv[h] = (L > 0.f) ? 1.f / L : 0.f;
+    // 1 / L on the reciprocal unit (about 1 ulp; the quotient feeds a
+    // bfloat16 or a 1e-4-relative float32 result)
+    inv[h] = (L > 0.f) ? __builtin_amdgcn_rcpf(L) : 0.f;
   }
   T* Ag = static_cast<T*>(a.A);
+  // A in the storage type, once: the same fragments are stored, feed A V and
+  // feed the edge update
+  Frag<T, 4> ak[MAXT][H];
 #pragma unroll
   for (int tt = 0; tt < MAXT; ++tt) {
     const int jt = w + kWaves * tt, j0 = 16 * jt;
 #pragma unroll
-    for (int h = 0; h < H; ++h)
+    for (int h = 0; h < H; ++h) {
+      float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[tt][h][r] = Num<T>::rnd(u[tt][h][r] * inv[h]);
+      for (int r = 0; r < 4; ++r) p[r] = u[tt][h][r] * inv[h];
+      ak[tt][h].set(p);
+    }
     if (jt < JT) {
-      if (i < n) {
-        const int jb = j0 + 4 * lg;
+      const int jb = j0 + 4 * lg;
+      if ((n & 3) == 0) {  // uniform: 4 keys in or out together, one vector store
+        if (i < n && jb < n) {
+#pragma unroll
+          for (int h = 0; h < H; ++h) ak[tt][h].store(Ag + (((size_t)b * H + h) * n + i) * n + jb);
+        }
+      } else if (i < n) {
 #pragma unroll
         for (int h = 0; h < H; ++h) {
           T* row = Ag + (((size_t)b * H + h) * n + i) * n;
-          if ((n & 3) == 0 && jb + 3 < n) {
-            Frag<T, 4> f;
-            f.set(u[tt][h]);
-            f.store(row + jb);
-          } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (jb + r < n) Num<T>::st(row + jb + r, u[tt][h][r]);
-          }
+          for (int r = 0; r < 4; ++r)
+            if (jb + r < n) Num<T>::st(row + jb + r, ak[tt][h].get(r));
         }
       }
-      if constexpr (MAXT > 1) sc.load_v(jt, vf);  // with one tile, loaded by the caller
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
-        Frag<T, 4> af;
-        af.set(u[tt][h]);
+      for (int h = 0; h < H; ++h)
 #pragma unroll
-        for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = mma(oacc[h][tc], vf[h][tc], af);
-      }
+        for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = mma(oacc[h][tc], vf[h][tc], ak[tt][h]);
     }
+    if constexpr (MAXT > 1)
+      if (tt + 1 < MAXT) sc.load_v(w + kWaves * (tt + 1), vf);
   }
   if constexpr (MODE == kFused) {
     up.finish();
@@ -951,7 +989,7 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
       const bool full = tile_full(sc.mi, bits[tt]);
       if (jt < JT)
         up.template tile<KEEP_E>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, 16 * jt, lg, bits[tt], full,
-                                 u[tt]);
+                                 ak[tt]);
     }
   }
   reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg, (uint32_t)(__ballot(sc.mi) & 0xffffull));
@@ -1234,12 +1272,15 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
     for (int h = 0; h < H; ++h)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : Num<T>::rnd(__expf(u[h][r] - L[h]));
+        A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : __expf(u[h][r] - L[h]);
   }
   up.finish();
   const bool full = tile_full(sc.mi, bits);
+  Frag<T, 4> ak[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) ak[h].set(A[h]);
   if (jt < JT)
-    up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, A);
+    up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak);
 }
 
 // ------------------------------------------------------------------ dispatch
