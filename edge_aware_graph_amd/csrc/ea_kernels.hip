@@ -716,10 +716,12 @@ struct Updater {
   // bits: real keys of the tile; full: every pair of the tile is real.
   // A: this lane's attention values in the storage type, keys 4*lg .. 4*lg+3
   // of each head (the layout of the A store and of the A V operand).
-  template <bool KEEP>
+  // mid() runs once, after the first 8 keys (every caller's wave must reach
+  // it exactly once: it may hold a barrier).
+  template <bool KEEP, typename Mid>
   __device__ __forceinline__ void tile(const ETile<T, DE>& et, const T* E, T* Eout, int b, int n, int i,
                                        bool mi, int j0, int lg, uint32_t bits, bool full,
-                                       const Frag<T, 4> (&A)[H]) const {
+                                       const Frag<T, 4> (&A)[H], Mid&& mid) const {
     float R[4][RW];
     if constexpr (kBF) {
       // R[x][2*r' + q2]: packed bfloat16 pair (head 4x + 2q2, head 4x + 2q2 + 1)
@@ -753,6 +755,7 @@ struct Updater {
     const size_t rowoff = ((size_t)b * n + i) * n * DE + lg * (DE / 4);
     if (bits == 0u) {  // no real pair in the tile (uniform): zeros only
       zero_edge_tile<T, DE>(Eout, b, n, i, j0, lg);
+      mid();
       return;
     }
     const uint32_t okj = mi ? bits : 0u;  // bit jj: pair (i, j0 + jj) is real
@@ -760,15 +763,21 @@ struct Updater {
     if constexpr (KEEP) {
       if (full) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) step<true>(et.f[jj], Eout, rowoff + (size_t)(j0 + jj) * DE, true, true, R, jj);
+        for (int jj = 0; jj < 16; ++jj) {
+          if (jj == 8) mid();
+          step<true>(et.f[jj], Eout, rowoff + (size_t)(j0 + jj) * DE, true, true, R, jj);
+        }
       } else {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
+        for (int jj = 0; jj < 16; ++jj) {
+          if (jj == 8) mid();
           step<false>(et.f[jj], Eout, rowoff + (size_t)(j0 + jj) * DE, iin & (j0 + jj < n), (okj >> jj) & 1u, R, jj);
+        }
       }
     } else if constexpr (kBF) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
+        if (jj == 8) mid();
         const size_t off = rowoff + (size_t)(j0 + jj) * DE;
         const bool real = (okj >> jj) & 1u;
         Frag<T, DE / 4> ef;
@@ -790,6 +799,7 @@ struct Updater {
       load_group(eg[0], 0);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (g == 2) mid();
         if (g < 3) load_group(eg[(g + 1) & 1], g + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -847,16 +857,19 @@ constexpr int kOPitch = D + 4;
 // Cross-wave reduction of the per-wave O^T partials and the store of O rows.
 // Lane (li, lg) holds O[i0 + li][h*DH + 16*tc + 4*lg + r] in oacc[h][tc][r]:
 // 4 consecutive channels, written to LDS as one 16-byte row piece.
-template <typename T, int H, int DH>
-__device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, const f32x4 (&oacc)[H][DH / 16],
-                                               int b, int i0, int w, int li, int lg, uint32_t qbits) {
+template <int H, int DH>
+__device__ __forceinline__ void o_partials_to_lds(float* os, const f32x4 (&oacc)[H][DH / 16], int w, int li, int lg) {
   constexpr int D = H * DH, OP = kOPitch<D>;
 #pragma unroll
   for (int h = 0; h < H; ++h)
 #pragma unroll
     for (int tc = 0; tc < DH / 16; ++tc)
       *reinterpret_cast<f32x4*>(os + (w * 16 + li) * OP + h * DH + tc * 16 + 4 * lg) = oacc[h][tc];
-  __syncthreads();
+}
+// After a barrier that follows every wave's o_partials_to_lds.
+template <typename T, int H, int DH>
+__device__ __forceinline__ void o_reduce_store(const LayerArgs& a, const float* os, int b, int i0, uint32_t qbits) {
+  constexpr int D = H * DH, OP = kOPitch<D>;
   for (int idx = threadIdx.x; idx < 16 * D / 4; idx += kThreads) {
     const int il = idx / (D / 4), c = (idx % (D / 4)) * 4, ii = i0 + il;
     if (ii >= a.n) continue;
@@ -871,6 +884,13 @@ __device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, co
     o.set(v);
     o.store(static_cast<T*>(a.O) + ((size_t)b * a.n + ii) * D + c);
   }
+}
+template <typename T, int H, int DH>
+__device__ __forceinline__ void reduce_store_O(const LayerArgs& a, float* os, const f32x4 (&oacc)[H][DH / 16],
+                                               int b, int i0, int w, int li, int lg, uint32_t qbits) {
+  o_partials_to_lds<H, DH>(os, oacc, w, li, lg);
+  __syncthreads();
+  o_reduce_store<T, H, DH>(a, os, b, i0, qbits);
 }
 
 // Whether all 16 queries of the block and all 16 keys of the tile are real.
@@ -981,18 +1001,35 @@ __device__ __forceinline__ void attn_rest(const LayerArgs& a, const Scorer<T, H,
     if constexpr (MAXT > 1)
       if (tt + 1 < MAXT) sc.load_v(w + kWaves * (tt + 1), vf);
   }
+  const uint32_t qbits = (uint32_t)(__ballot(sc.mi) & 0xffffull);
   if constexpr (MODE == kFused) {
+    // O's cross-wave reduction runs between the two halves of the first
+    // tile's update, while the first half's E' stores drain
+    o_partials_to_lds<H, DH>(os_s, oacc, w, li, lg);
+    auto reduce_O = [&] {
+      __syncthreads();
+      o_reduce_store<T, H, DH>(a, os_s, b, i0, qbits);
+    };
+    auto nothing = [] {};
     up.finish();
 #pragma unroll
     for (int tt = 0; tt < MAXT; ++tt) {
       const int jt = w + kWaves * tt;
       const bool full = tile_full(sc.mi, bits[tt]);
-      if (jt < JT)
+      if (tt == 0) {
+        if (jt < JT)
+          up.template tile<KEEP_E>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, 16 * jt, lg, bits[tt], full,
+                                   ak[tt], reduce_O);
+        else
+          reduce_O();
+      } else if (jt < JT) {
         up.template tile<KEEP_E>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, 16 * jt, lg, bits[tt], full,
-                                 ak[tt]);
+                                 ak[tt], nothing);
+      }
     }
+  } else {
+    reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg, qbits);
   }
-  reduce_store_O<T, H, DH>(a, os_s, oacc, b, i0, w, li, lg, (uint32_t)(__ballot(sc.mi) & 0xffffull));
 }
 
 // One block per (graph, 16-query block); wave w owns key tiles w, w+4, ... .
@@ -1280,7 +1317,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
 #pragma unroll
   for (int h = 0; h < H; ++h) ak[h].set(A[h]);
   if (jt < JT)
-    up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak);
+    up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak, [] {});
 }
 
 // ------------------------------------------------------------------ dispatch
