@@ -239,6 +239,46 @@ __device__ __forceinline__ void lane_group_transpose(float (&R)[4][NE]) {
 
 // ------------------------------------------------------------------ QKV
 
+// Global FiLM coefficients gamma_y = 1 + W_ymul y + b_ymul and
+// beta_y = W_yadd y + b_yadd of the graphs whose slot 0 lies in rows
+// [m0, m0 + mrows) of the padded batch; 16 lanes per coefficient (2H <= 16),
+// loads batched.
+template <typename T, int H>
+__device__ __forceinline__ void global_film(const LayerArgs& a, uint32_t m0, uint32_t mrows, uint32_t rows) {
+  const uint32_t NP = a.NP;
+  const int tid = threadIdx.x, o = tid >> 4, part = tid & 15;
+  const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)(o % H) * a.dy;
+  for (uint32_t m = (m0 + NP - 1) / NP * NP; m < m0 + mrows && m < rows; m += NP) {
+    const uint32_t b = m / NP;
+    const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
+    float acc = 0.f;
+    if (o < 2 * H) {
+      constexpr int kBatch = 8;
+      for (int c0 = 0; c0 < a.dy; c0 += 16 * kBatch) {
+        float yv[kBatch], wv[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int c = c0 + part + 16 * k;
+          const float yl = Num<T>::ld(yb + (c < a.dy ? c : 0));
+          const float wl = Num<T>::ld(Wy + (c < a.dy ? c : 0));
+          yv[k] = c < a.dy ? yl : 0.f;
+          wv[k] = c < a.dy ? wl : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) acc += yv[k] * wv[k];
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 8);
+    if (o < 2 * H && part == 0) {
+      const float bias = ld_or0<T>(o < H ? a.b_ymul : a.b_yadd, o % H);
+      a.gy[(size_t)b * 2 * H + o] = o < H ? 1.f + (bias + acc) : bias + acc;
+    }
+  }
+}
+
 // Q | K | V = X W^T + b for rows (b, i) of the padded batch; rows of padded
 // nodes and the slots i in [n, NP) are written as zeros. Q, K: [B, H, NP, DH];
 // V transposed: [B, H, DH, NP]. One block computes a 64-row x 64-feature tile:
@@ -264,40 +304,8 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   const uint32_t rows = (uint32_t)a.B * NP;  // < 2^31 (checked at context creation)
   const uint32_t m0 = blockIdx.x * 64u;
   const int f0 = blockIdx.y * 64;
-  if (f0 >= 3 * D) {
-    // extra column of blocks: global FiLM of the graphs whose slot 0 lies in
-    // this row block; 16 lanes per coefficient (2H <= 16), loads batched
-    const int o = tid >> 4, part = tid & 15;
-    const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)(o % H) * a.dy;
-    for (uint32_t m = (m0 + NP - 1) / NP * NP; m < m0 + 64 && m < rows; m += NP) {
-      const uint32_t b = m / NP;
-      const T* yb = static_cast<const T*>(a.y) + (size_t)b * a.dy;
-      float acc = 0.f;
-      if (o < 2 * H) {
-        constexpr int kBatch = 8;
-        for (int c0 = 0; c0 < a.dy; c0 += 16 * kBatch) {
-          float yv[kBatch], wv[kBatch];
-#pragma unroll
-          for (int k = 0; k < kBatch; ++k) {
-            const int c = c0 + part + 16 * k;
-            const float yl = Num<T>::ld(yb + (c < a.dy ? c : 0));
-            const float wl = Num<T>::ld(Wy + (c < a.dy ? c : 0));
-            yv[k] = c < a.dy ? yl : 0.f;
-            wv[k] = c < a.dy ? wl : 0.f;
-          }
-#pragma unroll
-          for (int k = 0; k < kBatch; ++k) acc += yv[k] * wv[k];
-        }
-      }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 4);
-      acc += __shfl_xor(acc, 8);
-      if (o < 2 * H && part == 0) {
-        const float bias = ld_or0<T>(o < H ? a.b_ymul : a.b_yadd, o % H);
-        a.gy[(size_t)b * 2 * H + o] = o < H ? 1.f + (bias + acc) : bias + acc;
-      }
-    }
+  if (f0 >= 3 * D) {  // extra column of blocks
+    global_film<T, H>(a, m0, 64u, rows);
     return;
   }
   const int which = f0 / D, fl0 = f0 % D;
@@ -603,7 +611,6 @@ struct Scorer {
     scores(R, kf, bits, u);
   }
 
- private:
   __device__ __forceinline__ static void no_keys(float (&u)[H][4]) {
 #pragma unroll
     for (int h = 0; h < H; ++h)
@@ -626,6 +633,17 @@ struct Scorer {
   // From the FiLM rows of the 16 keys to the masked logits.
   __device__ __forceinline__ void scores(float (&R)[4][16], const Frag<T, DH / 4> (&kf)[H], uint32_t bits,
                                          float (&u)[H][4]) const {
+    f32x4 S[H];
+    qk(kf, S);
+    scores_from(R, S, bits, u);
+  }
+  // S^T = K Q^T per head: lane (li, lg) gets query i0 + li, keys 4*lg + r.
+  __device__ __forceinline__ void qk(const Frag<T, DH / 4> (&kf)[H], f32x4 (&S)[H]) const {
+#pragma unroll
+    for (int h = 0; h < H; ++h) S[h] = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kf[h], qf[h]);
+  }
+  __device__ __forceinline__ void scores_from(float (&R)[4][16], const f32x4 (&S)[H], uint32_t bits,
+                                              float (&u)[H][4]) const {
     // now R[x][4*r' + r]: key 4*lg + r', film row 4*x + r
     lane_group_transpose<16>(R);
     // real pairs of this lane (bit r: key 4*lg + r), as plain bit tests: a
@@ -634,12 +652,11 @@ struct Scorer {
     const uint32_t okb = (bits >> (4 * lg)) & (mi ? 0xfu : 0u);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const f32x4 s = mma(f32x4{0.f, 0.f, 0.f, 0.f}, kf[h], qf[h]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gam = R[h >> 2][4 * r + (h & 3)];
         const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)];
-        const float v = ((s[r] * scale) * gam + bet) * gy[h] + gy[H + h];
+        const float v = ((S[h][r] * scale) * gam + bet) * gy[h] + gy[H + h];
         u[h][r] = ((okb >> r) & 1u) ? v : kNegInf;
       }
     }
@@ -1069,6 +1086,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
     float m_run[H], l_run[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) { m_run[h] = kNegInf; l_run[h] = 0.f; }
+    // online softmax step for one key tile with logits u and its V fragments
+    auto online_step = [&](float (&u)[H][4], const Frag<T, 4> (&vf)[H][DH / 16]) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const float tm = lg_max(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
+        const float mnew = fmaxf(m_run[h], tm);
+        const float alpha = (mnew == kNegInf) ? 1.f : __expf(m_run[h] - mnew);
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = (u[h][r] == kNegInf) ? 0.f : __expf(u[h][r] - mnew);
+          ps += p[r];
+        }
+        l_run[h] = l_run[h] * alpha + ps;
+        m_run[h] = mnew;
+        Frag<T, 4> af;
+        af.set(p);
+#pragma unroll
+        for (int tc = 0; tc < DH / 16; ++tc) {
+          oacc[h][tc] *= alpha;
+          oacc[h][tc] = mma(oacc[h][tc], vf[h][tc], af);
+        }
+      }
+    };
     for (int jt = w; jt < JT; jt += kWaves) {
       const uint32_t bits = key_bits(mk);
       if (bits == 0u || !sc.mi_any) {  // tile without real pairs: the running statistics do not change
@@ -1091,27 +1132,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
         sc.logits_streamed(16 * jt, kf, bits, u);
         sc.load_v(jt, vf);
       }
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        const float tm = lg_max(fmaxf(fmaxf(u[h][0], u[h][1]), fmaxf(u[h][2], u[h][3])));
-        const float mnew = fmaxf(m_run[h], tm);
-        const float alpha = (mnew == kNegInf) ? 1.f : __expf(m_run[h] - mnew);
-        float p[4], ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = (u[h][r] == kNegInf) ? 0.f : __expf(u[h][r] - mnew);
-          ps += p[r];
-        }
-        l_run[h] = l_run[h] * alpha + ps;
-        m_run[h] = mnew;
-        Frag<T, 4> af;
-        af.set(p);
-#pragma unroll
-        for (int tc = 0; tc < DH / 16; ++tc) {
-          oacc[h][tc] *= alpha;
-          oacc[h][tc] = mma(oacc[h][tc], vf[h][tc], af);
-        }
-      }
+      online_step(u, vf);
     }
     // combine lane groups, then waves
 #pragma unroll
@@ -1233,16 +1254,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
 
 // ------------------------------------------------------------------ update kernel
 
-// Grid (NP/16 query blocks, B, ceil(NP/64)); wave w of block z takes key tile
-// 4*z + w. kReadA reads A from the forward's output; kRecompute re-runs the
+// Grid (NP/16 query blocks x ceil(NP/64) key groups, B), key group fastest:
+// wave w of key group z takes key tile 4*z + w. Blocks running together then
+// cover whole rows of E (contiguous memory) rather than one column stripe of
+// many rows. kReadA reads A from the forward's output; kRecompute re-runs the
 // score stage and takes A = exp(u - lse) from pass 1's statistics. The E
 // fragments of the tile are read once (bfloat16) and serve both stages.
 template <typename T, int H, int DH, int DE, int MODE>
 __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int b = blockIdx.y, i0 = blockIdx.x * 16, i = i0 + li;
+  const int KG = (a.NP + kWaves * 16 - 1) / (kWaves * 16);  // key groups
+  const int b = blockIdx.y, i0 = (blockIdx.x / KG) * 16, i = i0 + li;
   const int n = a.n, NP = a.NP, JT = NP / 16;
-  const int jt = blockIdx.z * kWaves + w, j0 = 16 * jt;
+  const int jt = (blockIdx.x % KG) * kWaves + w, j0 = 16 * jt;
   constexpr bool kKeepE = sizeof(T) == 2;
   Scorer<T, H, DH, DE> sc;
   sc.setup(a, b, i0);
@@ -1251,15 +1275,14 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   const uint32_t mq = sc.query_mask_byte();
   const uint32_t mk = sc.key_mask_byte(jt);
   Updater<T, H, DE> up;
-  up.init(a, li, lg);
+  // recompute mode: the update weights and the row statistics are loaded
+  // after the score stage (not live next to the E tile and the FiLM rows)
+  if constexpr (MODE != kRecompute) up.init(a, li, lg);
   float A[H][4];
   Frag<T, DH / 4> kf[H];
-  float L[H];
   if constexpr (MODE == kRecompute) {
     sc.load_weights(a);
     sc.load_k(jt, kf);
-#pragma unroll
-    for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)b * H + h) * NP + i];
   } else {
     // entries outside the n x n map read entry (0, 0) of the head and are zeroed
     const T* Ag = static_cast<const T*>(a.A);
@@ -1303,8 +1326,24 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   if constexpr (kKeepE) et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
   if constexpr (MODE == kRecompute) {
     float u[H][4];
-    if constexpr (kKeepE) sc.logits(et, kf, bits, u);
-    else sc.logits_streamed(j0, kf, bits, u);
+    if constexpr (kKeepE) {
+      // S first, so that K and Q are dead while the E tile and the FiLM rows
+      // are live (two waves per SIMD fit in the register file)
+      f32x4 S[H];
+      sc.qk(kf, S);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 fc = sc.film_start();
+      float R[4][16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) sc.film(et.f[jj], fc, R, jj);
+      sc.scores_from(R, S, bits, u);
+    } else {
+      sc.logits_streamed(j0, kf, bits, u);
+    }
+    up.init(a, li, lg);
+    float L[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)b * H + h) * NP + i];
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
@@ -1353,7 +1392,7 @@ hipError_t attn_shape(const LayerArgs& a, int mode, hipStream_t s) {
 template <typename T, int H, int DH, int DE>
 hipError_t update_shape(const LayerArgs& a, int mode, hipStream_t s) {
   const int JT = a.NP / 16;
-  const dim3 grid(JT, a.B, (JT + kWaves - 1) / kWaves);
+  const dim3 grid((unsigned)JT * ((JT + kWaves - 1) / kWaves), a.B);  // < 2^31 for n <= 2^20
   if (mode == kReadA)
     hipLaunchKernelGGL((update_kernel<T, H, DH, DE, kReadA>), grid, dim3(kThreads), 0, s, a);
   else if (mode == kRecompute)

@@ -126,6 +126,19 @@ def test_ragged_sizes_random_masks(n, dtype):
     run_case("planar", dims, batch=batch)
 
 
+@pytest.mark.parametrize("n,dtype", [(37, "bf16"), (250, "bf16"), (100, "fp32")])
+def test_forced_two_pass_ragged_random_masks(n, dtype):
+    """The two-pass scheme with n not a multiple of 16 and non-prefix node masks."""
+    dims = dims_of("planar", n=n, B=3, dtype=dtype)
+    batch = W.make_batch("tiny", bias_scale=0.2, dims=dims)
+    rng = np.random.default_rng(1000 + n)
+    mask = (rng.random((3, n)) < 0.7).astype(np.uint8)
+    mask[0] = 1
+    mask[2] = 0
+    batch["mask"] = mask
+    run_case("planar", dims, batch=batch, force_two_pass=True)
+
+
 def test_all_masked_and_single_node_graphs():
     dims = dims_of("planar", n=20, B=3)
     batch = W.make_batch("planar", bias_scale=0.2, dims=dims)
