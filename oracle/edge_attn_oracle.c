@@ -35,6 +35,19 @@
  *     use; everything else stays in double here (the oracle does not round
  *     its outputs).
  *
+ * Ablation variants (dims.variant bits). The summary section of the same page
+ * reports ablations of the layer: without the per-edge modulation ("Light
+ * Edge") the model does not learn, neither the edge update nor the score
+ * modulation can be dropped, and normalized attention coefficients converge
+ * more stably than unnormalized ones. Readings taken, each the plainest one:
+ *   - 1, light edge: no per-edge FiLM, gamma_e = 1 and beta_e = 0 (the
+ *     global FiLM stays): u = s * gamma_y + beta_y;
+ *   - 2, no score modulation: neither FiLM, u = s (masked SDPA);
+ *   - 4, unnormalized update: the edge update takes the coefficients before
+ *     normalization, i.e. the masked logits u themselves (0 at masked pairs),
+ *     E'_ij = E_ij + W_e u_ij + b_e; O and A stay normalized. In bf16 mode
+ *     that operand is rounded to bfloat16 like A is.
+ *
  * Parity status: every function below is pinned by the CPU test suite
  * (closed forms, a hand-worked example, library SDPA special cases, mask
  * enumeration, invariants). Absolute agreement with the authors' trained layer
@@ -50,8 +63,11 @@
 
 typedef struct {
   int32_t B, n, d, de, dy, H, dh;
-  int32_t bf16; /* 1: apply the bfloat16 rounding points */
+  int32_t bf16;    /* 1: apply the bfloat16 rounding points */
+  int32_t variant; /* ablation bits: 1 light edge, 2 no score modulation, 4 unnormalized update */
 } eao_dims;
+
+enum { EAO_LIGHT_EDGE = 1, EAO_NO_SCORE_MOD = 2, EAO_UNNORMALIZED = 4 };
 
 /* All weights float32 in nn.Linear layout [out, in]; any bias may be NULL. */
 typedef struct {
@@ -114,6 +130,7 @@ void eao_project(const eao_dims* dm, const float* X, const uint8_t* mask,
 static void global_film(const eao_dims* dm, const float* y, int b, const eao_params* p,
                         double* gamma_y, double* beta_y) {
   for (int h = 0; h < dm->H; ++h) {
+    if (dm->variant & EAO_NO_SCORE_MOD) { gamma_y[h] = 1.0; beta_y[h] = 0.0; continue; }
     double gm = bias_at(p->b_ymul, h), ga = bias_at(p->b_yadd, h);
     for (int c = 0; c < dm->dy; ++c) {
       double yc = y[(size_t)b * dm->dy + c];
@@ -146,10 +163,14 @@ static void layer_row(const eao_dims* dm, const float* E, const uint8_t* mask,
     for (int j = 0; j < n; ++j) {
       if (!(m[i] && m[j])) { u[j] = -INFINITY; continue; }
       const float* e = Erow + (size_t)j * de;
-      double gm = bias_at(p->b_emul, h), ga = bias_at(p->b_eadd, h);
-      for (int c = 0; c < de; ++c) {
-        gm += (double)e[c] * (double)p->w_emul[(size_t)h * de + c];
-        ga += (double)e[c] * (double)p->w_eadd[(size_t)h * de + c];
+      double gm = 0.0, ga = 0.0;
+      if (!(dm->variant & (EAO_LIGHT_EDGE | EAO_NO_SCORE_MOD))) {
+        gm = bias_at(p->b_emul, h);
+        ga = bias_at(p->b_eadd, h);
+        for (int c = 0; c < de; ++c) {
+          gm += (double)e[c] * (double)p->w_emul[(size_t)h * de + c];
+          ga += (double)e[c] * (double)p->w_eadd[(size_t)h * de + c];
+        }
       }
       const double gamma_e = 1.0 + gm, beta_e = ga;
       double s = 0.0;
@@ -183,14 +204,20 @@ static void layer_row(const eao_dims* dm, const float* E, const uint8_t* mask,
       O[h * dh + t] = acc;
     }
   }
-  /* residual edge update */
+  /* residual edge update, from A (or, unnormalized variant, from u) */
+  const int unnorm = (dm->variant & EAO_UNNORMALIZED) != 0;
   for (int j = 0; j < n; ++j) {
     double* ep = Ep + (size_t)j * de;
     if (!(m[i] && m[j])) { for (int c = 0; c < de; ++c) ep[c] = 0.0; continue; }
     const float* e = Erow + (size_t)j * de;
+    double coef[64];
+    for (int h = 0; h < H; ++h) {
+      coef[h] = A[(size_t)h * n + j];
+      if (unnorm) coef[h] = dm->bf16 ? eao_bf16_round(U[(size_t)h * n + j]) : U[(size_t)h * n + j];
+    }
     for (int c = 0; c < de; ++c) {
       double acc = (double)e[c] + bias_at(p->b_e, c);
-      for (int h = 0; h < H; ++h) acc += (double)p->w_e[(size_t)c * H + h] * A[(size_t)h * n + j];
+      for (int h = 0; h < H; ++h) acc += (double)p->w_e[(size_t)c * H + h] * coef[h];
       ep[c] = acc;
     }
   }

@@ -29,7 +29,11 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 class _Dims(ctypes.Structure):
-    _fields_ = [(k, ctypes.c_int32) for k in ("B", "n", "d", "de", "dy", "H", "dh", "bf16")]
+    _fields_ = [(k, ctypes.c_int32) for k in ("B", "n", "d", "de", "dy", "H", "dh", "bf16", "variant")]
+
+
+# Ablation variants (bits of ``variant``; the C file states the readings).
+LIGHT_EDGE, NO_SCORE_MOD, UNNORMALIZED = 1, 2, 4
 
 
 _PARAM_NAMES = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v",
@@ -94,18 +98,19 @@ def dims_of(batch: Dict[str, np.ndarray], H: int, bf16: bool) -> Tuple[int, ...]
 
 def forward(batch: Dict[str, np.ndarray], H: int, bf16: bool = False,
             rows: Optional[Sequence[Tuple[int, int]]] = None,
-            zero_bias_names: Sequence[str] = ()) -> Dict[str, np.ndarray]:
+            zero_bias_names: Sequence[str] = (), variant: int = 0) -> Dict[str, np.ndarray]:
     """Run the layer definition.
 
     ``batch`` holds X, E, y, mask and the weights (as drawn by the workload
     generator). With ``rows=None`` every (b, i) row is computed and the result
     has full shapes: O [B,n,d], A [B,H,n,n], Ep [B,n,n,de], U [B,H,n,n],
     lse [B,H,n]. With a list of (b, i) rows the result is compact:
-    O [R,d], A [R,H,n], Ep [R,n,de], U [R,H,n], lse [R,H].
+    O [R,d], A [R,H,n], Ep [R,n,de], U [R,H,n], lse [R,H]. ``variant`` is a
+    combination of LIGHT_EDGE, NO_SCORE_MOD and UNNORMALIZED.
     """
     lib = _load()
     B, n, d, de, dy, Hh, dh, bf = dims_of(batch, H, bf16)
-    dims = _Dims(B, n, d, de, dy, Hh, dh, bf)
+    dims = _Dims(B, n, d, de, dy, Hh, dh, bf, int(variant))
     X, E, y = _f32(batch["X"]), _f32(batch["E"]), _f32(batch["y"])
     mask = np.ascontiguousarray(batch["mask"], dtype=np.uint8)
     keep = {}

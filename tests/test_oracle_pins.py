@@ -397,3 +397,91 @@ def test_bf16_rounding_points_zero_film():
     o_ref = np.einsum("bhij,bhjt->bhit", out["A"], v.numpy()).transpose(0, 2, 1, 3).reshape(B, n, d)
     assert np.abs(out["O"][rr] - o_ref[rr]).max() < 1e-12
     assert np.abs(out["O"][rr] - o[rr]).max() < 4e-3
+
+
+# ------------------------------------------------------------------ ablation variants
+
+def global_gamma_beta(batch):
+    """gamma_y, beta_y [B,H] from torch Linear on y."""
+    g = 1.0 + F.linear(t64(batch["y"]), t64(batch["w_ymul"]), t64(batch["b_ymul"])).numpy()
+    bb = F.linear(t64(batch["y"]), t64(batch["w_yadd"]), t64(batch["b_yadd"])).numpy()
+    return g, bb
+
+
+def without(batch, names):
+    return {k: v for k, v in batch.items() if k not in names}
+
+
+def test_variant_no_score_mod_is_masked_sdpa():
+    """No score modulation: the layer is torch SDPA on the masked batch, whatever the FiLM weights."""
+    b = small_batch(seed=21, n_real=[10, 7, 4])
+    ref_o, ref_a = sdpa_reference(b, H=2)
+    out = O.forward(b, H=2, variant=O.NO_SCORE_MOD)
+    check_vs_sdpa(out, ref_o, ref_a, b["mask"])
+    film = ("w_emul", "w_eadd", "b_emul", "b_eadd", "w_ymul", "w_yadd", "b_ymul", "b_yadd")
+    out2 = O.forward(without(b, film), H=2, variant=O.NO_SCORE_MOD)  # FiLM parameters absent
+    for k in ("O", "A", "Ep"):
+        assert np.array_equal(out[k], out2[k])
+    pm = real_pairs(b["mask"])
+    ref_e = (t64(b["E"]) + F.linear(t64(ref_a).permute(0, 2, 3, 1), t64(b["w_e"]), t64(b["b_e"]))).numpy()
+    assert np.abs(out["Ep"][pm] - ref_e[pm]).max() < 1e-12
+    assert np.all(out["Ep"][~pm] == 0.0)
+
+
+def test_variant_light_edge_is_sdpa_with_global_temperature():
+    """Light edge: the score is s * gamma_y + beta_y, so A is SDPA with queries scaled by gamma_y
+    (beta_y cancels in the softmax), independent of the edge FiLM weights and of E in the scores."""
+    b = small_batch(seed=22, n_real=[10, 9, 6])
+    g, _ = global_gamma_beta(b)
+    n = b["X"].shape[1]
+    ref_o, ref_a = sdpa_reference(b, H=2, q_scale=np.repeat(g[:, :, None], n, axis=2))
+    out = O.forward(b, H=2, variant=O.LIGHT_EDGE)
+    check_vs_sdpa(out, ref_o, ref_a, b["mask"])
+    edge_film = ("w_emul", "w_eadd", "b_emul", "b_eadd")
+    out2 = O.forward(without(b, edge_film), H=2, variant=O.LIGHT_EDGE)
+    for k in ("O", "A", "Ep", "U"):
+        assert np.array_equal(out[k], out2[k])
+    full = O.forward(b, H=2)  # the full layer differs: the edge FiLM matters there
+    assert np.abs(full["A"] - out["A"]).max() > 1e-3
+
+
+def test_variant_unnormalized_update_takes_the_logits():
+    """Unnormalized update: E' - E - b_e on real pairs is Linear(H -> de) of the masked logits u;
+    O, A and u are those of the full layer; masked pairs stay +0.0."""
+    b = small_batch(seed=23, n_real=[10, 8, 3])
+    full = O.forward(b, H=2)
+    out = O.forward(b, H=2, variant=O.UNNORMALIZED)
+    for k in ("O", "A", "U"):
+        assert np.array_equal(out[k], full[k])
+    pm = real_pairs(b["mask"])
+    u = np.where(np.isfinite(full["U"]), full["U"], 0.0)
+    ref = (t64(b["E"]) + F.linear(t64(u).permute(0, 2, 3, 1), t64(b["w_e"]), t64(b["b_e"]))).numpy()
+    assert np.abs(out["Ep"][pm] - ref[pm]).max() < 1e-12
+    assert np.all(out["Ep"][~pm] == 0.0)
+    assert np.abs(out["Ep"][pm] - full["Ep"][pm]).max() > 1e-2
+
+
+def test_variant_unnormalized_bf16_rounds_the_operand():
+    """bf16 mode: the unnormalized operand is the logit rounded to bfloat16 (torch's rounding)."""
+    b = small_batch(seed=24, n_real=[10, 10, 7])
+    out = O.forward(b, H=2, bf16=True, variant=O.UNNORMALIZED)
+    u = np.where(np.isfinite(out["U"]), out["U"], 0.0)
+    ur = torch.tensor(u, dtype=torch.float64).to(torch.bfloat16).to(torch.float64)
+    ref = (t64(b["E"]) + F.linear(ur.permute(0, 2, 3, 1), t64(b["w_e"]), t64(b["b_e"]))).numpy()
+    pm = real_pairs(b["mask"])
+    assert np.abs(out["Ep"][pm] - ref[pm]).max() < 1e-12
+
+
+def test_variant_combination_plain_sdpa_with_logit_update():
+    """No score modulation + unnormalized update: E' = E + W_e (q k / sqrt(dh)) + b_e on real pairs."""
+    b = small_batch(seed=25, n_real=[9, 10, 5])
+    out = O.forward(b, H=2, variant=O.NO_SCORE_MOD | O.UNNORMALIZED)
+    X = t64(b["X"])
+    B, n, d = X.shape
+    q = F.linear(X, t64(b["w_q"]), t64(b["b_q"])).view(B, n, 2, 8).transpose(1, 2)
+    k = F.linear(X, t64(b["w_k"]), t64(b["b_k"])).view(B, n, 2, 8).transpose(1, 2)
+    s = (q @ k.transpose(-1, -2)) / math.sqrt(8)
+    pm = real_pairs(b["mask"])
+    s = torch.where(torch.tensor(pm)[:, None], s, torch.zeros_like(s))
+    ref = (t64(b["E"]) + F.linear(s.permute(0, 2, 3, 1), t64(b["w_e"]), t64(b["b_e"]))).numpy()
+    assert np.abs(out["Ep"][pm] - ref[pm]).max() < 1e-12
