@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 INFINITY_CACHE_BYTES = 256 << 20
 KERNEL_SOURCE = os.path.join(ROOT, "edge_aware_graph_amd", "csrc", "ea_kernels.hip")
+# ablation variants (the EA_VARIANT_* desc flags)
+VARIANT_FLAGS = {"none": 0, "light_edge": 0x2, "no_score_mod": 0x4, "unnormalized": 0x8}
 
 
 def parse():
@@ -38,16 +40,22 @@ def parse():
     ap.add_argument("--workload", default="planar", choices=["planar", "tree", "sbm", "large", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hot", action="store_true", help="also time back-to-back calls on one buffer set")
+    ap.add_argument("--variant", default="none", choices=sorted(VARIANT_FLAGS),
+                    help="ablation variant of the layer (the default is the full layer)")
     return ap.parse_args()
 
 
-def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool) -> float:
+def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
+                      recompute: bool = None) -> float:
     """Bytes one launch of `kernel` must move (inputs read once, outputs written once).
 
     Per edge token (b, i, j): E read (real pairs only), E' written (whole
     padded layout), A written (single pass). Per node row: O written, the
     per-head Q, K, V read from the workspace. Per graph: lse for two-pass.
+    `recompute`: the edge update recomputes the logits (two-pass, or the
+    unnormalized variant) and reads Q and K instead of A.
     """
+    recompute = two_pass if recompute is None else recompute
     s = 2 if dims.dtype == "bf16" else 4
     B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
     tokens = B * n * n
@@ -64,7 +72,7 @@ def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool) -> 
     if kernel == "attn_kernel":
         return e_read + o_write + qkv + (lse if two_pass else a_io)
     if kernel == "update_kernel":
-        return e_read + e_write + ((2 * rows * d * s + lse) if two_pass else a_io)
+        return e_read + e_write + ((2 * rows * d * s + (lse if two_pass else 0)) if recompute else a_io)
     if kernel == "qkv_kernel":
         return rows * d * s + 3 * d * d * s + qkv
     raise ValueError(kernel)
@@ -88,7 +96,7 @@ def traffic_from_profiles(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(batch, dims, budget_s: float = 12.0):
+def cpu_baseline(batch, dims, budget_s: float = 12.0, oracle_variant: int = 0):
     """The oracle (as it stands) on whole graphs of the same batch, host cores."""
     from oracle import oracle as OR
     threads = OR.num_threads()
@@ -100,7 +108,7 @@ def cpu_baseline(batch, dims, budget_s: float = 12.0):
     g = int(max(1, min(dims.B, budget_s / per_graph)))
     sub = {k: (v[:g] if k in ("X", "E", "y", "mask", "adj", "n_real") else v) for k, v in batch.items()}
     t0 = time.perf_counter()
-    OR.forward(sub, dims.H, bf16=(dims.dtype == "bf16"))
+    OR.forward(sub, dims.H, bf16=(dims.dtype == "bf16"), variant=oracle_variant)
     dt = time.perf_counter() - t0
     return {"value": g / dt, "unit": "graphs/s", "cores": threads, "kind": "oracle",
             "sample": "the first %d of the %d graphs of the timed batch, every query row, all outputs "
@@ -128,8 +136,11 @@ def main():
     n_real = batch["n_real"]
     dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
 
-    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype)
+    variant = VARIANT_FLAGS[args.variant]
+    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype,
+                          variant=variant)
     two_pass = layer.two_pass
+    recompute = layer.recomputes_update
     weights = {k: torch.from_numpy(batch[k]).to(dev, dt) for k in batch if k.startswith(("w_", "b_"))}
     # biases are all zero in the timed configuration: pass NULL
     for k in list(weights):
@@ -185,13 +196,13 @@ def main():
     kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     avg_s = kernels[dominant]["avg_us"] * 1e-6
-    alg = algorithmic_bytes(dominant, dims, n_real, two_pass)
+    alg = algorithmic_bytes(dominant, dims, n_real, two_pass, recompute)
     achieved = alg / avg_s / 1e9
     for name in kernels:
-        b = algorithmic_bytes(name, dims, n_real, two_pass)
+        b = algorithmic_bytes(name, dims, n_real, two_pass, recompute)
         kernels[name]["alg_bytes"] = b
         kernels[name]["alg_GBps"] = b / (kernels[name]["avg_us"] * 1e-6) / 1e9
-    traffic = traffic_from_profiles(dominant, cfg.name)
+    traffic = traffic_from_profiles(dominant, cfg.name) if not variant else None
 
     out = {
         "metric": "graphs/s per fused layer forward (edge-aware attention + residual edge update)",
@@ -207,11 +218,11 @@ def main():
         "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded %s graphs, random Xavier weights)" % cfg.structure,
         "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "dy": dims.dy, "H": H,
-                   "dh": dims.dh, "structure": cfg.structure, "two_pass": two_pass,
+                   "dh": dims.dh, "structure": cfg.structure, "two_pass": two_pass, "variant": args.variant,
                    "edge_tokens_per_step": B * n * n, "real_edge_tokens_per_step": int(np.sum(n_real ** 2)),
                    "buffer_sets": nsets},
         "edge_tokens_per_s": B * n * n / (ms_per_step * 1e-3),
-        "layer_alg_GBps": sum(algorithmic_bytes(k, dims, n_real, two_pass) for k in kernels) / (ms_per_step * 1e-3) / 1e9,
+        "layer_alg_GBps": sum(algorithmic_bytes(k, dims, n_real, two_pass, recompute) for k in kernels) / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": alg, "avg_launch_us": kernels[dominant]["avg_us"]},
@@ -237,7 +248,8 @@ def main():
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(batch, dims)
+        out["cpu_baseline"] = cpu_baseline(batch, dims, oracle_variant={"none": 0, "light_edge": 1, "no_score_mod": 2,
+                                                                        "unnormalized": 4}[args.variant])
     print(json.dumps(out), flush=True)
 
 

@@ -56,15 +56,24 @@ ea_status check_ptr(const void* p, const char* name, size_t align, bool required
     if (s_ != EA_OK) return s_;   \
   } while (0)
 
-ea_status check_attn_params(const ea_attn_params* p) {
+constexpr uint32_t kVariants = EA_VARIANT_LIGHT_EDGE | EA_VARIANT_NO_SCORE_MOD | EA_VARIANT_UNNORMALIZED;
+
+bool edge_film_on(const ea_ctx* c) {
+  return (c->d.flags & (EA_VARIANT_LIGHT_EDGE | EA_VARIANT_NO_SCORE_MOD)) == 0;
+}
+bool global_film_on(const ea_ctx* c) { return (c->d.flags & EA_VARIANT_NO_SCORE_MOD) == 0; }
+bool unnormalized(const ea_ctx* c) { return (c->d.flags & EA_VARIANT_UNNORMALIZED) != 0; }
+
+// FiLM parameters the variant does not read may be NULL.
+ea_status check_attn_params(const ea_ctx* c, const ea_attn_params* p) {
   if (!p) return fail(EA_E_NULLPTR, "attention parameters are NULL");
   EA_TRY(check_ptr(p->w_q, "w_q", 16, true));
   EA_TRY(check_ptr(p->w_k, "w_k", 16, true));
   EA_TRY(check_ptr(p->w_v, "w_v", 16, true));
-  EA_TRY(check_ptr(p->w_emul, "w_emul", 16, true));
-  EA_TRY(check_ptr(p->w_eadd, "w_eadd", 16, true));
-  EA_TRY(check_ptr(p->w_ymul, "w_ymul", 4, true));
-  EA_TRY(check_ptr(p->w_yadd, "w_yadd", 4, true));
+  EA_TRY(check_ptr(p->w_emul, "w_emul", 16, edge_film_on(c)));
+  EA_TRY(check_ptr(p->w_eadd, "w_eadd", 16, edge_film_on(c)));
+  EA_TRY(check_ptr(p->w_ymul, "w_ymul", 4, global_film_on(c)));
+  EA_TRY(check_ptr(p->w_yadd, "w_yadd", 4, global_film_on(c)));
   EA_TRY(check_ptr(p->b_q, "b_q", 4, false));
   EA_TRY(check_ptr(p->b_k, "b_k", 4, false));
   EA_TRY(check_ptr(p->b_v, "b_v", 4, false));
@@ -104,6 +113,7 @@ ea::LayerArgs make_args(const ea_ctx* c, const ea_attn_params* p, const ea_updat
   a.gy = reinterpret_cast<float*>(base + c->off_gy);
   a.B = c->d.B; a.n = c->d.n; a.NP = c->NP; a.dy = c->d.dy;
   a.scale = (float)(1.0 / sqrt((double)c->d.dh));
+  a.variant = (int)(c->d.flags & kVariants);
   return a;
 }
 
@@ -133,9 +143,8 @@ ea_status check_io(const ea_ctx* c, const void* X, const void* E, const void* y,
                    const uint8_t* mask, bool needX) {
   if (needX) EA_TRY(check_ptr(X, "X", 16, true));
   EA_TRY(check_ptr(E, "E", 16, true));
-  EA_TRY(check_ptr(y, "y", 4, true));
+  EA_TRY(check_ptr(y, "y", 4, global_film_on(c)));
   if (!mask) return fail(EA_E_NULLPTR, "node_mask is NULL");
-  (void)c;
   return EA_OK;
 }
 
@@ -183,7 +192,7 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   if ((long long)d.B * ((d.n + 15) / 16 * 16) >= (1ll << 31))
     return fail(EA_E_SHAPE, "B * n (padded to 16) must stay below 2^31");
   if (d.dtype != EA_FP32 && d.dtype != EA_BF16) return fail(EA_E_UNSUPPORTED, "dtype %d", d.dtype);
-  if (d.flags & ~EA_FORCE_TWO_PASS) return fail(EA_E_UNSUPPORTED, "unknown flags 0x%x", d.flags);
+  if (d.flags & ~(EA_FORCE_TWO_PASS | kVariants)) return fail(EA_E_UNSUPPORTED, "unknown flags 0x%x", d.flags);
   if (!ea::shape_supported(d.dtype, d.H, d.dh, d.de))
     return fail(EA_E_UNSUPPORTED, "(H, dh, de) = (%d, %d, %d) is not built; supported: (4,16,16), (8,32,64)",
                 d.H, d.dh, d.de);
@@ -222,7 +231,7 @@ ea_status edge_attn_forward(ea_ctx* c, const ea_attn_params* p, const void* X, c
                             size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
-  EA_TRY(check_attn_params(p));
+  EA_TRY(check_attn_params(c, p));
   EA_TRY(check_io(c, X, E, y, mask, true));
   EA_TRY(check_ptr(O, "O", 16, true));
   if (c->two_pass) {
@@ -255,16 +264,19 @@ ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params
   EA_TRY(check_ptr(E, "E", 16, true));
   if (!mask) return fail(EA_E_NULLPTR, "node_mask is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (c->two_pass) {
-    EA_TRY(check_attn_params(p));
-    EA_TRY(check_ptr(y, "y", 4, true));
+  if (c->two_pass || unnormalized(c)) {
+    // the update recomputes the logits from E and the forward's workspace
+    EA_TRY(check_attn_params(c, p));
+    EA_TRY(check_ptr(y, "y", 4, global_film_on(c)));
     EA_TRY(check_ws(c, ws, ws_bytes));
     if (!c->forward_done)
-      return fail(EA_E_STATE, "two-pass edge_update needs a preceding edge_attn_forward on this context");
+      return fail(EA_E_STATE, "%s edge_update needs a preceding edge_attn_forward on this context",
+                  c->two_pass ? "two-pass" : "unnormalized-variant");
     ea::LayerArgs a = make_args(c, p, u, nullptr, E, y, mask, ws);
     a.E_out = E_out;
+    const int mode = unnormalized(c) ? ea::kRecomputeU : ea::kRecompute;
     return timed(c, EA_K_UPDATE, s, [&] {
-      return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kRecompute, s);
+      return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, mode, s);
     });
   }
   EA_TRY(check_ptr(A, "A", 16, true));
@@ -281,7 +293,7 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
                           void* O, void* A, void* E_out, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
-  if (c->two_pass) {
+  if (c->two_pass || unnormalized(c)) {
     // Validate everything before the first launch.
     if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
     EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
@@ -290,7 +302,7 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
     EA_TRY(edge_attn_forward(c, p, X, E, y, mask, O, A, ws, ws_bytes, stream));
     return edge_update(c, p, u, E, y, mask, nullptr, E_out, ws, ws_bytes, stream);
   }
-  EA_TRY(check_attn_params(p));
+  EA_TRY(check_attn_params(c, p));
   EA_TRY(check_io(c, X, E, y, mask, true));
   EA_TRY(check_ptr(O, "O", 16, true));
   EA_TRY(check_ptr(A, "A", 16, true));
@@ -318,7 +330,7 @@ ea_status ea_debug_logits(ea_ctx* c, const ea_attn_params* p, const void* X, con
                           void* stream) {
   g_err[0] = 0;
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
-  EA_TRY(check_attn_params(p));
+  EA_TRY(check_attn_params(c, p));
   EA_TRY(check_io(c, X, E, y, mask, true));
   EA_TRY(check_ptr(U, "U", 16, true));
   EA_TRY(check_ws(c, ws, ws_bytes));

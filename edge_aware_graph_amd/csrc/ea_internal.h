@@ -15,8 +15,16 @@ enum AttnMode : int {
 };
 // Kernel modes of the edge-update kernel.
 enum UpdateMode : int {
-  kReadA = 0,      // single pass: A comes from the forward's output
-  kRecompute = 1,  // two-pass pass 2: A = exp(u - lse) recomputed per tile
+  kReadA = 0,       // single pass: A comes from the forward's output
+  kRecompute = 1,   // two-pass pass 2: A = exp(u - lse) recomputed per tile
+  kRecomputeU = 2,  // unnormalized variant: the operand is the logit u itself
+};
+// Ablation variant bits (LayerArgs::variant); the same values as the
+// EA_VARIANT_* flags of the C ABI.
+enum Variant : int {
+  kLightEdge = 0x2,     // no per-edge FiLM: gamma_e = 1, beta_e = 0
+  kNoScoreMod = 0x4,    // no FiLM at all: u = s
+  kUnnormalized = 0x8,  // the edge update takes u (0 at masked pairs) instead of A
 };
 
 struct LayerArgs {
@@ -43,6 +51,7 @@ struct LayerArgs {
   // sizes
   int B, n, NP, dy;
   float scale;   // 1/sqrt(dh)
+  int variant;   // Variant bits
 };
 
 // Launchers; each returns the hipError_t of its launch. `dtype` 0 = fp32, 1 = bf16.

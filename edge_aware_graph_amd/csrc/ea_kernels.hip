@@ -243,10 +243,16 @@ __device__ __forceinline__ void lane_group_transpose(float (&R)[4][NE]) {
 // beta_y = W_yadd y + b_yadd of the graphs whose slot 0 lies in rows
 // [m0, m0 + mrows) of the padded batch; 16 lanes per coefficient (2H <= 16),
 // loads batched.
+// Without score modulation they are 1 and 0 and y is not read.
 template <typename T, int H>
 __device__ __forceinline__ void global_film(const LayerArgs& a, uint32_t m0, uint32_t mrows, uint32_t rows) {
   const uint32_t NP = a.NP;
   const int tid = threadIdx.x, o = tid >> 4, part = tid & 15;
+  if (a.variant & kNoScoreMod) {
+    for (uint32_t m = (m0 + NP - 1) / NP * NP; m < m0 + mrows && m < rows; m += NP)
+      if (o < 2 * H && part == 0) a.gy[(size_t)(m / NP) * 2 * H + o] = o < H ? 1.f : 0.f;
+    return;
+  }
   const T* Wy = static_cast<const T*>(o < H ? a.w_ymul : a.w_yadd) + (size_t)(o % H) * a.dy;
   for (uint32_t m = (m0 + NP - 1) / NP * NP; m < m0 + mrows && m < rows; m += NP) {
     const uint32_t b = m / NP;
@@ -524,14 +530,17 @@ struct Scorer {
     load_queries(a);
   }
   // Edge-FiLM weights and biases (all the score stage needs besides E).
+  // Without the per-edge FiLM (light-edge and no-score-modulation variants)
+  // the weights and biases are zeros: gamma_e = 1 and beta_e = 0 exactly.
   __device__ __forceinline__ void load_film(const LayerArgs& a) {
+    const bool ef = (a.variant & (kLightEdge | kNoScoreMod)) == 0;  // uniform
     const T* wrow = li < H ? static_cast<const T*>(a.w_emul) + (size_t)li * DE
                   : static_cast<const T*>(a.w_eadd) + (size_t)(li - H) * DE;
-    wf.load(li < 2 * H ? wrow + lg * (DE / 4) : zeros<T>());
+    wf.load(ef && li < 2 * H ? wrow + lg * (DE / 4) : zeros<T>());
     // FiLM rows 4*lg .. 4*lg+3 are all gamma rows or all beta rows (4 | H)
     static_assert(H % 4 == 0, "heads");
     const int r0 = 4 * lg;
-    fb.load(r0 < H ? elem_or_zero<T>(a.b_emul, r0, true) : elem_or_zero<T>(a.b_eadd, r0 - H, r0 < 2 * H));
+    fb.load(r0 < H ? elem_or_zero<T>(a.b_emul, r0, ef) : elem_or_zero<T>(a.b_eadd, r0 - H, ef && r0 < 2 * H));
   }
   // Query fragments and the graph's global FiLM coefficients.
   __device__ __forceinline__ void load_queries(const LayerArgs& a) {
@@ -1258,8 +1267,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
 // wave w of key group z takes key tile 4*z + w. Blocks running together then
 // cover whole rows of E (contiguous memory) rather than one column stripe of
 // many rows. kReadA reads A from the forward's output; kRecompute re-runs the
-// score stage and takes A = exp(u - lse) from pass 1's statistics. The E
-// fragments of the tile are read once (bfloat16) and serve both stages.
+// score stage and takes A = exp(u - lse) from pass 1's statistics;
+// kRecomputeU (unnormalized variant) re-runs it and takes the logit u itself.
+// The E fragments of the tile are read once (bfloat16) and serve both stages.
 template <typename T, int H, int DH, int DE, int MODE>
 __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
@@ -1275,12 +1285,13 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   const uint32_t mq = sc.query_mask_byte();
   const uint32_t mk = sc.key_mask_byte(jt);
   Updater<T, H, DE> up;
-  // recompute mode: the update weights and the row statistics are loaded
+  // recompute modes: the update weights and the row statistics are loaded
   // after the score stage (not live next to the E tile and the FiLM rows)
-  if constexpr (MODE != kRecompute) up.init(a, li, lg);
+  constexpr bool kRe = MODE == kRecompute || MODE == kRecomputeU;
+  if constexpr (!kRe) up.init(a, li, lg);
   float A[H][4];
   Frag<T, DH / 4> kf[H];
-  if constexpr (MODE == kRecompute) {
+  if constexpr (kRe) {
     sc.load_weights(a);
     sc.load_k(jt, kf);
   } else {
@@ -1324,7 +1335,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   }
   ETile<T, DE> et;
   if constexpr (kKeepE) et.load(sc.E, b, n, i, sc.mi, j0, lg, bits);
-  if constexpr (MODE == kRecompute) {
+  if constexpr (kRe) {
     float u[H][4];
     if constexpr (kKeepE) {
       // S first, so that K and Q are dead while the E tile and the FiLM rows
@@ -1341,14 +1352,22 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
       sc.logits_streamed(j0, kf, bits, u);
     }
     up.init(a, li, lg);
-    float L[H];
+    if constexpr (MODE == kRecomputeU) {
+      // unnormalized variant: the operand is the logit itself, 0 at masked pairs
 #pragma unroll
-    for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)b * H + h) * NP + i];
+      for (int h = 0; h < H; ++h)
 #pragma unroll
-    for (int h = 0; h < H; ++h)
+        for (int r = 0; r < 4; ++r) A[h][r] = u[h][r] == kNegInf ? 0.f : u[h][r];
+    } else {
+      float L[H];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : __expf(u[h][r] - L[h]);
+      for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)b * H + h) * NP + i];
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : __expf(u[h][r] - L[h]);
+    }
   }
   up.finish();
   const bool full = tile_full(sc.mi, bits);
@@ -1397,6 +1416,8 @@ hipError_t update_shape(const LayerArgs& a, int mode, hipStream_t s) {
     hipLaunchKernelGGL((update_kernel<T, H, DH, DE, kReadA>), grid, dim3(kThreads), 0, s, a);
   else if (mode == kRecompute)
     hipLaunchKernelGGL((update_kernel<T, H, DH, DE, kRecompute>), grid, dim3(kThreads), 0, s, a);
+  else if (mode == kRecomputeU)
+    hipLaunchKernelGGL((update_kernel<T, H, DH, DE, kRecomputeU>), grid, dim3(kThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

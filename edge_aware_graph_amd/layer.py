@@ -17,6 +17,13 @@ LIB_PATH = os.path.join(_PKG, "libedge_attn.so")
 EA_OK, EA_E_NULLPTR, EA_E_SHAPE, EA_E_UNSUPPORTED, EA_E_ALIGN, EA_E_WORKSPACE, EA_E_STATE, EA_E_HIP = range(8)
 EA_FP32, EA_BF16 = 0, 1
 EA_FORCE_TWO_PASS = 0x1
+# Ablation variants (desc.flags): no per-edge FiLM; no FiLM at all; the edge
+# update takes the masked logits instead of A.
+EA_VARIANT_LIGHT_EDGE = 0x2
+EA_VARIANT_NO_SCORE_MOD = 0x4
+EA_VARIANT_UNNORMALIZED = 0x8
+VARIANTS = {"light_edge": EA_VARIANT_LIGHT_EDGE, "no_score_mod": EA_VARIANT_NO_SCORE_MOD,
+            "unnormalized": EA_VARIANT_UNNORMALIZED}
 EA_SINGLE_PASS_MAX_N = 256
 KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)")
 
@@ -122,10 +129,10 @@ class EdgeAttention:
     """A layer context: shape, dtype, mode and workspace plan (host only)."""
 
     def __init__(self, B: int, n: int, d: int, de: int, dy: int, H: int, dh: int,
-                 dtype: str = "bf16", force_two_pass: bool = False):
+                 dtype: str = "bf16", force_two_pass: bool = False, variant: int = 0):
         self.lib = load_library()
         self.desc = Desc(B, n, d, de, dy, H, dh, EA_BF16 if dtype == "bf16" else EA_FP32,
-                         EA_FORCE_TWO_PASS if force_two_pass else 0)
+                         (EA_FORCE_TWO_PASS if force_two_pass else 0) | int(variant))
         ctx = ctypes.c_void_p()
         _check(self.lib, self.lib.ea_ctx_create(ctypes.byref(self.desc), ctypes.byref(ctx)))
         self.ctx = ctx
@@ -158,6 +165,11 @@ class EdgeAttention:
         _check(self.lib, self.lib.edge_attn_forward(
             self.ctx, ctypes.byref(p), _ptr(X), _ptr(E), _ptr(y), _ptr(mask), _ptr(O), _ptr(A),
             _ptr(ws), self._ws_len(ws), _stream(stream)))
+
+    @property
+    def recomputes_update(self) -> bool:
+        """edge_update recomputes the logits (two-pass mode or the unnormalized variant)."""
+        return self.two_pass or bool(self.desc.flags & EA_VARIANT_UNNORMALIZED)
 
     def update(self, w, E, y, mask, A, E_out, ws, stream=None):
         p = self.attn_params(w) if w.get("w_q") is not None else None

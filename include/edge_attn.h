@@ -66,6 +66,28 @@ typedef enum { EA_FP32 = 0, EA_BF16 = 1 } ea_dtype;
 
 /* desc.flags */
 #define EA_FORCE_TWO_PASS 0x1u /* use the two-pass scheme even when one pass fits */
+/*
+ * Ablation variants of the layer (desc.flags). "Efficient Edge-aware Attention
+ * Network for Graph Generation", full-text summary: the ablations drop the
+ * per-edge modulation ("Light Edge"), drop the score modulation, or feed the
+ * edge update unnormalized instead of normalized attention coefficients.
+ *   EA_VARIANT_LIGHT_EDGE: no per-edge FiLM (gamma_e = 1, beta_e = 0), so
+ *     u = s * gamma_y + beta_y; w_emul, w_eadd, b_emul, b_eadd are not read
+ *     and may be NULL.
+ *   EA_VARIANT_NO_SCORE_MOD: no FiLM at all, u = s (masked scaled dot-product
+ *     attention); every FiLM weight and bias and y are not read and may be
+ *     NULL.
+ *   EA_VARIANT_UNNORMALIZED: the edge update takes the masked logits u (0 at
+ *     masked pairs) instead of A: E' = E + W_e u + b_e. O and A are the
+ *     normalized ones. The edge update then recomputes u from E and the
+ *     forward's workspace (edge_update needs p, y, ws and a preceding
+ *     edge_attn_forward on the context, as in two-pass mode; A is ignored),
+ *     and edge_attn_layer runs the forward and that update as two kernels.
+ * The variants combine (LIGHT_EDGE with NO_SCORE_MOD is NO_SCORE_MOD).
+ */
+#define EA_VARIANT_LIGHT_EDGE 0x2u
+#define EA_VARIANT_NO_SCORE_MOD 0x4u
+#define EA_VARIANT_UNNORMALIZED 0x8u
 
 /* Largest n handled in one pass (full rows on chip); larger n is two-pass. */
 #define EA_SINGLE_PASS_MAX_N 256

@@ -39,11 +39,14 @@ def upload(batch: Dict[str, np.ndarray], dtype: str, device="cuda") -> Dict[str,
 class Run:
     """Device buffers and one layer context for a batch."""
 
-    def __init__(self, batch, dims: W.LayerDims, force_two_pass=False, device="cuda"):
+    def __init__(self, batch, dims: W.LayerDims, force_two_pass=False, device="cuda", variant=0,
+                 drop=()):
         self.dims = dims
         self.dev = upload(batch, dims.dtype, device)
+        for k in drop:  # parameters the variant does not read are passed as NULL
+            self.dev[k] = None
         self.layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh,
-                                   dims.dtype, force_two_pass)
+                                   dims.dtype, force_two_pass, variant)
         dt = tdtype(dims.dtype)
         B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
         self.ws = torch.empty(self.layer.workspace_bytes, dtype=torch.uint8, device=device)

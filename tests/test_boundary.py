@@ -167,3 +167,42 @@ def test_binding_raises_on_bad_shape():
     with pytest.raises(L.EaError) as e:
         L.EdgeAttention(1, 4, 64, 16, 16, 4, 8, "fp32")
     assert e.value.status == L.EA_E_SHAPE
+
+
+@pytest.mark.parametrize("flags", [L.EA_VARIANT_LIGHT_EDGE, L.EA_VARIANT_NO_SCORE_MOD, L.EA_VARIANT_UNNORMALIZED,
+                                   L.EA_VARIANT_LIGHT_EDGE | L.EA_VARIANT_UNNORMALIZED | L.EA_FORCE_TWO_PASS])
+def test_variant_flags_accepted(lib, flags):
+    st, ctx = create(lib, make_desc(flags=flags))
+    assert st == L.EA_OK, lib.ea_last_error()
+    lib.ea_ctx_destroy(ctx)
+
+
+def test_variant_parameters_that_are_not_read_may_be_null(lib):
+    """Light edge does not read the edge FiLM, no-score-modulation no FiLM and no y:
+    NULL passes the parameter checks (the call then stops at the missing workspace)."""
+    no_edge_film = attn_params(w_emul=None, w_eadd=None)
+    no_film = attn_params(w_emul=None, w_eadd=None, w_ymul=None, w_yadd=None)
+    st, plain = create(lib, make_desc())
+    assert fwd(lib, plain, p=no_edge_film, ws=None) == L.EA_E_NULLPTR
+    assert fwd(lib, plain, y=None, ws=None) == L.EA_E_NULLPTR
+    lib.ea_ctx_destroy(plain)
+    st, light = create(lib, make_desc(flags=L.EA_VARIANT_LIGHT_EDGE))
+    assert fwd(lib, light, p=no_edge_film, ws=None) == L.EA_E_WORKSPACE
+    assert fwd(lib, light, p=no_film, ws=None) == L.EA_E_NULLPTR  # the global FiLM is still read
+    lib.ea_ctx_destroy(light)
+    st, nomod = create(lib, make_desc(flags=L.EA_VARIANT_NO_SCORE_MOD))
+    assert fwd(lib, nomod, p=no_film, y=None, ws=None) == L.EA_E_WORKSPACE
+    lib.ea_ctx_destroy(nomod)
+
+
+def test_unnormalized_update_needs_the_forward(lib):
+    """The unnormalized variant's edge_update recomputes the logits: like two-pass mode it
+    needs a preceding forward on the context (A is not used)."""
+    st, ctx = create(lib, make_desc(flags=L.EA_VARIANT_UNNORMALIZED))
+    assert st == L.EA_OK and lib.ea_is_two_pass(ctx) == 0
+    p = attn_params()
+    u = L.UpdateParams(FAKE, None)
+    st = lib.edge_update(ctx, ctypes.byref(p), ctypes.byref(u), FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None)
+    assert st == L.EA_E_STATE
+    assert b"edge_attn_forward" in lib.ea_last_error()
+    lib.ea_ctx_destroy(ctx)
