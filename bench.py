@@ -42,7 +42,51 @@ def parse():
     ap.add_argument("--hot", action="store_true", help="also time back-to-back calls on one buffer set")
     ap.add_argument("--variant", default="none", choices=sorted(VARIANT_FLAGS),
                     help="ablation variant of the layer (the default is the full layer)")
+    ap.add_argument("--sampling-layers", type=int, default=0,
+                    help="instead of single layers, time denoising steps of this many stacked layers "
+                         "(a step is then one pass through all of them)")
     return ap.parse_args()
+
+
+def sampling_bench(args, cfg, dims, batch):
+    """Stacked-layer sampling loop: each timed step runs L layers with their own
+    random weights, O and E' of a layer feeding the next (same batch, HBM-resident)."""
+    import torch
+    from edge_aware_graph_amd import workloads as W
+    from edge_aware_graph_amd.sampling import SamplingLoop
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+    L = args.sampling_layers
+    weights = []
+    for k in range(L):
+        wb = W.make_batch(cfg.name, seed=1000 + k, bias_scale=0.0)
+        weights.append({kk: torch.from_numpy(v).to(dev, dt) for kk, v in wb.items() if kk.startswith("w_")})
+    loop = SamplingLoop(dims, weights)
+    X0 = torch.from_numpy(batch["X"]).to(dev, dt)
+    E0 = torch.from_numpy(batch["E"]).to(dev, dt)
+    y0 = torch.from_numpy(batch["y"]).to(dev, dt)
+    m0 = torch.from_numpy(batch["mask"]).to(dev)
+    loop.run(X0, E0, y0, m0, steps=args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop.run(X0, E0, y0, m0, steps=args.steps)
+    torch.cuda.synchronize()
+    dt_s = time.perf_counter() - t0
+    ms_per_step = dt_s * 1e3 / args.steps
+    B, n = dims.B, dims.n
+    return {
+        "metric": "graphs/s per denoising step of %d stacked edge-aware attention layers" % L,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "graphs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded %s graphs, random Xavier weights per layer)" % cfg.structure,
+        "config": {"workload": cfg.name, "B": B, "n": n, "layers": L, "two_pass": loop.layer.two_pass,
+                   "note": "a step is the L layers only (the block around the layer and the sampler are not modelled)"},
+        "layers_per_s": L / (ms_per_step * 1e-3),
+        "ms_per_layer": ms_per_step / L,
+    }
 
 
 def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
@@ -134,6 +178,9 @@ def main():
     print("[bench] workload %s: %s" % (cfg.name, cfg.description), file=sys.stderr, flush=True)
     batch = W.make_batch(cfg.name, bias_scale=0.0)
     n_real = batch["n_real"]
+    if args.sampling_layers > 0:
+        print(json.dumps(sampling_bench(args, cfg, dims, batch)), flush=True)
+        return
     dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
 
     variant = VARIANT_FLAGS[args.variant]
