@@ -184,6 +184,31 @@ def test_nan_poisoned_padding_and_inputs_untouched():
     assert torch.equal(torch.nan_to_num(run.dev["E"]), torch.nan_to_num(e0))
 
 
+@pytest.mark.parametrize("mode,two", [("fused", False), ("separate", False), ("fused", True)])
+def test_nan_poisoned_padding_one_tile_path(mode, two):
+    """The one-tile fused path reads every in-bounds pair (masked ones too) and discards them by
+    selects; NaN/Inf there, and in padded X rows, must change no output bit (also separate calls
+    and the two-pass scheme)."""
+    dims = dims_of("planar", B=4)
+    batch = W.make_batch("planar", bias_scale=0.1, dims=dims)
+    for g, k in enumerate([64, 50, 33, 1]):
+        batch["mask"][g] = 0
+        batch["mask"][g, :k] = 1
+    run_clean = HX.Run(batch, dims, force_two_pass=two)
+    clean = (run_clean.fused() if mode == "fused" else run_clean.separate()).results()
+    pois = dict(batch)
+    pm = HX.pair_mask(batch["mask"])
+    X = batch["X"].copy(); X[batch["mask"] == 0] = np.nan
+    E = batch["E"].copy(); E[~pm] = np.nan; E[~pm, 3] = -np.inf
+    pois["X"], pois["E"] = X, E
+    run = HX.Run(pois, dims, force_two_pass=two)
+    res = (run.fused() if mode == "fused" else run.separate()).results()
+    for k in clean:
+        assert np.array_equal(res[k], clean[k]), k
+    ref = OR.forward(batch, dims.H, bf16=True)
+    HX.compare(res, ref, batch["mask"], dims)
+
+
 def test_deterministic_and_in_place():
     """Bitwise run-to-run determinism; E_out aliasing E gives the out-of-place result."""
     dims = dims_of("planar", B=8)
