@@ -485,3 +485,65 @@ def test_variant_combination_plain_sdpa_with_logit_update():
     s = torch.where(torch.tensor(pm)[:, None], s, torch.zeros_like(s))
     ref = (t64(b["E"]) + F.linear(s.permute(0, 2, 3, 1), t64(b["w_e"]), t64(b["b_e"]))).numpy()
     assert np.abs(out["Ep"][pm] - ref[pm]).max() < 1e-12
+
+
+# ------------------------------------------------------------------ backward oracle
+
+from oracle import backward as OB  # noqa: E402
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_backward_restatement_matches_c_oracle_forward(bf16):
+    """The float64 torch restatement the backward differentiates is the C oracle's forward."""
+    b = small_batch(seed=31, n_real=[10, 7, 1])
+    if bf16:
+        for k in list(b):
+            if k not in ("mask", "adj", "n_real"):
+                b[k] = W.bf16_round_array(b[k])
+    ref = O.forward(b, H=2, bf16=bf16)
+    got = OB.forward(b, H=2, bf16=bf16)
+    for k in ("O", "A", "Ep"):
+        assert np.abs(got[k] - ref[k]).max() < 1e-12, k
+
+
+def test_backward_matches_finite_differences_of_c_oracle():
+    """Autograd gradients against central differences of the C oracle (a separate code base):
+    a few coordinates of every input and weight, masked graphs included."""
+    dims = W.LayerDims(B=2, n=5, d=8, de=4, dy=3, H=2, dh=4, dtype="fp32")
+    b = W.make_batch("tiny", seed=3, bias_scale=0.3, dims=dims)
+    b["mask"][1, 3:] = 0
+    for k in ("w_emul", "w_eadd", "w_ymul", "w_yadd"):
+        b[k] = (b[k] * 2.0).astype(np.float32)
+    rng = np.random.default_rng(5)
+    dO = rng.standard_normal(b["X"].shape)
+    dEp = rng.standard_normal(b["E"].shape)
+    grads = OB.backward(b, dO, dEp, H=2)
+
+    def loss(bb):
+        r = O.forward(bb, H=2)
+        return float((r["O"] * dO).sum() + (r["Ep"] * dEp).sum())
+
+    h = 2.0 ** -14  # exact offset for float32 values of magnitude < 2^9
+    checked = 0
+    for k in OB.INPUTS + OB.WEIGHTS:
+        g = grads[k]
+        flat = rng.choice(g.size, size=min(3, g.size), replace=False)
+        for idx in flat:
+            pos = np.unravel_index(idx, g.shape)
+            bp, bm = dict(b), dict(b)
+            bp[k] = b[k].copy(); bp[k][pos] += np.float32(h)
+            bm[k] = b[k].copy(); bm[k][pos] -= np.float32(h)
+            fd = (loss(bp) - loss(bm)) / (2 * h)
+            assert abs(fd - g[pos]) <= 1e-5 * max(1.0, abs(fd)), (k, pos, fd, g[pos])
+            checked += 1
+    assert checked >= 40
+
+
+def test_backward_masked_pairs_get_no_edge_gradient():
+    """E at masked pairs does not reach any output: its gradient is exactly 0."""
+    b = small_batch(seed=32, n_real=[10, 4, 7])
+    rng = np.random.default_rng(6)
+    g = OB.backward(b, rng.standard_normal(b["X"].shape), rng.standard_normal(b["E"].shape), H=2, wrt=("E",))
+    pm = real_pairs(b["mask"])
+    assert np.all(g["E"][~pm] == 0.0)
+    assert np.abs(g["E"][pm]).max() > 0.1
