@@ -21,6 +21,7 @@ struct ea_ctx {
   int forward_done;
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
+  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, bws_bytes;  // backward workspace
   // kernel timing window
   int prof_on;
   std::vector<hipEvent_t> ev_pool;
@@ -174,6 +175,7 @@ const char* ea_kernel_name(int k) {
     case EA_K_ATTN: return "attn_kernel";
     case EA_K_UPDATE: return "update_kernel";
     case EA_K_FUSED: return "attn_kernel(fused)";
+    case EA_K_BACKWARD: return "backward (7 kernels)";
   }
   return "?";
 }
@@ -210,6 +212,12 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->off_lse = 3 * qkv;
   c->off_gy = c->off_lse + round256((size_t)d.B * d.H * c->NP * sizeof(float));
   c->ws_bytes = c->off_gy + round256((size_t)d.B * 2 * d.H * sizeof(float));
+  const size_t pairs = (size_t)d.B * c->NP * c->NP;
+  c->boff_ds = qkv;  // V rows first
+  c->boff_df = c->boff_ds + round256(pairs * d.H * sizeof(float));
+  c->boff_dqkv = c->boff_df + round256(pairs * 2 * d.H * sizeof(float));
+  c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
+  c->bws_bytes = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->prof_on = 0;
   c->ev_used = 0;
   *out = c;
@@ -341,6 +349,63 @@ ea_status ea_debug_logits(ea_ctx* c, const ea_attn_params* p, const void* X, con
   EA_TRY(run_qkv(c, a, s));
   return timed(c, EA_K_ATTN, s, [&] {
     return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kLogits, s);
+  });
+}
+
+size_t ea_backward_workspace_bytes(const ea_ctx* c) { return c ? c->bws_bytes : 0; }
+
+ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                             const void* X, const void* E, const void* y, const uint8_t* mask,
+                             const void* A, const void* dO, const void* dEp,
+                             void* dX, void* dE, void* dy, const ea_grads* gr,
+                             void* ws, size_t ws_bytes, void* bws, size_t bws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  if (c->two_pass || c->NP > 64)
+    return fail(EA_E_UNSUPPORTED, "the backward is built for single-pass contexts with n <= 64 (n = %d)", c->d.n);
+  if (c->d.flags & kVariants) return fail(EA_E_UNSUPPORTED, "the backward is built for the full layer (no variant flag)");
+  if (c->d.dtype == EA_FP32 && c->d.de != 16)
+    return fail(EA_E_UNSUPPORTED, "the float32 backward is built for (H, dh, de) = (4, 16, 16)");
+  EA_TRY(check_attn_params(c, p));
+  EA_TRY(check_ptr(p->b_emul, "b_emul", 4, false));
+  if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
+  EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
+  EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
+  EA_TRY(check_io(c, X, E, y, mask, true));
+  EA_TRY(check_ptr(A, "A", 16, true));
+  EA_TRY(check_ptr(dO, "dO", 16, true));
+  EA_TRY(check_ptr(dEp, "dE_out", 16, true));
+  EA_TRY(check_ptr(dX, "dX", 16, true));
+  EA_TRY(check_ptr(dE, "dE", 16, true));
+  EA_TRY(check_ptr(dy, "dy", 4, true));
+  if (!gr) return fail(EA_E_NULLPTR, "grads is NULL");
+  const void* gp[] = {gr->w_q, gr->w_k, gr->w_v, gr->b_q, gr->b_k, gr->b_v, gr->w_emul, gr->w_eadd,
+                      gr->b_emul, gr->b_eadd, gr->w_ymul, gr->w_yadd, gr->b_ymul, gr->b_yadd, gr->w_e, gr->b_e};
+  for (const void* q : gp) EA_TRY(check_ptr(q, "a gradient buffer", 16, true));
+  EA_TRY(check_ws(c, ws, ws_bytes));
+  if (!bws) return fail(EA_E_WORKSPACE, "backward workspace is NULL (%zu bytes required)", c->bws_bytes);
+  if (!aligned(bws, 256)) return fail(EA_E_ALIGN, "backward workspace is not 256-byte aligned");
+  if (bws_bytes < c->bws_bytes)
+    return fail(EA_E_WORKSPACE, "backward workspace has %zu bytes, %zu required", bws_bytes, c->bws_bytes);
+  if (!c->forward_done)
+    return fail(EA_E_STATE, "edge_attn_backward needs a preceding forward on this context");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ea::LayerArgs a = make_args(c, p, u, X, E, y, mask, ws);
+  ea::BwdArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A; g.dO = dO; g.dEp = dEp; g.dX = dX; g.dE = dE; g.dy = dy;
+  g.gw_q = gr->w_q; g.gw_k = gr->w_k; g.gw_v = gr->w_v; g.gb_q = gr->b_q; g.gb_k = gr->b_k; g.gb_v = gr->b_v;
+  g.gw_em = gr->w_emul; g.gw_ea = gr->w_eadd; g.gb_em = gr->b_emul; g.gb_ea = gr->b_eadd;
+  g.gw_ym = gr->w_ymul; g.gw_ya = gr->w_yadd; g.gb_ym = gr->b_ymul; g.gb_ya = gr->b_yadd;
+  g.gw_e = gr->w_e; g.gb_e = gr->b_e;
+  char* bb = static_cast<char*>(bws);
+  g.Vr = bb;
+  g.DS = reinterpret_cast<float*>(bb + c->boff_ds);
+  g.DF = reinterpret_cast<float*>(bb + c->boff_df);
+  g.DQKV = reinterpret_cast<float*>(bb + c->boff_dqkv);
+  g.DGY = reinterpret_cast<float*>(bb + c->boff_dgy);
+  return timed(c, EA_K_BACKWARD, s, [&] {
+    return ea::launch_backward(a, g, c->d.dtype, c->d.H, c->d.dh, c->d.de, s);
   });
 }
 

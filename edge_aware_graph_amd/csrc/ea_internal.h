@@ -54,12 +54,36 @@ struct LayerArgs {
   int variant;   // Variant bits
 };
 
+// Backward of one layer (single pass, n <= 64): gradients and scratch.
+struct BwdArgs {
+  const void* A;    // the forward's attention map [B, H, n, n]
+  const void* dO;   // loss gradient of O [B, n, d]
+  const void* dEp;  // loss gradient of E' [B, n, n, de]
+  void* dX;         // [B, n, d]
+  void* dE;         // [B, n, n, de]
+  void* dy;         // [B, dy]
+  float *gw_q, *gw_k, *gw_v, *gb_q, *gb_k, *gb_v;  // float32 weight gradients
+  float *gw_em, *gw_ea, *gb_em, *gb_ea;
+  float *gw_ym, *gw_ya, *gb_ym, *gb_ya;
+  float *gw_e, *gb_e;
+  // scratch (the backward workspace)
+  void* Vr;      // V rows [B, H, NP, dh]
+  float* DS;     // ds [B, H, NP, NP]
+  float* DF;     // dgamma_e, dbeta_e [B, 2H, NP, NP]
+  float* DQKV;   // dQ | dK | dV [B, NP, 3, d]
+  float* DGY;    // dgamma_y, dbeta_y [B, 2H]
+};
+
 // Launchers; each returns the hipError_t of its launch. `dtype` 0 = fp32, 1 = bf16.
 hipError_t launch_qkv(const LayerArgs& a, int dtype, int H, int dh, int de, hipStream_t s);
 hipError_t launch_attn(const LayerArgs& a, int dtype, int H, int dh, int de, int mode,
                        hipStream_t s);
 hipError_t launch_update(const LayerArgs& a, int dtype, int H, int dh, int de, int mode,
                          hipStream_t s);
+// The backward's kernels in order (prep, pair, per-head, pair reduction,
+// dX, dW, small sums); returns the first launch error.
+hipError_t launch_backward(const LayerArgs& a, const BwdArgs& g, int dtype, int H, int dh, int de,
+                           hipStream_t s);
 // Whether (dtype, H, dh, de) is instantiated.
 bool shape_supported(int dtype, int H, int dh, int de);
 

@@ -1378,6 +1378,525 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
     up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak, [] {});
 }
 
+// ------------------------------------------------------------------ backward
+
+// Gradients of one layer (forward and residual edge update), single-pass
+// shapes with one key tile per wave (n <= 64), from the loss gradients dO of
+// the node output and dE' of the edge output. Per real pair (i, j), head h:
+//   dA = dO_i . V_j + sum_c W_e[c, h] dE'_ij[c]        (through A V and E')
+//   D_i = sum_j A_ij dA_ij,  du = A (dA - D)             (softmax)
+//   ds = du gamma_y gamma_e,  dgamma_e = du gamma_y s,  dbeta_e = du gamma_y
+//   (u = (s gamma_e + beta_e) gamma_y + beta_y, s = q_i . k_j / sqrt(dh))
+//   dE_ij = dE'_ij + W_em^T dgamma_e + W_ea^T dbeta_e   (0 at masked pairs)
+//   dQ = r ds K, dK = r ds^T Q, dV = A^T dO per (graph, head); the weight
+//   gradients are sums over real pairs (edge FiLM, W_e) or real rows (Q, K,
+//   V projections) or graphs (global FiLM).
+// A is the forward's stored map (bfloat16 in bf16 mode): the backward of a
+// rounding point counts as the identity.
+
+// bwd_prep: zero the gradients that are accumulated with atomics, and V in
+// row layout [B, H, NP, dh] (the forward keeps V^T).
+template <typename T, int H, int DH, int DE>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs g) {
+  const int NP = a.NP;
+  const size_t nz1 = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE, nz2 = (size_t)a.B * 2 * H;
+  const size_t nv = (size_t)a.B * H * NP * DH;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nz1 + nz2 + nv; k += stride) {
+    if (k < nz1) {
+      size_t q = k;
+      if (q < (size_t)H * DE) { g.gw_em[q] = 0.f; continue; }
+      q -= (size_t)H * DE;
+      if (q < (size_t)H * DE) { g.gw_ea[q] = 0.f; continue; }
+      q -= (size_t)H * DE;
+      if (q < (size_t)H) { g.gb_em[q] = 0.f; continue; }
+      q -= H;
+      if (q < (size_t)H) { g.gb_ea[q] = 0.f; continue; }
+      q -= H;
+      if (q < (size_t)DE * H) { g.gw_e[q] = 0.f; continue; }
+      q -= (size_t)DE * H;
+      g.gb_e[q] = 0.f;
+    } else if (k < nz1 + nz2) {
+      g.DGY[k - nz1] = 0.f;
+    } else {
+      const size_t q = k - nz1 - nz2;  // Vr index ((b H + h) NP + j) DH + t
+      const size_t t = q % DH, j = (q / DH) % NP, bh = q / ((size_t)DH * NP);
+      static_cast<T*>(g.Vr)[q] = static_cast<const T*>(a.Vt)[(bh * DH + t) * NP + j];
+    }
+  }
+}
+
+// bwd_pair: one block per (16 queries, graph), wave w = key tile w (n <= 64).
+template <typename T, int H, int DH, int DE>
+__global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs g) {
+  constexpr int D = H * DH, NCH = DE / 16;
+  __shared__ float red_s[kWaves][H][16];
+  __shared__ float sum_s[kWaves][4 * H];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int b = blockIdx.y, i0 = blockIdx.x * 16;
+  Scorer<T, H, DH, DE> sc;
+  sc.setup(a, b, i0);
+  const int n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, jt = w, j0 = 16 * jt;
+  const bool tile_ok = jt < JT;  // uniform per wave; waves past JT compute zeros
+  const uint32_t mq = sc.query_mask_byte();
+  const uint32_t mk = sc.key_mask_byte(jt);
+  sc.load_weights(a);
+  Frag<T, DH / 4> kf[H], vr[H], dof[H];
+  sc.load_k(jt, kf);
+  const int jc = tile_ok ? jt : JT - 1;
+  const T* Vr = static_cast<const T*>(g.Vr);
+  const T* dO = static_cast<const T*>(g.dO);
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    vr[h].load(Vr + (((size_t)b * H + h) * NP + 16 * jc + li) * DH + lg * (DH / 4));
+    dof[h].load(i < n ? dO + ((size_t)b * n + i) * D + h * DH + lg * (DH / 4) : zeros<T>());
+  }
+  // A of this lane's query and keys j0 + 4 lg + r (0 outside the n x n map)
+  float Av[H][4];
+  {
+    const T* Ag = static_cast<const T*>(g.A);
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + 4 * lg + r;
+        const bool ok = i < n && j < n;
+        const float v = Num<T>::ld(Ag + ((size_t)b * H + h) * n * n + (ok ? (size_t)i * n + j : 0));
+        Av[h][r] = ok ? v : 0.f;
+      }
+  }
+  // W_e^T row li (head li) over this lane group's channels, for dA through E'
+  Frag<T, DE / 4> wet;
+  {
+    const T* We = static_cast<const T*>(a.w_e);
+    float v[DE / 4];
+#pragma unroll
+    for (int k = 0; k < DE / 4; ++k) {
+      const int c = lg * (DE / 4) + k;
+      const float x = Num<T>::ld(li < H ? We + (size_t)c * H + li : zeros<T>());
+      v[k] = li < H ? x : 0.f;
+    }
+    wet.set(v);
+  }
+  // W_F^T rows for dE (operand A): row li of chunk ch is channel
+  // (li/4)(DE/4) + 4 ch + li%4; slot s of lane group lg is FiLM row 4 lg + s
+  // (rows 0..H-1: W_em, H..2H-1: W_ea, the rest zero)
+  Frag<T, 4> wF[NCH];
+  {
+    const T* Wm = static_cast<const T*>(a.w_emul);
+    const T* Wa = static_cast<const T*>(a.w_eadd);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int c = (li >> 2) * (DE / 4) + 4 * ch + (li & 3);
+      float v[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int fr = 4 * lg + s;
+        const T* p = fr < H ? Wm + (size_t)fr * DE + c : fr < 2 * H ? Wa + (size_t)(fr - H) * DE + c : zeros<T>();
+        const float x = Num<T>::ld(p);
+        v[s] = fr < 2 * H ? x : 0.f;
+      }
+      wF[ch].set(v);
+    }
+  }
+  sc.mi = mq != 0u;
+  const uint32_t bits = tile_ok ? key_bits(mk) : 0u;
+  const uint32_t okb = (bits >> (4 * lg)) & (sc.mi ? 0xfu : 0u);  // real pairs of this lane's 4 keys
+  const T* dEp = static_cast<const T*>(g.dEp);
+
+  // (1) dA through E': W_e^T dE' per pair, from the dE' tile
+  float dAe[H][4];
+  {
+    ETile<T, DE> dt;
+    dt.load_all(dEp, b, n, i, j0, lg);
+    float R2[4][16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const f32x4 F = mma(f32x4{0.f, 0.f, 0.f, 0.f}, wet, dt.f[jj]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R2[jj >> 2][4 * (jj & 3) + r] = F[r];
+    }
+    lane_group_transpose<16>(R2);
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dAe[h][r] = R2[h >> 2][4 * r + (h & 3)];
+  }
+  // (2) the FiLM rows (gamma_e, beta_e) from the E tile
+  float R[4][16];
+  {
+    ETile<T, DE> et;
+    et.load_all(sc.E, b, n, i, j0, lg);
+    const f32x4 fc = sc.film_start();
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) sc.film(et.f[jj], fc, R, jj);
+    lane_group_transpose<16>(R);
+  }
+  // (3) scores and dO . V (both as S^T = K Q^T: lane (li, lg) holds query li, keys 4 lg + r)
+  f32x4 S[H], P[H];
+  sc.qk(kf, S);
+#pragma unroll
+  for (int h = 0; h < H; ++h) P[h] = mma(f32x4{0.f, 0.f, 0.f, 0.f}, vr[h], dof[h]);
+  // (4) the softmax backward per pair and head
+  float dA[H][4];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dA[h][r] = ((okb >> r) & 1u) ? P[h][r] + dAe[h][r] : 0.f;
+      part += Av[h][r] * dA[h][r];
+    }
+    part = lg_sum(part);
+    if (lg == 0) red_s[w][h][li] = part;
+  }
+  __syncthreads();
+  float ds[H][4], dge[H][4], dbe[H][4];
+  float sgy[H], sby[H], sge[H], sbe[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float Dh = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) Dh += red_s[ww][h][li];
+    const float gyh = sc.gy[h];
+    sgy[h] = sby[h] = sge[h] = sbe[h] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (okb >> r) & 1u;
+      const float du = ok ? Av[h][r] * (dA[h][r] - Dh) : 0.f;
+      const float s = S[h][r] * sc.scale;
+      const float gam = R[h >> 2][4 * r + (h & 3)];
+      const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)];
+      ds[h][r] = ok ? du * gyh * gam : 0.f;
+      dge[h][r] = ok ? du * gyh * s : 0.f;
+      dbe[h][r] = du * gyh;
+      sgy[h] += ok ? du * (s * gam + bet) : 0.f;
+      sby[h] += du;
+      sge[h] += dge[h][r];
+      sbe[h] += dbe[h][r];
+    }
+  }
+  // ds and dgamma_e / dbeta_e for the (graph, head) and pair-reduction kernels
+  if (tile_ok) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      *reinterpret_cast<f32x4*>(g.DS + (((size_t)b * H + h) * NP + i) * NP + j0 + 4 * lg) =
+          f32x4{ds[h][0], ds[h][1], ds[h][2], ds[h][3]};
+      *reinterpret_cast<f32x4*>(g.DF + (((size_t)b * 2 * H + h) * NP + i) * NP + j0 + 4 * lg) =
+          f32x4{dge[h][0], dge[h][1], dge[h][2], dge[h][3]};
+      *reinterpret_cast<f32x4*>(g.DF + (((size_t)b * 2 * H + H + h) * NP + i) * NP + j0 + 4 * lg) =
+          f32x4{dbe[h][0], dbe[h][1], dbe[h][2], dbe[h][3]};
+    }
+  }
+  // (5) dE = dE' + W_F^T dF per key: dF regrouped so that lane group lg holds
+  // FiLM rows 4 lg .. 4 lg + 3 of every key (the FiLM output layout)
+  float dFa[4][16];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int rp = 0; rp < 4; ++rp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int fr = 4 * x + r;
+        dFa[x][4 * rp + r] = fr < H ? dge[fr < H ? fr : 0][rp] : fr < 2 * H ? dbe[fr >= H && fr < 2 * H ? fr - H : 0][rp] : 0.f;
+      }
+  lane_group_transpose<16>(dFa);
+  if (tile_ok) {
+    T* dE = static_cast<T*>(g.dE);
+    const size_t rowoff = ((size_t)b * n + (i < n ? i : 0)) * n * DE + lg * (DE / 4);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = j0 + jj;
+      const bool inb = i < n && j < n;
+      const bool real = sc.mi && ((bits >> jj) & 1u);
+      Frag<T, 4> bq;
+      bq.set(&dFa[jj >> 2][4 * (jj & 3)]);
+      Frag<T, DE / 4> ef;
+      ef.load(inb ? dEp + rowoff + (size_t)j * DE : zeros<T>());
+      float out[DE / 4];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const f32x4 c = mma(f32x4{0.f, 0.f, 0.f, 0.f}, wF[ch], bq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[4 * ch + r] = real ? c[r] + ef.get(4 * ch + r) : 0.f;
+      }
+      if (inb) {
+        Frag<T, DE / 4> of;
+        of.set(out);
+        of.store(dE + rowoff + (size_t)j * DE);
+      }
+    }
+  }
+  // (6) sums over the block's pairs: dgamma_y, dbeta_y (per graph), b_emul, b_eadd
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float v[4] = {sgy[h], sby[h], sge[h], sbe[h]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float x = lg_sum(v[q]);
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (l == 0) sum_s[w][4 * h + q] = x;
+    }
+  }
+  __syncthreads();
+  if (tid < 4 * H) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) x += sum_s[ww][tid];
+    const int h = tid >> 2, q = tid & 3;
+    float* dst = q == 0 ? g.DGY + (size_t)b * 2 * H + h : q == 1 ? g.DGY + (size_t)b * 2 * H + H + h
+               : q == 2 ? g.gb_em + h : g.gb_ea + h;
+    atomicAdd(dst, x);
+  }
+}
+
+// bwd_qkv: per (head, graph): dQ = r ds K, dK = r ds^T Q, dV = A^T dO into
+// DQKV [B, NP, 3, D] (float32), n <= 64.
+template <typename T, int H, int DH>
+__global__ __launch_bounds__(kThreads) void bwd_qkv_kernel(LayerArgs a, BwdArgs g) {
+  constexpr int D = H * DH, M = 64;
+  __shared__ float ds_s[M][M + 1], a_s[M][M + 1];
+  __shared__ float q_s[M][DH + 1], k_s[M][DH + 1], o_s[M][DH + 1];
+  const int h = blockIdx.x, b = blockIdx.y, NP = a.NP, n = a.n, tid = threadIdx.x;
+  const size_t bh = (size_t)b * H + h;
+  const T* Ag = static_cast<const T*>(g.A);
+  for (int idx = tid; idx < NP * NP; idx += kThreads) {
+    const int ii = idx / NP, jj = idx % NP;
+    ds_s[ii][jj] = g.DS[(bh * NP + ii) * NP + jj];
+    const bool ok = ii < n && jj < n;
+    const float v = Num<T>::ld(Ag + bh * n * n + (ok ? (size_t)ii * n + jj : 0));
+    a_s[ii][jj] = ok ? v : 0.f;
+  }
+  const T* Qw = static_cast<const T*>(a.Qw);
+  const T* Kw = static_cast<const T*>(a.Kw);
+  const T* dO = static_cast<const T*>(g.dO);
+  for (int idx = tid; idx < NP * DH; idx += kThreads) {
+    const int r = idx / DH, t = idx % DH;
+    q_s[r][t] = Num<T>::ld(Qw + (bh * NP + r) * DH + t);
+    k_s[r][t] = Num<T>::ld(Kw + (bh * NP + r) * DH + t);
+    const float v = Num<T>::ld(dO + ((size_t)b * n + (r < n ? r : 0)) * D + h * DH + t);
+    o_s[r][t] = r < n ? v : 0.f;
+  }
+  __syncthreads();
+  const float sc = a.scale;
+  for (int idx = tid; idx < 3 * NP * DH; idx += kThreads) {
+    const int which = idx / (NP * DH), r = (idx / DH) % NP, t = idx % DH;
+    float acc = 0.f;
+    if (which == 0) {
+      for (int j = 0; j < NP; ++j) acc += ds_s[r][j] * k_s[j][t];
+      acc *= sc;
+    } else if (which == 1) {
+      for (int q = 0; q < NP; ++q) acc += ds_s[q][r] * q_s[q][t];
+      acc *= sc;
+    } else {
+      for (int q = 0; q < NP; ++q) acc += a_s[q][r] * o_s[q][t];
+    }
+    g.DQKV[(((size_t)b * NP + r) * 3 + which) * D + h * DH + t] = acc;
+  }
+}
+
+// bwd_pair_reduce: sums over all real pairs of dgamma_e E, dbeta_e E (W_em,
+// W_ea), dE' A (W_e) and dE' (b_e). Each block takes chunks of 64 pairs
+// (b, i, j) in turn, keeps its outputs in registers, and adds them once.
+template <typename T, int H, int DE>
+__global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, BwdArgs g) {
+  constexpr int P = 64, NO1 = 2 * H * DE, NO2 = DE * H, NO = NO1 + NO2 + DE, PER = (NO + kThreads - 1) / kThreads;
+  __shared__ float e_s[P][DE + 1], d_s[P][DE + 1], f_s[2 * H][P + 1], a_s[H][P + 1];
+  const int tid = threadIdx.x, NP = a.NP, n = a.n;
+  const size_t npairs = (size_t)a.B * NP * NP, nchunks = (npairs + P - 1) / P;
+  const T* E = static_cast<const T*>(a.E);
+  const T* dEp = static_cast<const T*>(g.dEp);
+  const T* Ag = static_cast<const T*>(g.A);
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  for (size_t cidx = blockIdx.x; cidx < nchunks; cidx += gridDim.x) {
+    for (int idx = tid; idx < P * DE; idx += kThreads) {
+      const int p = idx / DE, c = idx % DE;
+      const size_t q = cidx * P + p;
+      const int bq = (int)(q / ((size_t)NP * NP)), ii = (int)((q / NP) % NP), jj = (int)(q % NP);
+      const int bc = q < npairs ? bq : 0;
+      const bool real = q < npairs && ii < n && jj < n && a.mask[(size_t)bc * n + (ii < n ? ii : 0)] &&
+                        a.mask[(size_t)bc * n + (jj < n ? jj : 0)];
+      const size_t off = real ? (((size_t)bq * n + ii) * n + jj) * DE + c : 0;
+      const float ev = Num<T>::ld(E + off), dv = Num<T>::ld(dEp + off);
+      e_s[p][c] = real ? ev : 0.f;
+      d_s[p][c] = real ? dv : 0.f;
+    }
+    for (int idx = tid; idx < P * 3 * H; idx += kThreads) {
+      const int p = idx % P, row = idx / P;  // rows 0..2H-1: dF, 2H..3H-1: A
+      const size_t q = cidx * P + p;
+      const int bq = (int)(q / ((size_t)NP * NP)), ii = (int)((q / NP) % NP), jj = (int)(q % NP);
+      const bool inr = q < npairs;
+      const int bc = inr ? bq : 0;  // addresses stay inside the buffers past the last pair
+      if (row < 2 * H) {
+        const float v = g.DF[(((size_t)bc * 2 * H + row) * NP + ii) * NP + jj];
+        f_s[row][p] = inr ? v : 0.f;
+      } else {
+        const int h = row - 2 * H;
+        const bool ok = inr && ii < n && jj < n;
+        const float v = Num<T>::ld(Ag + (((size_t)bc * H + h) * n + (ok ? ii : 0)) * n + (ok ? jj : 0));
+        a_s[h][p] = ok ? v : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int o = tid + k * kThreads;
+      float s = 0.f;
+      if (o < NO1) {
+        const int row = o / DE, c = o % DE;
+        for (int p = 0; p < P; ++p) s += f_s[row][p] * e_s[p][c];
+      } else if (o < NO1 + NO2) {
+        const int c = (o - NO1) / H, h = (o - NO1) % H;
+        for (int p = 0; p < P; ++p) s += d_s[p][c] * a_s[h][p];
+      } else if (o < NO) {
+        const int c = o - NO1 - NO2;
+        for (int p = 0; p < P; ++p) s += d_s[p][c];
+      }
+      acc[k] += s;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int o = tid + k * kThreads;
+    if (o < H * DE) atomicAdd(g.gw_em + o, acc[k]);
+    else if (o < NO1) atomicAdd(g.gw_ea + (o - H * DE), acc[k]);
+    else if (o < NO1 + NO2) atomicAdd(g.gw_e + (o - NO1), acc[k]);
+    else if (o < NO) atomicAdd(g.gb_e + (o - NO1 - NO2), acc[k]);
+  }
+}
+
+// Plain float32 GEMM tiles for the node-level gradients (64 x 64 outputs per
+// block, 4 x 4 per thread, 16-deep chunks through LDS):
+//   kDX: dX[row, c] = sum_f DQKV[row, f] W_f[c] over f < 3D (W_q; W_k; W_v),
+//        rows (b, i) with i < n;
+//   kDW: dW_w[f, c] = sum over real rows of DQKV[row, w D + f] X[row, c].
+enum BwdGemm : int { kDX = 0, kDW = 1 };
+template <typename T, int H, int DH, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs g) {
+  constexpr int D = H * DH, TM = 64, TN = 64, TK = 16;
+  __shared__ float as[TK][TM + 4], bs[TK][TN + 4];
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
+  const int NP = a.NP, n = a.n;
+  const int M = MODE == kDX ? a.B * NP : 3 * D, K = MODE == kDX ? 3 * D : a.B * NP;
+  const T* X = static_cast<const T*>(a.X);
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += TK) {
+    for (int idx = tid; idx < TK * TM; idx += kThreads) {
+      const int kk = idx / TM, mm = idx % TM, m = m0 + mm, k = k0 + kk;
+      float v = 0.f;
+      if (MODE == kDX) {
+        if (m < M && k < K) v = g.DQKV[(size_t)m * 3 * D + k];
+      } else {
+        // A(f, row) = DQKV[row][f]; rows of padded or masked nodes count as 0
+        if (m < M && k < K) v = g.DQKV[(size_t)k * 3 * D + m];
+      }
+      as[kk][mm] = v;
+    }
+    for (int idx = tid; idx < TK * TN; idx += kThreads) {
+      const int kk = idx / TN, nn = idx % TN, c = n0 + nn, k = k0 + kk;
+      float v = 0.f;
+      if (MODE == kDX) {
+        if (k < K && c < D) {
+          const int wsel = k / D, f = k % D;
+          const T* W = static_cast<const T*>(wsel == 0 ? a.w_q : wsel == 1 ? a.w_k : a.w_v);
+          v = Num<T>::ld(W + (size_t)f * D + c);
+        }
+      } else {
+        if (k < K && c < D) {
+          const int bq = k / NP, ii = k % NP;
+          const bool real = ii < n && a.mask[(size_t)bq * n + (ii < n ? ii : 0)];
+          const float x = Num<T>::ld(X + ((size_t)bq * n + (real ? ii : 0)) * D + c);
+          v = real ? x : 0.f;
+        }
+      }
+      bs[kk][nn] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { av[r] = as[kk][ty * 4 + r]; bv[r] = bs[kk][tx * 4 + r]; }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + ty * 4 + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = n0 + tx * 4 + c;
+      if (col >= D) continue;
+      if (MODE == kDX) {
+        const int bq = m / NP, ii = m % NP;
+        if (ii < n) Num<T>::st(static_cast<T*>(g.dX) + ((size_t)bq * n + ii) * D + col, acc[r][c]);
+      } else {
+        const int wsel = m / D, f = m % D;
+        float* dst = wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v;
+        dst[(size_t)f * D + col] = acc[r][c];
+      }
+    }
+  }
+}
+
+// bwd_small: bias gradients of the projections (blocks 0 .. 3D/64 - 1, 64
+// features each) and the global FiLM's gradients and dy (the last block).
+template <typename T, int H, int DH>
+__global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArgs g) {
+  constexpr int D = H * DH;
+  __shared__ float part_s[4][64];
+  const int tid = threadIdx.x, NP = a.NP, B = a.B;
+  if (blockIdx.x < 3 * D / 64) {
+    const int f = blockIdx.x * 64 + (tid & 63), q = tid >> 6;
+    float s = 0.f;
+    for (int row = q; row < B * NP; row += 4) s += g.DQKV[(size_t)row * 3 * D + f];
+    part_s[q][tid & 63] = s;
+    __syncthreads();
+    if (tid < 64) {
+      const float t = part_s[0][tid] + part_s[1][tid] + part_s[2][tid] + part_s[3][tid];
+      const int wsel = f / D;
+      float* dst = wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v;
+      dst[f % D] = t;
+    }
+    return;
+  }
+  const int dy = a.dy;
+  const T* y = static_cast<const T*>(a.y);
+  const T* Wm = static_cast<const T*>(a.w_ymul);
+  const T* Wa = static_cast<const T*>(a.w_yadd);
+  for (int idx = tid; idx < B * dy; idx += kThreads) {
+    const int bq = idx / dy, c = idx % dy;
+    float s = 0.f;
+    for (int h = 0; h < H; ++h)
+      s += Num<T>::ld(Wm + (size_t)h * dy + c) * g.DGY[(size_t)bq * 2 * H + h] +
+           Num<T>::ld(Wa + (size_t)h * dy + c) * g.DGY[(size_t)bq * 2 * H + H + h];
+    Num<T>::st(static_cast<T*>(g.dy) + idx, s);
+  }
+  for (int idx = tid; idx < 2 * H * dy; idx += kThreads) {
+    const int row = idx / dy, c = idx % dy;  // rows 0..H-1: W_ymul, H..2H-1: W_yadd
+    float s = 0.f;
+    for (int bq = 0; bq < B; ++bq) s += g.DGY[(size_t)bq * 2 * H + row] * Num<T>::ld(y + (size_t)bq * dy + c);
+    (row < H ? g.gw_ym : g.gw_ya)[(size_t)(row % H) * dy + c] = s;
+  }
+  for (int idx = tid; idx < 2 * H; idx += kThreads) {
+    float s = 0.f;
+    for (int bq = 0; bq < B; ++bq) s += g.DGY[(size_t)bq * 2 * H + idx];
+    (idx < H ? g.gb_ym : g.gb_ya)[idx % H] = s;
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 template <typename T, int H, int DH, int DE, int MODE>
@@ -1432,6 +1951,23 @@ hipError_t qkv_shape(const LayerArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int H, int DH, int DE>
+hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
+  constexpr int D = H * DH;
+  const int JT = a.NP / 16;
+  const size_t prep = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + (size_t)a.B * 2 * H +
+                      (size_t)a.B * H * a.NP * DH;
+  const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE>), dim3(JT, a.B), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(256), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX>), dim3((a.B * a.NP + 63) / 64, D / 64), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW>), dim3(3 * D / 64, D / 64), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH>), dim3(3 * D / 64 + 1), dim3(kThreads), 0, s, a, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool shape_supported(int dtype, int H, int dh, int de) {
@@ -1442,6 +1978,16 @@ bool shape_supported(int dtype, int H, int dh, int de) {
 #define EA_SHAPES(CALL, T)                                          \
   if (H == 4 && dh == 16 && de == 16) return CALL(T, 4, 16, 16);    \
   if (H == 8 && dh == 32 && de == 64) return CALL(T, 8, 32, 64);
+
+hipError_t launch_backward(const LayerArgs& a, const BwdArgs& g, int dtype, int H, int dh, int de,
+                           hipStream_t s) {
+  // float32 edge tiles of de = 64 do not fit in registers next to the rest
+  // of the pair kernel: float32 is built for the (4, 16, 16) shape only
+  if (dtype == 1 && H == 4 && dh == 16 && de == 16) return backward_shape<bf16_t, 4, 16, 16>(a, g, s);
+  if (dtype == 1 && H == 8 && dh == 32 && de == 64) return backward_shape<bf16_t, 8, 32, 64>(a, g, s);
+  if (dtype == 0 && H == 4 && dh == 16 && de == 16) return backward_shape<float, 4, 16, 16>(a, g, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_qkv(const LayerArgs& a, int dtype, int H, int dh, int de, hipStream_t s) {
 #define EA_QKV(T, HH, DHH, DEE) qkv_shape<T, HH * DHH, DHH>(a, s)

@@ -25,12 +25,13 @@ EA_VARIANT_UNNORMALIZED = 0x8
 VARIANTS = {"light_edge": EA_VARIANT_LIGHT_EDGE, "no_score_mod": EA_VARIANT_NO_SCORE_MOD,
             "unnormalized": EA_VARIANT_UNNORMALIZED}
 EA_SINGLE_PASS_MAX_N = 256
-KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)")
+KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)", "backward (7 kernels)")
 
 # Symbols declared in include/edge_attn.h.
 EXPORTS = ("ea_ctx_create", "ea_ctx_destroy", "ea_workspace_bytes", "ea_is_two_pass",
            "edge_attn_forward", "edge_update", "edge_attn_layer", "ea_status_str",
            "ea_last_error", "ea_debug_logits", "ea_profile_begin", "ea_profile_end",
+           "ea_backward_workspace_bytes", "edge_attn_backward",
            "ea_kernel_name")
 
 
@@ -57,6 +58,16 @@ class AttnParams(ctypes.Structure):
 
 class UpdateParams(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in UPDATE_PARAM_NAMES]
+
+
+GRAD_NAMES = ATTN_PARAM_NAMES + UPDATE_PARAM_NAMES
+
+
+class Grads(ctypes.Structure):
+    """ea_grads: float32 weight-gradient buffers."""
+    _fields_ = [(k, ctypes.c_void_p) for k in ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_emul", "w_eadd",
+                                               "b_emul", "b_eadd", "w_ymul", "w_yadd", "b_ymul", "b_yadd",
+                                               "w_e", "b_e")]
 
 
 _lib = None
@@ -98,6 +109,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ea_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.ea_kernel_name.restype = ctypes.c_char_p
     lib.ea_kernel_name.argtypes = [ctypes.c_int]
+    lib.ea_backward_workspace_bytes.restype = sz
+    lib.ea_backward_workspace_bytes.argtypes = [vp]
+    lib.edge_attn_backward.restype = ctypes.c_int
+    lib.edge_attn_backward.argtypes = [vp, ap, up, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.POINTER(Grads), vp, sz, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -202,6 +218,20 @@ class EdgeAttention:
         call.keep = keep
         return call
 
+    @property
+    def backward_workspace_bytes(self) -> int:
+        return int(self.lib.ea_backward_workspace_bytes(self.ctx))
+
+    def backward(self, w, X, E, y, mask, A, dO, dEp, dX, dE, dy, grads: Dict, ws, bws, stream=None):
+        """Gradients of the layer after a forward on this context (grads: float32 tensors by name)."""
+        p = self.attn_params(w)
+        u = self.update_params(w)
+        g = Grads(*[_ptr(grads[name]) for name, _ in Grads._fields_])
+        _check(self.lib, self.lib.edge_attn_backward(
+            self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask), _ptr(A),
+            _ptr(dO), _ptr(dEp), _ptr(dX), _ptr(dE), _ptr(dy), ctypes.byref(g),
+            _ptr(ws), self._ws_len(ws), _ptr(bws), self._ws_len(bws), _stream(stream)))
+
     def debug_logits(self, w, X, E, y, mask, U, ws, stream=None):
         p = self.attn_params(w)
         _check(self.lib, self.lib.ea_debug_logits(
@@ -212,10 +242,10 @@ class EdgeAttention:
         _check(self.lib, self.lib.ea_profile_begin(self.ctx))
 
     def profile_end(self) -> Dict[str, tuple]:
-        ms = (ctypes.c_double * 4)()
-        cnt = (ctypes.c_int64 * 4)()
+        ms = (ctypes.c_double * len(KERNELS))()
+        cnt = (ctypes.c_int64 * len(KERNELS))()
         _check(self.lib, self.lib.ea_profile_end(self.ctx, ms, cnt))
-        return {KERNELS[k]: (ms[k], cnt[k]) for k in range(4)}
+        return {KERNELS[k]: (ms[k], cnt[k]) for k in range(len(KERNELS))}
 
     def _ws_len(self, ws) -> int:
         if ws is None:

@@ -168,6 +168,43 @@ ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_
                           const uint8_t* node_mask, void* O, void* A, void* E_out,
                           void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Backward of the layer (forward plus residual edge update): the gradients
+ * of a loss L with respect to the inputs and every weight, given dL/dO and
+ * dL/dE'. The derivative of the definition ("Efficient Edge-aware Attention
+ * Network for Graph Generation", full-text summary: FiLM-modulated scaled
+ * dot-product scores, mask, normalized softmax, A [V | I], E' = E + W_e A +
+ * b_e), with the forward's stored A (bfloat16 mode: its rounding points pass
+ * gradients through unchanged). Supported: single-pass contexts with n <= 64,
+ * no variant flag, bfloat16 for both built shapes and float32 for (4, 16, 16)
+ * (else EA_E_UNSUPPORTED).
+ *
+ * Needs a preceding edge_attn_layer or edge_attn_forward on this context with
+ * the same inputs, parameters, ws and stream (its Q, K, V and global FiLM
+ * stay in ws), and that call's A (else EA_E_STATE). dO [B, n, d] and dE_out
+ * [B, n, n, de] are in the context's dtype, and so are the outputs dX
+ * [B, n, d], dE [B, n, n, de] and dy [B, dy]. Weight gradients are float32,
+ * in the parameters' layouts, overwritten (not accumulated). bws is the
+ * backward's own workspace (ea_backward_workspace_bytes, 256-byte aligned).
+ * Masked pairs get dE = +0.0; padded rows of dX are +0.0.
+ */
+typedef struct {
+  float *w_q, *w_k, *w_v;       /* [d, d] */
+  float *b_q, *b_k, *b_v;       /* [d]    */
+  float *w_emul, *w_eadd;       /* [H, de] */
+  float *b_emul, *b_eadd;       /* [H]    */
+  float *w_ymul, *w_yadd;       /* [H, dy] */
+  float *b_ymul, *b_yadd;       /* [H]    */
+  float *w_e, *b_e;             /* [de, H], [de] */
+} ea_grads;
+
+size_t ea_backward_workspace_bytes(const ea_ctx* ctx);
+ea_status edge_attn_backward(ea_ctx* ctx, const ea_attn_params* p, const ea_update_params* u,
+                             const void* X, const void* E, const void* y, const uint8_t* node_mask,
+                             const void* A, const void* dO, const void* dE_out,
+                             void* dX, void* dE, void* dy, const ea_grads* grads,
+                             void* ws, size_t ws_bytes, void* bws, size_t bws_bytes, void* stream);
+
 const char* ea_status_str(ea_status s);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* ea_last_error(void);
@@ -188,7 +225,7 @@ ea_status ea_debug_logits(ea_ctx* ctx, const ea_attn_params* p,
  * last event and returns, per kernel id, the summed milliseconds and the
  * launch count (arrays of EA_NUM_KERNELS entries).
  */
-enum { EA_K_QKV = 0, EA_K_ATTN = 1, EA_K_UPDATE = 2, EA_K_FUSED = 3, EA_NUM_KERNELS = 4 };
+enum { EA_K_QKV = 0, EA_K_ATTN = 1, EA_K_UPDATE = 2, EA_K_FUSED = 3, EA_K_BACKWARD = 4, EA_NUM_KERNELS = 5 };
 ea_status ea_profile_begin(ea_ctx* ctx);
 ea_status ea_profile_end(ea_ctx* ctx, double* total_ms, int64_t* launches);
 const char* ea_kernel_name(int kernel_id);

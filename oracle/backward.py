@@ -13,8 +13,11 @@ against central finite differences of the C oracle (tests/test_oracle_pins.py).
 
 bf16 mode keeps the forward's rounding points (Q, K, V after the projection,
 A after the softmax) with straight-through gradients (the rounding counts as
-the identity in the backward), which is what a backward built on the stored
-bfloat16 forward values computes.
+the identity in the backward), and takes the softmax Jacobian in terms of
+its stored output, diag(A) - A A^T at the rounded A: what a backward built on
+the stored bfloat16 forward values computes. (Taking it at the unrounded
+softmax instead differs by about 2^-8 relative per term; on gradients that
+nearly cancel, such as a key bias, that is a few percent of the result.)
 
 Masking follows the forward: rows of padded nodes give zero projections, a
 query row with no real key gives A = 0, masked pairs give E' = +0.0 (so their
@@ -38,6 +41,22 @@ def _st_round(x: torch.Tensor, on: bool) -> torch.Tensor:
     if not on:
         return x
     return x + (x.to(torch.bfloat16).to(torch.float64) - x).detach()
+
+
+class _RoundedSoftmax(torch.autograd.Function):
+    """bfloat16-rounded masked softmax whose backward uses the stored (rounded) output."""
+
+    @staticmethod
+    def forward(ctx, u, pmh):
+        A = torch.where(pmh, torch.softmax(u, -1), torch.zeros((), dtype=torch.float64))
+        A = A.to(torch.bfloat16).to(torch.float64)
+        ctx.save_for_backward(A)
+        return A
+
+    @staticmethod
+    def backward(ctx, g):
+        (A,) = ctx.saved_tensors
+        return A * (g - (A * g).sum(-1, keepdim=True)), None
 
 
 def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool):
@@ -68,8 +87,10 @@ def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool):
     has = pmh.any(-1, keepdim=True)
     u = torch.where(pmh, u, torch.tensor(float("-inf"), dtype=torch.float64))
     u = torch.where(has, u, torch.zeros((), dtype=torch.float64))  # rows without a real key
-    A = torch.where(pmh, torch.softmax(u, -1), torch.zeros((), dtype=torch.float64))
-    A = _st_round(A, bf16)
+    if bf16:
+        A = _RoundedSoftmax.apply(u, pmh)
+    else:
+        A = torch.where(pmh, torch.softmax(u, -1), torch.zeros((), dtype=torch.float64))
     O = (A @ v).transpose(1, 2).reshape(B, n, d)
     O = torch.where(m[..., None], O, torch.zeros((), dtype=torch.float64))
     Ep = E + lin(A.permute(0, 2, 3, 1), "w_e", "b_e")

@@ -1,0 +1,110 @@
+"""Backward of the layer on the GPU against the backward oracle (autograd of
+the definition, pinned by finite differences of the C oracle).
+
+Tolerances, per tensor, relative to the tensor's largest reference value:
+float32 1e-4 (the layer's float32 tolerance); bfloat16 2e-2. In bfloat16 the
+GPU takes the softmax Jacobian at the stored (rounded) A where the oracle
+takes it at the unrounded softmax, rounds dO . V-side and FiLM-side
+intermediates to bfloat16 as MFMA operands, and stores dX, dE and dy in
+bfloat16: each step is a relative error of about 2^-8, a few of them in a
+chain. Masked pairs' dE and padded rows' dX are +0.0 bit-exactly.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from edge_aware_graph_amd import workloads as W
+from oracle import backward as OB
+from tests import _layer_harness as HX
+
+pytestmark = pytest.mark.gpu
+
+GRAD_NAMES = ("w_q", "w_k", "w_v", "b_q", "b_k", "b_v", "w_emul", "w_eadd", "b_emul", "b_eadd",
+              "w_ymul", "w_yadd", "b_ymul", "b_yadd", "w_e", "b_e")
+
+
+def dims_of(name, **over):
+    return dataclasses.replace(W.CONFIGS[name].dims, **over)
+
+
+def run_backward(batch, dims, seed=0):
+    dt = HX.tdtype(dims.dtype)
+    run = HX.Run(batch, dims)
+    run.fused()
+    B, n, d, de, H, dy = dims.B, dims.n, dims.d, dims.de, dims.H, dims.dy
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal((B, n, d)).astype(np.float32)
+    dEp = rng.standard_normal((B, n, n, de)).astype(np.float32)
+    if dims.dtype == "bf16":
+        dO, dEp = W.bf16_round_array(dO), W.bf16_round_array(dEp)
+    dev = run.dev
+    t_dO = torch.from_numpy(dO).to("cuda", dt)
+    t_dEp = torch.from_numpy(dEp).to("cuda", dt)
+    dX = torch.full((B, n, d), float("nan"), dtype=dt, device="cuda")
+    dE = torch.full((B, n, n, de), float("nan"), dtype=dt, device="cuda")
+    dyv = torch.full((B, dy), float("nan"), dtype=dt, device="cuda")
+    grads = {k: torch.full(tuple(batch[k].shape), float("nan"), dtype=torch.float32, device="cuda") for k in GRAD_NAMES}
+    bws = torch.empty(run.layer.backward_workspace_bytes, dtype=torch.uint8, device="cuda")
+    run.layer.backward(dev, dev["X"], dev["E"], dev["y"], dev["mask"], run.A, t_dO, t_dEp, dX, dE, dyv,
+                       grads, run.ws, bws)
+    torch.cuda.synchronize()
+    got = {"X": dX.float().cpu().numpy(), "E": dE.float().cpu().numpy(), "y": dyv.float().cpu().numpy()}
+    got.update({k: v.cpu().numpy() for k, v in grads.items()})
+    ref = OB.backward(batch, dO.astype(np.float64), dEp.astype(np.float64), dims.H, bf16=(dims.dtype == "bf16"))
+    return got, ref
+
+
+# Gradients that vanish identically in float32: beta_e and beta_y add a
+# constant to each softmax row (their bias and global weights get
+# sum_j du = 0), so the GPU returns rounding noise of sums whose terms are as
+# large as those of their gamma siblings; their scale is the sibling's. (In
+# bfloat16 the stored A does not sum to exactly 1 and they are small but not
+# zero, the same on both sides.)
+ZERO_SIBLING = {"b_eadd": "b_emul", "b_yadd": "b_ymul", "w_yadd": "w_ymul"}
+
+
+def check(got, ref, batch, dims):
+    tol = 1e-4 if dims.dtype == "fp32" else 2e-2
+    for k in ref:
+        g = got[k].astype(np.float64)
+        assert g.shape == ref[k].shape, k
+        assert np.isfinite(g).all(), "%s has non-finite values" % k
+        scale = max(np.abs(ref[k]).max(), 1e-6)
+        if k in ZERO_SIBLING:
+            if dims.dtype == "fp32":
+                assert np.abs(ref[k]).max() < 1e-9, k
+            scale = max(scale, np.abs(ref[ZERO_SIBLING[k]]).max())
+        err = np.abs(g - ref[k]).max()
+        assert err <= tol * scale, "%s: max err %.3e > %.0e * %.3e" % (k, err, tol, scale)
+    m = batch["mask"].astype(bool)
+    pm = m[:, :, None] & m[:, None, :]
+    assert np.all(got["E"][~pm] == 0) and not np.any(np.signbit(got["E"][~pm]))
+    assert np.all(got["X"][~m] == 0) and not np.any(np.signbit(got["X"][~m]))
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"dtype": "bf16"}), ("planar", {"B": 4})],
+                         ids=["tiny-fp32", "tiny-bf16", "planar-bf16"])
+def test_backward_matches_autograd_oracle(name, over):
+    dims = dims_of(name, **over)
+    batch = W.make_batch(name, bias_scale=0.1, dims=dims)
+    got, ref = run_backward(batch, dims)
+    check(got, ref, batch, dims)
+
+
+@pytest.mark.parametrize("n,dtype", [(37, "bf16"), (50, "bf16"), (17, "fp32")])
+def test_backward_ragged_random_masks(n, dtype):
+    over = {"n": n, "B": 3, "dtype": dtype}
+    if dtype == "fp32":
+        dims = dims_of("tiny", **over)
+    else:
+        dims = dims_of("planar", **over)
+    batch = W.make_batch("tiny", bias_scale=0.2, dims=dims)
+    rng = np.random.default_rng(n)
+    mask = (rng.random((3, n)) < 0.7).astype(np.uint8)
+    mask[0] = 1
+    mask[2] = 0
+    batch["mask"] = mask
+    got, ref = run_backward(batch, dims, seed=n)
+    check(got, ref, batch, dims)
