@@ -42,10 +42,70 @@ def parse():
     ap.add_argument("--hot", action="store_true", help="also time back-to-back calls on one buffer set")
     ap.add_argument("--variant", default="none", choices=sorted(VARIANT_FLAGS),
                     help="ablation variant of the layer (the default is the full layer)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time training steps instead: the layer forward plus its backward")
     ap.add_argument("--sampling-layers", type=int, default=0,
                     help="instead of single layers, time denoising steps of this many stacked layers "
                          "(a step is then one pass through all of them)")
     return ap.parse_args()
+
+
+def backward_bench(args, cfg, dims, batch):
+    """Training step of the layer: edge_attn_layer then edge_attn_backward, on
+    buffer sets rotated so that every step reads from HBM."""
+    import torch
+    from edge_aware_graph_amd.layer import EdgeAttention
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype)
+    w = {k: torch.from_numpy(v).to(dev, dt) for k, v in batch.items() if k.startswith(("w_", "b_"))}
+    B, n, d, de, H, dy = dims.B, dims.n, dims.d, dims.de, dims.H, dims.dy
+    rng = np.random.default_rng(0)
+    sets = []
+    for _ in range(2):
+        sets.append(dict(
+            X=torch.from_numpy(batch["X"]).to(dev, dt), E=torch.from_numpy(batch["E"]).to(dev, dt),
+            y=torch.from_numpy(batch["y"]).to(dev, dt), m=torch.from_numpy(batch["mask"]).to(dev),
+            O=torch.empty(B, n, d, dtype=dt, device=dev), A=torch.empty(B, H, n, n, dtype=dt, device=dev),
+            Eo=torch.empty(B, n, n, de, dtype=dt, device=dev),
+            dO=torch.from_numpy(rng.standard_normal((B, n, d)).astype(np.float32)).to(dev, dt),
+            dEp=torch.from_numpy(rng.standard_normal((B, n, n, de)).astype(np.float32)).to(dev, dt),
+            dX=torch.empty(B, n, d, dtype=dt, device=dev), dE=torch.empty(B, n, n, de, dtype=dt, device=dev),
+            dy=torch.empty(B, dy, dtype=dt, device=dev),
+            g={k: torch.empty(tuple(batch[k].shape), dtype=torch.float32, device=dev)
+               for k in batch if k.startswith(("w_", "b_"))},
+            ws=torch.empty(layer.workspace_bytes, dtype=torch.uint8, device=dev),
+            bws=torch.empty(layer.backward_workspace_bytes, dtype=torch.uint8, device=dev)))
+
+    def step(k):
+        s = sets[k % len(sets)]
+        layer.layer(w, s["X"], s["E"], s["y"], s["m"], s["O"], s["A"], s["Eo"], s["ws"])
+        layer.backward(w, s["X"], s["E"], s["y"], s["m"], s["A"], s["dO"], s["dEp"], s["dX"], s["dE"], s["dy"],
+                       s["g"], s["ws"], s["bws"])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    layer.profile_begin()
+    for k in range(args.steps):
+        step(k)
+    prof = layer.profile_end()
+    kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
+    return {
+        "metric": "graphs/s per training step of the layer (forward + backward)",
+        "value": B / (ms_per_step * 1e-3), "unit": "graphs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded %s graphs, random Xavier weights, random output gradients)" % cfg.structure,
+        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "H": H, "buffer_sets": len(sets)},
+        "kernels": kernels,
+    }
 
 
 def sampling_bench(args, cfg, dims, batch):
@@ -180,6 +240,9 @@ def main():
     n_real = batch["n_real"]
     if args.sampling_layers > 0:
         print(json.dumps(sampling_bench(args, cfg, dims, batch)), flush=True)
+        return
+    if args.backward:
+        print(json.dumps(backward_bench(args, cfg, dims, batch)), flush=True)
         return
     dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
 

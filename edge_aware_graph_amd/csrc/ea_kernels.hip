@@ -1399,11 +1399,16 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
 template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs g) {
   const int NP = a.NP;
+  constexpr int D = H * DH;
   const size_t nz1 = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE, nz2 = (size_t)a.B * 2 * H;
-  const size_t nv = (size_t)a.B * H * NP * DH;
+  const size_t nv = (size_t)a.B * H * NP * DH, nw = (size_t)3 * D * D + 3 * D;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nz1 + nz2 + nv; k += stride) {
-    if (k < nz1) {
+  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nz1 + nz2 + nv + nw; k += stride) {
+    if (k >= nz1 + nz2 + nv) {  // projection weight and bias gradients
+      const size_t q = k - nz1 - nz2 - nv;
+      if (q < (size_t)3 * D * D) (q < (size_t)D * D ? g.gw_q : q < (size_t)2 * D * D ? g.gw_k : g.gw_v)[q % ((size_t)D * D)] = 0.f;
+      else (q - 3 * D * D < D ? g.gb_q : q - 3 * D * D < 2 * D ? g.gb_k : g.gb_v)[(q - 3 * D * D) % D] = 0.f;
+    } else if (k < nz1) {
       size_t q = k;
       if (q < (size_t)H * DE) { g.gw_em[q] = 0.f; continue; }
       q -= (size_t)H * DE;
@@ -1699,32 +1704,41 @@ __global__ __launch_bounds__(kThreads) void bwd_qkv_kernel(LayerArgs a, BwdArgs 
 }
 
 // bwd_pair_reduce: sums over all real pairs of dgamma_e E, dbeta_e E (W_em,
-// W_ea), dE' A (W_e) and dE' (b_e). Each block takes chunks of 64 pairs
-// (b, i, j) in turn, keeps its outputs in registers, and adds them once.
+// W_ea), dE' A (W_e) and dE' (b_e), as float32 MFMA contractions over the
+// pairs: each block takes chunks of 64 pairs (b, i, j) in turn through LDS,
+// wave w owns channels 16 w .. 16 w + 15 and keeps its partial sums in
+// registers; b_e rides along as a column of ones next to the heads.
 template <typename T, int H, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int P = 64, NO1 = 2 * H * DE, NO2 = DE * H, NO = NO1 + NO2 + DE, PER = (NO + kThreads - 1) / kThreads;
+  constexpr int P = 64;
+  static_assert(2 * H <= 16 && H < 16 && DE % 16 == 0 && DE / 16 <= kWaves, "one 16-channel chunk per wave");
   __shared__ float e_s[P][DE + 1], d_s[P][DE + 1], f_s[2 * H][P + 1], a_s[H][P + 1];
-  const int tid = threadIdx.x, NP = a.NP, n = a.n;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4, NP = a.NP, n = a.n;
   const size_t npairs = (size_t)a.B * NP * NP, nchunks = (npairs + P - 1) / P;
   const T* E = static_cast<const T*>(a.E);
   const T* dEp = static_cast<const T*>(g.dEp);
   const T* Ag = static_cast<const T*>(g.A);
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  f32x4 accF = {0.f, 0.f, 0.f, 0.f}, accE = {0.f, 0.f, 0.f, 0.f};
+  const int cb = 16 * w;  // this wave's channels (waves past DE / 16 only help staging)
   for (size_t cidx = blockIdx.x; cidx < nchunks; cidx += gridDim.x) {
-    for (int idx = tid; idx < P * DE; idx += kThreads) {
-      const int p = idx / DE, c = idx % DE;
+    // rows of E and dE': thread (p, quarter) loads a quarter row as fragments
+    static_assert(kThreads == 4 * P, "one thread per pair quarter");
+    {
+      const int p = tid >> 2, qt = tid & 3;
       const size_t q = cidx * P + p;
       const int bq = (int)(q / ((size_t)NP * NP)), ii = (int)((q / NP) % NP), jj = (int)(q % NP);
       const int bc = q < npairs ? bq : 0;
       const bool real = q < npairs && ii < n && jj < n && a.mask[(size_t)bc * n + (ii < n ? ii : 0)] &&
                         a.mask[(size_t)bc * n + (jj < n ? jj : 0)];
-      const size_t off = real ? (((size_t)bq * n + ii) * n + jj) * DE + c : 0;
-      const float ev = Num<T>::ld(E + off), dv = Num<T>::ld(dEp + off);
-      e_s[p][c] = real ? ev : 0.f;
-      d_s[p][c] = real ? dv : 0.f;
+      const size_t off = real ? (((size_t)bq * n + ii) * n + jj) * DE + qt * (DE / 4) : 0;
+      Frag<T, DE / 4> ef, df;
+      ef.load(E + off);
+      df.load(dEp + off);
+#pragma unroll
+      for (int k = 0; k < DE / 4; ++k) {
+        e_s[p][qt * (DE / 4) + k] = real ? ef.get(k) : 0.f;
+        d_s[p][qt * (DE / 4) + k] = real ? df.get(k) : 0.f;
+      }
     }
     for (int idx = tid; idx < P * 3 * H; idx += kThreads) {
       const int p = idx % P, row = idx / P;  // rows 0..2H-1: dF, 2H..3H-1: A
@@ -1743,109 +1757,118 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
       }
     }
     __syncthreads();
+    if (cb < DE) {
+      // MFMA 16x16x4: lane (li, lg) supplies A[li][k = lg] and B[k = lg][li]
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int o = tid + k * kThreads;
-      float s = 0.f;
-      if (o < NO1) {
-        const int row = o / DE, c = o % DE;
-        for (int p = 0; p < P; ++p) s += f_s[row][p] * e_s[p][c];
-      } else if (o < NO1 + NO2) {
-        const int c = (o - NO1) / H, h = (o - NO1) % H;
-        for (int p = 0; p < P; ++p) s += d_s[p][c] * a_s[h][p];
-      } else if (o < NO) {
-        const int c = o - NO1 - NO2;
-        for (int p = 0; p < P; ++p) s += d_s[p][c];
+      for (int ks = 0; ks < P / 4; ++ks) {
+        const int pk = 4 * ks + lg;
+        const float fa = li < 2 * H ? f_s[li < 2 * H ? li : 0][pk] : 0.f;  // FiLM row li
+        accF = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, e_s[pk][cb + li], accF, 0, 0, 0);
+        const float ab = li < H ? a_s[li < H ? li : 0][pk] : (li == H ? 1.f : 0.f);  // head li, or ones
+        accE = __builtin_amdgcn_mfma_f32_16x16x4f32(d_s[pk][cb + li], ab, accE, 0, 0, 0);
       }
-      acc[k] += s;
     }
     __syncthreads();
   }
+  if (cb < DE) {
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int o = tid + k * kThreads;
-    if (o < H * DE) atomicAdd(g.gw_em + o, acc[k]);
-    else if (o < NO1) atomicAdd(g.gw_ea + (o - H * DE), acc[k]);
-    else if (o < NO1 + NO2) atomicAdd(g.gw_e + (o - NO1), acc[k]);
-    else if (o < NO) atomicAdd(g.gb_e + (o - NO1 - NO2), acc[k]);
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lg + r;  // accF: FiLM row 4 lg + r, channel cb + li
+      if (row < H) atomicAdd(g.gw_em + (size_t)row * DE + cb + li, accF[r]);
+      else if (row < 2 * H) atomicAdd(g.gw_ea + (size_t)(row - H) * DE + cb + li, accF[r]);
+      const int ch = cb + 4 * lg + r;  // accE: channel cb + 4 lg + r, head li (or the sum)
+      if (li < H) atomicAdd(g.gw_e + (size_t)ch * H + li, accE[r]);
+      else if (li == H) atomicAdd(g.gb_e + ch, accE[r]);
+    }
   }
 }
 
-// Plain float32 GEMM tiles for the node-level gradients (64 x 64 outputs per
-// block, 4 x 4 per thread, 16-deep chunks through LDS):
+// Float32 GEMM tiles for the node-level gradients (64 x 64 outputs per block,
+// 32 x 32 per wave on float32 MFMA, 16-deep chunks through LDS, the next
+// chunk loaded into registers while the current one is used):
 //   kDX: dX[row, c] = sum_f DQKV[row, f] W_f[c] over f < 3D (W_q; W_k; W_v),
 //        rows (b, i) with i < n;
 //   kDW: dW_w[f, c] = sum over real rows of DQKV[row, w D + f] X[row, c].
 enum BwdGemm : int { kDX = 0, kDW = 1 };
 template <typename T, int H, int DH, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int D = H * DH, TM = 64, TN = 64, TK = 16;
+  constexpr int D = H * DH, TM = 64, TN = 64, TK = 16, PER = TK * TM / kThreads;
   __shared__ float as[TK][TM + 4], bs[TK][TN + 4];
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int wm = w & 1, wn = w >> 1;
   const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
   const int NP = a.NP, n = a.n;
   const int M = MODE == kDX ? a.B * NP : 3 * D, K = MODE == kDX ? 3 * D : a.B * NP;
+  // blockIdx.z takes a slice of the contraction (kDW: the partial sums are added atomically)
+  const int kslice = (K + gridDim.z - 1) / gridDim.z;
+  const int kbeg = blockIdx.z * kslice, kend = K < kbeg + kslice ? K : kbeg + kslice;
   const T* X = static_cast<const T*>(a.X);
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += TK) {
-    for (int idx = tid; idx < TK * TM; idx += kThreads) {
-      const int kk = idx / TM, mm = idx % TM, m = m0 + mm, k = k0 + kk;
-      float v = 0.f;
-      if (MODE == kDX) {
-        if (m < M && k < K) v = g.DQKV[(size_t)m * 3 * D + k];
-      } else {
-        // A(f, row) = DQKV[row][f]; rows of padded or masked nodes count as 0
-        if (m < M && k < K) v = g.DQKV[(size_t)k * 3 * D + m];
-      }
-      as[kk][mm] = v;
+  auto load_a = [&](int k0, int e) {
+    const int idx = tid + e * kThreads, kk = idx / TM, mm = idx % TM, m = m0 + mm, k = k0 + kk;
+    if (m >= M || k >= kend) return 0.f;
+    return MODE == kDX ? g.DQKV[(size_t)m * 3 * D + k] : g.DQKV[(size_t)k * 3 * D + m];
+  };
+  auto load_b = [&](int k0, int e) {
+    const int idx = tid + e * kThreads, kk = idx / TN, nn = idx % TN, c = n0 + nn, k = k0 + kk;
+    if (k >= kend || c >= D) return 0.f;
+    if (MODE == kDX) {
+      const int wsel = k / D, f = k % D;
+      const T* W = static_cast<const T*>(wsel == 0 ? a.w_q : wsel == 1 ? a.w_k : a.w_v);
+      return Num<T>::ld(W + (size_t)f * D + c);
     }
-    for (int idx = tid; idx < TK * TN; idx += kThreads) {
-      const int kk = idx / TN, nn = idx % TN, c = n0 + nn, k = k0 + kk;
-      float v = 0.f;
-      if (MODE == kDX) {
-        if (k < K && c < D) {
-          const int wsel = k / D, f = k % D;
-          const T* W = static_cast<const T*>(wsel == 0 ? a.w_q : wsel == 1 ? a.w_k : a.w_v);
-          v = Num<T>::ld(W + (size_t)f * D + c);
-        }
-      } else {
-        if (k < K && c < D) {
-          const int bq = k / NP, ii = k % NP;
-          const bool real = ii < n && a.mask[(size_t)bq * n + (ii < n ? ii : 0)];
-          const float x = Num<T>::ld(X + ((size_t)bq * n + (real ? ii : 0)) * D + c);
-          v = real ? x : 0.f;
-        }
-      }
-      bs[kk][nn] = v;
+    // rows of padded or masked nodes count as 0 (their X may hold anything)
+    const int bq = k / NP, ii = k % NP;
+    const bool real = ii < n && a.mask[(size_t)bq * n + (ii < n ? ii : 0)];
+    const float x = Num<T>::ld(X + ((size_t)bq * n + (real ? ii : 0)) * D + c);
+    return real ? x : 0.f;
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ra[PER], rb[PER];  // the next chunk, loaded while the current one is used
+#pragma unroll
+  for (int e = 0; e < PER; ++e) { ra[e] = load_a(kbeg, e); rb[e] = load_b(kbeg, e); }
+  for (int k0 = kbeg; k0 < kend; k0 += TK) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + e * kThreads;
+      as[idx / TM][idx % TM] = ra[e];
+      bs[idx / TN][idx % TN] = rb[e];
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < TK; ++kk) {
-      float av[4], bv[4];
+    for (int e = 0; e < PER; ++e) { ra[e] = load_a(k0 + TK, e); rb[e] = load_b(k0 + TK, e); }
+    // float32 MFMA 16x16x4: wave (wm, wn) computes rows wm*32 .., columns wn*32 ..
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { av[r] = as[kk][ty * 4 + r]; bv[r] = bs[kk][tx * 4 + r]; }
+    for (int ks = 0; ks < TK / 4; ++ks) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(as[4 * ks + lg][wm * 32 + mt * 16 + li],
+                                                             bs[4 * ks + lg][wn * 32 + nt * 16 + li],
+                                                             acc[mt][nt], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = m0 + ty * 4 + r;
+  for (int e = 0; e < 16; ++e) {
+    const int mt = e >> 3, nt = (e >> 2) & 1, r = e & 3;
+    const int m = m0 + wm * 32 + mt * 16 + 4 * lg + r;
     if (m >= M) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int col = n0 + tx * 4 + c;
+    {
+      const int col = n0 + wn * 32 + nt * 16 + li;
+      const float v = acc[mt][nt][r];
       if (col >= D) continue;
       if (MODE == kDX) {
         const int bq = m / NP, ii = m % NP;
-        if (ii < n) Num<T>::st(static_cast<T*>(g.dX) + ((size_t)bq * n + ii) * D + col, acc[r][c]);
+        if (ii < n) Num<T>::st(static_cast<T*>(g.dX) + ((size_t)bq * n + ii) * D + col, v);
       } else {
         const int wsel = m / D, f = m % D;
         float* dst = wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v;
-        dst[(size_t)f * D + col] = acc[r][c];
+        atomicAdd(dst + (size_t)f * D + col, v);
       }
     }
   }
@@ -1858,43 +1881,74 @@ __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArg
   constexpr int D = H * DH;
   __shared__ float part_s[4][64];
   const int tid = threadIdx.x, NP = a.NP, B = a.B;
-  if (blockIdx.x < 3 * D / 64) {
+  if (blockIdx.x < 3 * D / 64) {  // rows split over blockIdx.y, partial sums added atomically
     const int f = blockIdx.x * 64 + (tid & 63), q = tid >> 6;
     float s = 0.f;
-    for (int row = q; row < B * NP; row += 4) s += g.DQKV[(size_t)row * 3 * D + f];
+    for (int row = blockIdx.y * 4 + q; row < B * NP; row += 4 * gridDim.y) s += g.DQKV[(size_t)row * 3 * D + f];
     part_s[q][tid & 63] = s;
     __syncthreads();
     if (tid < 64) {
       const float t = part_s[0][tid] + part_s[1][tid] + part_s[2][tid] + part_s[3][tid];
       const int wsel = f / D;
       float* dst = wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v;
-      dst[f % D] = t;
+      atomicAdd(dst + f % D, t);
     }
     return;
   }
+  if (blockIdx.y != 0) return;
+  // global FiLM: dy = W_ymul^T dgamma_y + W_yadd^T dbeta_y per graph, and
+  // the weight and bias gradients as sums over graphs, in chunks of graphs
+  // staged through LDS (each thread keeps its weight-gradient outputs)
+  constexpr int GB = 16, MAXDY = 512;
+  __shared__ float dg_s[GB][2 * H];
+  __shared__ float w_s[2 * H][MAXDY], y_s[GB][MAXDY];
   const int dy = a.dy;
   const T* y = static_cast<const T*>(a.y);
   const T* Wm = static_cast<const T*>(a.w_ymul);
   const T* Wa = static_cast<const T*>(a.w_yadd);
-  for (int idx = tid; idx < B * dy; idx += kThreads) {
-    const int bq = idx / dy, c = idx % dy;
-    float s = 0.f;
-    for (int h = 0; h < H; ++h)
-      s += Num<T>::ld(Wm + (size_t)h * dy + c) * g.DGY[(size_t)bq * 2 * H + h] +
-           Num<T>::ld(Wa + (size_t)h * dy + c) * g.DGY[(size_t)bq * 2 * H + H + h];
-    Num<T>::st(static_cast<T*>(g.dy) + idx, s);
-  }
+  constexpr int OPT = (2 * H * MAXDY + kThreads - 1) / kThreads;
+  float accw[OPT], accb = 0.f;
+#pragma unroll
+  for (int k = 0; k < OPT; ++k) accw[k] = 0.f;
   for (int idx = tid; idx < 2 * H * dy; idx += kThreads) {
-    const int row = idx / dy, c = idx % dy;  // rows 0..H-1: W_ymul, H..2H-1: W_yadd
-    float s = 0.f;
-    for (int bq = 0; bq < B; ++bq) s += g.DGY[(size_t)bq * 2 * H + row] * Num<T>::ld(y + (size_t)bq * dy + c);
-    (row < H ? g.gw_ym : g.gw_ya)[(size_t)(row % H) * dy + c] = s;
+    const int row = idx / dy, c = idx % dy;
+    w_s[row][c] = Num<T>::ld((row < H ? Wm : Wa) + (size_t)(row % H) * dy + c);
   }
-  for (int idx = tid; idx < 2 * H; idx += kThreads) {
-    float s = 0.f;
-    for (int bq = 0; bq < B; ++bq) s += g.DGY[(size_t)bq * 2 * H + idx];
-    (idx < H ? g.gb_ym : g.gb_ya)[idx % H] = s;
+  for (int b0 = 0; b0 < B; b0 += GB) {
+    for (int idx = tid; idx < GB * 2 * H; idx += kThreads) {
+      const int bb = idx / (2 * H), o = idx % (2 * H);
+      dg_s[bb][o] = b0 + bb < B ? g.DGY[(size_t)(b0 + bb) * 2 * H + o] : 0.f;
+    }
+    for (int idx = tid; idx < GB * dy; idx += kThreads) {
+      const int bb = idx / dy, c = idx % dy;
+      y_s[bb][c] = b0 + bb < B ? Num<T>::ld(y + (size_t)(b0 + bb) * dy + c) : 0.f;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GB * dy; idx += kThreads) {
+      const int bb = idx / dy, c = idx % dy;
+      if (b0 + bb >= B) continue;
+      float s = 0.f;
+      for (int h = 0; h < H; ++h) s += w_s[h][c] * dg_s[bb][h] + w_s[H + h][c] * dg_s[bb][H + h];
+      Num<T>::st(static_cast<T*>(g.dy) + (size_t)(b0 + bb) * dy + c, s);
+    }
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      const int o = tid + k * kThreads, row = o / (dy > 0 ? dy : 1), c = o % (dy > 0 ? dy : 1);
+      if (o >= 2 * H * dy) continue;
+      float s = 0.f;
+      for (int bb = 0; bb < GB; ++bb) s += dg_s[bb][row] * y_s[bb][c];
+      accw[k] += s;
+    }
+    if (tid < 2 * H)
+      for (int bb = 0; bb < GB && b0 + bb < B; ++bb) accb += dg_s[bb][tid];
+    __syncthreads();
   }
+#pragma unroll
+  for (int k = 0; k < OPT; ++k) {
+    const int o = tid + k * kThreads;
+    if (o < 2 * H * dy) (o / dy < H ? g.gw_ym : g.gw_ya)[(size_t)((o / dy) % H) * dy + o % dy] = accw[k];
+  }
+  if (tid < 2 * H) (tid < H ? g.gb_ym : g.gb_ya)[tid % H] = accb;
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1956,15 +2010,20 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   constexpr int D = H * DH;
   const int JT = a.NP / 16;
   const size_t prep = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + (size_t)a.B * 2 * H +
-                      (size_t)a.B * H * a.NP * DH;
+                      (size_t)a.B * H * a.NP * DH + (size_t)3 * D * D + 3 * D;
   const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
   hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE>), dim3(JT, a.B), dim3(kThreads), 0, s, a, g);
   hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(256), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX>), dim3((a.B * a.NP + 63) / 64, D / 64), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW>), dim3(3 * D / 64, D / 64), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH>), dim3(3 * D / 64 + 1), dim3(kThreads), 0, s, a, g);
+  const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
+  const unsigned red_blocks = (unsigned)(chunks < 512 ? chunks : 512);  // atomics per output: one per block
+  hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX>), dim3((a.B * a.NP + 63) / 64, D / 64, 1), dim3(kThreads), 0, s, a, g);
+  // dW: the rows (contraction) split in slices of at least 256
+  const int rows = a.B * a.NP, ksplit = rows / 256 < 1 ? 1 : (rows / 256 > 16 ? 16 : rows / 256);
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW>), dim3(3 * D / 64, D / 64, ksplit), dim3(kThreads), 0, s, a, g);
+  const int bsplit = rows / 512 < 1 ? 1 : (rows / 512 > 32 ? 32 : rows / 512);
+  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH>), dim3(3 * D / 64 + 1, bsplit), dim3(kThreads), 0, s, a, g);
   return hipGetLastError();
 }
 
