@@ -366,7 +366,6 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   if (c->d.flags & kVariants) return fail(EA_E_UNSUPPORTED, "the backward is built for the full layer (no variant flag)");
   if (c->d.dtype == EA_FP32 && c->d.de != 16)
     return fail(EA_E_UNSUPPORTED, "the float32 backward is built for (H, dh, de) = (4, 16, 16)");
-  if (c->d.dy > 512) return fail(EA_E_UNSUPPORTED, "the backward is built for dy <= 512 (dy = %d)", c->d.dy);
   EA_TRY(check_attn_params(c, p));
   EA_TRY(check_ptr(p->b_emul, "b_emul", 4, false));
   if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");

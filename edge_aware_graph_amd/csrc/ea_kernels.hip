@@ -1400,7 +1400,8 @@ template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs g) {
   const int NP = a.NP;
   constexpr int D = H * DH;
-  const size_t nz1 = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE, nz2 = (size_t)a.B * 2 * H;
+  const size_t nzy = (size_t)2 * H * a.dy + 2 * H;  // global FiLM weight and bias gradients
+  const size_t nz1 = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + nzy, nz2 = (size_t)a.B * 2 * H;
   const size_t nv = (size_t)a.B * H * NP * DH, nw = (size_t)3 * D * D + 3 * D;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nz1 + nz2 + nv + nw; k += stride) {
@@ -1420,7 +1421,13 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
       q -= H;
       if (q < (size_t)DE * H) { g.gw_e[q] = 0.f; continue; }
       q -= (size_t)DE * H;
-      g.gb_e[q] = 0.f;
+      if (q < (size_t)DE) { g.gb_e[q] = 0.f; continue; }
+      q -= DE;
+      if (q < (size_t)H * a.dy) { g.gw_ym[q] = 0.f; continue; }
+      q -= (size_t)H * a.dy;
+      if (q < (size_t)H * a.dy) { g.gw_ya[q] = 0.f; continue; }
+      q -= (size_t)H * a.dy;
+      (q < (size_t)H ? g.gb_ym : g.gb_ya)[q % H] = 0.f;
     } else if (k < nz1 + nz2) {
       g.DGY[k - nz1] = 0.f;
     } else {
@@ -1714,49 +1721,71 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
   static_assert(2 * H <= 16 && H < 16 && DE % 16 == 0 && DE / 16 <= kWaves, "one 16-channel chunk per wave");
   __shared__ float e_s[P][DE + 1], d_s[P][DE + 1], f_s[2 * H][P + 1], a_s[H][P + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4, NP = a.NP, n = a.n;
-  const size_t npairs = (size_t)a.B * NP * NP, nchunks = (npairs + P - 1) / P;
+  // pair q = (b NP + i) NP + j; B NP^2 < 2^31 for n <= 64
+  const uint32_t npairs = (uint32_t)a.B * NP * NP, nchunks = (npairs + P - 1) / P;
   const T* E = static_cast<const T*>(a.E);
   const T* dEp = static_cast<const T*>(g.dEp);
   const T* Ag = static_cast<const T*>(g.A);
   f32x4 accF = {0.f, 0.f, 0.f, 0.f}, accE = {0.f, 0.f, 0.f, 0.f};
   const int cb = 16 * w;  // this wave's channels (waves past DE / 16 only help staging)
-  for (size_t cidx = blockIdx.x; cidx < nchunks; cidx += gridDim.x) {
-    // rows of E and dE': thread (p, quarter) loads a quarter row as fragments
-    static_assert(kThreads == 4 * P, "one thread per pair quarter");
+  static_assert(kThreads == 4 * P, "one thread per pair quarter");
+  constexpr int NS = (P * 3 * H + kThreads - 1) / kThreads;  // dF and A values per thread
+  // one chunk's loads into registers: a quarter row of E and dE' of pair
+  // tid / 4, and NS of the chunk's dF / A values
+  struct Regs {
+    Frag<T, DE / 4> ef, df;
+    bool real;
+    float v[NS];
+  };
+  auto load_chunk = [&](uint32_t cidx, Regs& r) {
     {
       const int p = tid >> 2, qt = tid & 3;
-      const size_t q = cidx * P + p;
-      const int bq = (int)(q / ((size_t)NP * NP)), ii = (int)((q / NP) % NP), jj = (int)(q % NP);
-      const int bc = q < npairs ? bq : 0;
-      const bool real = q < npairs && ii < n && jj < n && a.mask[(size_t)bc * n + (ii < n ? ii : 0)] &&
-                        a.mask[(size_t)bc * n + (jj < n ? jj : 0)];
-      const size_t off = real ? (((size_t)bq * n + ii) * n + jj) * DE + qt * (DE / 4) : 0;
-      Frag<T, DE / 4> ef, df;
-      ef.load(E + off);
-      df.load(dEp + off);
+      const uint32_t q = cidx * P + p;
+      const uint32_t bq = q / (NP * NP), ii = (q / NP) % NP, jj = q % NP;
+      const uint32_t bc = q < npairs ? bq : 0;
+      // both mask bytes are loaded unconditionally and combined without branches
+      const uint32_t mi = a.mask[(size_t)bc * n + (ii < (uint32_t)n ? ii : 0)];
+      const uint32_t mj = a.mask[(size_t)bc * n + (jj < (uint32_t)n ? jj : 0)];
+      r.real = ((uint32_t)(q < npairs) & (uint32_t)(ii < (uint32_t)n) & (uint32_t)(jj < (uint32_t)n) & (mi != 0) & (mj != 0)) != 0;
+      const size_t off = r.real ? (((size_t)bq * n + ii) * n + jj) * DE + qt * (DE / 4) : 0;
+      r.ef.load(E + off);
+      r.df.load(dEp + off);
+    }
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int idx = tid + k * kThreads, p = idx % P, row = idx / P;  // rows 0..2H-1: dF, 2H..3H-1: A
+      const uint32_t q = cidx * P + p;
+      const uint32_t bq = q / (NP * NP), ii = (q / NP) % NP, jj = q % NP;
+      const bool inr = q < npairs && row < 3 * H;
+      const uint32_t bc = inr ? bq : 0;  // addresses stay inside the buffers past the last pair
+      // both candidates are loaded (clamped addresses), then one is selected
+      const int fr = row < 2 * H ? row : 0, h = row >= 2 * H && row < 3 * H ? row - 2 * H : 0;
+      const bool ok = inr && ii < (uint32_t)n && jj < (uint32_t)n;
+      const float xf = g.DF[(((size_t)bc * 2 * H + fr) * NP + ii) * NP + jj];
+      const float xa = Num<T>::ld(Ag + (((size_t)bc * H + h) * n + (ok ? ii : 0)) * n + (ok ? jj : 0));
+      r.v[k] = row < 2 * H ? (inr ? xf : 0.f) : (ok ? xa : 0.f);
+    }
+  };
+  Regs cur, nxt;
+  uint32_t cidx = blockIdx.x;
+  if (cidx < nchunks) load_chunk(cidx, cur);
+  for (; cidx < nchunks; cidx += gridDim.x) {
+    {
+      const int p = tid >> 2, qt = tid & 3;
 #pragma unroll
       for (int k = 0; k < DE / 4; ++k) {
-        e_s[p][qt * (DE / 4) + k] = real ? ef.get(k) : 0.f;
-        d_s[p][qt * (DE / 4) + k] = real ? df.get(k) : 0.f;
+        e_s[p][qt * (DE / 4) + k] = cur.real ? cur.ef.get(k) : 0.f;
+        d_s[p][qt * (DE / 4) + k] = cur.real ? cur.df.get(k) : 0.f;
       }
-    }
-    for (int idx = tid; idx < P * 3 * H; idx += kThreads) {
-      const int p = idx % P, row = idx / P;  // rows 0..2H-1: dF, 2H..3H-1: A
-      const size_t q = cidx * P + p;
-      const int bq = (int)(q / ((size_t)NP * NP)), ii = (int)((q / NP) % NP), jj = (int)(q % NP);
-      const bool inr = q < npairs;
-      const int bc = inr ? bq : 0;  // addresses stay inside the buffers past the last pair
-      if (row < 2 * H) {
-        const float v = g.DF[(((size_t)bc * 2 * H + row) * NP + ii) * NP + jj];
-        f_s[row][p] = inr ? v : 0.f;
-      } else {
-        const int h = row - 2 * H;
-        const bool ok = inr && ii < n && jj < n;
-        const float v = Num<T>::ld(Ag + (((size_t)bc * H + h) * n + (ok ? ii : 0)) * n + (ok ? jj : 0));
-        a_s[h][p] = ok ? v : 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int idx = tid + k * kThreads, pp = idx % P, row = idx / P;
+        if (row < 2 * H) f_s[row][pp] = cur.v[k];
+        else if (row < 3 * H) a_s[row - 2 * H][pp] = cur.v[k];
       }
     }
     __syncthreads();
+    if (cidx + gridDim.x < nchunks) load_chunk(cidx + gridDim.x, nxt);
     if (cb < DE) {
       // MFMA 16x16x4: lane (li, lg) supplies A[li][k = lg] and B[k = lg][li]
 #pragma unroll
@@ -1769,6 +1798,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
       }
     }
     __syncthreads();
+    cur = nxt;
   }
   if (cb < DE) {
 #pragma unroll
@@ -1784,15 +1814,19 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
 }
 
 // Float32 GEMM tiles for the node-level gradients (64 x 64 outputs per block,
-// 32 x 32 per wave on float32 MFMA, 16-deep chunks through LDS, the next
+// 32 x 32 per wave on float32 MFMA, 64-deep chunks through LDS, the next
 // chunk loaded into registers while the current one is used):
 //   kDX: dX[row, c] = sum_f DQKV[row, f] W_f[c] over f < 3D (W_q; W_k; W_v),
 //        rows (b, i) with i < n;
-//   kDW: dW_w[f, c] = sum over real rows of DQKV[row, w D + f] X[row, c].
+//   kDW: dW_w[f, c] = sum over real rows of DQKV[row, w D + f] X[row, c],
+//        and (blocks of the first column tile) db_w[f] = sum over rows of
+//        DQKV[row, w D + f], read from the same staged chunks.
 enum BwdGemm : int { kDX = 0, kDW = 1 };
-template <typename T, int H, int DH, int MODE>
+template <typename T, int H, int DH, int MODE, int TM>
 __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int D = H * DH, TM = 64, TN = 64, TK = 16, PER = TK * TM / kThreads;
+  constexpr int D = H * DH, TN = 64, TK = 64, PERA = TK * TM / kThreads, PERB = TK * TN / kThreads;
+  constexpr int MT = TM / 32;  // 16-row MFMA tiles per wave (waves in a 2 x 2 grid)
+  static_assert((TM == 32 || TM == 64) && (MODE == kDX || TM == 64), "tile rows");
   __shared__ float as[TK][TM + 4], bs[TK][TN + 4];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int wm = w & 1, wn = w >> 1;
@@ -1803,60 +1837,93 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
   const int kslice = (K + gridDim.z - 1) / gridDim.z;
   const int kbeg = blockIdx.z * kslice, kend = K < kbeg + kslice ? K : kbeg + kslice;
   const T* X = static_cast<const T*>(a.X);
+  // element e of this thread's share of an A chunk: kDX reads DQKV rows (k
+  // fastest across the lanes), kDW reads DQKV columns (m fastest)
+  auto a_kk = [&](int e) { const int idx = tid + e * kThreads; return MODE == kDX ? idx % TK : idx / TM; };
+  auto a_mm = [&](int e) { const int idx = tid + e * kThreads; return MODE == kDX ? idx / TK : idx % TM; };
+  // Out-of-range elements load from a clamped address and are then replaced
+  // by 0: every load is issued unconditionally, so the loads of a chunk stay
+  // in flight together (a load under a branch is waited for at the branch's end).
   auto load_a = [&](int k0, int e) {
-    const int idx = tid + e * kThreads, kk = idx / TM, mm = idx % TM, m = m0 + mm, k = k0 + kk;
-    if (m >= M || k >= kend) return 0.f;
-    return MODE == kDX ? g.DQKV[(size_t)m * 3 * D + k] : g.DQKV[(size_t)k * 3 * D + m];
+    const int kk = a_kk(e), mm = a_mm(e), m = m0 + mm, k = k0 + kk;
+    const bool ok = m < M && k < kend;
+    const int mc = ok ? m : 0, kc = ok ? k : 0;
+    const float x = MODE == kDX ? g.DQKV[(size_t)mc * 3 * D + kc] : g.DQKV[(size_t)kc * 3 * D + mc];
+    return ok ? x : 0.f;
   };
   auto load_b = [&](int k0, int e) {
     const int idx = tid + e * kThreads, kk = idx / TN, nn = idx % TN, c = n0 + nn, k = k0 + kk;
-    if (k >= kend || c >= D) return 0.f;
+    const bool ok = k < kend && c < D;
+    const int kc = ok ? k : 0, cc = ok ? c : 0;
     if (MODE == kDX) {
-      const int wsel = k / D, f = k % D;
+      const int wsel = kc / D, f = kc % D;
       const T* W = static_cast<const T*>(wsel == 0 ? a.w_q : wsel == 1 ? a.w_k : a.w_v);
-      return Num<T>::ld(W + (size_t)f * D + c);
+      const float x = Num<T>::ld(W + (size_t)f * D + cc);
+      return ok ? x : 0.f;
     }
     // rows of padded or masked nodes count as 0 (their X may hold anything)
-    const int bq = k / NP, ii = k % NP;
-    const bool real = ii < n && a.mask[(size_t)bq * n + (ii < n ? ii : 0)];
-    const float x = Num<T>::ld(X + ((size_t)bq * n + (real ? ii : 0)) * D + c);
-    return real ? x : 0.f;
+    const int bq = kc / NP, ii = kc % NP, ic = ii < n ? ii : 0;
+    const bool mk = a.mask[(size_t)bq * n + ic] != 0;
+    const float x = Num<T>::ld(X + ((size_t)bq * n + ic) * D + cc);
+    return ok && ii < n && mk ? x : 0.f;
   };
-  f32x4 acc[2][2];
+  f32x4 acc[MT][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ra[PER], rb[PER];  // the next chunk, loaded while the current one is used
+  float ra[PERA], rb[PERB];  // the next chunk, loaded while the current one is used
+  float csum = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) { ra[e] = load_a(kbeg, e); rb[e] = load_b(kbeg, e); }
+  for (int e = 0; e < PERA; ++e) ra[e] = load_a(kbeg, e);
+#pragma unroll
+  for (int e = 0; e < PERB; ++e) rb[e] = load_b(kbeg, e);
   for (int k0 = kbeg; k0 < kend; k0 += TK) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
+    for (int e = 0; e < PERA; ++e) as[a_kk(e)][a_mm(e)] = ra[e];
+#pragma unroll
+    for (int e = 0; e < PERB; ++e) {
       const int idx = tid + e * kThreads;
-      as[idx / TM][idx % TM] = ra[e];
       bs[idx / TN][idx % TN] = rb[e];
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < PER; ++e) { ra[e] = load_a(k0 + TK, e); rb[e] = load_b(k0 + TK, e); }
-    // float32 MFMA 16x16x4: wave (wm, wn) computes rows wm*32 .., columns wn*32 ..
+    for (int e = 0; e < PERA; ++e) ra[e] = load_a(k0 + TK, e);
+#pragma unroll
+    for (int e = 0; e < PERB; ++e) rb[e] = load_b(k0 + TK, e);
+    // float32 MFMA 16x16x4: wave (wm, wn) computes rows wm*TM/2 .., columns wn*32 ..
 #pragma unroll
     for (int ks = 0; ks < TK / 4; ++ks) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(as[4 * ks + lg][wm * 32 + mt * 16 + li],
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(as[4 * ks + lg][wm * (TM / 2) + mt * 16 + li],
                                                              bs[4 * ks + lg][wn * 32 + nt * 16 + li],
                                                              acc[mt][nt], 0, 0, 0);
     }
+    if (MODE == kDW && blockIdx.y == 0) {
+      // bias gradients: column sums of this chunk of DQKV (all rows; rows of
+      // padded or masked nodes hold 0), thread t sums rows t / 64 * TK / 4 ..
+#pragma unroll
+      for (int kk = 0; kk < TK / 4; ++kk) csum += as[(tid >> 6) * (TK / 4) + kk][tid & 63];
+    }
     __syncthreads();
   }
+  if (MODE == kDW && blockIdx.y == 0) {
+    as[tid >> 6][tid & 63] = csum;
+    __syncthreads();
+    const int m = m0 + tid;
+    if (tid < 64 && m < M) {
+      const float t = as[0][tid] + as[1][tid] + as[2][tid] + as[3][tid];
+      const int wsel = m / D;
+      atomicAdd((wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v) + m % D, t);
+    }
+  }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 8 * MT; ++e) {
     const int mt = e >> 3, nt = (e >> 2) & 1, r = e & 3;
-    const int m = m0 + wm * 32 + mt * 16 + 4 * lg + r;
+    const int m = m0 + wm * (TM / 2) + mt * 16 + 4 * lg + r;
     if (m >= M) continue;
     {
       const int col = n0 + wn * 32 + nt * 16 + li;
@@ -1874,81 +1941,61 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
   }
 }
 
-// bwd_small: bias gradients of the projections (blocks 0 .. 3D/64 - 1, 64
-// features each) and the global FiLM's gradients and dy (the last block).
+// bwd_small: the global FiLM's gradients and dy. Block row blockIdx.y takes
+// graphs b0 = 16 blockIdx.y .. b0 + 15; each thread computes one item:
+//   dy[b][c]         = sum_h W_ymul[h][c] dgamma_y[b][h] + W_yadd[h][c] dbeta_y[b][h]
+//   dW_y(mul|add)[h][c] += sum_b dgamma_y|dbeta_y[b][h] y[b][c]   (atomic over blocks)
+//   db_y(mul|add)[h]    += sum_b dgamma_y|dbeta_y[b][h]           (atomic over blocks)
+// All of an item's loads are independent and issued together.
 template <typename T, int H, int DH>
 __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int D = H * DH;
-  __shared__ float part_s[4][64];
-  const int tid = threadIdx.x, NP = a.NP, B = a.B;
-  if (blockIdx.x < 3 * D / 64) {  // rows split over blockIdx.y, partial sums added atomically
-    const int f = blockIdx.x * 64 + (tid & 63), q = tid >> 6;
-    float s = 0.f;
-    for (int row = blockIdx.y * 4 + q; row < B * NP; row += 4 * gridDim.y) s += g.DQKV[(size_t)row * 3 * D + f];
-    part_s[q][tid & 63] = s;
-    __syncthreads();
-    if (tid < 64) {
-      const float t = part_s[0][tid] + part_s[1][tid] + part_s[2][tid] + part_s[3][tid];
-      const int wsel = f / D;
-      float* dst = wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v;
-      atomicAdd(dst + f % D, t);
-    }
-    return;
-  }
-  if (blockIdx.y != 0) return;
-  // global FiLM: dy = W_ymul^T dgamma_y + W_yadd^T dbeta_y per graph, and
-  // the weight and bias gradients as sums over graphs, in chunks of graphs
-  // staged through LDS (each thread keeps its weight-gradient outputs)
-  constexpr int GB = 16, MAXDY = 512;
-  __shared__ float dg_s[GB][2 * H];
-  __shared__ float w_s[2 * H][MAXDY], y_s[GB][MAXDY];
-  const int dy = a.dy;
+  constexpr int GB = 16;
+  const int B = a.B, dy = a.dy, b0 = blockIdx.y * GB;
+  const int item = blockIdx.x * kThreads + threadIdx.x;
+  const int n_dy = GB * dy, n_w = 2 * H * dy, n_b = 2 * H;
   const T* y = static_cast<const T*>(a.y);
   const T* Wm = static_cast<const T*>(a.w_ymul);
   const T* Wa = static_cast<const T*>(a.w_yadd);
-  constexpr int OPT = (2 * H * MAXDY + kThreads - 1) / kThreads;
-  float accw[OPT], accb = 0.f;
+  if (item < n_dy) {
+    const int bb = item / dy, c = item % dy, b = b0 + bb, bc = b < B ? b : 0;
+    float dg[2 * H], wv[2 * H];
 #pragma unroll
-  for (int k = 0; k < OPT; ++k) accw[k] = 0.f;
-  for (int idx = tid; idx < 2 * H * dy; idx += kThreads) {
-    const int row = idx / dy, c = idx % dy;
-    w_s[row][c] = Num<T>::ld((row < H ? Wm : Wa) + (size_t)(row % H) * dy + c);
-  }
-  for (int b0 = 0; b0 < B; b0 += GB) {
-    for (int idx = tid; idx < GB * 2 * H; idx += kThreads) {
-      const int bb = idx / (2 * H), o = idx % (2 * H);
-      dg_s[bb][o] = b0 + bb < B ? g.DGY[(size_t)(b0 + bb) * 2 * H + o] : 0.f;
+    for (int o = 0; o < 2 * H; ++o) {
+      dg[o] = g.DGY[(size_t)bc * 2 * H + o];
+      wv[o] = Num<T>::ld((o < H ? Wm : Wa) + (size_t)(o % H) * dy + c);
     }
-    for (int idx = tid; idx < GB * dy; idx += kThreads) {
-      const int bb = idx / dy, c = idx % dy;
-      y_s[bb][c] = b0 + bb < B ? Num<T>::ld(y + (size_t)(b0 + bb) * dy + c) : 0.f;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < GB * dy; idx += kThreads) {
-      const int bb = idx / dy, c = idx % dy;
-      if (b0 + bb >= B) continue;
-      float s = 0.f;
-      for (int h = 0; h < H; ++h) s += w_s[h][c] * dg_s[bb][h] + w_s[H + h][c] * dg_s[bb][H + h];
-      Num<T>::st(static_cast<T*>(g.dy) + (size_t)(b0 + bb) * dy + c, s);
-    }
+    float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < OPT; ++k) {
-      const int o = tid + k * kThreads, row = o / (dy > 0 ? dy : 1), c = o % (dy > 0 ? dy : 1);
-      if (o >= 2 * H * dy) continue;
-      float s = 0.f;
-      for (int bb = 0; bb < GB; ++bb) s += dg_s[bb][row] * y_s[bb][c];
-      accw[k] += s;
-    }
-    if (tid < 2 * H)
-      for (int bb = 0; bb < GB && b0 + bb < B; ++bb) accb += dg_s[bb][tid];
-    __syncthreads();
-  }
+    for (int o = 0; o < 2 * H; ++o) s += wv[o] * dg[o];
+    if (b < B) Num<T>::st(static_cast<T*>(g.dy) + (size_t)b * dy + c, s);
+  } else if (item < n_dy + n_w) {
+    const int o = (item - n_dy) / dy, c = (item - n_dy) % dy;
+    float dg[GB], yv[GB];
 #pragma unroll
-  for (int k = 0; k < OPT; ++k) {
-    const int o = tid + k * kThreads;
-    if (o < 2 * H * dy) (o / dy < H ? g.gw_ym : g.gw_ya)[(size_t)((o / dy) % H) * dy + o % dy] = accw[k];
+    for (int bb = 0; bb < GB; ++bb) {
+      const int b = b0 + bb, bc = b < B ? b : 0;
+      const float x = g.DGY[(size_t)bc * 2 * H + o], v = Num<T>::ld(y + (size_t)bc * dy + c);
+      dg[bb] = b < B ? x : 0.f;
+      yv[bb] = v;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < GB; ++bb) s += dg[bb] * yv[bb];
+    atomicAdd((o < H ? g.gw_ym : g.gw_ya) + (size_t)(o % H) * dy + c, s);
+  } else if (item < n_dy + n_w + n_b) {
+    const int o = item - n_dy - n_w;
+    float dg[GB];
+#pragma unroll
+    for (int bb = 0; bb < GB; ++bb) {
+      const int b = b0 + bb, bc = b < B ? b : 0;
+      const float x = g.DGY[(size_t)bc * 2 * H + o];
+      dg[bb] = b < B ? x : 0.f;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < GB; ++bb) s += dg[bb];
+    atomicAdd((o < H ? g.gb_ym : g.gb_ya) + o % H, s);
   }
-  if (tid < 2 * H) (tid < H ? g.gb_ym : g.gb_ya)[tid % H] = accb;
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -2009,7 +2056,7 @@ template <typename T, int H, int DH, int DE>
 hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   constexpr int D = H * DH;
   const int JT = a.NP / 16;
-  const size_t prep = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + (size_t)a.B * 2 * H +
+  const size_t prep = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + (size_t)2 * H * a.dy + 2 * H + (size_t)a.B * 2 * H +
                       (size_t)a.B * H * a.NP * DH + (size_t)3 * D * D + 3 * D;
   const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
@@ -2018,12 +2065,14 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
   const unsigned red_blocks = (unsigned)(chunks < 512 ? chunks : 512);  // atomics per output: one per block
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX>), dim3((a.B * a.NP + 63) / 64, D / 64, 1), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 32>), dim3((a.B * a.NP + 31) / 32, D / 64, 1), dim3(kThreads), 0, s, a,
+                     g);
   // dW: the rows (contraction) split in slices of at least 256
   const int rows = a.B * a.NP, ksplit = rows / 256 < 1 ? 1 : (rows / 256 > 16 ? 16 : rows / 256);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW>), dim3(3 * D / 64, D / 64, ksplit), dim3(kThreads), 0, s, a, g);
-  const int bsplit = rows / 512 < 1 ? 1 : (rows / 512 > 32 ? 32 : rows / 512);
-  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH>), dim3(3 * D / 64 + 1, bsplit), dim3(kThreads), 0, s, a, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW, 64>), dim3(3 * D / 64, D / 64, ksplit), dim3(kThreads), 0, s, a, g);
+  const int small_items = 16 * a.dy + 2 * H * a.dy + 2 * H;
+  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH>), dim3((small_items + kThreads - 1) / kThreads, (a.B + 15) / 16),
+                     dim3(kThreads), 0, s, a, g);
   return hipGetLastError();
 }
 

@@ -176,8 +176,8 @@ ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_
  * dot-product scores, mask, normalized softmax, A [V | I], E' = E + W_e A +
  * b_e), with the forward's stored A (bfloat16 mode: its rounding points pass
  * gradients through unchanged). Supported: single-pass contexts with n <= 64,
- * dy <= 512, no variant flag, bfloat16 for both built shapes and float32 for
- * (4, 16, 16) (else EA_E_UNSUPPORTED).
+ * no variant flag, bfloat16 for both built shapes and float32 for (4, 16, 16)
+ * (else EA_E_UNSUPPORTED).
  *
  * Needs a preceding edge_attn_layer or edge_attn_forward on this context with
  * the same inputs, parameters, ws and stream (its Q, K, V and global FiLM
