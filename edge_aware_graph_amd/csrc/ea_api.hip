@@ -21,7 +21,7 @@ struct ea_ctx {
   int forward_done;
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
-  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, bws_bytes;  // backward workspace
+  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_red, bws_bytes;  // backward workspace
   // kernel timing window
   int prof_on;
   std::vector<hipEvent_t> ev_pool;
@@ -217,7 +217,8 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_df = c->boff_ds + round256(pairs * d.H * sizeof(float));
   c->boff_dqkv = c->boff_df + round256(pairs * 2 * d.H * sizeof(float));
   c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
-  c->bws_bytes = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
+  c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
+  c->bws_bytes = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
   c->prof_on = 0;
   c->ev_used = 0;
   *out = c;
@@ -404,6 +405,7 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   g.DF = reinterpret_cast<float*>(bb + c->boff_df);
   g.DQKV = reinterpret_cast<float*>(bb + c->boff_dqkv);
   g.DGY = reinterpret_cast<float*>(bb + c->boff_dgy);
+  g.RED = reinterpret_cast<float*>(bb + c->boff_red);
   return timed(c, EA_K_BACKWARD, s, [&] {
     return ea::launch_backward(a, g, c->d.dtype, c->d.H, c->d.dh, c->d.de, s);
   });

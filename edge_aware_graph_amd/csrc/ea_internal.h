@@ -72,7 +72,13 @@ struct BwdArgs {
   float* DF;     // dgamma_e, dbeta_e [B, 2H, NP, NP]
   float* DQKV;   // dQ | dK | dV [B, NP, 3, d]
   float* DGY;    // dgamma_y, dbeta_y [B, 2H]
+  float* RED;    // pair-reduction partial sums [kRedCopies][2 H de + de H + de]
 };
+
+// Copies of the pair reduction's outputs: blocks of the reduction add into
+// copy blockIdx % kRedCopies, which keeps the number of atomic adds per
+// address low; a later kernel sums the copies.
+constexpr int kRedCopies = 32;
 
 // Launchers; each returns the hipError_t of its launch. `dtype` 0 = fp32, 1 = bf16.
 hipError_t launch_qkv(const LayerArgs& a, int dtype, int H, int dh, int de, hipStream_t s);

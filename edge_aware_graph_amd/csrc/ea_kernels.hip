@@ -1400,8 +1400,10 @@ template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs g) {
   const int NP = a.NP;
   constexpr int D = H * DH;
-  const size_t nzy = (size_t)2 * H * a.dy + 2 * H;  // global FiLM weight and bias gradients
-  const size_t nz1 = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + nzy, nz2 = (size_t)a.B * 2 * H;
+  // the pair reduction's copies, the FiLM-bias gradients (b_emul, b_eadd),
+  // and the global FiLM's weight and bias gradients, all summed atomically
+  const size_t nred = (size_t)kRedCopies * (3 * H * DE + DE), nzy = (size_t)2 * H * a.dy + 2 * H;
+  const size_t nz1 = nred + 2 * H + nzy, nz2 = (size_t)a.B * 2 * H;
   const size_t nv = (size_t)a.B * H * NP * DH, nw = (size_t)3 * D * D + 3 * D;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nz1 + nz2 + nv + nw; k += stride) {
@@ -1411,18 +1413,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
       else (q - 3 * D * D < D ? g.gb_q : q - 3 * D * D < 2 * D ? g.gb_k : g.gb_v)[(q - 3 * D * D) % D] = 0.f;
     } else if (k < nz1) {
       size_t q = k;
-      if (q < (size_t)H * DE) { g.gw_em[q] = 0.f; continue; }
-      q -= (size_t)H * DE;
-      if (q < (size_t)H * DE) { g.gw_ea[q] = 0.f; continue; }
-      q -= (size_t)H * DE;
+      if (q < nred) { g.RED[q] = 0.f; continue; }
+      q -= nred;
       if (q < (size_t)H) { g.gb_em[q] = 0.f; continue; }
       q -= H;
       if (q < (size_t)H) { g.gb_ea[q] = 0.f; continue; }
       q -= H;
-      if (q < (size_t)DE * H) { g.gw_e[q] = 0.f; continue; }
-      q -= (size_t)DE * H;
-      if (q < (size_t)DE) { g.gb_e[q] = 0.f; continue; }
-      q -= DE;
       if (q < (size_t)H * a.dy) { g.gw_ym[q] = 0.f; continue; }
       q -= (size_t)H * a.dy;
       if (q < (size_t)H * a.dy) { g.gw_ya[q] = 0.f; continue; }
@@ -1801,14 +1797,15 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
     cur = nxt;
   }
   if (cb < DE) {
+    // copy layout: dW_emul [H][DE], dW_eadd [H][DE], dW_e [DE][H], db_e [DE]
+    float* red = g.RED + (size_t)(blockIdx.x % kRedCopies) * (3 * H * DE + DE);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * lg + r;  // accF: FiLM row 4 lg + r, channel cb + li
-      if (row < H) atomicAdd(g.gw_em + (size_t)row * DE + cb + li, accF[r]);
-      else if (row < 2 * H) atomicAdd(g.gw_ea + (size_t)(row - H) * DE + cb + li, accF[r]);
+      if (row < 2 * H) atomicAdd(red + (size_t)row * DE + cb + li, accF[r]);
       const int ch = cb + 4 * lg + r;  // accE: channel cb + 4 lg + r, head li (or the sum)
-      if (li < H) atomicAdd(g.gw_e + (size_t)ch * H + li, accE[r]);
-      else if (li == H) atomicAdd(g.gb_e + ch, accE[r]);
+      if (li < H) atomicAdd(red + 2 * H * DE + (size_t)ch * H + li, accE[r]);
+      else if (li == H) atomicAdd(red + 3 * H * DE + ch, accE[r]);
     }
   }
 }
@@ -1851,21 +1848,37 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
     const float x = MODE == kDX ? g.DQKV[(size_t)mc * 3 * D + kc] : g.DQKV[(size_t)kc * 3 * D + mc];
     return ok ? x : 0.f;
   };
+  // kDW: lane l describes row k0 + l of the chunk being loaded (TK == TN ==
+  // 64 == the wave size): its node's row of X (clamped), whether it is a
+  // real node and its mask byte; element e of a thread lies in row
+  // w + 4 e of the chunk, the same for the whole wave, read with readlane.
+  static_assert(MODE == kDX || (TK == 64 && TN == 64), "one chunk row per lane");
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int xr = 0;
+  uint32_t mbr = 0u, okr = 0u;
+  auto kdw_rows = [&](int k0) {
+    const int k = k0 + l, kc = k < kend ? k : 0, bq = kc / NP, ii = kc % NP;
+    xr = bq * n + (ii < n ? ii : 0);
+    mbr = a.mask[(size_t)xr];
+    okr = (uint32_t)(k < kend && ii < n);
+  };
   auto load_b = [&](int k0, int e) {
     const int idx = tid + e * kThreads, kk = idx / TN, nn = idx % TN, c = n0 + nn, k = k0 + kk;
-    const bool ok = k < kend && c < D;
-    const int kc = ok ? k : 0, cc = ok ? c : 0;
     if (MODE == kDX) {
+      const bool ok = k < kend && c < D;
+      const int kc = ok ? k : 0, cc = ok ? c : 0;
       const int wsel = kc / D, f = kc % D;
       const T* W = static_cast<const T*>(wsel == 0 ? a.w_q : wsel == 1 ? a.w_k : a.w_v);
       const float x = Num<T>::ld(W + (size_t)f * D + cc);
       return ok ? x : 0.f;
     }
-    // rows of padded or masked nodes count as 0 (their X may hold anything)
-    const int bq = kc / NP, ii = kc % NP, ic = ii < n ? ii : 0;
-    const bool mk = a.mask[(size_t)bq * n + ic] != 0;
-    const float x = Num<T>::ld(X + ((size_t)bq * n + ic) * D + cc);
-    return ok && ii < n && mk ? x : 0.f;
+    const int xrow = __builtin_amdgcn_readlane(xr, wu + 4 * e);
+    return Num<T>::ld(X + (size_t)xrow * D + c);
+  };
+  // kDW: rows of padded or masked nodes count as 0 (their X may hold
+  // anything); applied when the chunk is stored, after its loads completed
+  auto b_ok = [&](int e) {
+    return MODE == kDX || __builtin_amdgcn_readlane(okr * mbr, wu + 4 * e) != 0u;
   };
   f32x4 acc[MT][2];
 #pragma unroll
@@ -1874,6 +1887,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ra[PERA], rb[PERB];  // the next chunk, loaded while the current one is used
   float csum = 0.f;
+  if (MODE == kDW) kdw_rows(kbeg);
 #pragma unroll
   for (int e = 0; e < PERA; ++e) ra[e] = load_a(kbeg, e);
 #pragma unroll
@@ -1884,9 +1898,10 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
 #pragma unroll
     for (int e = 0; e < PERB; ++e) {
       const int idx = tid + e * kThreads;
-      bs[idx / TN][idx % TN] = rb[e];
+      bs[idx / TN][idx % TN] = b_ok(e) ? rb[e] : 0.f;
     }
     __syncthreads();
+    if (MODE == kDW) kdw_rows(k0 + TK);
 #pragma unroll
     for (int e = 0; e < PERA; ++e) ra[e] = load_a(k0 + TK, e);
 #pragma unroll
@@ -1946,8 +1961,9 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
 //   dy[b][c]         = sum_h W_ymul[h][c] dgamma_y[b][h] + W_yadd[h][c] dbeta_y[b][h]
 //   dW_y(mul|add)[h][c] += sum_b dgamma_y|dbeta_y[b][h] y[b][c]   (atomic over blocks)
 //   db_y(mul|add)[h]    += sum_b dgamma_y|dbeta_y[b][h]           (atomic over blocks)
-// All of an item's loads are independent and issued together.
-template <typename T, int H, int DH>
+// and (block row 0) the sums of the pair reduction's copies: dW_emul, dW_eadd,
+// dW_e, db_e. All of an item's loads are independent and issued together.
+template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArgs g) {
   constexpr int GB = 16;
   const int B = a.B, dy = a.dy, b0 = blockIdx.y * GB;
@@ -1982,7 +1998,21 @@ __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArg
 #pragma unroll
     for (int bb = 0; bb < GB; ++bb) s += dg[bb] * yv[bb];
     atomicAdd((o < H ? g.gw_ym : g.gw_ya) + (size_t)(o % H) * dy + c, s);
-  } else if (item < n_dy + n_w + n_b) {
+  } else if (item >= n_dy + n_w + n_b) {
+    constexpr int NR = 3 * H * DE + DE;
+    const int o = item - n_dy - n_w - n_b;
+    if (blockIdx.y != 0 || o >= NR) return;
+    float v[kRedCopies];
+#pragma unroll
+    for (int k = 0; k < kRedCopies; ++k) v[k] = g.RED[(size_t)k * NR + o];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRedCopies; ++k) s += v[k];
+    if (o < H * DE) g.gw_em[o] = s;
+    else if (o < 2 * H * DE) g.gw_ea[o - H * DE] = s;
+    else if (o < 3 * H * DE) g.gw_e[o - 2 * H * DE] = s;
+    else g.gb_e[o - 3 * H * DE] = s;
+  } else {
     const int o = item - n_dy - n_w;
     float dg[GB];
 #pragma unroll
@@ -2056,7 +2086,7 @@ template <typename T, int H, int DH, int DE>
 hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   constexpr int D = H * DH;
   const int JT = a.NP / 16;
-  const size_t prep = (size_t)2 * H * DE + 2 * H + (size_t)DE * H + DE + (size_t)2 * H * a.dy + 2 * H + (size_t)a.B * 2 * H +
+  const size_t prep = (size_t)kRedCopies * (3 * H * DE + DE) + 2 * H + (size_t)2 * H * a.dy + 2 * H + (size_t)a.B * 2 * H +
                       (size_t)a.B * H * a.NP * DH + (size_t)3 * D * D + 3 * D;
   const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
@@ -2065,13 +2095,13 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
   const unsigned red_blocks = (unsigned)(chunks < 512 ? chunks : 512);  // atomics per output: one per block
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 32>), dim3((a.B * a.NP + 31) / 32, D / 64, 1), dim3(kThreads), 0, s, a,
+  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 64>), dim3((a.B * a.NP + 63) / 64, D / 64, 1), dim3(kThreads), 0, s, a,
                      g);
   // dW: the rows (contraction) split in slices of at least 256
   const int rows = a.B * a.NP, ksplit = rows / 256 < 1 ? 1 : (rows / 256 > 16 ? 16 : rows / 256);
   hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW, 64>), dim3(3 * D / 64, D / 64, ksplit), dim3(kThreads), 0, s, a, g);
-  const int small_items = 16 * a.dy + 2 * H * a.dy + 2 * H;
-  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH>), dim3((small_items + kThreads - 1) / kThreads, (a.B + 15) / 16),
+  const int small_items = 16 * a.dy + 2 * H * a.dy + 2 * H + 3 * H * DE + DE;
+  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH, DE>), dim3((small_items + kThreads - 1) / kThreads, (a.B + 15) / 16),
                      dim3(kThreads), 0, s, a, g);
   return hipGetLastError();
 }
