@@ -52,12 +52,18 @@ template <typename T>
 struct Num;
 template <>
 struct Num<float> {
+  // ldraw / fromraw: a load whose conversion to float is left for later
+  // (kept apart so that the conversion does not wait for the load early)
+  static __device__ __forceinline__ uint32_t ldraw(const float* p) { return __float_as_uint(*p); }
+  static __device__ __forceinline__ float fromraw(uint32_t r) { return __uint_as_float(r); }
   static __device__ __forceinline__ float ld(const float* p) { return *p; }
   static __device__ __forceinline__ float rnd(float v) { return v; }
   static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
 };
 template <>
 struct Num<bf16_t> {
+  static __device__ __forceinline__ uint32_t ldraw(const bf16_t* p) { return *p; }
+  static __device__ __forceinline__ float fromraw(uint32_t r) { return bf_bits_to_f(r); }
   static __device__ __forceinline__ float ld(const bf16_t* p) { return bf_bits_to_f(*p); }
   static __device__ __forceinline__ float rnd(float v) { return bf_bits_to_f(pack_bf2(v, 0.f) & 0xffffu); }
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = (bf16_t)(pack_bf2(v, 0.f) & 0xffffu); }
@@ -1669,40 +1675,67 @@ __global__ __launch_bounds__(kThreads) void bwd_qkv_kernel(LayerArgs a, BwdArgs 
   __shared__ float ds_s[M][M + 1], a_s[M][M + 1];
   __shared__ float q_s[M][DH + 1], k_s[M][DH + 1], o_s[M][DH + 1];
   const int h = blockIdx.x, b = blockIdx.y, NP = a.NP, n = a.n, tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const size_t bh = (size_t)b * H + h;
   const T* Ag = static_cast<const T*>(g.A);
-  for (int idx = tid; idx < NP * NP; idx += kThreads) {
-    const int ii = idx / NP, jj = idx % NP;
-    ds_s[ii][jj] = g.DS[(bh * NP + ii) * NP + jj];
-    const bool ok = ii < n && jj < n;
-    const float v = Num<T>::ld(Ag + bh * n * n + (ok ? (size_t)ii * n + jj : 0));
-    a_s[ii][jj] = ok ? v : 0.f;
-  }
   const T* Qw = static_cast<const T*>(a.Qw);
   const T* Kw = static_cast<const T*>(a.Kw);
   const T* dO = static_cast<const T*>(g.dO);
-  for (int idx = tid; idx < NP * DH; idx += kThreads) {
-    const int r = idx / DH, t = idx % DH;
-    q_s[r][t] = Num<T>::ld(Qw + (bh * NP + r) * DH + t);
-    k_s[r][t] = Num<T>::ld(Kw + (bh * NP + r) * DH + t);
-    const float v = Num<T>::ld(dO + ((size_t)b * n + (r < n ? r : 0)) * D + h * DH + t);
-    o_s[r][t] = r < n ? v : 0.f;
+  // staging: every load is issued (clamped index) before any is used, then
+  // out-of-range elements are replaced by 0
+  constexpr int NPP = M * M / kThreads, NPD = M * DH / kThreads;
+  float vd[NPP], va[NPP], vq[NPD], vk[NPD], vo[NPD];
+#pragma unroll
+  for (int k = 0; k < NPP; ++k) {
+    const int idx = tid + k * kThreads, ii = idx / M, jj = idx % M;
+    const bool okp = ii < NP && jj < NP, oka = ii < n && jj < n;
+    vd[k] = g.DS[(bh * NP + (okp ? ii : 0)) * NP + (okp ? jj : 0)];
+    va[k] = Num<T>::ld(Ag + bh * n * n + (oka ? (size_t)ii * n + jj : 0));
+  }
+#pragma unroll
+  for (int k = 0; k < NPD; ++k) {
+    const int idx = tid + k * kThreads, r = idx / DH, t = idx % DH, rp = r < NP ? r : 0, rn = r < n ? r : 0;
+    vq[k] = Num<T>::ld(Qw + (bh * NP + rp) * DH + t);
+    vk[k] = Num<T>::ld(Kw + (bh * NP + rp) * DH + t);
+    vo[k] = Num<T>::ld(dO + ((size_t)b * n + rn) * D + h * DH + t);
+  }
+#pragma unroll
+  for (int k = 0; k < NPP; ++k) {
+    const int idx = tid + k * kThreads, ii = idx / M, jj = idx % M;
+    ds_s[ii][jj] = ii < NP && jj < NP ? vd[k] : 0.f;
+    a_s[ii][jj] = ii < n && jj < n ? va[k] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < NPD; ++k) {
+    const int idx = tid + k * kThreads, r = idx / DH, t = idx % DH;
+    q_s[r][t] = r < NP ? vq[k] : 0.f;
+    k_s[r][t] = r < NP ? vk[k] : 0.f;
+    o_s[r][t] = r < n ? vo[k] : 0.f;
   }
   __syncthreads();
+  // 16 x 16 output tiles of dQ = s ds K, dK = s ds^T Q, dV = A^T dO (s the
+  // score scale) on float32 MFMA 16x16x4, spread over the waves; lane
+  // (li, lg) supplies row li of the left operand and column li of the right
+  // one at contraction index 4 step + lg
   const float sc = a.scale;
-  for (int idx = tid; idx < 3 * NP * DH; idx += kThreads) {
-    const int which = idx / (NP * DH), r = (idx / DH) % NP, t = idx % DH;
-    float acc = 0.f;
-    if (which == 0) {
-      for (int j = 0; j < NP; ++j) acc += ds_s[r][j] * k_s[j][t];
-      acc *= sc;
-    } else if (which == 1) {
-      for (int q = 0; q < NP; ++q) acc += ds_s[q][r] * q_s[q][t];
-      acc *= sc;
-    } else {
-      for (int q = 0; q < NP; ++q) acc += a_s[q][r] * o_s[q][t];
+  const int mtn = NP / 16, ntn = DH / 16, ntiles = 3 * mtn * ntn;
+  for (int ti = w; ti < ntiles; ti += kWaves) {
+    const int which = ti / (mtn * ntn), mt = (ti / ntn) % mtn, nt = ti % ntn;
+    const int row = 16 * mt + li, col = 16 * nt + li;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s4 = 0; s4 < NP / 4; ++s4) {
+      const int kk = 4 * s4 + lg;
+      const float av = which == 0 ? ds_s[row][kk] : which == 1 ? ds_s[kk][row] : a_s[kk][row];
+      const float bv = which == 0 ? k_s[kk][col] : which == 1 ? q_s[kk][col] : o_s[kk][col];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
     }
-    g.DQKV[(((size_t)b * NP + r) * 3 + which) * D + h * DH + t] = acc;
+    const float f = which < 2 ? sc : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = 16 * mt + 4 * lg + r;
+      g.DQKV[(((size_t)b * NP + rr) * 3 + which) * D + h * DH + col] = f * acc[r];
+    }
   }
 }
 
@@ -1728,60 +1761,68 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
   constexpr int NS = (P * 3 * H + kThreads - 1) / kThreads;  // dF and A values per thread
   // one chunk's loads into registers: a quarter row of E and dE' of pair
   // tid / 4, and NS of the chunk's dF / A values
+  static_assert((2 * H) % 4 == 0, "dF / A rows: row w + 4 k is a dF row exactly when k < H / 2");
   struct Regs {
     Frag<T, DE / 4> ef, df;
-    bool real;
-    float v[NS];
+    uint8_t mi, mj;   // mask bytes of the pair's nodes
+    bool inb;         // the pair exists and both nodes are below n
+    uint32_t v[NS];   // raw dF (float32) / A (T) words, converted at the store
+    bool inr, okv;    // pair l of the chunk exists / exists with both nodes below n
   };
+  // Raw values only: the masks and bounds are applied when the chunk is
+  // stored to LDS, after its loads completed.
   auto load_chunk = [&](uint32_t cidx, Regs& r) {
     {
       const int p = tid >> 2, qt = tid & 3;
       const uint32_t q = cidx * P + p;
       const uint32_t bq = q / (NP * NP), ii = (q / NP) % NP, jj = q % NP;
       const uint32_t bc = q < npairs ? bq : 0;
-      // both mask bytes are loaded unconditionally and combined without branches
-      const uint32_t mi = a.mask[(size_t)bc * n + (ii < (uint32_t)n ? ii : 0)];
-      const uint32_t mj = a.mask[(size_t)bc * n + (jj < (uint32_t)n ? jj : 0)];
-      r.real = ((uint32_t)(q < npairs) & (uint32_t)(ii < (uint32_t)n) & (uint32_t)(jj < (uint32_t)n) & (mi != 0) & (mj != 0)) != 0;
-      const size_t off = r.real ? (((size_t)bq * n + ii) * n + jj) * DE + qt * (DE / 4) : 0;
+      r.inb = q < npairs && ii < (uint32_t)n && jj < (uint32_t)n;
+      r.mi = a.mask[(size_t)bc * n + (ii < (uint32_t)n ? ii : 0)];
+      r.mj = a.mask[(size_t)bc * n + (jj < (uint32_t)n ? jj : 0)];
+      const size_t off = r.inb ? (((size_t)bq * n + ii) * n + jj) * DE + qt * (DE / 4) : 0;
       r.ef.load(E + off);
       r.df.load(dEp + off);
     }
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      const int idx = tid + k * kThreads, p = idx % P, row = idx / P;  // rows 0..2H-1: dF, 2H..3H-1: A
-      const uint32_t q = cidx * P + p;
+    {
+      const uint32_t q = cidx * P + l;  // pair l of the chunk for every k (P == 64)
       const uint32_t bq = q / (NP * NP), ii = (q / NP) % NP, jj = q % NP;
-      const bool inr = q < npairs && row < 3 * H;
-      const uint32_t bc = inr ? bq : 0;  // addresses stay inside the buffers past the last pair
-      // both candidates are loaded (clamped addresses), then one is selected
-      const int fr = row < 2 * H ? row : 0, h = row >= 2 * H && row < 3 * H ? row - 2 * H : 0;
-      const bool ok = inr && ii < (uint32_t)n && jj < (uint32_t)n;
-      const float xf = g.DF[(((size_t)bc * 2 * H + fr) * NP + ii) * NP + jj];
-      const float xa = Num<T>::ld(Ag + (((size_t)bc * H + h) * n + (ok ? ii : 0)) * n + (ok ? jj : 0));
-      r.v[k] = row < 2 * H ? (inr ? xf : 0.f) : (ok ? xa : 0.f);
+      r.inr = q < npairs;
+      r.okv = r.inr && ii < (uint32_t)n && jj < (uint32_t)n;
+      const uint32_t bc = r.inr ? bq : 0;  // addresses stay inside the buffers past the last pair
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int row = w + 4 * k;  // rows 0..2H-1: dF, 2H..3H-1: A
+        if (k < H / 2) {
+          r.v[k] = Num<float>::ldraw(g.DF + (((size_t)bc * 2 * H + row) * NP + ii) * NP + jj);
+        } else {
+          const int h = row < 3 * H ? row - 2 * H : 0;
+          r.v[k] = Num<T>::ldraw(Ag + (((size_t)bc * H + h) * n + (r.okv ? ii : 0)) * n + (r.okv ? jj : 0));
+        }
+      }
     }
   };
-  Regs cur, nxt;
-  uint32_t cidx = blockIdx.x;
-  if (cidx < nchunks) load_chunk(cidx, cur);
-  for (; cidx < nchunks; cidx += gridDim.x) {
+  // one chunk: stage `cur` in LDS, load the chunk after it into `nxt`, then
+  // the MFMAs; the loop alternates the two register sets (no copies)
+  auto step = [&](uint32_t cidx, Regs& cur, Regs& nxt) {
     {
       const int p = tid >> 2, qt = tid & 3;
+      const bool real = cur.inb && cur.mi != 0 && cur.mj != 0;
 #pragma unroll
       for (int k = 0; k < DE / 4; ++k) {
-        e_s[p][qt * (DE / 4) + k] = cur.real ? cur.ef.get(k) : 0.f;
-        d_s[p][qt * (DE / 4) + k] = cur.real ? cur.df.get(k) : 0.f;
+        e_s[p][qt * (DE / 4) + k] = real ? cur.ef.get(k) : 0.f;
+        d_s[p][qt * (DE / 4) + k] = real ? cur.df.get(k) : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        const int idx = tid + k * kThreads, pp = idx % P, row = idx / P;
-        if (row < 2 * H) f_s[row][pp] = cur.v[k];
-        else if (row < 3 * H) a_s[row - 2 * H][pp] = cur.v[k];
+        const int row = w + 4 * k;
+        if (k < H / 2) f_s[row][l] = cur.inr ? Num<float>::fromraw(cur.v[k]) : 0.f;
+        else if (row < 3 * H) a_s[row - 2 * H][l] = cur.okv ? Num<T>::fromraw(cur.v[k]) : 0.f;
       }
     }
     __syncthreads();
     if (cidx + gridDim.x < nchunks) load_chunk(cidx + gridDim.x, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's MFMAs
     if (cb < DE) {
       // MFMA 16x16x4: lane (li, lg) supplies A[li][k = lg] and B[k = lg][li]
 #pragma unroll
@@ -1794,7 +1835,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
       }
     }
     __syncthreads();
-    cur = nxt;
+  };
+  Regs r0, r1;
+  if (blockIdx.x < nchunks) load_chunk(blockIdx.x, r0);
+  for (uint32_t cidx = blockIdx.x; cidx < nchunks; cidx += 2 * gridDim.x) {
+    step(cidx, r0, r1);
+    if (cidx + gridDim.x >= nchunks) break;
+    step(cidx + gridDim.x, r1, r0);
   }
   if (cb < DE) {
     // copy layout: dW_emul [H][DE], dW_eadd [H][DE], dW_e [DE][H], db_e [DE]
@@ -1841,12 +1888,14 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
   // Out-of-range elements load from a clamped address and are then replaced
   // by 0: every load is issued unconditionally, so the loads of a chunk stay
   // in flight together (a load under a branch is waited for at the branch's end).
+  // The replacement happens when the chunk is stored to LDS (a_ok, b_ok),
+  // after its loads completed.
+  auto a_ok = [&](int k0, int e) { return m0 + a_mm(e) < M && k0 + a_kk(e) < kend; };
   auto load_a = [&](int k0, int e) {
-    const int kk = a_kk(e), mm = a_mm(e), m = m0 + mm, k = k0 + kk;
+    const int m = m0 + a_mm(e), k = k0 + a_kk(e);
     const bool ok = m < M && k < kend;
     const int mc = ok ? m : 0, kc = ok ? k : 0;
-    const float x = MODE == kDX ? g.DQKV[(size_t)mc * 3 * D + kc] : g.DQKV[(size_t)kc * 3 * D + mc];
-    return ok ? x : 0.f;
+    return MODE == kDX ? g.DQKV[(size_t)mc * 3 * D + kc] : g.DQKV[(size_t)kc * 3 * D + mc];
   };
   // kDW: lane l describes row k0 + l of the chunk being loaded (TK == TN ==
   // 64 == the wave size): its node's row of X (clamped), whether it is a
@@ -1862,30 +1911,36 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
     mbr = a.mask[(size_t)xr];
     okr = (uint32_t)(k < kend && ii < n);
   };
+  // raw bits (converted at the store); kDX: a chunk lies inside one of
+  // W_q, W_k, W_v (D is a multiple of TK), chosen once per chunk
+  static_assert(MODE == kDW || D % TK == 0, "a chunk inside one weight");
   auto load_b = [&](int k0, int e) {
     const int idx = tid + e * kThreads, kk = idx / TN, nn = idx % TN, c = n0 + nn, k = k0 + kk;
     if (MODE == kDX) {
-      const bool ok = k < kend && c < D;
-      const int kc = ok ? k : 0, cc = ok ? c : 0;
-      const int wsel = kc / D, f = kc % D;
+      const int wsel = k0 / D;
       const T* W = static_cast<const T*>(wsel == 0 ? a.w_q : wsel == 1 ? a.w_k : a.w_v);
-      const float x = Num<T>::ld(W + (size_t)f * D + cc);
-      return ok ? x : 0.f;
+      const bool ok = k < kend && c < D && wsel < 3;
+      return Num<T>::ldraw(ok ? W + (size_t)(k - wsel * D) * D + c : static_cast<const T*>(a.w_q));
     }
     const int xrow = __builtin_amdgcn_readlane(xr, wu + 4 * e);
-    return Num<T>::ld(X + (size_t)xrow * D + c);
+    return Num<T>::ldraw(X + (size_t)xrow * D + c);
   };
   // kDW: rows of padded or masked nodes count as 0 (their X may hold
   // anything); applied when the chunk is stored, after its loads completed
-  auto b_ok = [&](int e) {
-    return MODE == kDX || __builtin_amdgcn_readlane(okr * mbr, wu + 4 * e) != 0u;
+  auto b_ok = [&](int k0, int e) {
+    if (MODE == kDX) {
+      const int idx = tid + e * kThreads;
+      return k0 + idx / TN < kend && n0 + idx % TN < D;
+    }
+    return __builtin_amdgcn_readlane(okr * mbr, wu + 4 * e) != 0u;
   };
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ra[PERA], rb[PERB];  // the next chunk, loaded while the current one is used
+  float ra[PERA];  // the next chunk, loaded while the current one is used
+  uint32_t rb[PERB];
   float csum = 0.f;
   if (MODE == kDW) kdw_rows(kbeg);
 #pragma unroll
@@ -1894,11 +1949,11 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
   for (int e = 0; e < PERB; ++e) rb[e] = load_b(kbeg, e);
   for (int k0 = kbeg; k0 < kend; k0 += TK) {
 #pragma unroll
-    for (int e = 0; e < PERA; ++e) as[a_kk(e)][a_mm(e)] = ra[e];
+    for (int e = 0; e < PERA; ++e) as[a_kk(e)][a_mm(e)] = a_ok(k0, e) ? ra[e] : 0.f;
 #pragma unroll
     for (int e = 0; e < PERB; ++e) {
       const int idx = tid + e * kThreads;
-      bs[idx / TN][idx % TN] = b_ok(e) ? rb[e] : 0.f;
+      bs[idx / TN][idx % TN] = b_ok(k0, e) ? Num<T>::fromraw(rb[e]) : 0.f;
     }
     __syncthreads();
     if (MODE == kDW) kdw_rows(k0 + TK);
@@ -1906,6 +1961,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
     for (int e = 0; e < PERA; ++e) ra[e] = load_a(k0 + TK, e);
 #pragma unroll
     for (int e = 0; e < PERB; ++e) rb[e] = load_b(k0 + TK, e);
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's MFMAs
     // float32 MFMA 16x16x4: wave (wm, wn) computes rows wm*TM/2 .., columns wn*32 ..
 #pragma unroll
     for (int ks = 0; ks < TK / 4; ++ks) {
