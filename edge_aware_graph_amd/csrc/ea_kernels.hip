@@ -2012,6 +2012,202 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
   }
 }
 
+// The same two GEMMs on bfloat16 MFMA (bfloat16 mode): the float32 dQ, dK,
+// dV are rounded to bfloat16 (nearest even) when staged, products are
+// accumulated in float32 (the projection bias sums of kDW stay float32 and
+// are taken before the rounding). 64 x 64 outputs per block, 32 x 32 per
+// wave on MFMA 16x16x32 bf16; chunks of 128 along the contraction are staged
+// in LDS with the contraction contiguous, so each MFMA operand is one
+// 16-byte LDS read (row r, contraction 8 lg .. 8 lg + 7 for lane (li, lg)).
+//   kDX: rows m = (b, i) of DQKV against W_cat[k][c] = W_{k / D}[k % D][c];
+//   kDW: rows f of DQKV^T against X rows (masked and padded rows count as 0).
+// Staging: a thread holds 4 contraction rows x 4 columns of a source whose
+// columns are contiguous, and writes each column's 4 values as one 8-byte
+// LDS store (a 4 x 4 transpose in registers); kDX's DQKV rows are already
+// contraction-contiguous and are written as they are.
+template <int H, int DH, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, BwdArgs g) {
+  // chunk depth TK divides D: a kDX chunk lies inside one of W_q, W_k, W_v
+  constexpr int D = H * DH, TM = 64, TN = 64, TK = D >= 128 ? 128 : 64, LK = TK + 8;
+  constexpr int NA = TM * TK / 4 / kThreads, NB = TN / 4 * (TK / 4) / kThreads;
+  static_assert(D % 64 == 0 && D % TK == 0 && NB >= 1, "whole tiles");
+  __shared__ __align__(16) uint16_t as[TM][LK];
+  __shared__ __align__(16) uint16_t bs[TN][LK];
+  __shared__ float cs_s[16][64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int wm = w & 1, wn = w >> 1;
+  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
+  const int NP = a.NP, n = a.n;
+  const int M = MODE == kDX ? a.B * NP : 3 * D, K = MODE == kDX ? 3 * D : a.B * NP;
+  // slices of whole chunks, so that a row quad (4 rows from a multiple of 4)
+  // never straddles a slice or a graph (NP is a multiple of 16)
+  const int kslice = ((K + gridDim.z - 1) / gridDim.z + TK - 1) / TK * TK;
+  const int kbeg = blockIdx.z * kslice, kend = K < kbeg + kslice ? K : kbeg + kslice;
+  const bf16_t* X = static_cast<const bf16_t*>(a.X);
+  // per thread and chunk: 2 groups of (4 contraction rows x 4 columns); the
+  // group's column quad cq = idx % 16 and row quad kq = idx / 16, idx = tid + 256 e
+  struct Stage {
+    u32x4 fa[NB][4];  // float32 source (DQKV): [group][row] 4 columns
+    u32x2 hb[NB][4];  // bfloat16 source (W or X): [group][row] 4 columns
+    uint8_t mk[NB][4];  // kDW: mask bytes of the X rows
+    bool ok[NB][4];     // kDW: the X row exists (below kend, node below n)
+  };
+  // kDX's A: NA float4 per thread, rows mm = idx / (TK / 4), columns 4 (idx % (TK / 4))
+  u32x4 xa[NA];
+  Stage st;
+  auto load = [&](int k0) {
+    if (MODE == kDX) {
+      // a chunk lies wholly inside the contraction or wholly past it (the
+      // prefetch after the last one, which loads chunk 0 again, unused); rows
+      // m >= M load row 0 and only reach output rows that are not stored
+      const int kc0 = k0 < kend ? k0 : 0, ws = kc0 / D;
+#pragma unroll
+      for (int e = 0; e < NA; ++e) {
+        const int idx = tid + e * kThreads, m = m0 + idx / (TK / 4), mc = m < M ? m : 0;
+        xa[e] = *reinterpret_cast<const u32x4*>(g.DQKV + (size_t)mc * 3 * D + kc0 + 4 * (idx % (TK / 4)));
+      }
+      const bf16_t* W = static_cast<const bf16_t*>(ws == 0 ? a.w_q : ws == 1 ? a.w_k : a.w_v) +
+                        (size_t)(kc0 - ws * D) * D + n0;
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const int idx = tid + e * kThreads, cq = idx % 16, kq = idx / 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.hb[e][j] = *reinterpret_cast<const u32x2*>(W + (size_t)(4 * kq + j) * D + 4 * cq);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const int idx = tid + e * kThreads, cq = idx % 16, kq = idx / 16, r0 = k0 + 4 * kq;
+        // the 4 rows r0 .. r0 + 3 lie in one graph (NP is a multiple of 16)
+        const int rc = r0 < kend ? r0 : 0, bq = rc / NP, i0 = rc % NP;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool okr = r0 + j < kend;
+          st.fa[e][j] = *reinterpret_cast<const u32x4*>(g.DQKV + (size_t)(okr ? r0 + j : 0) * 3 * D + m0 + 4 * cq);
+          const int i = i0 + j, ic = i < n ? i : 0;
+          st.ok[e][j] = okr && i < n;
+          st.mk[e][j] = a.mask[(size_t)bq * n + ic];
+          st.hb[e][j] = *reinterpret_cast<const u32x2*>(X + ((size_t)bq * n + ic) * D + n0 + 4 * cq);
+        }
+      }
+    }
+  };
+  float csum[4] = {0.f, 0.f, 0.f, 0.f};  // kDW bias sums of columns m0 + 4 (tid % 16) + q
+  // 4 rows x 4 bfloat16 columns (u32x2 each) -> per column the 4 rows packed
+  auto tr_store = [&](uint16_t (*dst)[LK], int col0, int row0, const u32x2 (&v)[4], const bool (&keep)[4]) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = keep[j] ? v[j].x : 0u;
+      hi[j] = keep[j] ? v[j].y : 0u;
+    }
+    // column q is the low (q even) or high (q odd) half of word q / 2 of every
+    // row; rows 2 t and 2 t + 1 share one output word (row 2 t in the low half)
+    auto lo2 = [](uint32_t r0w, uint32_t r1w) { return (r0w & 0xffffu) | (r1w << 16); };
+    auto hi2 = [](uint32_t r0w, uint32_t r1w) { return (r0w >> 16) | (r1w & 0xffff0000u); };
+    *reinterpret_cast<u32x2*>(&dst[col0 + 0][row0]) = u32x2{lo2(lo[0], lo[1]), lo2(lo[2], lo[3])};
+    *reinterpret_cast<u32x2*>(&dst[col0 + 1][row0]) = u32x2{hi2(lo[0], lo[1]), hi2(lo[2], lo[3])};
+    *reinterpret_cast<u32x2*>(&dst[col0 + 2][row0]) = u32x2{lo2(hi[0], hi[1]), lo2(hi[2], hi[3])};
+    *reinterpret_cast<u32x2*>(&dst[col0 + 3][row0]) = u32x2{hi2(hi[0], hi[1]), hi2(hi[2], hi[3])};
+  };
+  auto store = [&](int k0) {
+    if (MODE == kDX) {
+#pragma unroll
+      for (int e = 0; e < NA; ++e) {
+        const int idx = tid + e * kThreads, mm = idx / (TK / 4), kk = 4 * (idx % (TK / 4));
+        const u32x4 v = xa[e];
+        *reinterpret_cast<u32x2*>(&as[mm][kk]) =
+            u32x2{pack_bf2(__uint_as_float(v.x), __uint_as_float(v.y)), pack_bf2(__uint_as_float(v.z), __uint_as_float(v.w))};
+      }
+      const bool keep[4] = {true, true, true, true};
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const int idx = tid + e * kThreads, cq = idx % 16, kq = idx / 16;
+        tr_store(bs, 4 * cq, 4 * kq, st.hb[e], keep);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const int idx = tid + e * kThreads, cq = idx % 16, kq = idx / 16;
+        bool keep[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) keep[j] = st.ok[e][j] && st.mk[e][j] != 0;
+        tr_store(bs, 4 * cq, 4 * kq, st.hb[e], keep);
+        // DQKV^T: columns f = m0 + 4 cq + q, rows 4 kq + j (float32 -> bfloat16)
+        float f[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool okr = k0 + 4 * kq + j < kend;
+          f[j][0] = okr ? __uint_as_float(st.fa[e][j].x) : 0.f;
+          f[j][1] = okr ? __uint_as_float(st.fa[e][j].y) : 0.f;
+          f[j][2] = okr ? __uint_as_float(st.fa[e][j].z) : 0.f;
+          f[j][3] = okr ? __uint_as_float(st.fa[e][j].w) : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          csum[q] += (f[0][q] + f[1][q]) + (f[2][q] + f[3][q]);
+          *reinterpret_cast<u32x2*>(&as[4 * cq + q][4 * kq]) = u32x2{pack_bf2(f[0][q], f[1][q]), pack_bf2(f[2][q], f[3][q])};
+        }
+      }
+    }
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += TK) {
+    store(k0);
+    __syncthreads();
+    load(k0 + TK);
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's MFMAs
+#pragma unroll
+    for (int ks = 0; ks < TK / 32; ++ks) {
+      u32x4 af[2], bf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = *reinterpret_cast<const u32x4*>(&as[wm * 32 + t * 16 + li][32 * ks + 8 * lg]);
+        bf[t] = *reinterpret_cast<const u32x4*>(&bs[wn * 32 + t * 16 + li][32 * ks + 8 * lg]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[mt]),
+                                                                __builtin_bit_cast(bf16x8, bf[nt]), acc[mt][nt], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  if (MODE == kDW && blockIdx.y == 0) {
+    // bias sums: the 16 threads of a column quad (tid % 16) reduce through LDS
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cs_s[tid / 16][4 * (tid % 16) + q] = csum[q];
+    __syncthreads();
+    if (tid < 64 && m0 + tid < M) {
+      float t = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t += cs_s[r][tid];
+      const int m = m0 + tid, wsel = m / D;
+      atomicAdd((wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v) + m % D, t);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int mt = e >> 3, nt = (e >> 2) & 1, r = e & 3;
+    const int m = m0 + wm * 32 + mt * 16 + 4 * lg + r, col = n0 + wn * 32 + nt * 16 + li;
+    if (m >= M) continue;
+    const float v = acc[mt][nt][r];
+    if (MODE == kDX) {
+      const int bq = m / NP, ii = m % NP;
+      if (ii < n) Num<bf16_t>::st(static_cast<bf16_t*>(g.dX) + ((size_t)bq * n + ii) * D + col, v);
+    } else {
+      const int wsel = m / D, f = m % D;
+      atomicAdd((wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v) + (size_t)f * D + col, v);
+    }
+  }
+}
+
 // bwd_small: the global FiLM's gradients and dy. Block row blockIdx.y takes
 // graphs b0 = 16 blockIdx.y .. b0 + 15; each thread computes one item:
 //   dy[b][c]         = sum_h W_ymul[h][c] dgamma_y[b][h] + W_yadd[h][c] dbeta_y[b][h]
@@ -2151,11 +2347,16 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
   const unsigned red_blocks = (unsigned)(chunks < 512 ? chunks : 512);  // atomics per output: one per block
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 64>), dim3((a.B * a.NP + 63) / 64, D / 64, 1), dim3(kThreads), 0, s, a,
-                     g);
   // dW: the rows (contraction) split in slices of at least 256
   const int rows = a.B * a.NP, ksplit = rows / 256 < 1 ? 1 : (rows / 256 > 16 ? 16 : rows / 256);
-  hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW, 64>), dim3(3 * D / 64, D / 64, ksplit), dim3(kThreads), 0, s, a, g);
+  const dim3 gdx((a.B * a.NP + 63) / 64, D / 64, 1), gdw(3 * D / 64, D / 64, ksplit);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH, kDX>), gdx, dim3(kThreads), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH, kDW>), gdw, dim3(kThreads), 0, s, a, g);
+  } else {
+    hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 64>), gdx, dim3(kThreads), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW, 64>), gdw, dim3(kThreads), 0, s, a, g);
+  }
   const int small_items = 16 * a.dy + 2 * H * a.dy + 2 * H + 3 * H * DE + DE;
   hipLaunchKernelGGL((bwd_small_kernel<T, H, DH, DE>), dim3((small_items + kThreads - 1) / kThreads, (a.B + 15) / 16),
                      dim3(kThreads), 0, s, a, g);
