@@ -96,6 +96,9 @@ def backward_bench(args, cfg, dims, batch):
         step(k)
     prof = layer.profile_end()
     kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
+    bwd_name = [k for k in kernels if k.startswith("backward")][0]
+    alg = algorithmic_bytes("backward", dims, batch["n_real"], False)
+    bwd_us = kernels[bwd_name]["avg_us"]
     return {
         "metric": "graphs/s per training step of the layer (forward + backward)",
         "value": B / (ms_per_step * 1e-3), "unit": "graphs/s",
@@ -104,6 +107,10 @@ def backward_bench(args, cfg, dims, batch):
         "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded %s graphs, random Xavier weights, random output gradients)" % cfg.structure,
         "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "H": H, "buffer_sets": len(sets)},
+        # the backward's launches taken together (HIP events around the call)
+        "roofline": {"kernel": bwd_name, "bound": "hbm", "achieved": alg / (bwd_us * 1e3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": alg / (bwd_us * 1e3) / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": alg, "avg_launch_us": bwd_us},
         "kernels": kernels,
     }
 
@@ -179,6 +186,11 @@ def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
         return e_read + e_write + ((2 * rows * d * s + (lse if two_pass else 0)) if recompute else a_io)
     if kernel == "qkv_kernel":
         return rows * d * s + 3 * d * d * s + qkv
+    if kernel == "backward":
+        # E and dE' read (real pairs), dE written, A read; X and dO read, dX
+        # written; Q, K, V read back from the workspace; the projection
+        # weights read and their float32 gradients written
+        return 2 * e_read + e_write + a_io + 3 * rows * d * s + qkv + 3 * d * d * (s + 4)
     raise ValueError(kernel)
 
 
