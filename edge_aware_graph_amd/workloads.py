@@ -264,3 +264,39 @@ def make_batch(name_or_cfg, seed: Optional[int] = None, bias_scale: float = 0.0,
     out["adj"] = adj
     out["n_real"] = np.array(counts, dtype=np.int64)
     return out
+
+
+# Parameters of the graph-transformer block around the layer (node path,
+# edge path, global-feature path), nn.Linear [out, in] layout. Widths of the
+# feed-forward layers: d for the nodes, 2 de for the edges, dy for y.
+BLOCK_WEIGHTS = ("w_o", "w_x1", "w_x2", "w_e1", "w_e2", "w_yy", "w_yx", "w_ye", "w_y1", "w_y2")
+BLOCK_VECTORS = ("b_o", "b_x1", "b_x2", "b_e1", "b_e2", "b_yo", "b_y1", "b_y2")
+BLOCK_NORMS = ("x1", "x2", "e1", "e2", "y1", "y2")
+
+
+def block_widths(dims: LayerDims):
+    """Feed-forward widths (nodes, edges, y) of the block for a layer shape."""
+    return dims.d, 2 * dims.de, dims.dy
+
+
+def make_block_params(dims: LayerDims, seed: int = 7, scale: float = 0.1) -> Dict[str, np.ndarray]:
+    """Seeded block parameters: Xavier-uniform weights, N(0, scale^2) biases,
+    LayerNorm gains 1 + N(0, scale^2) and shifts N(0, scale^2) (scale = 0:
+    zero biases, unit gains, zero shifts). bfloat16-representable when the
+    shape's dtype is bf16."""
+    rng = np.random.default_rng(seed)
+    d, de, dy = dims.d, dims.de, dims.dy
+    fx, fe, fy = block_widths(dims)
+    shapes = {"w_o": (d, d), "w_x1": (fx, d), "w_x2": (d, fx), "w_e1": (fe, de), "w_e2": (de, fe),
+              "w_yy": (dy, dy), "w_yx": (dy, d), "w_ye": (dy, de), "w_y1": (fy, dy), "w_y2": (dy, fy)}
+    vec = {"b_o": d, "b_x1": fx, "b_x2": d, "b_e1": fe, "b_e2": de, "b_yo": dy, "b_y1": fy, "b_y2": dy}
+    norm = {"x1": d, "x2": d, "e1": de, "e2": de, "y1": dy, "y2": dy}
+    p = {k: _xavier(rng, *s) for k, s in shapes.items()}
+    for k, m in vec.items():
+        p[k] = (scale * rng.standard_normal(m)).astype(np.float32)
+    for k, m in norm.items():
+        p["ln_%s_g" % k] = (1.0 + scale * rng.standard_normal(m)).astype(np.float32)
+        p["ln_%s_b" % k] = (scale * rng.standard_normal(m)).astype(np.float32)
+    if dims.dtype == "bf16":
+        p = {k: bf16_round_array(v) for k, v in p.items()}
+    return p
