@@ -9,7 +9,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libedge_attn.so")
-SOURCES = [os.path.join(PKG, "csrc", "ea_kernels.hip"), os.path.join(PKG, "csrc", "ea_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "ea_kernels.hip"), os.path.join(PKG, "csrc", "ea_block.hip"),
+           os.path.join(PKG, "csrc", "ea_api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are disabled: only scalar fp32 VALU and MFMA are used.

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "edge_attn.h"
@@ -22,6 +23,8 @@ struct ea_ctx {
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
   size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_red, bws_bytes;  // backward workspace
+  int blk_nxb, blk_exb;  // block: node and edge blocks per graph
+  size_t blk_off_o, blk_off_a, blk_off_px, blk_off_pe, blk_bytes;  // block workspace (after the layer's)
   // kernel timing window
   int prof_on;
   std::vector<hipEvent_t> ev_pool;
@@ -176,6 +179,7 @@ const char* ea_kernel_name(int k) {
     case EA_K_UPDATE: return "update_kernel";
     case EA_K_FUSED: return "attn_kernel(fused)";
     case EA_K_BACKWARD: return "backward (7 kernels)";
+    case EA_K_BLOCK: return "block (node, edge, y kernels)";
   }
   return "?";
 }
@@ -219,6 +223,18 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
   c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->bws_bytes = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
+  {
+    // block: 64 nodes per node block; edge blocks of 4 waves with at least 4
+    // tiles of 16 tokens per wave, at most 256 per graph
+    const size_t tiles = ((size_t)d.n * d.n + 15) / 16;
+    c->blk_nxb = (d.n + 63) / 64;
+    c->blk_exb = (int)std::min<size_t>(256, std::max<size_t>(1, (tiles + 15) / 16));
+    c->blk_off_o = c->ws_bytes;
+    c->blk_off_a = c->blk_off_o + round256((size_t)d.B * d.n * d.d * c->esz);
+    c->blk_off_px = c->blk_off_a + (c->two_pass ? 0 : round256((size_t)d.B * d.H * d.n * d.n * c->esz));
+    c->blk_off_pe = c->blk_off_px + round256((size_t)d.B * c->blk_nxb * d.d * sizeof(float));
+    c->blk_bytes = c->blk_off_pe + round256((size_t)d.B * c->blk_exb * d.de * sizeof(float));
+  }
   c->prof_on = 0;
   c->ev_used = 0;
   *out = c;
@@ -351,6 +367,55 @@ ea_status ea_debug_logits(ea_ctx* c, const ea_attn_params* p, const void* X, con
   return timed(c, EA_K_ATTN, s, [&] {
     return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kLogits, s);
   });
+}
+
+size_t ea_block_workspace_bytes(const ea_ctx* c) { return c ? c->blk_bytes : 0; }
+
+ea_status edge_attn_block(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                          const ea_block_params* bp, const void* X, const void* E, const void* y,
+                          const uint8_t* mask, void* X_out, void* E_out, void* y_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  if (c->d.flags & kVariants) return fail(EA_E_UNSUPPORTED, "the block is built for the full layer (no variant flag)");
+  const bool shape_ok = (c->d.d == 64 && c->d.de == 16) || (c->d.d == 256 && c->d.de == 64 && c->d.dtype == EA_BF16);
+  if (!shape_ok)
+    return fail(EA_E_UNSUPPORTED, "the block is built for (d, de) = (64, 16) and, in bfloat16, (256, 64)");
+  if (c->d.dy > ea::kMaxBlockDy) return fail(EA_E_UNSUPPORTED, "the block is built for dy <= %d", ea::kMaxBlockDy);
+  if (!bp) return fail(EA_E_NULLPTR, "block parameters are NULL");
+  const void* const* bpp = reinterpret_cast<const void* const*>(bp);
+  static_assert(sizeof(ea_block_params) == ea::kBlockParams * sizeof(void*), "block parameter list");
+  static const char* const kNames[ea::kBlockParams] = {
+      "w_o", "b_o", "ln_x1_g", "ln_x1_b", "w_x1", "b_x1", "w_x2", "b_x2", "ln_x2_g", "ln_x2_b",
+      "ln_e1_g", "ln_e1_b", "w_e1", "b_e1", "w_e2", "b_e2", "ln_e2_g", "ln_e2_b",
+      "w_yy", "w_yx", "w_ye", "b_yo", "ln_y1_g", "ln_y1_b", "w_y1", "b_y1", "w_y2", "b_y2", "ln_y2_g", "ln_y2_b"};
+  for (int q = 0; q < ea::kBlockParams; ++q) EA_TRY(check_ptr(bpp[q], kNames[q], 16, true));
+  EA_TRY(check_attn_params(c, p));
+  EA_TRY(check_io(c, X, E, y, mask, true));
+  if (!y) return fail(EA_E_NULLPTR, "y is NULL (the block updates it)");
+  EA_TRY(check_ptr(X_out, "X_out", 16, true));
+  EA_TRY(check_ptr(E_out, "E_out", 16, true));
+  EA_TRY(check_ptr(y_out, "y_out", 4, true));
+  if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
+  EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
+  EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
+  if (!ws) return fail(EA_E_WORKSPACE, "workspace is NULL (%zu bytes required)", c->blk_bytes);
+  if (!aligned(ws, 256)) return fail(EA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < c->blk_bytes)
+    return fail(EA_E_WORKSPACE, "block workspace has %zu bytes, %zu required", ws_bytes, c->blk_bytes);
+  char* wb = static_cast<char*>(ws);
+  void* O = wb + c->blk_off_o;
+  void* A = c->two_pass ? nullptr : wb + c->blk_off_a;
+  EA_TRY(edge_attn_layer(c, p, u, X, E, y, mask, O, A, E_out, ws, c->ws_bytes, stream));
+  ea::BlockArgs k;
+  memset(&k, 0, sizeof(k));
+  for (int q = 0; q < ea::kBlockParams; ++q) k.p[q] = bpp[q];
+  k.X = X; k.y = y; k.mask = mask; k.O = O; k.E_io = E_out; k.X_out = X_out; k.y_out = y_out;
+  k.part_x = reinterpret_cast<float*>(wb + c->blk_off_px);
+  k.part_e = reinterpret_cast<float*>(wb + c->blk_off_pe);
+  k.B = c->d.B; k.n = c->d.n; k.dy = c->d.dy; k.nxb = c->blk_nxb; k.exb = c->blk_exb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, EA_K_BLOCK, s, [&] { return ea::launch_block(k, c->d.dtype, c->d.d, c->d.de, s); });
 }
 
 size_t ea_backward_workspace_bytes(const ea_ctx* c) { return c ? c->bws_bytes : 0; }

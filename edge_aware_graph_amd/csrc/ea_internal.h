@@ -80,6 +80,30 @@ struct BwdArgs {
 // address low; a later kernel sums the copies.
 constexpr int kRedCopies = 32;
 
+// Graph-transformer block around the layer: parameters (in this order; the
+// nn.Linear [out, in] layout, all in the layer's dtype) and arguments.
+enum BlockParam : int {
+  kBW_o, kBb_o, kBln_x1_g, kBln_x1_b, kBW_x1, kBb_x1, kBW_x2, kBb_x2, kBln_x2_g, kBln_x2_b,
+  kBln_e1_g, kBln_e1_b, kBW_e1, kBb_e1, kBW_e2, kBb_e2, kBln_e2_g, kBln_e2_b,
+  kBW_yy, kBW_yx, kBW_ye, kBb_yo, kBln_y1_g, kBln_y1_b, kBW_y1, kBb_y1, kBW_y2, kBb_y2, kBln_y2_g, kBln_y2_b,
+  kBlockParams
+};
+constexpr int kMaxBlockDy = 512;
+struct BlockArgs {
+  const void* p[kBlockParams];
+  const void* X;          // [B, n, d]
+  const void* y;          // [B, dy]
+  const uint8_t* mask;    // [B, n]
+  const void* O;          // the layer's node output [B, n, d]
+  void* E_io;             // E' in, E2 out [B, n, n, de]
+  void* X_out;            // [B, n, d]
+  void* y_out;            // [B, dy]
+  float* part_x;          // [B, nxb, d] sums of X2 over real nodes per node block
+  float* part_e;          // [B, exb, de] sums of E2 over real pairs per edge block
+  int B, n, dy, nxb, exb;
+};
+hipError_t launch_block(const BlockArgs& k, int dtype, int d, int de, hipStream_t s);
+
 // Launchers; each returns the hipError_t of its launch. `dtype` 0 = fp32, 1 = bf16.
 hipError_t launch_qkv(const LayerArgs& a, int dtype, int H, int dh, int de, hipStream_t s);
 hipError_t launch_attn(const LayerArgs& a, int dtype, int H, int dh, int de, int mode,

@@ -25,14 +25,22 @@ EA_VARIANT_UNNORMALIZED = 0x8
 VARIANTS = {"light_edge": EA_VARIANT_LIGHT_EDGE, "no_score_mod": EA_VARIANT_NO_SCORE_MOD,
             "unnormalized": EA_VARIANT_UNNORMALIZED}
 EA_SINGLE_PASS_MAX_N = 256
-KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)", "backward (7 kernels)")
+KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)", "backward (7 kernels)",
+           "block (node, edge, y kernels)")
 
 # Symbols declared in include/edge_attn.h.
 EXPORTS = ("ea_ctx_create", "ea_ctx_destroy", "ea_workspace_bytes", "ea_is_two_pass",
            "edge_attn_forward", "edge_update", "edge_attn_layer", "ea_status_str",
            "ea_last_error", "ea_debug_logits", "ea_profile_begin", "ea_profile_end",
            "ea_backward_workspace_bytes", "edge_attn_backward",
+           "ea_block_workspace_bytes", "edge_attn_block",
            "ea_kernel_name")
+
+# Parameters of the graph-transformer block, in the order of ea_block_params.
+BLOCK_PARAM_NAMES = ("w_o", "b_o", "ln_x1_g", "ln_x1_b", "w_x1", "b_x1", "w_x2", "b_x2", "ln_x2_g", "ln_x2_b",
+                     "ln_e1_g", "ln_e1_b", "w_e1", "b_e1", "w_e2", "b_e2", "ln_e2_g", "ln_e2_b",
+                     "w_yy", "w_yx", "w_ye", "b_yo", "ln_y1_g", "ln_y1_b", "w_y1", "b_y1", "w_y2", "b_y2",
+                     "ln_y2_g", "ln_y2_b")
 
 
 class EaError(RuntimeError):
@@ -61,6 +69,11 @@ class UpdateParams(ctypes.Structure):
 
 
 GRAD_NAMES = ATTN_PARAM_NAMES + UPDATE_PARAM_NAMES
+
+
+class BlockParams(ctypes.Structure):
+    """ea_block_params: device pointers to the block's parameters."""
+    _fields_ = [(k, ctypes.c_void_p) for k in BLOCK_PARAM_NAMES]
 
 
 class Grads(ctypes.Structure):
@@ -114,6 +127,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_attn_backward.restype = ctypes.c_int
     lib.edge_attn_backward.argtypes = [vp, ap, up, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.POINTER(Grads), vp, sz, vp, sz, vp]
+    lib.ea_block_workspace_bytes.restype = sz
+    lib.ea_block_workspace_bytes.argtypes = [vp]
+    lib.edge_attn_block.restype = ctypes.c_int
+    lib.edge_attn_block.argtypes = [vp, ap, up, ctypes.POINTER(BlockParams), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -231,6 +248,32 @@ class EdgeAttention:
             self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask), _ptr(A),
             _ptr(dO), _ptr(dEp), _ptr(dX), _ptr(dE), _ptr(dy), ctypes.byref(g),
             _ptr(ws), self._ws_len(ws), _ptr(bws), self._ws_len(bws), _stream(stream)))
+
+    @property
+    def block_workspace_bytes(self) -> int:
+        return int(self.lib.ea_block_workspace_bytes(self.ctx))
+
+    def bind_block(self, w, bp: Dict, X, E, y, mask, X_out, E_out, y_out, ws, stream=None):
+        """Marshal the arguments of one block call (layer weights w, block
+        parameters bp by name) once; returns a callable that launches it."""
+        p = self.attn_params(w)
+        u = self.update_params(w)
+        b = BlockParams(*[_ptr(bp[name]) for name in BLOCK_PARAM_NAMES])
+        args = (self.ctx, ctypes.byref(p), ctypes.byref(u), ctypes.byref(b), _ptr(X), _ptr(E), _ptr(y), _ptr(mask),
+                _ptr(X_out), _ptr(E_out), _ptr(y_out), _ptr(ws), self._ws_len(ws), _stream(stream))
+        fn, lib = self.lib.edge_attn_block, self.lib
+        keep = (p, u, b, w, bp, X, E, y, mask, X_out, E_out, y_out, ws)
+
+        def call():
+            st = fn(*args)
+            if st != EA_OK:
+                _check(lib, st)
+        call.keep = keep
+        return call
+
+    def block(self, w, bp: Dict, X, E, y, mask, X_out, E_out, y_out, ws, stream=None):
+        """One graph-transformer block (the layer, then the node, edge and y paths)."""
+        self.bind_block(w, bp, X, E, y, mask, X_out, E_out, y_out, ws, stream)()
 
     def debug_logits(self, w, X, E, y, mask, U, ws, stream=None):
         p = self.attn_params(w)

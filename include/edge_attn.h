@@ -219,13 +219,53 @@ ea_status ea_debug_logits(ea_ctx* ctx, const ea_attn_params* p,
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Graph-transformer block around the layer. The method's page ("Efficient
+ * Edge-aware Attention Network for Graph Generation", full-text summary)
+ * swaps the attention inside a graph transformer and keeps the block around
+ * it, which it does not write out; the block computed here is the usual one
+ * of the denoising graph transformers it builds on:
+ *   (O, A, E') = edge_attn_layer(X, E, y, mask)
+ *   X1 = LN(X + O W_o^T + b_o),   X2 = LN(X1 + W_x2 relu(W_x1 X1 + b_x1) + b_x2)
+ *   E1 = LN(E'),                  E2 = LN(E1 + W_e2 relu(W_e1 E1 + b_e1) + b_e2)
+ *   y1 = LN(y + W_yy y + W_yx xbar + W_ye ebar + b_yo)
+ *   y2 = LN(y1 + W_y2 relu(W_y1 y1 + b_y1) + b_y2)
+ * xbar and ebar are the means of X2 over real nodes and of E2 over real
+ * pairs (0 for a graph without real nodes); LN normalizes over the feature
+ * axis (population variance, eps 1e-5) with a gain and a shift. Widths:
+ * W_o, W_x1, W_x2 [d, d]; W_e1 [2 de, de], W_e2 [de, 2 de]; W_yy, W_y1,
+ * W_y2 [dy, dy]; W_yx [dy, d]; W_ye [dy, de]; every parameter in the
+ * context's dtype, nn.Linear [out, in] layout, 16-byte aligned, none NULL.
+ * Rows of masked nodes of X2 and masked pairs of E2 are +0.0.
+ *
+ * Built for the (d, de) = (64, 16) shape (float32 and bfloat16) and
+ * (256, 64) (bfloat16), dy <= 512, no variant flag (else EA_E_UNSUPPORTED);
+ * single-pass and two-pass contexts. X_out may alias X, E_out may alias E
+ * and y_out may alias y. ws holds ea_block_workspace_bytes (the layer's
+ * workspace, then O, A and per-block partial sums). bfloat16 mode stores O
+ * and E' in bfloat16 and rounds X1, E1 and the hidden layers to bfloat16
+ * where they enter a matrix product (float32 accumulation).
+ */
+typedef struct {
+  const void *w_o, *b_o, *ln_x1_g, *ln_x1_b, *w_x1, *b_x1, *w_x2, *b_x2, *ln_x2_g, *ln_x2_b;
+  const void *ln_e1_g, *ln_e1_b, *w_e1, *b_e1, *w_e2, *b_e2, *ln_e2_g, *ln_e2_b;
+  const void *w_yy, *w_yx, *w_ye, *b_yo, *ln_y1_g, *ln_y1_b, *w_y1, *b_y1, *w_y2, *b_y2, *ln_y2_g, *ln_y2_b;
+} ea_block_params;
+
+size_t ea_block_workspace_bytes(const ea_ctx* ctx);
+ea_status edge_attn_block(ea_ctx* ctx, const ea_attn_params* p, const ea_update_params* u,
+                          const ea_block_params* bp, const void* X, const void* E, const void* y,
+                          const uint8_t* node_mask, void* X_out, void* E_out, void* y_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing with HIP events recorded on the launch stream around every
  * kernel the context launches while enabled. ea_profile_begin starts a
  * window (at most 4096 launches are recorded); ea_profile_end waits for the
  * last event and returns, per kernel id, the summed milliseconds and the
  * launch count (arrays of EA_NUM_KERNELS entries).
  */
-enum { EA_K_QKV = 0, EA_K_ATTN = 1, EA_K_UPDATE = 2, EA_K_FUSED = 3, EA_K_BACKWARD = 4, EA_NUM_KERNELS = 5 };
+enum { EA_K_QKV = 0, EA_K_ATTN = 1, EA_K_UPDATE = 2, EA_K_FUSED = 3, EA_K_BACKWARD = 4, EA_K_BLOCK = 5,
+       EA_NUM_KERNELS = 6 };
 ea_status ea_profile_begin(ea_ctx* ctx);
 ea_status ea_profile_end(ea_ctx* ctx, double* total_ms, int64_t* launches);
 const char* ea_kernel_name(int kernel_id);

@@ -231,3 +231,40 @@ def test_backward_rules(lib):
     assert bwd(ctx, bwsb=16) == L.EA_E_WORKSPACE
     assert bwd(ctx) == L.EA_E_STATE  # no forward on this context yet
     lib.ea_ctx_destroy(ctx)
+
+
+def test_block_rules(lib):
+    """The block: built shapes, no variant, every parameter present and aligned, a workspace of the block's size."""
+    p = attn_params()
+    u = L.UpdateParams(FAKE, None)
+    bp = L.BlockParams(*([FAKE] * len(L.BLOCK_PARAM_NAMES)))
+
+    def blk(ctx, **k):
+        return lib.edge_attn_block(ctx, ctypes.byref(p), ctypes.byref(u), k.get("bp", ctypes.byref(bp)),
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("y_out", FAKE),
+                                   k.get("ws", FAKE), k.get("wsb", 1 << 40), None)
+    assert ctypes.sizeof(L.BlockParams) == 30 * ctypes.sizeof(ctypes.c_void_p)
+    for kw in (dict(flags=L.EA_VARIANT_NO_SCORE_MOD), dict(d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_FP32),
+               dict(d=128, de=32, H=4, dh=32), dict(dy=1024)):
+        st, ctx = create(lib, make_desc(**kw))
+        if st != L.EA_OK:  # a shape the library does not build at all
+            continue
+        assert blk(ctx) == L.EA_E_UNSUPPORTED, kw
+        lib.ea_ctx_destroy(ctx)
+    for two_pass in (False, True):
+        st, ctx = create(lib, make_desc(n=300 if two_pass else 12))
+        assert st == L.EA_OK
+        wsb = lib.ea_block_workspace_bytes(ctx)
+        assert wsb > lib.ea_workspace_bytes(ctx)
+        assert blk(ctx, bp=None) == L.EA_E_NULLPTR
+        for q in range(len(L.BLOCK_PARAM_NAMES)):
+            vals = [FAKE] * len(L.BLOCK_PARAM_NAMES)
+            vals[q] = None
+            assert blk(ctx, bp=ctypes.byref(L.BlockParams(*vals))) == L.EA_E_NULLPTR, L.BLOCK_PARAM_NAMES[q]
+            vals[q] = MISALIGNED
+            assert blk(ctx, bp=ctypes.byref(L.BlockParams(*vals))) == L.EA_E_ALIGN, L.BLOCK_PARAM_NAMES[q]
+        assert blk(ctx, y_out=None) == L.EA_E_NULLPTR
+        assert blk(ctx, ws=None) == L.EA_E_WORKSPACE
+        assert blk(ctx, wsb=wsb - 1) == L.EA_E_WORKSPACE
+        assert "block" in lib.ea_kernel_name(L.KERNELS.index("block (node, edge, y kernels)")).decode()
+        lib.ea_ctx_destroy(ctx)

@@ -1,0 +1,108 @@
+"""The graph-transformer block on the GPU (edge_attn_block through the C ABI)
+against the block oracle (oracle/block.py: the C layer oracle, then the node,
+edge and global-feature paths in float64).
+
+Tolerances per output tensor: float32 1e-4 of the tensor's largest reference
+value; bfloat16 2e-2 absolute (the outputs are layer-normalized, O(1)), with
+the oracle applying the same bfloat16 rounding points (O and E' stored,
+X1, E1 and the hidden layers rounded where they enter a product). Rows of
+masked nodes of X2 and masked pairs of E2 are +0.0 bit-exactly.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from edge_aware_graph_amd import workloads as W
+from oracle import block as OBK
+from tests import _layer_harness as HX
+
+pytestmark = pytest.mark.gpu
+
+
+def dims_of(name, **over):
+    return dataclasses.replace(W.CONFIGS[name].dims, **over)
+
+
+def run_block(batch, dims, bp, force_two_pass=False, alias=False):
+    dt = HX.tdtype(dims.dtype)
+    run = HX.Run(batch, dims, force_two_pass=force_two_pass)
+    dev = run.dev
+    tbp = {k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to("cuda", dt) for k, v in bp.items()}
+    B, n, d, de, dy = dims.B, dims.n, dims.d, dims.de, dims.dy
+    ws = torch.empty(run.layer.block_workspace_bytes, dtype=torch.uint8, device="cuda")
+    if alias:  # outputs over the inputs
+        X_out, E_out, y_out = dev["X"], dev["E"], dev["y"]
+    else:
+        X_out = torch.full((B, n, d), float("nan"), dtype=dt, device="cuda")
+        E_out = torch.full((B, n, n, de), float("nan"), dtype=dt, device="cuda")
+        y_out = torch.full((B, dy), float("nan"), dtype=dt, device="cuda")
+    run.layer.block(dev, tbp, dev["X"], dev["E"], dev["y"], dev["mask"], X_out, E_out, y_out, ws)
+    torch.cuda.synchronize()
+    got = {"X2": X_out.float().cpu().numpy(), "E2": E_out.float().cpu().numpy(), "y2": y_out.float().cpu().numpy()}
+    ref = OBK.block(batch, bp, dims.H, dims.dtype == "bf16")
+    return got, ref
+
+
+def check(got, ref, batch, dims):
+    for k in ("X2", "E2", "y2"):
+        g = got[k].astype(np.float64)
+        assert g.shape == ref[k].shape, k
+        assert np.isfinite(g).all(), "%s has non-finite values" % k
+        err = np.abs(g - ref[k]).max()
+        if dims.dtype == "fp32":
+            tol = HX.FP32_REL_TOL * max(np.abs(ref[k]).max(), 1e-6)
+        else:
+            tol = HX.BF16_ABS_TOL
+        assert err <= tol, "%s: max err %.3e > %.3e" % (k, err, tol)
+    m = batch["mask"].astype(bool)
+    pm = m[:, :, None] & m[:, None, :]
+    assert np.all(got["X2"][~m] == 0) and not np.any(np.signbit(got["X2"][~m]))
+    assert np.all(got["E2"][~pm] == 0) and not np.any(np.signbit(got["E2"][~pm]))
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"dtype": "bf16"}), ("planar", {"B": 4})],
+                         ids=["tiny-fp32", "tiny-bf16", "planar-bf16"])
+def test_block_matches_oracle(name, over):
+    dims = dims_of(name, **over)
+    batch = W.make_batch(name, bias_scale=0.1, dims=dims)
+    bp = W.make_block_params(dims)
+    got, ref = run_block(batch, dims, bp)
+    check(got, ref, batch, dims)
+
+
+@pytest.mark.parametrize("n,dtype", [(37, "bf16"), (70, "bf16"), (17, "fp32")])
+def test_block_ragged_random_masks(n, dtype):
+    """Non-prefix masks, a graph with every node real and one with none, n not
+    a multiple of 16 (node tiles and edge tiles with invalid lanes)."""
+    over = {"n": n, "B": 3, "dtype": dtype}
+    dims = dims_of("tiny" if dtype == "fp32" else "planar", **over)
+    batch = W.make_batch("tiny", bias_scale=0.2, dims=dims)
+    rng = np.random.default_rng(n)
+    mask = (rng.random((3, n)) < 0.7).astype(np.uint8)
+    mask[0] = 1
+    mask[2] = 0
+    batch["mask"] = mask
+    bp = W.make_block_params(dims, seed=n)
+    got, ref = run_block(batch, dims, bp)
+    check(got, ref, batch, dims)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_block_two_pass_and_aliased_outputs(dtype):
+    """Forced two-pass layer inside the block, outputs written over the inputs."""
+    dims = dims_of("tiny", dtype=dtype)
+    batch = W.make_batch("tiny", bias_scale=0.1, dims=dims)
+    bp = W.make_block_params(dims, seed=3)
+    got, ref = run_block(batch, dims, bp, force_two_pass=True, alias=True)
+    check(got, ref, batch, dims)
+
+
+def test_block_sbm_bf16_reduced():
+    """SBM-shaped batch (varying graph sizes, padded to n), a few graphs."""
+    dims = dims_of("sbm", B=3)
+    batch = W.make_batch("sbm", bias_scale=0.1, dims=dims)
+    bp = W.make_block_params(dims, seed=5)
+    got, ref = run_block(batch, dims, bp)
+    check(got, ref, batch, dims)
