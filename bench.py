@@ -44,6 +44,8 @@ def parse():
                     help="ablation variant of the layer (the default is the full layer)")
     ap.add_argument("--backward", action="store_true",
                     help="time training steps instead: the layer forward plus its backward")
+    ap.add_argument("--block", action="store_true",
+                    help="time the graph-transformer block around the layer (layer + node, edge and y paths)")
     ap.add_argument("--sampling-layers", type=int, default=0,
                     help="instead of single layers, time denoising steps of this many stacked layers "
                          "(a step is then one pass through all of them)")
@@ -111,6 +113,65 @@ def backward_bench(args, cfg, dims, batch):
         "roofline": {"kernel": bwd_name, "bound": "hbm", "achieved": alg / (bwd_us * 1e3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": alg / (bwd_us * 1e3) / HBM_PEAK_GBS, "traffic": None,
                      "alg_bytes_per_launch": alg, "avg_launch_us": bwd_us},
+        "kernels": kernels,
+    }
+
+
+def block_bench(args, cfg, dims, batch):
+    """Forward of the graph-transformer block around the layer (the layer,
+    then the node, edge and global-feature paths), on buffer sets rotated so
+    that every step reads from HBM."""
+    import torch
+    from edge_aware_graph_amd import workloads as W
+    from edge_aware_graph_amd.layer import EdgeAttention
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype)
+    w = {k: torch.from_numpy(v).to(dev, dt) for k, v in batch.items() if k.startswith(("w_", "b_"))}
+    bp = {k: torch.from_numpy(v).to(dev, dt) for k, v in W.make_block_params(dims, scale=0.0).items()}
+    B, n, d, de, dy = dims.B, dims.n, dims.d, dims.de, dims.dy
+    s = 2 if dims.dtype == "bf16" else 4
+    set_bytes = (2 * B * n * n * de + 2 * B * n * d + 2 * B * dy) * s + layer.block_workspace_bytes
+    nsets = int(max(1, min(16, -(-2 * INFINITY_CACHE_BYTES // set_bytes))))
+    calls = []
+    for _ in range(nsets):
+        X = torch.from_numpy(batch["X"]).to(dev, dt)
+        E = torch.from_numpy(batch["E"]).to(dev, dt)
+        y = torch.from_numpy(batch["y"]).to(dev, dt)
+        m = torch.from_numpy(batch["mask"]).to(dev)
+        Xo, Eo, yo = torch.empty_like(X), torch.empty_like(E), torch.empty_like(y)
+        ws = torch.empty(layer.block_workspace_bytes, dtype=torch.uint8, device=dev)
+        calls.append(layer.bind_block(w, bp, X, E, y, m, Xo, Eo, yo, ws))
+    for k in range(args.warmup):
+        calls[k % nsets]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        calls[k % nsets]()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    layer.profile_begin()
+    for k in range(args.steps):
+        calls[k % nsets]()
+    prof = layer.profile_end()
+    kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
+    bname = [k for k in kernels if k.startswith("block")][0]
+    alg = algorithmic_bytes("block", dims, batch["n_real"], layer.two_pass)
+    bus = kernels[bname]["avg_us"]
+    return {
+        "metric": "graphs/s per graph-transformer block forward (edge-aware attention layer + node, edge "
+                  "and global-feature paths)",
+        "value": B / (ms_per_step * 1e-3), "unit": "graphs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded %s graphs, random Xavier weights)" % cfg.structure,
+        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "dy": dy, "H": dims.H,
+                   "two_pass": layer.two_pass, "buffer_sets": nsets},
+        # the block's own three launches taken together (HIP events around them)
+        "roofline": {"kernel": bname, "bound": "hbm", "achieved": alg / (bus * 1e3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": alg / (bus * 1e3) / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": alg, "avg_launch_us": bus},
         "kernels": kernels,
     }
 
@@ -186,6 +247,13 @@ def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
         return e_read + e_write + ((2 * rows * d * s + (lse if two_pass else 0)) if recompute else a_io)
     if kernel == "qkv_kernel":
         return rows * d * s + 3 * d * d * s + qkv
+    if kernel == "block":
+        # node path: O and X read, X2 written; edge path: E' read, E2 written
+        # (real pairs only carry data, but the padded layout is written);
+        # parameters read once
+        fx, fe, fy = d, 2 * de, dims.dy
+        params = (3 * d * d + 2 * de * fe + dims.dy * (2 * dims.dy + d + de)) * s
+        return 3 * rows * d * s + e_read + e_write + params
     if kernel == "backward":
         # E and dE' read (real pairs), dE written, A read; X and dO read, dX
         # written; Q, K, V read back from the workspace; the projection
@@ -255,6 +323,9 @@ def main():
         return
     if args.backward:
         print(json.dumps(backward_bench(args, cfg, dims, batch)), flush=True)
+        return
+    if args.block:
+        print(json.dumps(block_bench(args, cfg, dims, batch)), flush=True)
         return
     dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
 

@@ -224,10 +224,10 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->bws_bytes = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
   {
-    // block: 64 nodes per node block; edge blocks of 4 waves with at least 4
+    // block: 16 nodes per node block; edge blocks of 4 waves with at least 4
     // tiles of 16 tokens per wave, at most 256 per graph
     const size_t tiles = ((size_t)d.n * d.n + 15) / 16;
-    c->blk_nxb = (d.n + 63) / 64;
+    c->blk_nxb = (d.n + 15) / 16;
     c->blk_exb = (int)std::min<size_t>(256, std::max<size_t>(1, (tiles + 15) / 16));
     c->blk_off_o = c->ws_bytes;
     c->blk_off_a = c->blk_off_o + round256((size_t)d.B * d.n * d.d * c->esz);

@@ -78,163 +78,280 @@ struct RowIn {
 #pragma unroll
     for (int s = 0; s < S::NS; ++s) f[s].set(v + s * S::Q);
   }
-  __device__ __forceinline__ void load(const T* row, int lg) {  // straight from a row in memory
-    constexpr int DW = 4 * (int)sizeof(T) / 4;  // dwords per group of four
-#pragma unroll
-    for (int s = 0; s < S::NS; ++s) {
-      ld4w<T>(f[s].w, row + 32 * s + 4 * lg);
-      if constexpr (S::Q == 8) ld4w<T>(f[s].w + DW, row + 32 * s + 16 + 4 * lg);
-    }
-  }
 };
 
-// Left-operand fragment: row o of W [NO, K], step s, in the row-layout order.
+// Fragment in the row-layout contraction order from a row of K elements
+// (global memory or LDS): elements 32 s + 4 lg .. + 3 and 32 s + 16 + 4 lg .. + 3.
 template <typename T, int K>
-__device__ __forceinline__ Frag<T, Steps<K>::Q> w_frag(const T* W, int o, int s, int lg) {
+__device__ __forceinline__ Frag<T, Steps<K>::Q> frag_at(const T* row, int s, int lg) {
   using S = Steps<K>;
   constexpr int DW = 4 * (int)sizeof(T) / 4;
   Frag<T, S::Q> a;
-  const T* row = W + (size_t)o * K;
   ld4w<T>(a.w, row + 32 * s + 4 * lg);
   if constexpr (S::Q == 8) ld4w<T>(a.w + DW, row + 32 * s + 16 + 4 * lg);
   return a;
 }
 
-// out[NO / 4] (row layout) = W in (+ bias), W streamed from memory.
-template <typename T, int K, int NO>
-__device__ __forceinline__ void row_gemm(float* out, const RowIn<T, K>& in, const T* W, const T* bias, int li,
-                                         int lg) {
+// 16-byte pieces of a [ROWS, COLS] matrix: thread tid takes pieces tid,
+// tid + 256, ...; piece q is row q / (COLS / EPC), columns EPC (q % (COLS / EPC)) ..
+template <typename T, int ROWS, int COLS>
+struct Pieces {
+  static constexpr int EPC = 16 / (int)sizeof(T), N = ROWS * COLS / EPC, PER = (N + kThreads - 1) / kThreads;
+  u32x4 v[PER];
+  __device__ __forceinline__ void load(const T* src, int tid) {  // src: row-major, row stride COLS
 #pragma unroll
-  for (int to = 0; to < NO / 16; ++to) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < Steps<K>::NS; ++s) acc = mma(acc, w_frag<T, K>(W, 16 * to + li, s, lg), in.f[s]);
-    float bv[4];
-    ld4f<T>(bv, bias + 16 * to + 4 * lg);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) out[4 * to + r] = acc[r] + bv[r];
+    for (int e = 0; e < PER; ++e) {
+      const int q = tid + e * kThreads, qc = q < N ? q : 0;
+      v[e] = *reinterpret_cast<const u32x4*>(src + (size_t)(qc / (COLS / EPC)) * COLS + EPC * (qc % (COLS / EPC)));
+    }
   }
-}
-
-// In-place layer norm of a row-layout vector of F features (gain g, shift b).
-template <typename T, int F>
-__device__ __forceinline__ void row_ln(float* v, const T* g, const T* b, int lg) {
-  float s = 0.f;
+  template <int LD>
+  __device__ __forceinline__ void store(T (*dst)[LD], int tid) const {
 #pragma unroll
-  for (int k = 0; k < F / 4; ++k) s += v[k];
-  const float mean = lg_sum(s) * (1.f / F);
-  float q = 0.f;
-#pragma unroll
-  for (int k = 0; k < F / 4; ++k) {
-    v[k] -= mean;
-    q += v[k] * v[k];
+    for (int e = 0; e < PER; ++e) {
+      const int q = tid + e * kThreads;
+      if (PER * kThreads == N || q < N) *reinterpret_cast<u32x4*>(&dst[q / (COLS / EPC)][EPC * (q % (COLS / EPC))]) = v[e];
+    }
   }
-  const float inv = 1.f / sqrtf(lg_sum(q) * (1.f / F) + kLnEps);
-#pragma unroll
-  for (int t = 0; t < F / 16; ++t) {
-    float gv[4], bv[4];
-    ld4f<T>(gv, g + 16 * t + 4 * lg);
-    ld4f<T>(bv, b + 16 * t + 4 * lg);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[4 * t + r] = v[4 * t + r] * inv * gv[r] + bv[r];
-  }
-}
+};
 
 // ------------------------------------------------------------------ nodes
 
-// Grid (ceil(n / 64), B); wave w takes nodes 64 blockIdx.x + 16 w .. + 15 of
-// graph blockIdx.y. Writes X2 and the block's sum of X2 over its real nodes
-// (partial_x [B][gridDim.x][D]).
+// Grid (ceil(n / 16), B): a block takes 16 nodes of graph blockIdx.y; wave w
+// computes output features w D / 4 .. (w + 1) D / 4 - 1 (D / 64 tiles of 16)
+// of all 16 rows. Each product's weight matrix is staged whole in LDS (the next one
+// is loaded into registers while the current product and its layer norm
+// run), and so is the product's input (O, then X1, then the hidden layer,
+// rounded to T); layer-norm statistics combine over the waves through LDS.
+// Writes X2 and the block's sums of X2 over its real nodes (part_x).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void blk_node_kernel(BlockArgs k) {
-  __shared__ float sum_s[D];
+  // FW features (TPW tiles of 16) per wave
+  constexpr int EPC = 16 / (int)sizeof(T), LD = D + EPC, TPW = D / 64, FW = D / 4;
+  static_assert(D % 64 == 0, "four waves of whole tiles");
+  __shared__ __align__(16) T w_s[D][LD];
+  __shared__ __align__(16) T in_s[16][LD];
+  __shared__ float red_s[2][kWaves][16];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int b = blockIdx.y, n = k.n, i = blockIdx.x * 64 + 16 * w + li;
+  const int b = blockIdx.y, n = k.n, i = blockIdx.x * 16 + li;
   const bool inr = i < n;
   const size_t row = (size_t)b * n + (inr ? i : 0);
-  const bool real = inr && k.mask[row] != 0;
-  for (int f = tid; f < D; f += kThreads) sum_s[f] = 0.f;
   auto par = [&](int q) { return static_cast<const T*>(k.p[q]); };
-  RowIn<T, D> o_in;
-  o_in.load(static_cast<const T*>(k.O) + row * D, lg);
-  float x1[D / 4], z[D / 4];
+  const size_t row0 = (size_t)b * n + blockIdx.x * 16;  // the block's first node row
+  const int nrows = n - (int)blockIdx.x * 16 < 16 ? n - (int)blockIdx.x * 16 : 16;
+  // the block's 16 rows of O (rows past n are clamped to the first row)
+  auto load_rows = [&](Pieces<T, 16, D>& pc, const T* base) {
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) ld4f<T>(x1 + 4 * t, static_cast<const T*>(k.X) + row * D + 16 * t + 4 * lg);
-  row_gemm<T, D, D>(z, o_in, par(kBW_o), par(kBb_o), li, lg);
+    for (int e = 0; e < Pieces<T, 16, D>::PER; ++e) {
+      const int q = tid + e * kThreads, r = q / (D / EPC), rr = r < nrows ? r : 0;
+      pc.v[e] = *reinterpret_cast<const u32x4*>(base + (row0 + rr) * D + EPC * (q % (D / EPC)));
+    }
+  };
+  Pieces<T, D, D> wp;
+  Pieces<T, 16, D> ip;
+  wp.load(par(kBW_o), tid);
+  load_rows(ip, static_cast<const T*>(k.O));
+  const bool real = inr && k.mask[row] != 0;
+  float xr[4 * TPW];  // X, this wave's features of row li
 #pragma unroll
-  for (int q = 0; q < D / 4; ++q) x1[q] += z[q];
-  row_ln<T, D>(x1, par(kBln_x1_g), par(kBln_x1_b), lg);
-  {
-    RowIn<T, D> in;
-    in.set(x1);
-    row_gemm<T, D, D>(z, in, par(kBW_x1), par(kBb_x1), li, lg);
-  }
+  for (int t = 0; t < TPW; ++t) ld4f<T>(xr + 4 * t, static_cast<const T*>(k.X) + row * D + FW * w + 16 * t + 4 * lg);
+  wp.store(w_s, tid);
+  ip.store(in_s, tid);
+  __syncthreads();
+  wp.load(par(kBW_x1), tid);  // in flight during the first product and its layer norm
+
+  // out[4 TPW] = this wave's features of W in + bias, W and in from LDS
+  auto gemm = [&](float* out, int bias_q) {
 #pragma unroll
-  for (int q = 0; q < D / 4; ++q) z[q] = fmaxf(z[q], 0.f);
-  {
-    RowIn<T, D> in;
-    in.set(z);
-    row_gemm<T, D, D>(z, in, par(kBW_x2), par(kBb_x2), li, lg);
-  }
+    for (int t = 0; t < TPW; ++t) {
+      const int o0 = FW * w + 16 * t;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < D / 4; ++q) z[q] += x1[q];
-  row_ln<T, D>(z, par(kBln_x2_g), par(kBln_x2_b), lg);
+      for (int s2 = 0; s2 < Steps<D>::NS; ++s2)
+        acc = mma(acc, frag_at<T, D>(&w_s[o0 + li][0], s2, lg), frag_at<T, D>(&in_s[li][0], s2, lg));
+      float bv[4];
+      ld4f<T>(bv, par(bias_q) + o0 + 4 * lg);
 #pragma unroll
-  for (int q = 0; q < D / 4; ++q) z[q] = real ? z[q] : 0.f;
+      for (int r = 0; r < 4; ++r) out[4 * t + r] = acc[r] + bv[r];
+    }
+  };
+  // layer norm over all D features of row li (this wave holds 4 TPW of them)
+  auto ln = [&](float* v, int gq, int bq) {
+    float sm = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4 * TPW; ++q) sm += v[q];
+    sm = lg_sum(sm);
+    if (lg == 0) red_s[0][w][li] = sm;
+    __syncthreads();
+    const float mean = (red_s[0][0][li] + red_s[0][1][li] + red_s[0][2][li] + red_s[0][3][li]) * (1.f / D);
+    float sq = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4 * TPW; ++q) {
+      v[q] -= mean;
+      sq += v[q] * v[q];
+    }
+    sq = lg_sum(sq);
+    if (lg == 0) red_s[1][w][li] = sq;
+    __syncthreads();
+    const float inv =
+        1.f / sqrtf((red_s[1][0][li] + red_s[1][1][li] + red_s[1][2][li] + red_s[1][3][li]) * (1.f / D) + kLnEps);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float gv[4], bv[4];
+      ld4f<T>(gv, par(gq) + FW * w + 16 * t + 4 * lg);
+      ld4f<T>(bv, par(bq) + FW * w + 16 * t + 4 * lg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * t + r] = v[4 * t + r] * inv * gv[r] + bv[r];
+    }
+  };
+  // this wave's features of a row-layout vector into in_s (rounded to T)
+  auto put_row = [&](const float* v) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) st4f<T>(&in_s[li][FW * w + 16 * t + 4 * lg], v + 4 * t);
+  };
+
+  float x1[4 * TPW], z[4 * TPW];
+  gemm(z, kBb_o);
+#pragma unroll
+  for (int q = 0; q < 4 * TPW; ++q) x1[q] = z[q] + xr[q];
+  ln(x1, kBln_x1_g, kBln_x1_b);  // its barriers also end every wave's reads of w_s and in_s
+  put_row(x1);
+  wp.store(w_s, tid);
+  __syncthreads();
+  wp.load(par(kBW_x2), tid);
+  gemm(z, kBb_x1);
+#pragma unroll
+  for (int q = 0; q < 4 * TPW; ++q) z[q] = fmaxf(z[q], 0.f);
+  __syncthreads();  // every wave is done with w_s and in_s
+  put_row(z);
+  wp.store(w_s, tid);
+  __syncthreads();
+  gemm(z, kBb_x2);
+#pragma unroll
+  for (int q = 0; q < 4 * TPW; ++q) z[q] += x1[q];
+  ln(z, kBln_x2_g, kBln_x2_b);
+#pragma unroll
+  for (int q = 0; q < 4 * TPW; ++q) z[q] = real ? z[q] : 0.f;
   if (inr) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) st4f<T>(static_cast<T*>(k.X_out) + row * D + 16 * t + 4 * lg, z + 4 * t);
+    for (int t = 0; t < TPW; ++t) st4f<T>(static_cast<T*>(k.X_out) + row * D + FW * w + 16 * t + 4 * lg, z + 4 * t);
   }
-  __syncthreads();
+  // sums over the 16 rows (lanes li of a lane group) of the block's real nodes
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
+  for (int q = 0; q < 4 * TPW; ++q) {
+    float v = z[q];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    z[q] = v;
+  }
+  if (li == 0) {
+    float* part = k.part_x + ((size_t)b * gridDim.x + blockIdx.x) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) atomicAdd(&sum_s[16 * t + 4 * lg + r], z[4 * t + r]);
-  __syncthreads();
-  float* part = k.part_x + ((size_t)b * gridDim.x + blockIdx.x) * D;
-  for (int f = tid; f < D; f += kThreads) part[f] = sum_s[f];
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[FW * w + 16 * t + 4 * lg + r] = z[4 * t + r];
+  }
 }
 
 // ------------------------------------------------------------------ edges
 
-// Grid (EX, B): the edge tokens (i, j) of graph blockIdx.y in tiles of 16,
-// tile q for wave slot blockIdx.x * 4 + w, stepping by 4 EX. E2 is written
-// over E' in place (each lane reads its token's row before writing it).
-// Also the block's sum of E2 over its real pairs (partial_e [B][EX][DE]).
+// Grid (EX, B): the edge tokens (i, j) of graph blockIdx.y in tiles of 16;
+// wave slot blockIdx.x * 4 + w takes tiles slot, slot + 4 EX, ... . Weights,
+// biases and layer-norm parameters are staged in LDS once per block; the
+// next tile's E' and mask bytes are loaded (raw, into the other of two
+// register sets) while the current tile is computed. E2 is written over E'
+// in place (each lane reads its token's row before writing it). Also the
+// block's sums of E2 over its real pairs (part_e).
 template <typename T, int DE>
 __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
-  constexpr int FE = 2 * DE;
-  __shared__ float sum_s[DE];
+  constexpr int FE = 2 * DE, EPC = 16 / (int)sizeof(T);
+  __shared__ __align__(16) T w1_s[FE][DE + EPC];
+  __shared__ __align__(16) T w2_s[DE][FE + EPC];
+  __shared__ float pv_s[6][FE];  // b_e1, b_e2, ln_e1 g / b, ln_e2 g / b
+  __shared__ float sum_s[kWaves][DE];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, n = k.n;
-  for (int f = tid; f < DE; f += kThreads) sum_s[f] = 0.f;
   auto par = [&](int q) { return static_cast<const T*>(k.p[q]); };
-  // both weights stay in registers for all tiles of the wave
-  Frag<T, Steps<DE>::Q> w1[FE / 16][Steps<DE>::NS];
-  Frag<T, Steps<FE>::Q> w2[DE / 16][Steps<FE>::NS];
+  {
+    Pieces<T, FE, DE> p1;
+    Pieces<T, DE, FE> p2;
+    p1.load(par(kBW_e1), tid);
+    p2.load(par(kBW_e2), tid);
+    const int pq[6] = {kBb_e1, kBb_e2, kBln_e1_g, kBln_e1_b, kBln_e2_g, kBln_e2_b};
+    for (int q = tid; q < 6 * FE; q += kThreads) {
+      const int v = q / FE, c = q % FE;
+      if (v == 0 || c < DE) pv_s[v][c] = Num<T>::ld(par(pq[v]) + c);
+    }
+    p1.store(w1_s, tid);
+    p2.store(w2_s, tid);
+  }
+  __syncthreads();
+  T* Eio = static_cast<T*>(k.E_io);
+  const int ntok = n * n, ntile = (ntok + 15) / 16;
+  constexpr int DW = 4 * (int)sizeof(T) / 4;
+  struct Raw {
+    uint32_t e[DE / 16][DW];  // groups 16 t + 4 lg .. + 3 of the token's row
+    uint8_t mi, mj;
+  };
+  auto tok = [&](int tile, int& i, int& j) {
+    const int tk = 16 * tile + li, tc = tk < ntok ? tk : 0;
+    i = tc / n;
+    j = tc % n;
+    return tk < ntok;
+  };
+  auto load = [&](int tile, Raw& r) {
+    int i, j;
+    tok(tile < ntile ? tile : 0, i, j);
+    const T* rowp = Eio + (((size_t)b * n + i) * n + j) * DE;
 #pragma unroll
-  for (int to = 0; to < FE / 16; ++to)
+    for (int t = 0; t < DE / 16; ++t) ld4w<T>(r.e[t], rowp + 16 * t + 4 * lg);
+    r.mi = k.mask[(size_t)b * n + i];
+    r.mj = k.mask[(size_t)b * n + j];
+  };
+  // layer norm of this lane's DE / 4 features of its token (gain row gq, shift row bq of pv_s)
+  auto lnv = [&](float* v, int gq, int bq) {
+    float sm = 0.f;
 #pragma unroll
-    for (int s = 0; s < Steps<DE>::NS; ++s) w1[to][s] = w_frag<T, DE>(par(kBW_e1), 16 * to + li, s, lg);
+    for (int q = 0; q < DE / 4; ++q) sm += v[q];
+    const float mean = lg_sum(sm) * (1.f / DE);
+    float sq = 0.f;
 #pragma unroll
-  for (int to = 0; to < DE / 16; ++to)
+    for (int q = 0; q < DE / 4; ++q) {
+      v[q] -= mean;
+      sq += v[q] * v[q];
+    }
+    const float inv = 1.f / sqrtf(lg_sum(sq) * (1.f / DE) + kLnEps);
 #pragma unroll
-    for (int s = 0; s < Steps<FE>::NS; ++s) w2[to][s] = w_frag<T, FE>(par(kBW_e2), 16 * to + li, s, lg);
+    for (int t = 0; t < DE / 16; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * t + 4 * lg + r;
+        v[4 * t + r] = v[4 * t + r] * inv * pv_s[gq][c] + pv_s[bq][c];
+      }
+  };
   float esum[DE / 4];
 #pragma unroll
   for (int q = 0; q < DE / 4; ++q) esum[q] = 0.f;
-  T* Eio = static_cast<T*>(k.E_io);
-  const int ntok = n * n, ntile = (ntok + 15) / 16;
-  for (int tile = blockIdx.x * kWaves + w; tile < ntile; tile += gridDim.x * kWaves) {
-    const int tk = 16 * tile + li;
-    const bool valid = tk < ntok;
-    const int tc = valid ? tk : 0, i = tc / n, j = tc % n;
-    const bool real = valid && k.mask[(size_t)b * n + i] != 0 && k.mask[(size_t)b * n + j] != 0;
-    T* rowp = Eio + (((size_t)b * n + i) * n + j) * DE;
-    float e1[DE / 4], z[DE / 4], h[FE / 4];
+  auto step = [&](int tile, const Raw& cur, Raw& nxt) {
+    load(tile + gridDim.x * kWaves, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay ahead of this tile's work
+    int i, j;
+    const bool valid = tok(tile, i, j);
+    const bool real = valid && cur.mi != 0 && cur.mj != 0;
+    float e1[DE / 4], h[FE / 4], z[DE / 4];
 #pragma unroll
-    for (int t = 0; t < DE / 16; ++t) ld4f<T>(e1 + 4 * t, rowp + 16 * t + 4 * lg);
-    row_ln<T, DE>(e1, par(kBln_e1_g), par(kBln_e1_b), lg);
+    for (int t = 0; t < DE / 16; ++t) {
+      if constexpr (sizeof(T) == 2) {
+        e1[4 * t] = __uint_as_float(cur.e[t][0] << 16); e1[4 * t + 1] = __uint_as_float(cur.e[t][0] & 0xffff0000u);
+        e1[4 * t + 2] = __uint_as_float(cur.e[t][1] << 16); e1[4 * t + 3] = __uint_as_float(cur.e[t][1] & 0xffff0000u);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e1[4 * t + r] = __uint_as_float(cur.e[t][r]);
+      }
+    }
+    lnv(e1, 2, 3);
     {
       RowIn<T, DE> in;
       in.set(e1);
@@ -242,11 +359,9 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
       for (int to = 0; to < FE / 16; ++to) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < Steps<DE>::NS; ++s) acc = mma(acc, w1[to][s], in.f[s]);
-        float bv[4];
-        ld4f<T>(bv, par(kBb_e1) + 16 * to + 4 * lg);
+        for (int s2 = 0; s2 < Steps<DE>::NS; ++s2) acc = mma(acc, frag_at<T, DE>(&w1_s[16 * to + li][0], s2, lg), in.f[s2]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[4 * to + r] = fmaxf(acc[r] + bv[r], 0.f);
+        for (int r = 0; r < 4; ++r) h[4 * to + r] = fmaxf(acc[r] + pv_s[0][16 * to + 4 * lg + r], 0.f);
       }
     }
     {
@@ -256,46 +371,79 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
       for (int to = 0; to < DE / 16; ++to) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < Steps<FE>::NS; ++s) acc = mma(acc, w2[to][s], in.f[s]);
-        float bv[4];
-        ld4f<T>(bv, par(kBb_e2) + 16 * to + 4 * lg);
+        for (int s2 = 0; s2 < Steps<FE>::NS; ++s2) acc = mma(acc, frag_at<T, FE>(&w2_s[16 * to + li][0], s2, lg), in.f[s2]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[4 * to + r] = acc[r] + bv[r] + e1[4 * to + r];
+        for (int r = 0; r < 4; ++r) z[4 * to + r] = acc[r] + pv_s[1][16 * to + 4 * lg + r] + e1[4 * to + r];
       }
     }
-    row_ln<T, DE>(z, par(kBln_e2_g), par(kBln_e2_b), lg);
+    lnv(z, 4, 5);
 #pragma unroll
     for (int q = 0; q < DE / 4; ++q) {
       z[q] = real ? z[q] : 0.f;
       esum[q] += z[q];
     }
     if (valid) {
+      T* rowp = Eio + (((size_t)b * n + i) * n + j) * DE;
 #pragma unroll
       for (int t = 0; t < DE / 16; ++t) st4f<T>(rowp + 16 * t + 4 * lg, z + 4 * t);
     }
+  };
+  const int stride = gridDim.x * kWaves;
+  Raw r0, r1;
+  int tile = blockIdx.x * kWaves + w;
+  if (tile < ntile) load(tile, r0);
+  for (; tile < ntile; tile += 2 * stride) {
+    step(tile, r0, r1);
+    if (tile + stride >= ntile) break;
+    step(tile + stride, r1, r0);
+  }
+  // sums over the 16 tokens (lanes li), then over the waves
+#pragma unroll
+  for (int q = 0; q < DE / 4; ++q) {
+    float v = esum[q];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    esum[q] = v;
+  }
+  if (li == 0) {
+#pragma unroll
+    for (int t = 0; t < DE / 16; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum_s[w][16 * t + 4 * lg + r] = esum[4 * t + r];
   }
   __syncthreads();
-#pragma unroll
-  for (int t = 0; t < DE / 16; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) atomicAdd(&sum_s[16 * t + 4 * lg + r], esum[4 * t + r]);
-  __syncthreads();
   float* part = k.part_e + ((size_t)b * gridDim.x + blockIdx.x) * DE;
-  for (int f = tid; f < DE; f += kThreads) part[f] = sum_s[f];
+  for (int f = tid; f < DE; f += kThreads) part[f] = sum_s[0][f] + sum_s[1][f] + sum_s[2][f] + sum_s[3][f];
 }
 
 // ------------------------------------------------------------------ y
 
+// Quarter qt of sum over c < LEN of W[c] v[c]: all LEN / 4 weights are loaded
+// before the first multiply-add.
+template <typename T, int LEN>
+__device__ __forceinline__ float dot_quarter(const T* Wrow, const float* v, int qt) {
+  float wv[LEN / 4];
+#pragma unroll
+  for (int u = 0; u < LEN / 4; ++u) wv[u] = Num<T>::ld(Wrow + qt + 4 * u);
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < LEN / 4; ++u) s += wv[u] * v[qt + 4 * u];
+  return s;
+}
+
 // One block per graph: the means from the partial sums, then the y path in
-// float32 (thread per output feature, loops over the inputs).
+// float32. Each output feature is computed by 4 threads over interleaved
+// quarters of its inputs (adjacent threads read adjacent weights), combined
+// with two shuffles.
 template <typename T, int D, int DE>
 __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
   __shared__ float xbar[D], ebar[DE];
-  __shared__ float yv[kMaxBlockDy], y1[kMaxBlockDy], hy[kMaxBlockDy], red[2];
+  __shared__ float yv[kMaxBlockDy], y1[kMaxBlockDy], hy[kMaxBlockDy], red4[2][kWaves];
   __shared__ int cnt;
-  const int tid = threadIdx.x, b = blockIdx.x, n = k.n, dy = k.dy;
+  const int tid = threadIdx.x, b = blockIdx.x, n = k.n, dy = k.dy, qt = tid & 3;
   auto par = [&](int q) { return static_cast<const T*>(k.p[q]); };
-  auto P = [&](int q, size_t idx) { return Num<T>::ld(par(q) + idx); };
   if (tid == 0) cnt = 0;
   __syncthreads();
   int c0 = 0;
@@ -306,49 +454,78 @@ __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
   const float nr = (float)cnt;
   for (int f = tid; f < D; f += kThreads) {
     float s = 0.f;
+#pragma unroll 8
     for (int q = 0; q < k.nxb; ++q) s += k.part_x[((size_t)b * k.nxb + q) * D + f];
     xbar[f] = s / fmaxf(nr, 1.f);
   }
   for (int f = tid; f < DE; f += kThreads) {
     float s = 0.f;
+#pragma unroll 8
     for (int q = 0; q < k.exb; ++q) s += k.part_e[((size_t)b * k.exb + q) * DE + f];
     ebar[f] = s / fmaxf(nr * nr, 1.f);
   }
   __syncthreads();
-  // layer norm of v[0 .. dy) in place (gain / shift parameters gq, bq)
-  auto block_ln = [&](float* v, int gq, int bq) {
-    if (tid == 0) {
-      float s = 0.f;
-      for (int c = 0; c < dy; ++c) s += v[c];
-      const float mean = s / dy;
-      float q = 0.f;
-      for (int c = 0; c < dy; ++c) q += (v[c] - mean) * (v[c] - mean);
-      red[0] = mean;
-      red[1] = 1.f / sqrtf(q / dy + kLnEps);
+  // sum over c < len of W[o][c] v[c], quarter qt of the inputs, 16 weights
+  // loaded before they are used; all 4 threads get the total
+  auto dot = [&](const T* Wrow, const float* v, int len) {
+    float s = 0.f;
+    for (int c0 = qt; c0 < len; c0 += 64) {
+      float wv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = c0 + 4 * u;
+        const float x = Num<T>::ld(Wrow + (c < len ? c : 0));
+        wv[u] = c < len ? x : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += wv[u] * v[c0 + 4 * u < len ? c0 + 4 * u : 0];
     }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    return s;
+  };
+  // sum of x over all threads of the block (every thread gets it)
+  auto block_sum = [&](float x, int slot) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+    if ((tid & 63) == 0) red4[slot][tid >> 6] = x;
     __syncthreads();
-    for (int c = tid; c < dy; c += kThreads) v[c] = (v[c] - red[0]) * red[1] * P(gq, c) + P(bq, c);
+    return red4[slot][0] + red4[slot][1] + red4[slot][2] + red4[slot][3];
+  };
+  auto block_ln = [&](float* v, int gq, int bq) {
+    float s = 0.f;
+    for (int c = tid; c < dy; c += kThreads) s += v[c];
+    const float mean = block_sum(s, 0) / dy;
+    float q = 0.f;
+    for (int c = tid; c < dy; c += kThreads) q += (v[c] - mean) * (v[c] - mean);
+    const float inv = 1.f / sqrtf(block_sum(q, 1) / dy + kLnEps);
+    for (int c = tid; c < dy; c += kThreads)
+      v[c] = (v[c] - mean) * inv * Num<T>::ld(par(gq) + c) + Num<T>::ld(par(bq) + c);
     __syncthreads();
   };
-  for (int o = tid; o < dy; o += kThreads) {
-    float s = yv[o] + P(kBb_yo, o);
-    for (int c = 0; c < dy; ++c) s += P(kBW_yy, (size_t)o * dy + c) * yv[c];
-    for (int f = 0; f < D; ++f) s += P(kBW_yx, (size_t)o * D + f) * xbar[f];
-    for (int f = 0; f < DE; ++f) s += P(kBW_ye, (size_t)o * DE + f) * ebar[f];
-    y1[o] = s;
+  // every thread runs the same number of rounds (the shuffles need all lanes)
+  const int rounds = (dy + kThreads / 4 - 1) / (kThreads / 4);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int o = rd * (kThreads / 4) + tid / 4, oc = o < dy ? o : 0;
+    float sx = dot_quarter<T, D>(par(kBW_yx) + (size_t)oc * D, xbar, qt) +
+               dot_quarter<T, DE>(par(kBW_ye) + (size_t)oc * DE, ebar, qt);
+    sx += __shfl_xor(sx, 1);
+    sx += __shfl_xor(sx, 2);
+    const float s = sx + dot(par(kBW_yy) + (size_t)oc * dy, yv, dy);
+    if (o < dy && qt == 0) y1[o] = s + yv[o] + Num<T>::ld(par(kBb_yo) + o);
   }
   __syncthreads();
   block_ln(y1, kBln_y1_g, kBln_y1_b);
-  for (int o = tid; o < dy; o += kThreads) {
-    float s = P(kBb_y1, o);
-    for (int c = 0; c < dy; ++c) s += P(kBW_y1, (size_t)o * dy + c) * y1[c];
-    hy[o] = fmaxf(s, 0.f);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int o = rd * (kThreads / 4) + tid / 4, oc = o < dy ? o : 0;
+    const float s = dot(par(kBW_y1) + (size_t)oc * dy, y1, dy);
+    if (o < dy && qt == 0) hy[o] = fmaxf(s + Num<T>::ld(par(kBb_y1) + o), 0.f);
   }
   __syncthreads();
-  for (int o = tid; o < dy; o += kThreads) {
-    float s = y1[o] + P(kBb_y2, o);
-    for (int c = 0; c < dy; ++c) s += P(kBW_y2, (size_t)o * dy + c) * hy[c];
-    yv[o] = s;  // y is no longer needed: y2 takes its place
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int o = rd * (kThreads / 4) + tid / 4, oc = o < dy ? o : 0;
+    const float s = dot(par(kBW_y2) + (size_t)oc * dy, hy, dy);
+    if (o < dy && qt == 0) yv[o] = y1[o] + s + Num<T>::ld(par(kBb_y2) + o);  // y is no longer needed
   }
   __syncthreads();
   block_ln(yv, kBln_y2_g, kBln_y2_b);
