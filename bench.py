@@ -27,7 +27,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 INFINITY_CACHE_BYTES = 256 << 20
-KERNEL_SOURCE = os.path.join(ROOT, "edge_aware_graph_amd", "csrc", "ea_kernels.hip")
+# the layer's kernels and the device headers they are built from
+KERNEL_SOURCES = [os.path.join(ROOT, "edge_aware_graph_amd", "csrc", f)
+                  for f in ("ea_kernels.hip", "ea_device.h", "ea_internal.h")]
 # ablation variants (the EA_VARIANT_* desc flags)
 VARIANT_FLAGS = {"none": 0, "light_edge": 0x2, "no_score_mod": 0x4, "unnormalized": 0x8}
 
@@ -263,8 +265,12 @@ def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of the layer kernels' sources, concatenated."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel: str, workload: str):
