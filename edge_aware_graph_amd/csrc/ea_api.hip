@@ -224,8 +224,8 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->bws_bytes = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
   {
-    // block: 16 nodes per node block; edge blocks of 4 waves with at least 4
-    // tiles of 16 tokens per wave, at most 256 per graph
+    // block: 16 nodes per node block; edge blocks of 4 waves with at least
+    // 4 tiles of 16 tokens per wave, at most 256 per graph
     const size_t tiles = ((size_t)d.n * d.n + 15) / 16;
     c->blk_nxb = (d.n + 15) / 16;
     c->blk_exb = (int)std::min<size_t>(256, std::max<size_t>(1, (tiles + 15) / 16));
@@ -378,10 +378,8 @@ ea_status edge_attn_block(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
   g_err[0] = 0;
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
   if (c->d.flags & kVariants) return fail(EA_E_UNSUPPORTED, "the block is built for the full layer (no variant flag)");
-  const bool shape_ok = (c->d.d == 64 && c->d.de == 16) || (c->d.d == 256 && c->d.de == 64 && c->d.dtype == EA_BF16);
-  if (!shape_ok)
-    return fail(EA_E_UNSUPPORTED, "the block is built for (d, de) = (64, 16) and, in bfloat16, (256, 64)");
-  if (c->d.dy > ea::kMaxBlockDy) return fail(EA_E_UNSUPPORTED, "the block is built for dy <= %d", ea::kMaxBlockDy);
+  if (!ea::block_supported(c->d.dtype == EA_BF16 ? 1 : 0, c->d.d, c->d.de, c->d.dy))
+    return fail(EA_E_UNSUPPORTED, "the block is built for (d, de, dy) = (64, 16, 16) and, in bfloat16, (256, 64, 64)");
   if (!bp) return fail(EA_E_NULLPTR, "block parameters are NULL");
   const void* const* bpp = reinterpret_cast<const void* const*>(bp);
   static_assert(sizeof(ea_block_params) == ea::kBlockParams * sizeof(void*), "block parameter list");

@@ -28,6 +28,9 @@ namespace ea {
 namespace {
 
 constexpr float kLnEps = 1e-5f;
+// Waves per block of the edge kernel: large blocks stage the weights once
+// for many token tiles.
+constexpr int kEdgeWaves = 4;
 
 // Four consecutive elements (one row-layout group) as floats.
 template <typename T>
@@ -94,14 +97,14 @@ __device__ __forceinline__ Frag<T, Steps<K>::Q> frag_at(const T* row, int s, int
 
 // 16-byte pieces of a [ROWS, COLS] matrix: thread tid takes pieces tid,
 // tid + 256, ...; piece q is row q / (COLS / EPC), columns EPC (q % (COLS / EPC)) ..
-template <typename T, int ROWS, int COLS>
+template <typename T, int ROWS, int COLS, int NT = kThreads>
 struct Pieces {
-  static constexpr int EPC = 16 / (int)sizeof(T), N = ROWS * COLS / EPC, PER = (N + kThreads - 1) / kThreads;
+  static constexpr int EPC = 16 / (int)sizeof(T), N = ROWS * COLS / EPC, PER = (N + NT - 1) / NT;
   u32x4 v[PER];
   __device__ __forceinline__ void load(const T* src, int tid) {  // src: row-major, row stride COLS
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int q = tid + e * kThreads, qc = q < N ? q : 0;
+      const int q = tid + e * NT, qc = q < N ? q : 0;
       v[e] = *reinterpret_cast<const u32x4*>(src + (size_t)(qc / (COLS / EPC)) * COLS + EPC * (qc % (COLS / EPC)));
     }
   }
@@ -109,8 +112,8 @@ struct Pieces {
   __device__ __forceinline__ void store(T (*dst)[LD], int tid) const {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int q = tid + e * kThreads;
-      if (PER * kThreads == N || q < N) *reinterpret_cast<u32x4*>(&dst[q / (COLS / EPC)][EPC * (q % (COLS / EPC))]) = v[e];
+      const int q = tid + e * NT;
+      if (PER * NT == N || q < N) *reinterpret_cast<u32x4*>(&dst[q / (COLS / EPC)][EPC * (q % (COLS / EPC))]) = v[e];
     }
   }
 };
@@ -238,14 +241,7 @@ __global__ __launch_bounds__(kThreads) void blk_node_kernel(BlockArgs k) {
   }
   // sums over the 16 rows (lanes li of a lane group) of the block's real nodes
 #pragma unroll
-  for (int q = 0; q < 4 * TPW; ++q) {
-    float v = z[q];
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    z[q] = v;
-  }
+  for (int q = 0; q < 4 * TPW; ++q) z[q] = row16_sum(z[q]);
   if (li == 0) {
     float* part = k.part_x + ((size_t)b * gridDim.x + blockIdx.x) * D;
 #pragma unroll
@@ -257,37 +253,24 @@ __global__ __launch_bounds__(kThreads) void blk_node_kernel(BlockArgs k) {
 
 // ------------------------------------------------------------------ edges
 
-// Grid (EX, B): the edge tokens (i, j) of graph blockIdx.y in tiles of 16;
-// wave slot blockIdx.x * 4 + w takes tiles slot, slot + 4 EX, ... . Weights,
+// Grid (EX, B), kEdgeWaves waves per block: the edge tokens (i, j) of graph
+// blockIdx.y in tiles of 16; wave slot blockIdx.x * kEdgeWaves + w takes
+// tiles slot, slot + kEdgeWaves EX, ... . Weights,
 // biases and layer-norm parameters are staged in LDS once per block; the
 // next tile's E' and mask bytes are loaded (raw, into the other of two
 // register sets) while the current tile is computed. E2 is written over E'
 // in place (each lane reads its token's row before writing it). Also the
 // block's sums of E2 over its real pairs (part_e).
 template <typename T, int DE>
-__global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
-  constexpr int FE = 2 * DE, EPC = 16 / (int)sizeof(T);
+__global__ __launch_bounds__(kEdgeWaves * 64) void blk_edge_kernel(BlockArgs k) {
+  constexpr int FE = 2 * DE, EPC = 16 / (int)sizeof(T), NT = kEdgeWaves * 64;
   __shared__ __align__(16) T w1_s[FE][DE + EPC];
   __shared__ __align__(16) T w2_s[DE][FE + EPC];
   __shared__ float pv_s[6][FE];  // b_e1, b_e2, ln_e1 g / b, ln_e2 g / b
-  __shared__ float sum_s[kWaves][DE];
+  __shared__ float sum_s[kEdgeWaves][DE];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, n = k.n;
   auto par = [&](int q) { return static_cast<const T*>(k.p[q]); };
-  {
-    Pieces<T, FE, DE> p1;
-    Pieces<T, DE, FE> p2;
-    p1.load(par(kBW_e1), tid);
-    p2.load(par(kBW_e2), tid);
-    const int pq[6] = {kBb_e1, kBb_e2, kBln_e1_g, kBln_e1_b, kBln_e2_g, kBln_e2_b};
-    for (int q = tid; q < 6 * FE; q += kThreads) {
-      const int v = q / FE, c = q % FE;
-      if (v == 0 || c < DE) pv_s[v][c] = Num<T>::ld(par(pq[v]) + c);
-    }
-    p1.store(w1_s, tid);
-    p2.store(w2_s, tid);
-  }
-  __syncthreads();
   T* Eio = static_cast<T*>(k.E_io);
   const int ntok = n * n, ntile = (ntok + 15) / 16;
   constexpr int DW = 4 * (int)sizeof(T) / 4;
@@ -310,6 +293,24 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
     r.mi = k.mask[(size_t)b * n + i];
     r.mj = k.mask[(size_t)b * n + j];
   };
+  const int stride = gridDim.x * kEdgeWaves;
+  Raw r0, r1;
+  int tile = blockIdx.x * kEdgeWaves + w;
+  if (tile < ntile) load(tile, r0);  // the first tile is in flight during the staging
+  {
+    Pieces<T, FE, DE, NT> p1;
+    Pieces<T, DE, FE, NT> p2;
+    p1.load(par(kBW_e1), tid);
+    p2.load(par(kBW_e2), tid);
+    const int pq[6] = {kBb_e1, kBb_e2, kBln_e1_g, kBln_e1_b, kBln_e2_g, kBln_e2_b};
+    for (int q = tid; q < 6 * FE; q += NT) {
+      const int v = q / FE, c = q % FE;
+      if (v == 0 || c < DE) pv_s[v][c] = Num<T>::ld(par(pq[v]) + c);
+    }
+    p1.store(w1_s, tid);
+    p2.store(w2_s, tid);
+  }
+  __syncthreads();
   // layer norm of this lane's DE / 4 features of its token (gain row gq, shift row bq of pv_s)
   auto lnv = [&](float* v, int gq, int bq) {
     float sm = 0.f;
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
 #pragma unroll
   for (int q = 0; q < DE / 4; ++q) esum[q] = 0.f;
   auto step = [&](int tile, const Raw& cur, Raw& nxt) {
-    load(tile + gridDim.x * kWaves, nxt);
+    load(tile + gridDim.x * kEdgeWaves, nxt);
     __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay ahead of this tile's work
     int i, j;
     const bool valid = tok(tile, i, j);
@@ -388,10 +389,6 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
       for (int t = 0; t < DE / 16; ++t) st4f<T>(rowp + 16 * t + 4 * lg, z + 4 * t);
     }
   };
-  const int stride = gridDim.x * kWaves;
-  Raw r0, r1;
-  int tile = blockIdx.x * kWaves + w;
-  if (tile < ntile) load(tile, r0);
   for (; tile < ntile; tile += 2 * stride) {
     step(tile, r0, r1);
     if (tile + stride >= ntile) break;
@@ -399,14 +396,7 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
   }
   // sums over the 16 tokens (lanes li), then over the waves
 #pragma unroll
-  for (int q = 0; q < DE / 4; ++q) {
-    float v = esum[q];
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    esum[q] = v;
-  }
+  for (int q = 0; q < DE / 4; ++q) esum[q] = row16_sum(esum[q]);
   if (li == 0) {
 #pragma unroll
     for (int t = 0; t < DE / 16; ++t)
@@ -415,41 +405,74 @@ __global__ __launch_bounds__(kThreads) void blk_edge_kernel(BlockArgs k) {
   }
   __syncthreads();
   float* part = k.part_e + ((size_t)b * gridDim.x + blockIdx.x) * DE;
-  for (int f = tid; f < DE; f += kThreads) part[f] = sum_s[0][f] + sum_s[1][f] + sum_s[2][f] + sum_s[3][f];
+  for (int f = tid; f < DE; f += NT) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < kEdgeWaves; ++q) t += sum_s[q][f];
+    part[f] = t;
+  }
 }
 
 // ------------------------------------------------------------------ y
 
-// Quarter qt of sum over c < LEN of W[c] v[c]: all LEN / 4 weights are loaded
-// before the first multiply-add.
+// Weights of one output row, lane l taking inputs l, l + 64, ... (raw words;
+// lanes past LEN load element 0 and later count as 0).
 template <typename T, int LEN>
-__device__ __forceinline__ float dot_quarter(const T* Wrow, const float* v, int qt) {
-  float wv[LEN / 4];
+struct RowW {
+  static constexpr int U = (LEN + 63) / 64;
+  uint32_t w[U];
+  __device__ __forceinline__ void load(const T* row, int l) {
 #pragma unroll
-  for (int u = 0; u < LEN / 4; ++u) wv[u] = Num<T>::ld(Wrow + qt + 4 * u);
-  float s = 0.f;
+    for (int u = 0; u < U; ++u) w[u] = Num<T>::ldraw(row + (l + 64 * u < LEN ? l + 64 * u : 0));
+  }
+  // this lane's part of the row times v (v in LDS)
+  __device__ __forceinline__ float dot(const float* v, int l) const {
+    float s = 0.f;
 #pragma unroll
-  for (int u = 0; u < LEN / 4; ++u) s += wv[u] * v[qt + 4 * u];
-  return s;
-}
+    for (int u = 0; u < U; ++u)
+      if (LEN % 64 == 0 || l + 64 * u < LEN) s += Num<T>::fromraw(w[u]) * v[l + 64 * u];
+    return s;
+  }
+};
+
 
 // One block per graph: the means from the partial sums, then the y path in
-// float32. Each output feature is computed by 4 threads over interleaved
-// quarters of its inputs (adjacent threads read adjacent weights), combined
-// with two shuffles.
-template <typename T, int D, int DE>
+// float32. Wave w computes outputs o = w, w + 4, ...; its lanes read
+// consecutive weights of the output's row (one cache line per load) and sum
+// over the wave. Every weight and parameter is loaded at the start, so the
+// chain of products and norms that follows waits on no memory.
+template <typename T, int D, int DE, int DY>
 __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
+  constexpr int OPW = DY / kWaves;  // outputs per wave
+  static_assert(DY % kWaves == 0 && DY <= kThreads, "outputs over the waves");
   __shared__ float xbar[D], ebar[DE];
-  __shared__ float yv[kMaxBlockDy], y1[kMaxBlockDy], hy[kMaxBlockDy], red4[2][kWaves];
+  __shared__ float yv[DY], y1[DY], hy[DY], red4[2][kWaves];
   __shared__ int cnt;
-  const int tid = threadIdx.x, b = blockIdx.x, n = k.n, dy = k.dy, qt = tid & 3;
+  const int tid = threadIdx.x, b = blockIdx.x, n = k.n, w = tid >> 6, l = tid & 63;
   auto par = [&](int q) { return static_cast<const T*>(k.p[q]); };
+  RowW<T, D> wyx[OPW];
+  RowW<T, DE> wye[OPW];
+  RowW<T, DY> wyy[OPW], wy1[OPW], wy2[OPW];
+#pragma unroll
+  for (int m = 0; m < OPW; ++m) {
+    const size_t o = w + kWaves * m;
+    wyx[m].load(par(kBW_yx) + o * D, l);
+    wye[m].load(par(kBW_ye) + o * DE, l);
+    wyy[m].load(par(kBW_yy) + o * DY, l);
+    wy1[m].load(par(kBW_y1) + o * DY, l);
+    wy2[m].load(par(kBW_y2) + o * DY, l);
+  }
+  const int cc = tid < DY ? tid : 0;  // feature of the norm and bias steps
+  const uint32_t pb[3] = {Num<T>::ldraw(par(kBb_yo) + cc), Num<T>::ldraw(par(kBb_y1) + cc),
+                          Num<T>::ldraw(par(kBb_y2) + cc)};
+  const uint32_t pl[4] = {Num<T>::ldraw(par(kBln_y1_g) + cc), Num<T>::ldraw(par(kBln_y1_b) + cc),
+                          Num<T>::ldraw(par(kBln_y2_g) + cc), Num<T>::ldraw(par(kBln_y2_b) + cc)};
   if (tid == 0) cnt = 0;
   __syncthreads();
   int c0 = 0;
   for (int i = tid; i < n; i += kThreads) c0 += k.mask[(size_t)b * n + i] != 0;
   atomicAdd(&cnt, c0);
-  for (int c = tid; c < dy; c += kThreads) yv[c] = Num<T>::ld(static_cast<const T*>(k.y) + (size_t)b * dy + c);
+  if (tid < DY) yv[tid] = Num<T>::ld(static_cast<const T*>(k.y) + (size_t)b * DY + tid);
   __syncthreads();
   const float nr = (float)cnt;
   for (int f = tid; f < D; f += kThreads) {
@@ -465,87 +488,68 @@ __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
     ebar[f] = s / fmaxf(nr * nr, 1.f);
   }
   __syncthreads();
-  // sum over c < len of W[o][c] v[c], quarter qt of the inputs, 16 weights
-  // loaded before they are used; all 4 threads get the total
-  auto dot = [&](const T* Wrow, const float* v, int len) {
-    float s = 0.f;
-    for (int c0 = qt; c0 < len; c0 += 64) {
-      float wv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = c0 + 4 * u;
-        const float x = Num<T>::ld(Wrow + (c < len ? c : 0));
-        wv[u] = c < len ? x : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) s += wv[u] * v[c0 + 4 * u < len ? c0 + 4 * u : 0];
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    return s;
-  };
   // sum of x over all threads of the block (every thread gets it)
   auto block_sum = [&](float x, int slot) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-    if ((tid & 63) == 0) red4[slot][tid >> 6] = x;
+    x = wave64_sum(x);
+    if (l == 0) red4[slot][w] = x;
     __syncthreads();
     return red4[slot][0] + red4[slot][1] + red4[slot][2] + red4[slot][3];
   };
-  auto block_ln = [&](float* v, int gq, int bq) {
-    float s = 0.f;
-    for (int c = tid; c < dy; c += kThreads) s += v[c];
-    const float mean = block_sum(s, 0) / dy;
-    float q = 0.f;
-    for (int c = tid; c < dy; c += kThreads) q += (v[c] - mean) * (v[c] - mean);
-    const float inv = 1.f / sqrtf(block_sum(q, 1) / dy + kLnEps);
-    for (int c = tid; c < dy; c += kThreads)
-      v[c] = (v[c] - mean) * inv * Num<T>::ld(par(gq) + c) + Num<T>::ld(par(bq) + c);
+  auto block_ln = [&](float* v, uint32_t g, uint32_t bb) {
+    const float x = tid < DY ? v[cc] : 0.f;
+    const float mean = block_sum(x, 0) * (1.f / DY);
+    const float dv = tid < DY ? x - mean : 0.f;
+    const float inv = 1.f / sqrtf(block_sum(dv * dv, 1) * (1.f / DY) + kLnEps);
+    if (tid < DY) v[tid] = dv * inv * Num<T>::fromraw(g) + Num<T>::fromraw(bb);
     __syncthreads();
   };
-  // every thread runs the same number of rounds (the shuffles need all lanes)
-  const int rounds = (dy + kThreads / 4 - 1) / (kThreads / 4);
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int o = rd * (kThreads / 4) + tid / 4, oc = o < dy ? o : 0;
-    float sx = dot_quarter<T, D>(par(kBW_yx) + (size_t)oc * D, xbar, qt) +
-               dot_quarter<T, DE>(par(kBW_ye) + (size_t)oc * DE, ebar, qt);
-    sx += __shfl_xor(sx, 1);
-    sx += __shfl_xor(sx, 2);
-    const float s = sx + dot(par(kBW_yy) + (size_t)oc * dy, yv, dy);
-    if (o < dy && qt == 0) y1[o] = s + yv[o] + Num<T>::ld(par(kBb_yo) + o);
+#pragma unroll
+  for (int m = 0; m < OPW; ++m) {
+    const float s = wave64_sum(wyx[m].dot(xbar, l) + wye[m].dot(ebar, l) + wyy[m].dot(yv, l));
+    if (l == 0) y1[w + kWaves * m] = s;
   }
   __syncthreads();
-  block_ln(y1, kBln_y1_g, kBln_y1_b);
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int o = rd * (kThreads / 4) + tid / 4, oc = o < dy ? o : 0;
-    const float s = dot(par(kBW_y1) + (size_t)oc * dy, y1, dy);
-    if (o < dy && qt == 0) hy[o] = fmaxf(s + Num<T>::ld(par(kBb_y1) + o), 0.f);
+  if (tid < DY) y1[tid] += yv[tid] + Num<T>::fromraw(pb[0]);
+  __syncthreads();
+  block_ln(y1, pl[0], pl[1]);
+#pragma unroll
+  for (int m = 0; m < OPW; ++m) {
+    const float s = wave64_sum(wy1[m].dot(y1, l));
+    if (l == 0) hy[w + kWaves * m] = s;
   }
   __syncthreads();
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int o = rd * (kThreads / 4) + tid / 4, oc = o < dy ? o : 0;
-    const float s = dot(par(kBW_y2) + (size_t)oc * dy, hy, dy);
-    if (o < dy && qt == 0) yv[o] = y1[o] + s + Num<T>::ld(par(kBb_y2) + o);  // y is no longer needed
+  if (tid < DY) hy[tid] = fmaxf(hy[tid] + Num<T>::fromraw(pb[1]), 0.f);
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < OPW; ++m) {
+    const float s = wave64_sum(wy2[m].dot(hy, l));
+    if (l == 0) yv[w + kWaves * m] = s;  // y is no longer needed
   }
   __syncthreads();
-  block_ln(yv, kBln_y2_g, kBln_y2_b);
-  for (int o = tid; o < dy; o += kThreads) Num<T>::st(static_cast<T*>(k.y_out) + (size_t)b * dy + o, yv[o]);
+  if (tid < DY) yv[tid] += y1[tid] + Num<T>::fromraw(pb[2]);
+  __syncthreads();
+  block_ln(yv, pl[2], pl[3]);
+  if (tid < DY) Num<T>::st(static_cast<T*>(k.y_out) + (size_t)b * DY + tid, yv[tid]);
 }
 
-template <typename T, int D, int DE>
+template <typename T, int D, int DE, int DY>
 hipError_t block_shape(const BlockArgs& k, hipStream_t s) {
   hipLaunchKernelGGL((blk_node_kernel<T, D>), dim3(k.nxb, k.B), dim3(kThreads), 0, s, k);
-  hipLaunchKernelGGL((blk_edge_kernel<T, DE>), dim3(k.exb, k.B), dim3(kThreads), 0, s, k);
-  hipLaunchKernelGGL((blk_y_kernel<T, D, DE>), dim3(k.B), dim3(kThreads), 0, s, k);
+  hipLaunchKernelGGL((blk_edge_kernel<T, DE>), dim3(k.exb, k.B), dim3(kEdgeWaves * 64), 0, s, k);
+  hipLaunchKernelGGL((blk_y_kernel<T, D, DE, DY>), dim3(k.B), dim3(kThreads), 0, s, k);
   return hipGetLastError();
 }
 
 }  // namespace
 
+bool block_supported(int dtype, int d, int de, int dy) {
+  return (dtype == 1 && d == 256 && de == 64 && dy == 64) || (d == 64 && de == 16 && dy == 16);
+}
+
 hipError_t launch_block(const BlockArgs& k, int dtype, int d, int de, hipStream_t s) {
-  if (dtype == 1 && d == 256 && de == 64) return block_shape<bf16_t, 256, 64>(k, s);
-  if (dtype == 1 && d == 64 && de == 16) return block_shape<bf16_t, 64, 16>(k, s);
-  if (dtype == 0 && d == 64 && de == 16) return block_shape<float, 64, 16>(k, s);
+  if (dtype == 1 && d == 256 && de == 64 && k.dy == 64) return block_shape<bf16_t, 256, 64, 64>(k, s);
+  if (dtype == 1 && d == 64 && de == 16 && k.dy == 16) return block_shape<bf16_t, 64, 16, 16>(k, s);
+  if (dtype == 0 && d == 64 && de == 16 && k.dy == 16) return block_shape<float, 64, 16, 16>(k, s);
   return hipErrorInvalidValue;
 }
 

@@ -182,5 +182,24 @@ __device__ __forceinline__ float lg_sum(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Data-parallel-primitive moves within a row of 16 lanes (VALU, no LDS round
+// trip): quad_perm [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E), row_half_mirror
+// (0x141), row_mirror (0x140).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a row (lanes 16 lg .. 16 lg + 15): pairs, quads,
+// halves, then the whole row; every lane receives the same bits.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+// Sum over all 64 lanes of the wave; every lane receives the same bits.
+__device__ __forceinline__ float wave64_sum(float v) { return lg_sum(row16_sum(v)); }
+
 }  // namespace
 }  // namespace ea

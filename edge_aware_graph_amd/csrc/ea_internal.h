@@ -88,7 +88,6 @@ enum BlockParam : int {
   kBW_yy, kBW_yx, kBW_ye, kBb_yo, kBln_y1_g, kBln_y1_b, kBW_y1, kBb_y1, kBW_y2, kBb_y2, kBln_y2_g, kBln_y2_b,
   kBlockParams
 };
-constexpr int kMaxBlockDy = 512;
 struct BlockArgs {
   const void* p[kBlockParams];
   const void* X;          // [B, n, d]
@@ -102,6 +101,7 @@ struct BlockArgs {
   float* part_e;          // [B, exb, de] sums of E2 over real pairs per edge block
   int B, n, dy, nxb, exb;
 };
+bool block_supported(int dtype, int d, int de, int dy);
 hipError_t launch_block(const BlockArgs& k, int dtype, int d, int de, hipStream_t s);
 
 // Launchers; each returns the hipError_t of its launch. `dtype` 0 = fp32, 1 = bf16.

@@ -237,8 +237,8 @@ ea_status ea_debug_logits(ea_ctx* ctx, const ea_attn_params* p,
  * context's dtype, nn.Linear [out, in] layout, 16-byte aligned, none NULL.
  * Rows of masked nodes of X2 and masked pairs of E2 are +0.0.
  *
- * Built for the (d, de) = (64, 16) shape (float32 and bfloat16) and
- * (256, 64) (bfloat16), dy <= 512, no variant flag (else EA_E_UNSUPPORTED);
+ * Built for (d, de, dy) = (64, 16, 16) (float32 and bfloat16) and
+ * (256, 64, 64) (bfloat16), no variant flag (else EA_E_UNSUPPORTED);
  * single-pass and two-pass contexts. X_out may alias X, E_out may alias E
  * and y_out may alias y. ws holds ea_block_workspace_bytes (the layer's
  * workspace, then O, A and per-block partial sums). bfloat16 mode stores O
