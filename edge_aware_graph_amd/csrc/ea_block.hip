@@ -24,6 +24,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace ea {
 namespace {
 
@@ -117,6 +119,57 @@ struct Pieces {
     }
   }
 };
+
+// A weight matrix [ROWS, COLS] staged in LDS with its columns regrouped so
+// that a lane's left-operand fragment is contiguous: column 32 s + 16 h +
+// 4 g + r (h < 2, g, r < 4) is stored at 32 s + 8 g + 4 h + r, so the
+// contraction values 32 s + 4 lg .. + 3 and 32 s + 16 + 4 lg .. + 3 of lane
+// group lg are the 8 elements at 32 s + 8 lg (one 16-byte LDS read). Needs
+// COLS a multiple of 32; staged in groups of four elements.
+template <typename T, int ROWS, int COLS, int NT>
+struct PermStage {
+  static_assert(COLS % 32 == 0, "whole steps");
+  static constexpr int DW = 4 * (int)sizeof(T) / 4, N = ROWS * COLS / 4, PER = (N + NT - 1) / NT;
+  uint32_t v[PER][DW];
+  __device__ __forceinline__ void load(const T* src, int tid) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int q = tid + e * NT, qc = q < N ? q : 0;
+      ld4w<T>(v[e], src + (size_t)(qc / (COLS / 4)) * COLS + 4 * (qc % (COLS / 4)));
+    }
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(T (*dst)[LD], int tid) const {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int q = tid + e * NT;
+      if (PER * NT != N && q >= N) continue;
+      const int row = q / (COLS / 4), c = 4 * (q % (COLS / 4));
+      const int sblk = c / 32, h = (c / 16) & 1, g = (c / 4) & 3;
+      T* d = &dst[row][32 * sblk + 8 * g + 4 * h];
+      if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(d) = u32x2{v[e][0], v[e][1]};
+      else *reinterpret_cast<u32x4*>(d) = u32x4{v[e][0], v[e][1], v[e][2], v[e][3]};
+    }
+  }
+};
+
+// Left-operand fragment of step s from a row staged by PermStage.
+template <typename T, int K>
+__device__ __forceinline__ Frag<T, Steps<K>::Q> frag_perm(const T* row, int s, int lg) {
+  using S = Steps<K>;
+  static_assert(S::Q == 8, "two groups per step");
+  Frag<T, 8> a;
+  const T* p = row + 32 * s + 8 * lg;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    a.w[0] = v.x; a.w[1] = v.y; a.w[2] = v.z; a.w[3] = v.w;
+  } else {
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(p), v1 = *reinterpret_cast<const u32x4*>(p + 4);
+    a.w[0] = v0.x; a.w[1] = v0.y; a.w[2] = v0.z; a.w[3] = v0.w;
+    a.w[4] = v1.x; a.w[5] = v1.y; a.w[6] = v1.z; a.w[7] = v1.w;
+  }
+  return a;
+}
 
 // ------------------------------------------------------------------ nodes
 
@@ -264,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void blk_node_kernel(BlockArgs k) {
 template <typename T, int DE>
 __global__ __launch_bounds__(kEdgeWaves * 64) void blk_edge_kernel(BlockArgs k) {
   constexpr int FE = 2 * DE, EPC = 16 / (int)sizeof(T), NT = kEdgeWaves * 64;
+  constexpr bool kPerm1 = Steps<DE>::Q == 8;
   __shared__ __align__(16) T w1_s[FE][DE + EPC];
   __shared__ __align__(16) T w2_s[DE][FE + EPC];
   __shared__ float pv_s[6][FE];  // b_e1, b_e2, ln_e1 g / b, ln_e2 g / b
@@ -298,8 +352,11 @@ __global__ __launch_bounds__(kEdgeWaves * 64) void blk_edge_kernel(BlockArgs k) 
   int tile = blockIdx.x * kEdgeWaves + w;
   if (tile < ntile) load(tile, r0);  // the first tile is in flight during the staging
   {
-    Pieces<T, FE, DE, NT> p1;
-    Pieces<T, DE, FE, NT> p2;
+    // W_e1 keeps the plain layout when its contraction (DE = 16) is one group;
+    // otherwise both are staged with the fragment-contiguous column order
+    using P1 = typename std::conditional<kPerm1, PermStage<T, FE, DE, NT>, Pieces<T, FE, DE, NT>>::type;
+    P1 p1;
+    PermStage<T, DE, FE, NT> p2;
     p1.load(par(kBW_e1), tid);
     p2.load(par(kBW_e2), tid);
     const int pq[6] = {kBb_e1, kBb_e2, kBln_e1_g, kBln_e1_b, kBln_e2_g, kBln_e2_b};
@@ -360,7 +417,10 @@ __global__ __launch_bounds__(kEdgeWaves * 64) void blk_edge_kernel(BlockArgs k) 
       for (int to = 0; to < FE / 16; ++to) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s2 = 0; s2 < Steps<DE>::NS; ++s2) acc = mma(acc, frag_at<T, DE>(&w1_s[16 * to + li][0], s2, lg), in.f[s2]);
+        for (int s2 = 0; s2 < Steps<DE>::NS; ++s2) {
+          if constexpr (kPerm1) acc = mma(acc, frag_perm<T, DE>(&w1_s[16 * to + li][0], s2, lg), in.f[s2]);
+          else acc = mma(acc, frag_at<T, DE>(&w1_s[16 * to + li][0], s2, lg), in.f[s2]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) h[4 * to + r] = fmaxf(acc[r] + pv_s[0][16 * to + 4 * lg + r], 0.f);
       }
@@ -372,7 +432,7 @@ __global__ __launch_bounds__(kEdgeWaves * 64) void blk_edge_kernel(BlockArgs k) 
       for (int to = 0; to < DE / 16; ++to) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s2 = 0; s2 < Steps<FE>::NS; ++s2) acc = mma(acc, frag_at<T, FE>(&w2_s[16 * to + li][0], s2, lg), in.f[s2]);
+        for (int s2 = 0; s2 < Steps<FE>::NS; ++s2) acc = mma(acc, frag_perm<T, FE>(&w2_s[16 * to + li][0], s2, lg), in.f[s2]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) z[4 * to + r] = acc[r] + pv_s[1][16 * to + 4 * lg + r] + e1[4 * to + r];
       }
@@ -444,12 +504,32 @@ struct RowW {
 template <typename T, int D, int DE, int DY>
 __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
   constexpr int OPW = DY / kWaves;  // outputs per wave
-  static_assert(DY % kWaves == 0 && DY <= kThreads, "outputs over the waves");
+  static_assert(DY % kWaves == 0 && DY <= kThreads && D <= kThreads && DE <= kThreads, "one feature per thread");
   __shared__ float xbar[D], ebar[DE];
   __shared__ float yv[DY], y1[DY], hy[DY], red4[2][kWaves];
   __shared__ int cnt;
   const int tid = threadIdx.x, b = blockIdx.x, n = k.n, w = tid >> 6, l = tid & 63;
   auto par = [&](int q) { return static_cast<const T*>(k.p[q]); };
+  // First-phase loads (mask bytes, y, the first partial sums) are issued
+  // before the weights: loads complete in issue order, so waiting for them
+  // does not wait for the weights, which arrive during the sums.
+  constexpr int NMK = 4, NPB = 16;  // mask bytes and partials per thread held in registers
+  uint8_t mk[NMK];
+#pragma unroll
+  for (int q = 0; q < NMK; ++q) {
+    const int i = tid + q * kThreads;
+    mk[q] = k.mask[(size_t)b * n + (i < n ? i : 0)];
+  }
+  const int cc = tid < DY ? tid : 0;  // feature of the norm and bias steps
+  const float yr = Num<T>::ld(static_cast<const T*>(k.y) + (size_t)b * DY + cc);
+  const int fx = tid < D ? tid : 0, fe = tid < DE ? tid : 0;
+  float px[NPB], pe[NPB];
+#pragma unroll
+  for (int q = 0; q < NPB; ++q) {
+    px[q] = k.part_x[((size_t)b * k.nxb + (q < k.nxb ? q : 0)) * D + fx];
+    pe[q] = k.part_e[((size_t)b * k.exb + (q < k.exb ? q : 0)) * DE + fe];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   RowW<T, D> wyx[OPW];
   RowW<T, DE> wye[OPW];
   RowW<T, DY> wyy[OPW], wy1[OPW], wy2[OPW];
@@ -462,30 +542,34 @@ __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
     wy1[m].load(par(kBW_y1) + o * DY, l);
     wy2[m].load(par(kBW_y2) + o * DY, l);
   }
-  const int cc = tid < DY ? tid : 0;  // feature of the norm and bias steps
   const uint32_t pb[3] = {Num<T>::ldraw(par(kBb_yo) + cc), Num<T>::ldraw(par(kBb_y1) + cc),
                           Num<T>::ldraw(par(kBb_y2) + cc)};
   const uint32_t pl[4] = {Num<T>::ldraw(par(kBln_y1_g) + cc), Num<T>::ldraw(par(kBln_y1_b) + cc),
                           Num<T>::ldraw(par(kBln_y2_g) + cc), Num<T>::ldraw(par(kBln_y2_b) + cc)};
+  __builtin_amdgcn_sched_barrier(0);
   if (tid == 0) cnt = 0;
   __syncthreads();
   int c0 = 0;
-  for (int i = tid; i < n; i += kThreads) c0 += k.mask[(size_t)b * n + i] != 0;
+#pragma unroll
+  for (int q = 0; q < NMK; ++q) c0 += (tid + q * kThreads < n && mk[q] != 0) ? 1 : 0;
+  for (int i = tid + NMK * kThreads; i < n; i += kThreads) c0 += k.mask[(size_t)b * n + i] != 0;
   atomicAdd(&cnt, c0);
-  if (tid < DY) yv[tid] = Num<T>::ld(static_cast<const T*>(k.y) + (size_t)b * DY + tid);
+  if (tid < DY) yv[tid] = yr;
   __syncthreads();
   const float nr = (float)cnt;
-  for (int f = tid; f < D; f += kThreads) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < k.nxb; ++q) s += k.part_x[((size_t)b * k.nxb + q) * D + f];
-    xbar[f] = s / fmaxf(nr, 1.f);
+  if (tid < D) {
+    float sx = 0.f;
+#pragma unroll
+    for (int q = 0; q < NPB; ++q) sx += q < k.nxb ? px[q] : 0.f;
+    for (int q = NPB; q < k.nxb; ++q) sx += k.part_x[((size_t)b * k.nxb + q) * D + tid];
+    xbar[tid] = sx / fmaxf(nr, 1.f);
   }
-  for (int f = tid; f < DE; f += kThreads) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < k.exb; ++q) s += k.part_e[((size_t)b * k.exb + q) * DE + f];
-    ebar[f] = s / fmaxf(nr * nr, 1.f);
+  if (tid < DE) {
+    float se = 0.f;
+#pragma unroll
+    for (int q = 0; q < NPB; ++q) se += q < k.exb ? pe[q] : 0.f;
+    for (int q = NPB; q < k.exb; ++q) se += k.part_e[((size_t)b * k.exb + q) * DE + tid];
+    ebar[tid] = se / fmaxf(nr * nr, 1.f);
   }
   __syncthreads();
   // sum of x over all threads of the block (every thread gets it)

@@ -106,3 +106,17 @@ def test_block_sbm_bf16_reduced():
     bp = W.make_block_params(dims, seed=5)
     got, ref = run_block(batch, dims, bp)
     check(got, ref, batch, dims)
+
+
+def test_block_natural_two_pass_n300():
+    """n = 300 > 256: the layer inside the block runs its two-pass scheme
+    (edge tiles of several thousand per graph, node blocks of 16 rows with a
+    ragged last one), ragged non-prefix masks."""
+    dims = dims_of("planar", B=2, n=300)
+    batch = W.make_batch("planar", bias_scale=0.1, dims=dims)
+    rng = np.random.default_rng(300)
+    mask = (rng.random((2, 300)) < 0.8).astype(np.uint8)
+    batch["mask"] = mask
+    bp = W.make_block_params(dims, seed=11)
+    got, ref = run_block(batch, dims, bp)
+    check(got, ref, batch, dims)
