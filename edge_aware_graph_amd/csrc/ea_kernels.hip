@@ -1423,6 +1423,18 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       sbe[h] += dbe[h][r];
     }
   }
+  // dE' rows of the first PD keys of step (5), issued before the stores below:
+  // vector memory operations complete in issue order, so a wait for a row
+  // loaded after a store would wait for that store too
+  constexpr int PD = 4;
+  const size_t dErow = ((size_t)b * n + (i < n ? i : 0)) * n * DE + lg * (DE / 4);
+  auto ld_dep = [&](int jj, Frag<T, DE / 4>& f) {
+    const int j = j0 + jj;
+    f.load(i < n && j < n ? dEp + dErow + (size_t)j * DE : zeros<T>());
+  };
+  Frag<T, DE / 4> ring[PD];
+#pragma unroll
+  for (int jj = 0; jj < PD; ++jj) ld_dep(jj, ring[jj]);
   // ds and dgamma_e / dbeta_e for the (graph, head) and pair-reduction kernels
   if (tile_ok) {
 #pragma unroll
@@ -1450,7 +1462,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   lane_group_transpose<16>(dFa);
   if (tile_ok) {
     T* dE = static_cast<T*>(g.dE);
-    const size_t rowoff = ((size_t)b * n + (i < n ? i : 0)) * n * DE + lg * (DE / 4);
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       const int j = j0 + jj;
@@ -1458,8 +1469,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       const bool real = sc.mi && ((bits >> jj) & 1u);
       Frag<T, 4> bq;
       bq.set(&dFa[jj >> 2][4 * (jj & 3)]);
-      Frag<T, DE / 4> ef;
-      ef.load(inb ? dEp + rowoff + (size_t)j * DE : zeros<T>());
+      const Frag<T, DE / 4> ef = ring[jj % PD];
+      if (jj + PD < 16) ld_dep(jj + PD, ring[jj % PD]);  // PD keys ahead
       float out[DE / 4];
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
@@ -1470,7 +1481,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       if (inb) {
         Frag<T, DE / 4> of;
         of.set(out);
-        of.store(dE + rowoff + (size_t)j * DE);
+        of.store(dE + dErow + (size_t)j * DE);
       }
     }
   }
