@@ -219,7 +219,7 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   const size_t pairs = (size_t)d.B * c->NP * c->NP;
   c->boff_ds = qkv;  // V rows first
   c->boff_df = c->boff_ds + round256(pairs * d.H * sizeof(float));
-  c->boff_dqkv = c->boff_df + round256(pairs * 2 * d.H * sizeof(float));
+  c->boff_dqkv = c->boff_df + round256(pairs * 2 * d.H * c->esz);
   c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
   c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->bws_bytes = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
@@ -465,7 +465,7 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   char* bb = static_cast<char*>(bws);
   g.Vr = bb;
   g.DS = reinterpret_cast<float*>(bb + c->boff_ds);
-  g.DF = reinterpret_cast<float*>(bb + c->boff_df);
+  g.DF = bb + c->boff_df;
   g.DQKV = reinterpret_cast<float*>(bb + c->boff_dqkv);
   g.DGY = reinterpret_cast<float*>(bb + c->boff_dgy);
   g.RED = reinterpret_cast<float*>(bb + c->boff_red);

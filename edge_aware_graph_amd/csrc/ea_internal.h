@@ -68,8 +68,8 @@ struct BwdArgs {
   float *gw_e, *gb_e;
   // scratch (the backward workspace)
   void* Vr;      // V rows [B, H, NP, dh]
-  float* DS;     // ds [B, H, NP, NP]
-  float* DF;     // dgamma_e, dbeta_e [B, 2H, NP, NP]
+  float* DS;     // ds [B, H, NP, NP] (float32: the key-bias gradient, a sum of ds over keys, nearly cancels)
+  void* DF;      // dgamma_e, dbeta_e [B, 2H, NP, NP], the layer's dtype
   float* DQKV;   // dQ | dK | dV [B, NP, 3, d]
   float* DGY;    // dgamma_y, dbeta_y [B, 2H]
   float* RED;    // pair-reduction partial sums [kRedCopies][2 H de + de H + de]

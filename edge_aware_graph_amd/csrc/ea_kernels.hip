@@ -1233,6 +1233,16 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
 // A is the forward's stored map (bfloat16 in bf16 mode): the backward of a
 // rounding point counts as the identity.
 
+// Four consecutive values of type T (8 or 16 bytes) from floats.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 // bwd_prep: zero the gradients that are accumulated with atomics, and V in
 // row layout [B, H, NP, dh] (the forward keeps V^T).
 template <typename T, int H, int DH, int DE>
@@ -1439,12 +1449,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   if (tile_ok) {
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      *reinterpret_cast<f32x4*>(g.DS + (((size_t)b * H + h) * NP + i) * NP + j0 + 4 * lg) =
-          f32x4{ds[h][0], ds[h][1], ds[h][2], ds[h][3]};
-      *reinterpret_cast<f32x4*>(g.DF + (((size_t)b * 2 * H + h) * NP + i) * NP + j0 + 4 * lg) =
-          f32x4{dge[h][0], dge[h][1], dge[h][2], dge[h][3]};
-      *reinterpret_cast<f32x4*>(g.DF + (((size_t)b * 2 * H + H + h) * NP + i) * NP + j0 + 4 * lg) =
-          f32x4{dbe[h][0], dbe[h][1], dbe[h][2], dbe[h][3]};
+      store4<float>(g.DS + (((size_t)b * H + h) * NP + i) * NP + j0 + 4 * lg, ds[h]);
+      store4<T>(static_cast<T*>(g.DF) + (((size_t)b * 2 * H + h) * NP + i) * NP + j0 + 4 * lg, dge[h]);
+      store4<T>(static_cast<T*>(g.DF) + (((size_t)b * 2 * H + H + h) * NP + i) * NP + j0 + 4 * lg, dbe[h]);
     }
   }
   // (5) dE = dE' + W_F^T dF per key: dF regrouped so that lane group lg holds
@@ -1610,7 +1617,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
     Frag<T, DE / 4> ef, df;
     uint8_t mi, mj;   // mask bytes of the pair's nodes
     bool inb;         // the pair exists and both nodes are below n
-    uint32_t v[NS];   // raw dF (float32) / A (T) words, converted at the store
+    uint32_t v[NS];   // raw dF / A words (T), converted at the store
     bool inr, okv;    // pair l of the chunk exists / exists with both nodes below n
   };
   // Raw values only: the masks and bounds are applied when the chunk is
@@ -1638,7 +1645,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
       for (int k = 0; k < NS; ++k) {
         const int row = w + 4 * k;  // rows 0..2H-1: dF, 2H..3H-1: A
         if (k < H / 2) {
-          r.v[k] = Num<float>::ldraw(g.DF + (((size_t)bc * 2 * H + row) * NP + ii) * NP + jj);
+          r.v[k] = Num<T>::ldraw(static_cast<const T*>(g.DF) + (((size_t)bc * 2 * H + row) * NP + ii) * NP + jj);
         } else {
           const int h = row < 3 * H ? row - 2 * H : 0;
           r.v[k] = Num<T>::ldraw(Ag + (((size_t)bc * H + h) * n + (r.okv ? ii : 0)) * n + (r.okv ? jj : 0));
@@ -1660,7 +1667,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const int row = w + 4 * k;
-        if (k < H / 2) f_s[row][l] = cur.inr ? Num<float>::fromraw(cur.v[k]) : 0.f;
+        if (k < H / 2) f_s[row][l] = cur.inr ? Num<T>::fromraw(cur.v[k]) : 0.f;
         else if (row < 3 * H) a_s[row - 2 * H][l] = cur.okv ? Num<T>::fromraw(cur.v[k]) : 0.f;
       }
     }
