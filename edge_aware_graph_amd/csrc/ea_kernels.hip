@@ -1220,7 +1220,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
 // ------------------------------------------------------------------ backward
 
 // Gradients of one layer (forward and residual edge update), single-pass
-// shapes with one key tile per wave (n <= 64), from the loss gradients dO of
+// shapes (the stored A is reused), from the loss gradients dO of
 // the node output and dE' of the edge output. Per real pair (i, j), head h:
 //   dA = dO_i . V_j + sum_c W_e[c, h] dE'_ij[c]        (through A V and E')
 //   D_i = sum_j A_ij dA_ij,  du = A (dA - D)             (softmax)
@@ -1283,8 +1283,13 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
   }
 }
 
-// bwd_pair: one block per (16 queries, graph), wave w = key tile w (n <= 64).
-template <typename T, int H, int DH, int DE>
+// bwd_pair: one block per (16 queries, graph, 64 keys), wave w = key tile
+// 4 blockIdx.z + w. The row sums D_i = sum_j A_ij dA_ij span every key:
+//   kPairAll  (n <= 64, one key block): D from the block's four waves;
+//   kPairPart (64 < n): only dA, and the block's part of D into DP;
+//   kPairUse  (64 < n): D as the sum of the key blocks' parts, then the rest.
+enum PairMode : int { kPairAll = 0, kPairPart = 1, kPairUse = 2 };
+template <typename T, int H, int DH, int DE, int PM>
 __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs g) {
   constexpr int D = H * DH, NCH = DE / 16;
   __shared__ float red_s[kWaves][H][16];
@@ -1293,7 +1298,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   const int b = blockIdx.y, i0 = blockIdx.x * 16;
   Scorer<T, H, DH, DE> sc;
   sc.setup(a, b, i0);
-  const int n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, jt = w, j0 = 16 * jt;
+  const int n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, jt = kWaves * blockIdx.z + w, j0 = 16 * jt;
+  const int KB = gridDim.z;  // key blocks of the row
   const bool tile_ok = jt < JT;  // uniform per wave; waves past JT compute zeros
   const uint32_t mq = sc.query_mask_byte();
   const uint32_t mk = sc.key_mask_byte(jt);
@@ -1379,9 +1385,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
 #pragma unroll
       for (int r = 0; r < 4; ++r) dAe[h][r] = R2[h >> 2][4 * r + (h & 3)];
   }
-  // (2) the FiLM rows (gamma_e, beta_e) from the E tile
+  // (2) the FiLM rows (gamma_e, beta_e) from the E tile (not needed for D alone)
   float R[4][16];
-  {
+  if constexpr (PM != kPairPart) {
     ETile<T, DE> et;
     et.load_all(sc.E, b, n, i, j0, lg);
     const f32x4 fc = sc.film_start();
@@ -1391,7 +1397,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   }
   // (3) scores and dO . V (both as S^T = K Q^T: lane (li, lg) holds query li, keys 4 lg + r)
   f32x4 S[H], P[H];
-  sc.qk(kf, S);
+  if constexpr (PM != kPairPart) sc.qk(kf, S);
 #pragma unroll
   for (int h = 0; h < H; ++h) P[h] = mma(f32x4{0.f, 0.f, 0.f, 0.f}, vr[h], dof[h]);
   // (4) the softmax backward per pair and head
@@ -1408,13 +1414,28 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
     if (lg == 0) red_s[w][h][li] = part;
   }
   __syncthreads();
+  if constexpr (PM == kPairPart) {
+    // this key block's part of D for the 16 queries
+    if (tid < H * 16) {
+      const int h = tid >> 4, q = tid & 15, iq = i - li + q;
+      float x = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) x += red_s[ww][h][q];
+      g.DP[(((size_t)b * H + h) * NP + iq) * KB + blockIdx.z] = x;
+    }
+    return;
+  }
   float ds[H][4], dge[H][4], dbe[H][4];
   float sgy[H], sby[H], sge[H], sbe[H];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     float Dh = 0.f;
+    if constexpr (PM == kPairAll) {
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) Dh += red_s[ww][h][li];
+      for (int ww = 0; ww < kWaves; ++ww) Dh += red_s[ww][h][li];
+    } else {
+      for (int kb = 0; kb < KB; ++kb) Dh += g.DP[(((size_t)b * H + h) * NP + i) * KB + kb];
+    }
     const float gyh = sc.gy[h];
     sgy[h] = sby[h] = sge[h] = sbe[h] = 0.f;
 #pragma unroll
@@ -1518,74 +1539,94 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   }
 }
 
-// bwd_qkv: per (head, graph): dQ = r ds K, dK = r ds^T Q, dV = A^T dO into
-// DQKV [B, NP, 3, D] (float32), n <= 64.
+// bwd_qkv: per (head, graph, 64 output rows r0 = 64 blockIdx.z ..):
+// dQ = s ds K, dK = s ds^T Q, dV = A^T dO (s the score scale) into DQKV
+// [B, NP, 3, D] (float32), the contraction taken in chunks of 64 staged in
+// LDS (every load of a chunk issued before any is used, out-of-range
+// elements replaced by 0), products on float32 MFMA 16x16x4 tiles spread
+// over the waves: lane (li, lg) supplies row li of the left operand and
+// column li of the right one at contraction index 4 step + lg.
 template <typename T, int H, int DH>
 __global__ __launch_bounds__(kThreads) void bwd_qkv_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int D = H * DH, M = 64;
-  __shared__ float ds_s[M][M + 1], a_s[M][M + 1];
+  constexpr int D = H * DH, M = 64, NTN = DH / 16, TPW = 3 * 4 * NTN / kWaves;
+  static_assert((3 * 4 * NTN) % kWaves == 0, "tiles over the waves");
+  __shared__ float dsr_s[M][M + 1], dsc_s[M][M + 1], a_s[M][M + 1];
   __shared__ float q_s[M][DH + 1], k_s[M][DH + 1], o_s[M][DH + 1];
-  const int h = blockIdx.x, b = blockIdx.y, NP = a.NP, n = a.n, tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y, r0 = blockIdx.z * M, NP = a.NP, n = a.n, tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const size_t bh = (size_t)b * H + h;
   const T* Ag = static_cast<const T*>(g.A);
   const T* Qw = static_cast<const T*>(a.Qw);
   const T* Kw = static_cast<const T*>(a.Kw);
   const T* dO = static_cast<const T*>(g.dO);
-  // staging: every load is issued (clamped index) before any is used, then
-  // out-of-range elements are replaced by 0
+  const int mtn = NP - r0 < M ? (NP - r0) / 16 : 4;  // 16-row tiles of this block
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int NPP = M * M / kThreads, NPD = M * DH / kThreads;
-  float vd[NPP], va[NPP], vq[NPD], vk[NPD], vo[NPD];
+  for (int c0 = 0; c0 < NP; c0 += M) {
+    float vr[NPP], vc[NPP], va[NPP], vq[NPD], vk[NPD], vo[NPD];
 #pragma unroll
-  for (int k = 0; k < NPP; ++k) {
-    const int idx = tid + k * kThreads, ii = idx / M, jj = idx % M;
-    const bool okp = ii < NP && jj < NP, oka = ii < n && jj < n;
-    vd[k] = g.DS[(bh * NP + (okp ? ii : 0)) * NP + (okp ? jj : 0)];
-    va[k] = Num<T>::ld(Ag + bh * n * n + (oka ? (size_t)ii * n + jj : 0));
-  }
-#pragma unroll
-  for (int k = 0; k < NPD; ++k) {
-    const int idx = tid + k * kThreads, r = idx / DH, t = idx % DH, rp = r < NP ? r : 0, rn = r < n ? r : 0;
-    vq[k] = Num<T>::ld(Qw + (bh * NP + rp) * DH + t);
-    vk[k] = Num<T>::ld(Kw + (bh * NP + rp) * DH + t);
-    vo[k] = Num<T>::ld(dO + ((size_t)b * n + rn) * D + h * DH + t);
-  }
-#pragma unroll
-  for (int k = 0; k < NPP; ++k) {
-    const int idx = tid + k * kThreads, ii = idx / M, jj = idx % M;
-    ds_s[ii][jj] = ii < NP && jj < NP ? vd[k] : 0.f;
-    a_s[ii][jj] = ii < n && jj < n ? va[k] : 0.f;
-  }
-#pragma unroll
-  for (int k = 0; k < NPD; ++k) {
-    const int idx = tid + k * kThreads, r = idx / DH, t = idx % DH;
-    q_s[r][t] = r < NP ? vq[k] : 0.f;
-    k_s[r][t] = r < NP ? vk[k] : 0.f;
-    o_s[r][t] = r < n ? vo[k] : 0.f;
-  }
-  __syncthreads();
-  // 16 x 16 output tiles of dQ = s ds K, dK = s ds^T Q, dV = A^T dO (s the
-  // score scale) on float32 MFMA 16x16x4, spread over the waves; lane
-  // (li, lg) supplies row li of the left operand and column li of the right
-  // one at contraction index 4 step + lg
-  const float sc = a.scale;
-  const int mtn = NP / 16, ntn = DH / 16, ntiles = 3 * mtn * ntn;
-  for (int ti = w; ti < ntiles; ti += kWaves) {
-    const int which = ti / (mtn * ntn), mt = (ti / ntn) % mtn, nt = ti % ntn;
-    const int row = 16 * mt + li, col = 16 * nt + li;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s4 = 0; s4 < NP / 4; ++s4) {
-      const int kk = 4 * s4 + lg;
-      const float av = which == 0 ? ds_s[row][kk] : which == 1 ? ds_s[kk][row] : a_s[kk][row];
-      const float bv = which == 0 ? k_s[kk][col] : which == 1 ? q_s[kk][col] : o_s[kk][col];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    for (int k = 0; k < NPP; ++k) {
+      const int idx = tid + k * kThreads, hi = idx / M, lo = idx % M;
+      // dsr: row r0 + hi, column c0 + lo;  dsc and A: row c0 + hi, column r0 + lo
+      const bool okr = r0 + hi < NP && c0 + lo < NP, okc = c0 + hi < NP && r0 + lo < NP;
+      const bool oka = c0 + hi < n && r0 + lo < n;
+      vr[k] = g.DS[(bh * NP + (okr ? r0 + hi : 0)) * NP + (okr ? c0 + lo : 0)];
+      vc[k] = g.DS[(bh * NP + (okc ? c0 + hi : 0)) * NP + (okc ? r0 + lo : 0)];
+      va[k] = Num<T>::ld(Ag + bh * n * n + (oka ? (size_t)(c0 + hi) * n + r0 + lo : 0));
     }
+#pragma unroll
+    for (int k = 0; k < NPD; ++k) {
+      const int idx = tid + k * kThreads, rr = idx / DH, t = idx % DH, c = c0 + rr;
+      const int cp = c < NP ? c : 0, cn = c < n ? c : 0;
+      vq[k] = Num<T>::ld(Qw + (bh * NP + cp) * DH + t);
+      vk[k] = Num<T>::ld(Kw + (bh * NP + cp) * DH + t);
+      vo[k] = Num<T>::ld(dO + ((size_t)b * n + cn) * D + h * DH + t);
+    }
+#pragma unroll
+    for (int k = 0; k < NPP; ++k) {
+      const int idx = tid + k * kThreads, hi = idx / M, lo = idx % M;
+      dsr_s[hi][lo] = r0 + hi < NP && c0 + lo < NP ? vr[k] : 0.f;
+      dsc_s[lo][hi] = c0 + hi < NP && r0 + lo < NP ? vc[k] : 0.f;  // [output row][contraction]
+      a_s[lo][hi] = c0 + hi < n && r0 + lo < n ? va[k] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NPD; ++k) {
+      const int idx = tid + k * kThreads, rr = idx / DH, t = idx % DH, c = c0 + rr;
+      q_s[rr][t] = c < NP ? vq[k] : 0.f;
+      k_s[rr][t] = c < NP ? vk[k] : 0.f;
+      o_s[rr][t] = c < n ? vo[k] : 0.f;
+    }
+    __syncthreads();
+    const int csteps = (NP - c0 < M ? NP - c0 : M) / 4;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int ti = w + kWaves * t, which = ti / (4 * NTN), mt = (ti / NTN) % 4, nt = ti % NTN;
+      if (mt >= mtn) continue;  // uniform per wave
+      const int row = 16 * mt + li, col = 16 * nt + li;
+      f32x4 c = acc[t];
+#pragma unroll 4
+      for (int s4 = 0; s4 < csteps; ++s4) {
+        const int kk = 4 * s4 + lg;
+        const float av = which == 0 ? dsr_s[row][kk] : which == 1 ? dsc_s[row][kk] : a_s[row][kk];
+        const float bv = which == 0 ? k_s[kk][col] : which == 1 ? q_s[kk][col] : o_s[kk][col];
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+      }
+      acc[t] = c;
+    }
+    __syncthreads();
+  }
+  const float sc = a.scale;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int ti = w + kWaves * t, which = ti / (4 * NTN), mt = (ti / NTN) % 4, nt = ti % NTN;
+    if (mt >= mtn) continue;
     const float f = which < 2 ? sc : 1.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rr = 16 * mt + 4 * lg + r;
-      g.DQKV[(((size_t)b * NP + rr) * 3 + which) * D + h * DH + col] = f * acc[r];
+      const int rr = r0 + 16 * mt + 4 * lg + r;
+      g.DQKV[(((size_t)b * NP + rr) * 3 + which) * D + h * DH + 16 * nt + li] = f * acc[t][r];
     }
   }
 }
@@ -1601,7 +1642,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
   static_assert(2 * H <= 16 && H < 16 && DE % 16 == 0 && DE / 16 <= kWaves, "one 16-channel chunk per wave");
   __shared__ float e_s[P][DE + 1], d_s[P][DE + 1], f_s[2 * H][P + 1], a_s[H][P + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4, NP = a.NP, n = a.n;
-  // pair q = (b NP + i) NP + j; B NP^2 < 2^31 for n <= 64
+  // pair q = (b NP + i) NP + j; B NP^2 < 2^31 (checked by the library)
   const uint32_t npairs = (uint32_t)a.B * NP * NP, nchunks = (npairs + P - 1) / P;
   const T* E = static_cast<const T*>(a.E);
   const T* dEp = static_cast<const T*>(g.dEp);
@@ -2193,8 +2234,14 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
                       (size_t)a.B * H * a.NP * DH + (size_t)3 * D * D + 3 * D;
   const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE>), dim3(JT, a.B), dim3(kThreads), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B), dim3(kThreads), 0, s, a, g);
+  if (a.NP <= 64) {
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairAll>), dim3(JT, a.B, 1), dim3(kThreads), 0, s, a, g);
+  } else {  // key blocks of 64: the row sums of D first, then the rest
+    const int KB = (a.NP + 63) / 64;
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairPart>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
+  }
+  hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B, (a.NP + 63) / 64), dim3(kThreads), 0, s, a, g);
   const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
   const unsigned red_blocks = (unsigned)(chunks < 512 ? chunks : 512);  // atomics per output: one per block
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);

@@ -175,8 +175,9 @@ ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_
  * Network for Graph Generation", full-text summary: FiLM-modulated scaled
  * dot-product scores, mask, normalized softmax, A [V | I], E' = E + W_e A +
  * b_e), with the forward's stored A (bfloat16 mode: its rounding points pass
- * gradients through unchanged). Supported: single-pass contexts with n <= 64,
- * no variant flag, bfloat16 for both built shapes and float32 for (4, 16, 16)
+ * gradients through unchanged). Supported: single-pass contexts (n <=
+ * EA_SINGLE_PASS_MAX_N, B n_p^2 < 2^31 with n_p = n rounded up to 16), no
+ * variant flag, bfloat16 for both built shapes and float32 for (4, 16, 16)
  * (else EA_E_UNSUPPORTED).
  *
  * Needs a preceding edge_attn_layer or edge_attn_forward on this context with

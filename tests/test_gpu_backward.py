@@ -108,3 +108,19 @@ def test_backward_ragged_random_masks(n, dtype):
     batch["mask"] = mask
     got, ref = run_backward(batch, dims, seed=n)
     check(got, ref, batch, dims)
+
+
+@pytest.mark.parametrize("n,dtype,B", [(100, "bf16", 2), (192, "bf16", 2), (256, "bf16", 1), (100, "fp32", 2)])
+def test_backward_several_key_blocks(n, dtype, B):
+    """64 < n <= 256 (single pass): the pair kernel runs over key blocks of 64,
+    the row sums D_i in a first pass; dQ, dK, dV over contraction chunks.
+    Ragged random masks with one graph fully real."""
+    over = {"n": n, "B": B, "dtype": dtype}
+    dims = dims_of("tiny" if dtype == "fp32" else "planar", **over)
+    batch = W.make_batch("tiny", bias_scale=0.2, dims=dims)
+    rng = np.random.default_rng(1000 + n)
+    mask = (rng.random((B, n)) < 0.75).astype(np.uint8)
+    mask[0] = 1
+    batch["mask"] = mask
+    got, ref = run_backward(batch, dims, seed=n)
+    check(got, ref, batch, dims)
