@@ -178,7 +178,7 @@ const char* ea_kernel_name(int k) {
     case EA_K_ATTN: return "attn_kernel";
     case EA_K_UPDATE: return "update_kernel";
     case EA_K_FUSED: return "attn_kernel(fused)";
-    case EA_K_BACKWARD: return "backward (7 kernels)";
+    case EA_K_BACKWARD: return "backward (all kernels)";
     case EA_K_BLOCK: return "block (node, edge, y kernels)";
   }
   return "?";

@@ -25,7 +25,7 @@ EA_VARIANT_UNNORMALIZED = 0x8
 VARIANTS = {"light_edge": EA_VARIANT_LIGHT_EDGE, "no_score_mod": EA_VARIANT_NO_SCORE_MOD,
             "unnormalized": EA_VARIANT_UNNORMALIZED}
 EA_SINGLE_PASS_MAX_N = 256
-KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)", "backward (7 kernels)",
+KERNELS = ("qkv_kernel", "attn_kernel", "update_kernel", "attn_kernel(fused)", "backward (all kernels)",
            "block (node, edge, y kernels)")
 
 # Symbols declared in include/edge_attn.h.
