@@ -22,7 +22,7 @@ struct ea_ctx {
   int forward_done;
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
-  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_red, boff_dp, bws_bytes;  // backward workspace
+  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_red, boff_dp, boff_ar, bws_bytes;  // backward workspace
   int blk_nxb, blk_exb;  // block: node and edge blocks per graph
   size_t blk_off_o, blk_off_a, blk_off_px, blk_off_pe, blk_bytes;  // block workspace (after the layer's)
   // kernel timing window
@@ -223,7 +223,9 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
   c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
   c->boff_dp = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
-  c->bws_bytes = c->boff_dp + round256((size_t)d.B * d.H * c->NP * ((c->NP + 63) / 64) * sizeof(float));
+  c->boff_ar = c->boff_dp + round256((size_t)d.B * d.H * c->NP * ((c->NP + 63) / 64) * sizeof(float));
+  // two-pass contexts: the backward recomputes A [B, H, n, n] into its workspace
+  c->bws_bytes = c->boff_ar + (c->two_pass ? round256((size_t)d.B * d.H * d.n * d.n * c->esz) : 0);
   {
     // block: 16 nodes per node block; edge blocks of 4 waves with at least
     // 4 tiles of 16 tokens per wave, at most 256 per graph
@@ -426,9 +428,6 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
                              void* ws, size_t ws_bytes, void* bws, size_t bws_bytes, void* stream) {
   g_err[0] = 0;
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
-  if (c->two_pass)
-    return fail(EA_E_UNSUPPORTED, "the backward is built for single-pass contexts (n <= %d; n = %d)",
-                EA_SINGLE_PASS_MAX_N, c->d.n);
   if ((uint64_t)c->d.B * c->NP * c->NP >= (1ull << 31))
     return fail(EA_E_UNSUPPORTED, "the backward indexes pairs in 32 bits: B n_p^2 must stay below 2^31");
   if (c->d.flags & kVariants) return fail(EA_E_UNSUPPORTED, "the backward is built for the full layer (no variant flag)");
@@ -440,7 +439,7 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
   EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
   EA_TRY(check_io(c, X, E, y, mask, true));
-  EA_TRY(check_ptr(A, "A", 16, true));
+  EA_TRY(check_ptr(A, "A", 16, !c->two_pass));  // two-pass: not produced by the forward, ignored
   EA_TRY(check_ptr(dO, "dO", 16, true));
   EA_TRY(check_ptr(dEp, "dE_out", 16, true));
   EA_TRY(check_ptr(dX, "dX", 16, true));
@@ -474,6 +473,10 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   g.DGY = reinterpret_cast<float*>(bb + c->boff_dgy);
   g.RED = reinterpret_cast<float*>(bb + c->boff_red);
   g.DP = reinterpret_cast<float*>(bb + c->boff_dp);
+  if (c->two_pass) {  // A recomputed from the logits and lse into the workspace
+    g.A = bb + c->boff_ar;
+    g.recompute_a = 1;
+  }
   return timed(c, EA_K_BACKWARD, s, [&] {
     return ea::launch_backward(a, g, c->d.dtype, c->d.H, c->d.dh, c->d.de, s);
   });

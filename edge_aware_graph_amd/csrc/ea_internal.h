@@ -74,6 +74,7 @@ struct BwdArgs {
   float* DGY;    // dgamma_y, dbeta_y [B, 2H]
   float* RED;    // pair-reduction partial sums [kRedCopies][2 H de + de H + de]
   float* DP;     // n > 64: parts of D_i = sum_j A_ij dA_ij per key block [B, H, NP, ceil(NP / 64)]
+  int recompute_a;  // two-pass context: A [B, H, n, n] is recomputed into the buffer g.A points to
 };
 
 // Copies of the pair reduction's outputs: blocks of the reduction add into

@@ -1287,8 +1287,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
 // 4 blockIdx.z + w. The row sums D_i = sum_j A_ij dA_ij span every key:
 //   kPairAll  (n <= 64, one key block): D from the block's four waves;
 //   kPairPart (64 < n): only dA, and the block's part of D into DP;
-//   kPairUse  (64 < n): D as the sum of the key blocks' parts, then the rest.
-enum PairMode : int { kPairAll = 0, kPairPart = 1, kPairUse = 2 };
+//   kPairUse  (64 < n): D as the sum of the key blocks' parts, then the rest;
+//   kPairPartA (two-pass contexts, where A is not stored): as kPairPart, with
+//     A recomputed from the logits and the forward's row statistics,
+//     A = exp(u - lse_i) rounded to T (the operand the forward's update used),
+//     and written to g.A for the kernels that follow.
+enum PairMode : int { kPairAll = 0, kPairPart = 1, kPairUse = 2, kPairPartA = 3 };
 template <typename T, int H, int DH, int DE, int PM>
 __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs g) {
   constexpr int D = H * DH, NCH = DE / 16;
@@ -1316,7 +1320,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   }
   // A of this lane's query and keys j0 + 4 lg + r (0 outside the n x n map)
   float Av[H][4];
-  {
+  if constexpr (PM != kPairPartA) {
     const T* Ag = static_cast<const T*>(g.A);
 #pragma unroll
     for (int h = 0; h < H; ++h)
@@ -1400,6 +1404,24 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   if constexpr (PM != kPairPart) sc.qk(kf, S);
 #pragma unroll
   for (int h = 0; h < H; ++h) P[h] = mma(f32x4{0.f, 0.f, 0.f, 0.f}, vr[h], dof[h]);
+  if constexpr (PM == kPairPartA) {
+    // A = exp(u - lse_i) on real pairs, rounded to T, stored for what follows
+    T* Aw = static_cast<T*>(const_cast<void*>(g.A));
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const float L = a.lse[((size_t)b * H + h) * NP + i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gam = R[h >> 2][4 * r + (h & 3)];
+        const float bet = R[(H + h) >> 2][4 * r + ((H + h) & 3)];
+        const float u = ((S[h][r] * sc.scale) * gam + bet) * sc.gy[h] + sc.gy[H + h];
+        const bool ok = ((okb >> r) & 1u) && L != kNegInf;
+        Av[h][r] = ok ? Num<T>::rnd(__expf(u - L)) : 0.f;
+        const int j = j0 + 4 * lg + r;
+        if (i < n && j < n) Num<T>::st(Aw + (((size_t)b * H + h) * n + i) * n + j, Av[h][r]);
+      }
+    }
+  }
   // (4) the softmax backward per pair and head
   float dA[H][4];
 #pragma unroll
@@ -1414,7 +1436,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
     if (lg == 0) red_s[w][h][li] = part;
   }
   __syncthreads();
-  if constexpr (PM == kPairPart) {
+  if constexpr (PM == kPairPart || PM == kPairPartA) {
     // this key block's part of D for the 16 queries
     if (tid < H * 16) {
       const int h = tid >> 4, q = tid & 15, iq = i - li + q;
@@ -2234,10 +2256,13 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
                       (size_t)a.B * H * a.NP * DH + (size_t)3 * D * D + 3 * D;
   const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
-  if (a.NP <= 64) {
+  const int KB = (a.NP + 63) / 64;
+  if (g.recompute_a) {  // two-pass context: A recomputed (and stored) by the first pass
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairPartA>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
+  } else if (a.NP <= 64) {
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairAll>), dim3(JT, a.B, 1), dim3(kThreads), 0, s, a, g);
   } else {  // key blocks of 64: the row sums of D first, then the rest
-    const int KB = (a.NP + 63) / 64;
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairPart>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
   }

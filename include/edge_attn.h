@@ -175,14 +175,16 @@ ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_
  * Network for Graph Generation", full-text summary: FiLM-modulated scaled
  * dot-product scores, mask, normalized softmax, A [V | I], E' = E + W_e A +
  * b_e), with the forward's stored A (bfloat16 mode: its rounding points pass
- * gradients through unchanged). Supported: single-pass contexts (n <=
- * EA_SINGLE_PASS_MAX_N, B n_p^2 < 2^31 with n_p = n rounded up to 16), no
- * variant flag, bfloat16 for both built shapes and float32 for (4, 16, 16)
- * (else EA_E_UNSUPPORTED).
+ * gradients through unchanged). Supported: B n_p^2 < 2^31 (n_p = n rounded
+ * up to 16), no variant flag, bfloat16 for both built shapes and float32 for
+ * (4, 16, 16) (else EA_E_UNSUPPORTED). Two-pass contexts store no A: the
+ * backward recomputes it, exp(u - lse) from the forward's row statistics, in
+ * its own workspace, and the A argument is ignored (may be NULL).
  *
  * Needs a preceding edge_attn_layer or edge_attn_forward on this context with
- * the same inputs, parameters, ws and stream (its Q, K, V and global FiLM
- * stay in ws), and that call's A (else EA_E_STATE). dO [B, n, d] and dE_out
+ * the same inputs, parameters, ws and stream (its Q, K, V, global FiLM and,
+ * two-pass, row statistics stay in ws), and, single-pass, that call's A
+ * (else EA_E_STATE). dO [B, n, d] and dE_out
  * [B, n, n, de] are in the context's dtype, and so are the outputs dX
  * [B, n, d], dE [B, n, n, de] and dy [B, dy]. Weight gradients are float32,
  * in the parameters' layouts, overwritten (not accumulated). bws is the

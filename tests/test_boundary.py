@@ -218,7 +218,7 @@ def test_backward_rules(lib):
         return lib.edge_attn_backward(ctx, ctypes.byref(p), ctypes.byref(u), FAKE, FAKE, FAKE, FAKE, FAKE,
                                       FAKE, FAKE, FAKE, FAKE, FAKE, k.get("g", ctypes.byref(g)), FAKE, 1 << 40,
                                       k.get("bws", FAKE), k.get("bwsb", 1 << 40), None)
-    for kw in (dict(flags=L.EA_VARIANT_LIGHT_EDGE), dict(n=300),
+    for kw in (dict(flags=L.EA_VARIANT_LIGHT_EDGE),
                dict(d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_FP32)):
         st, ctx = create(lib, make_desc(**kw))
         assert st == L.EA_OK
@@ -231,10 +231,11 @@ def test_backward_rules(lib):
     assert bwd(ctx, bwsb=16) == L.EA_E_WORKSPACE
     assert bwd(ctx) == L.EA_E_STATE  # no forward on this context yet
     lib.ea_ctx_destroy(ctx)
-    st, ctx = create(lib, make_desc(n=200, B=3))  # single pass with several key blocks: supported
-    assert st == L.EA_OK
-    assert bwd(ctx) == L.EA_E_STATE
-    lib.ea_ctx_destroy(ctx)
+    for kw in (dict(n=200, B=3), dict(n=300), dict(flags=L.EA_FORCE_TWO_PASS)):  # several key blocks / two-pass
+        st, ctx = create(lib, make_desc(**kw))
+        assert st == L.EA_OK
+        assert bwd(ctx) == L.EA_E_STATE, kw
+        lib.ea_ctx_destroy(ctx)
 
 
 def test_block_rules(lib):

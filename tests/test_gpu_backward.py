@@ -29,9 +29,9 @@ def dims_of(name, **over):
     return dataclasses.replace(W.CONFIGS[name].dims, **over)
 
 
-def run_backward(batch, dims, seed=0):
+def run_backward(batch, dims, seed=0, force_two_pass=False):
     dt = HX.tdtype(dims.dtype)
-    run = HX.Run(batch, dims)
+    run = HX.Run(batch, dims, force_two_pass=force_two_pass)
     run.fused()
     B, n, d, de, H, dy = dims.B, dims.n, dims.d, dims.de, dims.H, dims.dy
     rng = np.random.default_rng(seed)
@@ -123,4 +123,30 @@ def test_backward_several_key_blocks(n, dtype, B):
     mask[0] = 1
     batch["mask"] = mask
     got, ref = run_backward(batch, dims, seed=n)
+    check(got, ref, batch, dims)
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"dtype": "bf16"}), ("planar", {"B": 2, "n": 100})],
+                         ids=["tiny-fp32", "tiny-bf16", "n100-bf16"])
+def test_backward_forced_two_pass(name, over):
+    """Two-pass contexts keep no A: the backward recomputes it as exp(u - lse)
+    from the forward's row statistics (forced two-pass at small n)."""
+    dims = dims_of(name, **over)
+    batch = W.make_batch(name, bias_scale=0.1, dims=dims)
+    if "n" in over:
+        rng = np.random.default_rng(7)
+        mask = (rng.random((dims.B, dims.n)) < 0.8).astype(np.uint8)
+        mask[0] = 1
+        batch["mask"] = mask
+    got, ref = run_backward(batch, dims, force_two_pass=True)
+    check(got, ref, batch, dims)
+
+
+def test_backward_natural_two_pass_n300():
+    """n = 300 > 256: the layer runs two passes, the backward recomputes A."""
+    dims = dims_of("planar", B=1, n=300)
+    batch = W.make_batch("planar", bias_scale=0.1, dims=dims)
+    rng = np.random.default_rng(300)
+    batch["mask"] = (rng.random((1, 300)) < 0.85).astype(np.uint8)
+    got, ref = run_backward(batch, dims, seed=3)
     check(got, ref, batch, dims)
