@@ -56,7 +56,9 @@ def parse():
 
 def backward_bench(args, cfg, dims, batch):
     """Training step of the layer: edge_attn_layer then edge_attn_backward, on
-    buffer sets rotated so that every step reads from HBM."""
+    buffer sets rotated so that every step reads from HBM (two buffer sets:
+    at the large shape one set holds several GB). Two-pass shapes store no A;
+    the backward recomputes it."""
     import torch
     from edge_aware_graph_amd.layer import EdgeAttention
     dev = torch.device("cuda:0")
@@ -70,7 +72,8 @@ def backward_bench(args, cfg, dims, batch):
         sets.append(dict(
             X=torch.from_numpy(batch["X"]).to(dev, dt), E=torch.from_numpy(batch["E"]).to(dev, dt),
             y=torch.from_numpy(batch["y"]).to(dev, dt), m=torch.from_numpy(batch["mask"]).to(dev),
-            O=torch.empty(B, n, d, dtype=dt, device=dev), A=torch.empty(B, H, n, n, dtype=dt, device=dev),
+            O=torch.empty(B, n, d, dtype=dt, device=dev),
+            A=None if layer.two_pass else torch.empty(B, H, n, n, dtype=dt, device=dev),
             Eo=torch.empty(B, n, n, de, dtype=dt, device=dev),
             dO=torch.from_numpy(rng.standard_normal((B, n, d)).astype(np.float32)).to(dev, dt),
             dEp=torch.from_numpy(rng.standard_normal((B, n, n, de)).astype(np.float32)).to(dev, dt),
@@ -101,7 +104,7 @@ def backward_bench(args, cfg, dims, batch):
     prof = layer.profile_end()
     kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
     bwd_name = [k for k in kernels if k.startswith("backward")][0]
-    alg = algorithmic_bytes("backward", dims, batch["n_real"], False)
+    alg = algorithmic_bytes("backward", dims, batch["n_real"], layer.two_pass)
     bwd_us = kernels[bwd_name]["avg_us"]
     return {
         "metric": "graphs/s per training step of the layer (forward + backward)",
@@ -257,10 +260,12 @@ def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
         params = (3 * d * d + 2 * de * fe + dims.dy * (2 * dims.dy + d + de)) * s
         return 3 * rows * d * s + e_read + e_write + params
     if kernel == "backward":
-        # E and dE' read (real pairs), dE written, A read; X and dO read, dX
-        # written; Q, K, V read back from the workspace; the projection
-        # weights read and their float32 gradients written
-        return 2 * e_read + e_write + a_io + 3 * rows * d * s + qkv + 3 * d * d * (s + 4)
+        # E and dE' read (real pairs), dE written, A read (two-pass: lse
+        # read, A recomputed from E, Q and K); X and dO read, dX written;
+        # Q, K, V read back from the workspace; the projection weights read
+        # and their float32 gradients written
+        return (2 * e_read + e_write + (lse if two_pass else a_io) + 3 * rows * d * s + qkv +
+                3 * d * d * (s + 4))
     raise ValueError(kernel)
 
 
