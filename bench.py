@@ -50,7 +50,7 @@ def parse():
                     help="time the graph-transformer block around the layer (layer + node, edge and y paths)")
     ap.add_argument("--sampling-layers", type=int, default=0,
                     help="instead of single layers, time denoising steps of this many stacked layers "
-                         "(a step is then one pass through all of them)")
+                         "(a step is then one pass through all of them; with --block, whole blocks)")
     return ap.parse_args()
 
 
@@ -183,7 +183,9 @@ def block_bench(args, cfg, dims, batch):
 
 def sampling_bench(args, cfg, dims, batch):
     """Stacked-layer sampling loop: each timed step runs L layers with their own
-    random weights, O and E' of a layer feeding the next (same batch, HBM-resident)."""
+    random weights, O and E' of a layer feeding the next (same batch,
+    HBM-resident). With --block every layer is a whole graph-transformer
+    block (X2, E2 and y2 feed the next one)."""
     import torch
     from edge_aware_graph_amd import workloads as W
     from edge_aware_graph_amd.sampling import SamplingLoop
@@ -194,7 +196,11 @@ def sampling_bench(args, cfg, dims, batch):
     for k in range(L):
         wb = W.make_batch(cfg.name, seed=1000 + k, bias_scale=0.0)
         weights.append({kk: torch.from_numpy(v).to(dev, dt) for kk, v in wb.items() if kk.startswith("w_")})
-    loop = SamplingLoop(dims, weights)
+    bps = None
+    if args.block:
+        bps = [{kk: torch.from_numpy(v).to(dev, dt) for kk, v in W.make_block_params(dims, seed=2000 + k).items()}
+               for k in range(L)]
+    loop = SamplingLoop(dims, weights, block_params=bps)
     X0 = torch.from_numpy(batch["X"]).to(dev, dt)
     E0 = torch.from_numpy(batch["E"]).to(dev, dt)
     y0 = torch.from_numpy(batch["y"]).to(dev, dt)
@@ -208,7 +214,8 @@ def sampling_bench(args, cfg, dims, batch):
     ms_per_step = dt_s * 1e3 / args.steps
     B, n = dims.B, dims.n
     return {
-        "metric": "graphs/s per denoising step of %d stacked edge-aware attention layers" % L,
+        "metric": "graphs/s per denoising step of %d stacked %s" % (
+            L, "graph-transformer blocks" if args.block else "edge-aware attention layers"),
         "value": B / (ms_per_step * 1e-3),
         "unit": "graphs/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -216,7 +223,9 @@ def sampling_bench(args, cfg, dims, batch):
         "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded %s graphs, random Xavier weights per layer)" % cfg.structure,
         "config": {"workload": cfg.name, "B": B, "n": n, "layers": L, "two_pass": loop.layer.two_pass,
-                   "note": "a step is the L layers only (the block around the layer and the sampler are not modelled)"},
+                   "blocks": loop.blocks,
+                   "note": "a step is the L %s only (the sampler's update rule is not modelled)" % (
+                       "blocks" if loop.blocks else "attention layers")},
         "layers_per_s": L / (ms_per_step * 1e-3),
         "ms_per_layer": ms_per_step / L,
     }
