@@ -505,7 +505,8 @@ template <typename T, int D, int DE, int DY>
 __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
   constexpr int OPW = DY / kWaves;  // outputs per wave
   static_assert(DY % kWaves == 0 && DY <= kThreads && D <= kThreads && DE <= kThreads, "one feature per thread");
-  __shared__ float xbar[D], ebar[DE];
+  static_assert(kThreads % D == 0 && kThreads % DE == 0, "partial-sum groups");
+  __shared__ float xbar[D], ebar[DE], tail_x[kThreads], tail_e[kThreads];
   __shared__ float yv[DY], y1[DY], hy[DY], red4[2][kWaves];
   __shared__ int cnt;
   const int tid = threadIdx.x, b = blockIdx.x, n = k.n, w = tid >> 6, l = tid & 63;
@@ -555,20 +556,46 @@ __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
   for (int i = tid + NMK * kThreads; i < n; i += kThreads) c0 += k.mask[(size_t)b * n + i] != 0;
   atomicAdd(&cnt, c0);
   if (tid < DY) yv[tid] = yr;
+  // Partial sums past the first NPB (large graphs have up to 256 edge blocks):
+  // every thread takes feature tid % F of partials NPB + tid / F, stepping by
+  // kThreads / F, with U independent loads in flight, instead of one thread
+  // per feature walking a chain of dependent loads.
+  auto tail = [&](const float* part, int cnt, int F) {
+    constexpr int U = 8;
+    const int G = kThreads / F, f = tid % F;
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = 0.f;
+    int q = NPB + tid / F;
+    for (; q + (U - 1) * G < cnt; q += U * G) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = part[(size_t)(q + u * G) * F + f];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] += v[u];
+    }
+    for (; q < cnt; q += G) acc[0] += part[(size_t)q * F + f];
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) t += acc[u];
+    return t;
+  };
+  tail_x[tid] = tail(k.part_x + (size_t)b * k.nxb * D, k.nxb, D);
+  tail_e[tid] = tail(k.part_e + (size_t)b * k.exb * DE, k.exb, DE);
   __syncthreads();
   const float nr = (float)cnt;
   if (tid < D) {
     float sx = 0.f;
 #pragma unroll
     for (int q = 0; q < NPB; ++q) sx += q < k.nxb ? px[q] : 0.f;
-    for (int q = NPB; q < k.nxb; ++q) sx += k.part_x[((size_t)b * k.nxb + q) * D + tid];
+    for (int g = 0; g < kThreads / D; ++g) sx += tail_x[g * D + tid];
     xbar[tid] = sx / fmaxf(nr, 1.f);
   }
   if (tid < DE) {
     float se = 0.f;
 #pragma unroll
     for (int q = 0; q < NPB; ++q) se += q < k.exb ? pe[q] : 0.f;
-    for (int q = NPB; q < k.exb; ++q) se += k.part_e[((size_t)b * k.exb + q) * DE + tid];
+    for (int g = 0; g < kThreads / DE; ++g) se += tail_e[g * DE + tid];
     ebar[tid] = se / fmaxf(nr * nr, 1.f);
   }
   __syncthreads();
