@@ -116,7 +116,8 @@ def backward_bench(args, cfg, dims, batch):
         "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "H": H, "buffer_sets": len(sets)},
         # the backward's launches taken together (HIP events around the call)
         "roofline": {"kernel": bwd_name, "bound": "hbm", "achieved": alg / (bwd_us * 1e3), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": alg / (bwd_us * 1e3) / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": alg / (bwd_us * 1e3) / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("backward", cfg.name),
                      "alg_bytes_per_launch": alg, "avg_launch_us": bwd_us},
         "kernels": kernels,
     }
@@ -175,7 +176,8 @@ def block_bench(args, cfg, dims, batch):
                    "two_pass": layer.two_pass, "buffer_sets": nsets},
         # the block's own three launches taken together (HIP events around them)
         "roofline": {"kernel": bname, "bound": "hbm", "achieved": alg / (bus * 1e3), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": alg / (bus * 1e3) / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": alg / (bus * 1e3) / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("block", cfg.name),
                      "alg_bytes_per_launch": alg, "avg_launch_us": bus},
         "kernels": kernels,
     }
@@ -278,10 +280,10 @@ def algorithmic_bytes(kernel: str, dims, n_real: np.ndarray, two_pass: bool,
     raise ValueError(kernel)
 
 
-def source_digest() -> str:
-    """sha256 prefix of the layer kernels' sources, concatenated."""
+def source_digest(paths=None) -> str:
+    """sha256 prefix of kernel sources, concatenated (default: the layer's)."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in (KERNEL_SOURCES if paths is None else paths):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -289,13 +291,19 @@ def source_digest() -> str:
 
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel.split("(")[0], workload))
+    were taken on the current kernel sources (the record lists the sources it
+    was taken on, relative to the repository; the layer's by default); else
+    None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel.split("(")[0].strip(), workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != source_digest():
+    srcs = rec.get("sources")
+    paths = None if srcs is None else [os.path.join(ROOT, p) for p in srcs]
+    if paths is not None and not all(os.path.exists(p) for p in paths):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_digest(paths):
         return None
     return rec.get("hbm_bytes_per_launch")
 
