@@ -1296,10 +1296,18 @@ enum PairMode : int { kPairAll = 0, kPairPart = 1, kPairUse = 2, kPairPartA = 3 
 template <typename T, int H, int DH, int DE, int PM>
 __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs g) {
   constexpr int D = H * DH, NCH = DE / 16;
+  // Modes that write dE keep the dE' tile of step (1) in LDS for step (5)
+  // (each lane reads back its own words), so dE' crosses HBM once
+  constexpr bool kKeepDep = PM == kPairAll || PM == kPairUse;
+  constexpr int NDW = Frag<T, DE / 4>::ND;  // words of one lane's fragment
+  constexpr int NDC = NDW % 4 == 0 ? 4 : NDW;  // words per LDS access
   __shared__ float red_s[kWaves][H][16];
   __shared__ float sum_s[kWaves][4 * H];
+  __shared__ __align__(16) uint32_t dep_s[kKeepDep ? kWaves * 16 * NDW * 64 : 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, i0 = blockIdx.x * 16;
+  // word group c of key jj of this lane: 16-byte pieces of consecutive lanes side by side
+  auto dep_at = [&](int jj, int c) { return dep_s + (((w * 16 + jj) * (NDW / NDC) + c) * 64 + l) * NDC; };
   Scorer<T, H, DH, DE> sc;
   sc.setup(a, b, i0);
   const int n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, jt = kWaves * blockIdx.z + w, j0 = 16 * jt;
@@ -1376,6 +1384,20 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   {
     ETile<T, DE> dt;
     dt.load_all(dEp, b, n, i, j0, lg);
+    if constexpr (kKeepDep) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+        for (int c = 0; c < NDW / NDC; ++c) {
+          uint32_t* q = dep_at(jj, c);
+          if constexpr (NDC == 4)
+            *reinterpret_cast<u32x4*>(q) = u32x4{dt.f[jj].w[4 * c], dt.f[jj].w[4 * c + 1], dt.f[jj].w[4 * c + 2],
+                                                 dt.f[jj].w[4 * c + 3]};
+          else
+#pragma unroll
+            for (int k = 0; k < NDC; ++k) q[k] = dt.f[jj].w[NDC * c + k];
+        }
+    }
     float R2[4][16];
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
@@ -1476,18 +1498,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       sbe[h] += dbe[h][r];
     }
   }
-  // dE' rows of the first PD keys of step (5), issued before the stores below:
-  // vector memory operations complete in issue order, so a wait for a row
-  // loaded after a store would wait for that store too
-  constexpr int PD = 4;
   const size_t dErow = ((size_t)b * n + (i < n ? i : 0)) * n * DE + lg * (DE / 4);
-  auto ld_dep = [&](int jj, Frag<T, DE / 4>& f) {
-    const int j = j0 + jj;
-    f.load(i < n && j < n ? dEp + dErow + (size_t)j * DE : zeros<T>());
-  };
-  Frag<T, DE / 4> ring[PD];
-#pragma unroll
-  for (int jj = 0; jj < PD; ++jj) ld_dep(jj, ring[jj]);
   // ds and dgamma_e / dbeta_e for the (graph, head) and pair-reduction kernels
   if (tile_ok) {
 #pragma unroll
@@ -1519,8 +1530,18 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       const bool real = sc.mi && ((bits >> jj) & 1u);
       Frag<T, 4> bq;
       bq.set(&dFa[jj >> 2][4 * (jj & 3)]);
-      const Frag<T, DE / 4> ef = ring[jj % PD];
-      if (jj + PD < 16) ld_dep(jj + PD, ring[jj % PD]);  // PD keys ahead
+      Frag<T, DE / 4> ef;
+#pragma unroll
+      for (int c = 0; c < NDW / NDC; ++c) {
+        const uint32_t* q = dep_at(jj, c);
+        if constexpr (NDC == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(q);
+          ef.w[4 * c] = v.x; ef.w[4 * c + 1] = v.y; ef.w[4 * c + 2] = v.z; ef.w[4 * c + 3] = v.w;
+        } else {
+#pragma unroll
+          for (int k = 0; k < NDC; ++k) ef.w[NDC * c + k] = q[k];
+        }
+      }
       float out[DE / 4];
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
