@@ -561,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void blk_y_kernel(BlockArgs k) {
   // kThreads / F, with U independent loads in flight, instead of one thread
   // per feature walking a chain of dependent loads.
   auto tail = [&](const float* part, int cnt, int F) {
-    constexpr int U = 8;
+    constexpr int U = 16;
     const int G = kThreads / F, f = tid % F;
     float acc[U];
 #pragma unroll
