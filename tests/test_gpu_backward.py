@@ -126,6 +126,25 @@ def test_backward_several_key_blocks(n, dtype, B):
     check(got, ref, batch, dims)
 
 
+@pytest.mark.parametrize("n,dtype,n_real,two_pass", [
+    (192, "bf16", (44, 100, 187), False), (40, "fp32", (5, 20, 40), False), (100, "bf16", (9, 70), True)],
+    ids=["sbm-like-bf16", "n40-fp32", "n100-two-pass-bf16"])
+def test_backward_prefix_masks_padded_tiles(n, dtype, n_real, two_pass):
+    """SBM-style padding: graphs of n_real nodes padded to n with prefix masks,
+    so that whole 16 x 16 pair tiles hold no real pair (zeros only) next to
+    partial and full ones."""
+    B = len(n_real)
+    over = {"n": n, "B": B, "dtype": dtype}
+    dims = dims_of("tiny" if dtype == "fp32" else "planar", **over)
+    batch = W.make_batch("tiny", bias_scale=0.2, dims=dims)
+    mask = np.zeros((B, n), np.uint8)
+    for b, k in enumerate(n_real):
+        mask[b, :k] = 1
+    batch["mask"] = mask
+    got, ref = run_backward(batch, dims, seed=n + 1, force_two_pass=two_pass)
+    check(got, ref, batch, dims)
+
+
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"dtype": "bf16"}), ("planar", {"B": 2, "n": 100})],
                          ids=["tiny-fp32", "tiny-bf16", "n100-bf16"])
 def test_backward_forced_two_pass(name, over):
