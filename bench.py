@@ -289,12 +289,13 @@ def source_digest(paths=None) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload: str):
+def traffic_from_profiles(kernel: str, workload: str, profiles_dir: str = None):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they
     were taken on the current kernel sources (the record lists the sources it
     was taken on, relative to the repository; the layer's by default); else
     None."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel.split("(")[0].strip(), workload))
+    profiles_dir = os.path.join(ROOT, "profiles") if profiles_dir is None else profiles_dir
+    path = os.path.join(profiles_dir, "traffic_%s_%s.json" % (kernel.split("(")[0].strip(), workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
