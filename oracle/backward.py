@@ -59,13 +59,21 @@ class _RoundedSoftmax(torch.autograd.Function):
         return A * (g - (A * g).sum(-1, keepdim=True)), None
 
 
-def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool):
-    """Forward of the layer on float64 tensors; returns O [B,n,d], A [B,H,n,n], E' [B,n,n,de]."""
+def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool, rows=None):
+    """Forward of the layer on float64 tensors; returns O [B,n,d], A [B,H,n,n], E' [B,n,n,de].
+
+    `rows` (a list of query indices): only those query rows, with t["E"]
+    holding just their edge rows [B, R, n, de]; the outputs are then O
+    [B,R,d], A [B,H,R,n], E' [B,R,n,de]. Query row i reads E only in row i,
+    so these are exactly the full layer's rows.
+    """
     X, E, y = t["X"], t["E"], t["y"]
     B, n, d = X.shape
     dh = d // H
     m = torch.tensor(mask.astype(bool))
-    pm = m[:, :, None] & m[:, None, :]
+    mq = m if rows is None else m[:, list(rows)]
+    pm = mq[:, :, None] & m[:, None, :]
+    R = mq.shape[1]
 
     def lin(x, w, b):
         out = x @ t[w].transpose(0, 1)
@@ -76,6 +84,8 @@ def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool):
         return _st_round(P, bf16).view(B, n, H, dh).transpose(1, 2)  # [B,H,n,dh]
 
     q, k, v = proj("w_q", "b_q"), proj("w_k", "b_k"), proj("w_v", "b_v")
+    if rows is not None:
+        q = q[:, :, list(rows)]
     gy = 1.0 + lin(y, "w_ymul", "b_ymul")  # [B,H]
     by = lin(y, "w_yadd", "b_yadd")
     ge = (1.0 + lin(E, "w_emul", "b_emul")).permute(0, 3, 1, 2)  # [B,H,n,n]
@@ -83,7 +93,7 @@ def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool):
     r = 1.0 / math.sqrt(dh)
     s = (q @ k.transpose(-1, -2)) * r
     u = (s * ge + be) * gy[:, :, None, None] + by[:, :, None, None]
-    pmh = pm[:, None].expand(B, H, n, n)
+    pmh = pm[:, None].expand(B, H, R, n)
     has = pmh.any(-1, keepdim=True)
     u = torch.where(pmh, u, torch.tensor(float("-inf"), dtype=torch.float64))
     u = torch.where(has, u, torch.zeros((), dtype=torch.float64))  # rows without a real key
@@ -91,8 +101,8 @@ def layer(t: Dict[str, torch.Tensor], mask: np.ndarray, H: int, bf16: bool):
         A = _RoundedSoftmax.apply(u, pmh)
     else:
         A = torch.where(pmh, torch.softmax(u, -1), torch.zeros((), dtype=torch.float64))
-    O = (A @ v).transpose(1, 2).reshape(B, n, d)
-    O = torch.where(m[..., None], O, torch.zeros((), dtype=torch.float64))
+    O = (A @ v).transpose(1, 2).reshape(B, R, d)
+    O = torch.where(mq[..., None], O, torch.zeros((), dtype=torch.float64))
     Ep = E + lin(A.permute(0, 2, 3, 1), "w_e", "b_e")
     Ep = torch.where(pm[..., None], Ep, torch.zeros((), dtype=torch.float64))
     return O, A, Ep
@@ -119,6 +129,32 @@ def backward(batch: Dict[str, np.ndarray], dO: np.ndarray, dEp: np.ndarray, H: i
     for k, g in zip(keys, grads):
         out[k] = np.zeros(t[k].shape) if g is None else g.detach().numpy()
     return out
+
+
+def edge_grad_rows(batch: Dict[str, np.ndarray], dO: np.ndarray, dEp: np.ndarray, H: int, bf16: bool,
+                   b: int, rows: Sequence[int]) -> np.ndarray:
+    """dL/dE[b, rows, :, :] for L = sum(O * dO) + sum(E' * dEp), from the
+    layer restricted to graph b and those query rows: E[b, i] reaches L only
+    through row i's scores, softmax, O_i and E'_i, so the restricted
+    derivative is the full one. For checks at sizes the full backward cannot
+    handle; returns [len(rows), n, de]."""
+    rows = list(rows)
+    t = {}
+    for k in INPUTS + WEIGHTS:
+        v = batch.get(k)
+        if v is None:
+            t[k] = None
+            continue
+        if k == "E":
+            v = np.asarray(v)[b:b + 1][:, rows]
+        elif k in ("X", "y"):
+            v = np.asarray(v)[b:b + 1]
+        t[k] = torch.tensor(np.asarray(v, dtype=np.float64), requires_grad=k == "E")
+    O, _, Ep = layer(t, batch["mask"][b:b + 1], H, bf16, rows=rows)
+    loss = (O * torch.tensor(np.asarray(dO)[b:b + 1][:, rows].astype(np.float64))).sum() + \
+        (Ep * torch.tensor(np.asarray(dEp)[b:b + 1][:, rows].astype(np.float64))).sum()
+    (g,) = torch.autograd.grad(loss, [t["E"]])
+    return g.detach().numpy()[0]
 
 
 def forward(batch: Dict[str, np.ndarray], H: int, bf16: bool = False) -> Dict[str, np.ndarray]:

@@ -169,3 +169,44 @@ def test_backward_natural_two_pass_n300():
     batch["mask"] = (rng.random((1, 300)) < 0.85).astype(np.uint8)
     got, ref = run_backward(batch, dims, seed=3)
     check(got, ref, batch, dims)
+
+
+def test_backward_large_full_size_sampled_rows():
+    """The large configuration at its full size (B = 4, n = 1024, bfloat16; the
+    layer runs two passes and the backward recomputes A), as the training
+    benchmark launches it: dE on sampled query rows of every graph against
+    the row-restricted oracle (each row's edge gradient depends on that row
+    alone), 2e-2 of the largest reference value over the samples; every
+    gradient finite."""
+    dims = dims_of("large")
+    batch = W.make_batch("large", bias_scale=0.1)
+    run = HX.Run(batch, dims)
+    assert run.layer.two_pass
+    run.fused()
+    B, n, d, de, dy = dims.B, dims.n, dims.d, dims.de, dims.dy
+    rng = np.random.default_rng(11)
+    dO = W.bf16_round_array(rng.standard_normal((B, n, d), dtype=np.float32))
+    dEp = W.bf16_round_array(rng.standard_normal((B, n, n, de), dtype=np.float32))
+    dt = HX.tdtype(dims.dtype)
+    t_dO = torch.from_numpy(dO).to("cuda", dt)
+    t_dEp = torch.from_numpy(dEp).to("cuda", dt)
+    dX = torch.full((B, n, d), float("nan"), dtype=dt, device="cuda")
+    dE = torch.full((B, n, n, de), float("nan"), dtype=dt, device="cuda")
+    dyv = torch.full((B, dy), float("nan"), dtype=dt, device="cuda")
+    grads = {k: torch.full(tuple(batch[k].shape), float("nan"), dtype=torch.float32, device="cuda")
+             for k in GRAD_NAMES}
+    bws = torch.empty(run.layer.backward_workspace_bytes, dtype=torch.uint8, device="cuda")
+    dev = run.dev
+    run.layer.backward(dev, dev["X"], dev["E"], dev["y"], dev["mask"], None, t_dO, t_dEp, dX, dE, dyv,
+                       grads, run.ws, bws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dE).all()) and bool(torch.isfinite(dX).all()) and bool(torch.isfinite(dyv).all())
+    for k, v in grads.items():
+        assert bool(torch.isfinite(v).all()), k
+    for b in range(B):
+        rows = [0, int(rng.integers(1, n - 1)), n - 1]
+        ref = OB.edge_grad_rows(batch, dO, dEp, dims.H, True, b, rows)
+        got = dE[b, rows].float().cpu().numpy().astype(np.float64)
+        scale = max(np.abs(ref).max(), 1e-6)
+        err = np.abs(got - ref).max()
+        assert err <= 2e-2 * scale, "graph %d rows %s: max err %.3e > 2e-2 * %.3e" % (b, rows, err, scale)

@@ -547,3 +547,22 @@ def test_backward_masked_pairs_get_no_edge_gradient():
     pm = real_pairs(b["mask"])
     assert np.all(g["E"][~pm] == 0.0)
     assert np.abs(g["E"][pm]).max() > 0.1
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_backward_edge_rows_match_full_backward(bf16):
+    """dL/dE on a few query rows of one graph from the row-restricted layer
+    equals those rows of the full backward (float64, both modes), masked and
+    padded rows included: the restriction used for checks at full size."""
+    b = small_batch(seed=33, n_real=[10, 6, 1])
+    if bf16:
+        for k in list(b):
+            if k not in ("mask", "adj", "n_real"):
+                b[k] = W.bf16_round_array(b[k])
+    rng = np.random.default_rng(8)
+    dO = rng.standard_normal(b["X"].shape)
+    dEp = rng.standard_normal(b["E"].shape)
+    full = OB.backward(b, dO, dEp, H=2, bf16=bf16, wrt=("E",))["E"]
+    for gb, rows in ((0, [0, 3, 9]), (1, [2, 5, 7]), (2, [0, 4])):
+        got = OB.edge_grad_rows(b, dO, dEp, H=2, bf16=bf16, b=gb, rows=rows)
+        np.testing.assert_allclose(got, full[gb, rows], rtol=0, atol=1e-12)
