@@ -69,27 +69,46 @@ def relu(x: np.ndarray) -> np.ndarray:
     return np.where(x > 0, x, 0.0)
 
 
+def _rounder(bf16_mode: bool):
+    return bf16 if bf16_mode else (lambda v: np.asarray(v, np.float64))
+
+
+def node_path(X: np.ndarray, O: np.ndarray, bp: Dict[str, np.ndarray], bf16_mode: bool):
+    """X1 and X2 (before masking) of node rows, any leading shape; O as stored."""
+    r = _rounder(bf16_mode)
+    ln = lambda z, k: layer_norm(z, bp["ln_%s_g" % k], bp["ln_%s_b" % k])
+    X1 = ln(np.asarray(X, np.float64) + linear(O, bp["w_o"], bp["b_o"]), "x1")
+    Hx = relu(linear(r(X1), bp["w_x1"], bp["b_x1"]))
+    X2 = ln(X1 + linear(r(Hx), bp["w_x2"], bp["b_x2"]), "x2")
+    return X1, Hx, X2
+
+
+def edge_path(Ep: np.ndarray, bp: Dict[str, np.ndarray], bf16_mode: bool):
+    """E1 and E2 (before masking) of edge tokens, any leading shape; E' as stored."""
+    r = _rounder(bf16_mode)
+    ln = lambda z, k: layer_norm(z, bp["ln_%s_g" % k], bp["ln_%s_b" % k])
+    E1 = ln(Ep, "e1")
+    He = relu(linear(r(E1), bp["w_e1"], bp["b_e1"]))
+    E2 = ln(E1 + linear(r(He), bp["w_e2"], bp["b_e2"]), "e2")
+    return E1, He, E2
+
+
 def block(batch: Dict[str, np.ndarray], bp: Dict[str, np.ndarray], H: int, bf16_mode: bool = False,
           layer_out: Dict[str, np.ndarray] = None) -> Dict[str, np.ndarray]:
     """The block on a batch; returns X2 [B,n,d], E2 [B,n,n,de], y2 [B,dy] and
     the intermediates (O, Ep, X1, Hx, E1, He, xbar, ebar, y1)."""
     f = layer_out if layer_out is not None else _layer.forward(batch, H, bf16_mode)
-    r = bf16 if bf16_mode else (lambda v: np.asarray(v, np.float64))
+    r = _rounder(bf16_mode)
     O, Ep = r(f["O"]), r(f["Ep"])
     m = batch["mask"].astype(bool)
     pm = m[:, :, None] & m[:, None, :]
-    X = np.asarray(batch["X"], np.float64)
     y = np.asarray(batch["y"], np.float64)
     ln = lambda z, k: layer_norm(z, bp["ln_%s_g" % k], bp["ln_%s_b" % k])
 
-    X1 = ln(X + linear(O, bp["w_o"], bp["b_o"]), "x1")
-    Hx = relu(linear(r(X1), bp["w_x1"], bp["b_x1"]))
-    X2 = ln(X1 + linear(r(Hx), bp["w_x2"], bp["b_x2"]), "x2")
+    X1, Hx, X2 = node_path(batch["X"], O, bp, bf16_mode)
     X2 = np.where(m[..., None], X2, 0.0)
 
-    E1 = ln(Ep, "e1")
-    He = relu(linear(r(E1), bp["w_e1"], bp["b_e1"]))
-    E2 = ln(E1 + linear(r(He), bp["w_e2"], bp["b_e2"]), "e2")
+    E1, He, E2 = edge_path(Ep, bp, bf16_mode)
     E2 = np.where(pm[..., None], E2, 0.0)
 
     nr = m.sum(1).astype(np.float64)
@@ -100,3 +119,22 @@ def block(batch: Dict[str, np.ndarray], bp: Dict[str, np.ndarray], H: int, bf16_
     y2 = ln(y1 + linear(Hy, bp["w_y2"], bp["b_y2"]), "y2")
     return {"X2": X2, "E2": E2, "y2": y2, "O": O, "Ep": Ep, "X1": X1, "Hx": Hx, "E1": E1, "He": He,
             "xbar": xbar, "ebar": ebar, "y1": y1}
+
+
+def block_rows(batch: Dict[str, np.ndarray], bp: Dict[str, np.ndarray], H: int, bf16_mode: bool,
+               rows) -> Dict[str, np.ndarray]:
+    """X2 [R,d] and E2 [R,n,de] of the given (b, i) rows: node row i depends
+    on its own O row and X row, edge token (i, j) on E'_ij alone, so only the
+    layer's rows are needed (for checks at sizes the whole block cannot be
+    computed); y2 needs every row and is not returned."""
+    f = _layer.forward(batch, H, bf16_mode, rows=rows)
+    r = _rounder(bf16_mode)
+    rb = np.array([q[0] for q in f["rows"]])
+    ri = np.array([q[1] for q in f["rows"]])
+    m = batch["mask"].astype(bool)
+    mi = m[rb, ri]
+    pm = mi[:, None] & m[rb]
+    _, _, X2 = node_path(np.asarray(batch["X"])[rb, ri], r(f["O"]), bp, bf16_mode)
+    _, _, E2 = edge_path(r(f["Ep"]), bp, bf16_mode)
+    return {"rows": f["rows"], "X2": np.where(mi[:, None], X2, 0.0), "E2": np.where(pm[..., None], E2, 0.0)}
+

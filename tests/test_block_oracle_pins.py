@@ -182,3 +182,25 @@ def test_widths():
         assert bp["w_x1"].shape == (dims.d, dims.d)
         assert bp["w_e1"].shape == (2 * dims.de, dims.de) and bp["w_e2"].shape == (dims.de, 2 * dims.de)
         assert bp["w_y1"].shape == (dims.dy, dims.dy)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_block_rows_match_the_whole_block(bf16):
+    """The row-restricted block (node path of the row, edge path of the row's
+    tokens) equals those rows of the whole block, masked rows included."""
+    cfg = W.CONFIGS["tiny"]
+    mask = np.ones((cfg.dims.B, cfg.dims.n), np.uint8)
+    mask[1, 9:] = 0
+    _, batch = _tiny(seed=17, mask=mask)
+    if bf16:
+        for k in list(batch):
+            if k not in ("mask", "adj", "n_real"):
+                batch[k] = W.bf16_round_array(batch[k])
+    bp = _params(cfg)
+    full = OBK.block(batch, bp, cfg.dims.H, bf16)
+    rows = [(0, 0), (0, 7), (1, 3), (1, 10), (1, 11)]
+    part = OBK.block_rows(batch, bp, cfg.dims.H, bf16, rows)
+    rb = np.array([r[0] for r in part["rows"]])
+    ri = np.array([r[1] for r in part["rows"]])
+    np.testing.assert_allclose(part["X2"], full["X2"][rb, ri], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(part["E2"], full["E2"][rb, ri], rtol=0, atol=1e-12)

@@ -120,3 +120,41 @@ def test_block_natural_two_pass_n300():
     bp = W.make_block_params(dims, seed=11)
     got, ref = run_block(batch, dims, bp)
     check(got, ref, batch, dims)
+
+
+def test_block_large_full_size_sampled_rows():
+    """The large configuration at its full size (B = 4, n = 1024, bfloat16,
+    two-pass layer) with the benchmark's parameters (unit gains, zero shifts
+    and biases): X2 rows and the E2 tokens of those rows against the
+    row-restricted block oracle; y2, which needs every row, by what the
+    final normalization fixes (zero mean and unit variance per graph, within
+    bfloat16 output rounding); every output finite."""
+    dims = dims_of("large")
+    batch = W.make_batch("large", bias_scale=0.1)
+    bp = W.make_block_params(dims, seed=21, scale=0.0)
+    dt = HX.tdtype(dims.dtype)
+    run = HX.Run(batch, dims)
+    assert run.layer.two_pass
+    tbp = {k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to("cuda", dt) for k, v in bp.items()}
+    B, n, d, de, dy = dims.B, dims.n, dims.d, dims.de, dims.dy
+    ws = torch.empty(run.layer.block_workspace_bytes, dtype=torch.uint8, device="cuda")
+    X_out = torch.full((B, n, d), float("nan"), dtype=dt, device="cuda")
+    E_out = torch.full((B, n, n, de), float("nan"), dtype=dt, device="cuda")
+    y_out = torch.full((B, dy), float("nan"), dtype=dt, device="cuda")
+    dev = run.dev
+    run.layer.block(dev, tbp, dev["X"], dev["E"], dev["y"], dev["mask"], X_out, E_out, y_out, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(E_out).all()) and bool(torch.isfinite(X_out).all())
+    rows = HX.sample_rows(batch, 24, seed=2)
+    ref = OBK.block_rows(batch, bp, dims.H, True, rows)
+    rb = torch.tensor([r[0] for r in ref["rows"]], device="cuda")
+    ri = torch.tensor([r[1] for r in ref["rows"]], device="cuda")
+    gx = X_out[rb, ri].float().cpu().numpy().astype(np.float64)
+    ge = E_out[rb, ri].float().cpu().numpy().astype(np.float64)
+    for name, g, want in (("X2", gx, ref["X2"]), ("E2", ge, ref["E2"])):
+        err = np.abs(g - want).max()
+        assert err <= HX.BF16_ABS_TOL, "%s: max err %.3e > %.3e" % (name, err, HX.BF16_ABS_TOL)
+    y2 = y_out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(y2).all()
+    np.testing.assert_allclose(y2.mean(-1), 0.0, atol=2e-2)
+    np.testing.assert_allclose(y2.var(-1), 1.0, atol=5e-2)
