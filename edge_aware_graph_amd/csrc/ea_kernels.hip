@@ -1178,7 +1178,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
     float u[H][4];
     if constexpr (kKeepE) {
       // S first, so that K and Q are dead while the E tile and the FiLM rows
-      // are live (two waves per SIMD fit in the register file)
+      // are live (fewer registers live at once; the E tile alone takes 128)
       f32x4 S[H];
       sc.qk(kf, S);
       __builtin_amdgcn_sched_barrier(0);
