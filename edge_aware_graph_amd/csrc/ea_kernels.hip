@@ -2289,7 +2289,9 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   }
   hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B, (a.NP + 63) / 64), dim3(kThreads), 0, s, a, g);
   const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
-  const unsigned red_blocks = (unsigned)(chunks < 512 ? chunks : 512);  // atomics per output: one per block
+  // 1024 blocks: four per CU (the LDS fits four), all resident; each output
+  // takes one atomic add per block, spread over the 32 copies
+  const unsigned red_blocks = (unsigned)(chunks < 1024 ? chunks : 1024);
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);
   // dW: the rows (contraction) split in slices of at least 256
   const int rows = a.B * a.NP, ksplit = rows / 256 < 1 ? 1 : (rows / 256 > 16 ? 16 : rows / 256);
