@@ -1248,16 +1248,43 @@ __device__ __forceinline__ void store4(T* p, const float* v) {
 template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs g) {
   const int NP = a.NP;
-  constexpr int D = H * DH;
-  // the pair reduction's copies, the FiLM-bias gradients (b_emul, b_eadd),
-  // and the global FiLM's weight and bias gradients, all summed atomically
+  constexpr int D = H * DH, EPC = 16 / (int)sizeof(T);
+  // The first B H ceil(NP / 64) blocks: V rows from V^T through LDS, one
+  // (graph, head, 64 keys) tile each, 16-byte reads and writes on both sides
+  const int JB = (NP + 63) / 64, nvt = a.B * H * JB;
+  if ((int)blockIdx.x < nvt) {
+    __shared__ __align__(16) T vt_s[DH][64 + EPC];
+    const int bh = blockIdx.x / JB, j0 = (blockIdx.x % JB) * 64;
+    const T* src = static_cast<const T*>(a.Vt) + (size_t)bh * DH * NP;
+    // NP is a multiple of 16: a chunk of EPC keys is wholly inside or outside
+    for (int c = threadIdx.x; c < DH * 64 / EPC; c += kThreads) {
+      const int t = c / (64 / EPC), jj = (c % (64 / EPC)) * EPC;
+      if (j0 + jj < NP)
+        *reinterpret_cast<u32x4*>(&vt_s[t][jj]) = *reinterpret_cast<const u32x4*>(src + (size_t)t * NP + j0 + jj);
+    }
+    __syncthreads();
+    T* dst = static_cast<T*>(g.Vr) + (size_t)bh * NP * DH;
+    for (int c = threadIdx.x; c < 64 * DH / EPC; c += kThreads) {
+      const int jj = c / (DH / EPC), t0 = (c % (DH / EPC)) * EPC;
+      if (j0 + jj < NP) {
+        __align__(16) T v[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) v[e] = vt_s[t0 + e][jj];
+        *reinterpret_cast<u32x4*>(dst + (size_t)(j0 + jj) * DH + t0) = *reinterpret_cast<const u32x4*>(v);
+      }
+    }
+    return;
+  }
+  // The other blocks zero what is summed atomically: the pair reduction's
+  // copies, the FiLM-bias gradients (b_emul, b_eadd), the global FiLM's
+  // weight and bias gradients, and the projection weight and bias gradients
   const size_t nred = (size_t)kRedCopies * (3 * H * DE + DE), nzy = (size_t)2 * H * a.dy + 2 * H;
   const size_t nz1 = nred + 2 * H + nzy, nz2 = (size_t)a.B * 2 * H;
-  const size_t nv = (size_t)a.B * H * NP * DH, nw = (size_t)3 * D * D + 3 * D;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nz1 + nz2 + nv + nw; k += stride) {
-    if (k >= nz1 + nz2 + nv) {  // projection weight and bias gradients
-      const size_t q = k - nz1 - nz2 - nv;
+  const size_t nw = (size_t)3 * D * D + 3 * D;
+  const size_t stride = (size_t)(gridDim.x - nvt) * blockDim.x;
+  for (size_t k = (size_t)(blockIdx.x - nvt) * blockDim.x + threadIdx.x; k < nz1 + nz2 + nw; k += stride) {
+    if (k >= nz1 + nz2) {  // projection weight and bias gradients
+      const size_t q = k - nz1 - nz2;
       if (q < (size_t)3 * D * D) (q < (size_t)D * D ? g.gw_q : q < (size_t)2 * D * D ? g.gw_k : g.gw_v)[q % ((size_t)D * D)] = 0.f;
       else (q - 3 * D * D < D ? g.gb_q : q - 3 * D * D < 2 * D ? g.gb_k : g.gb_v)[(q - 3 * D * D) % D] = 0.f;
     } else if (k < nz1) {
@@ -1273,12 +1300,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
       if (q < (size_t)H * a.dy) { g.gw_ya[q] = 0.f; continue; }
       q -= (size_t)H * a.dy;
       (q < (size_t)H ? g.gb_ym : g.gb_ya)[q % H] = 0.f;
-    } else if (k < nz1 + nz2) {
-      g.DGY[k - nz1] = 0.f;
     } else {
-      const size_t q = k - nz1 - nz2;  // Vr index ((b H + h) NP + j) DH + t
-      const size_t t = q % DH, j = (q / DH) % NP, bh = q / ((size_t)DH * NP);
-      static_cast<T*>(g.Vr)[q] = static_cast<const T*>(a.Vt)[(bh * DH + t) * NP + j];
+      g.DGY[k - nz1] = 0.f;
     }
   }
 }
@@ -2273,9 +2296,11 @@ template <typename T, int H, int DH, int DE>
 hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
   constexpr int D = H * DH;
   const int JT = a.NP / 16;
-  const size_t prep = (size_t)kRedCopies * (3 * H * DE + DE) + 2 * H + (size_t)2 * H * a.dy + 2 * H + (size_t)a.B * 2 * H +
-                      (size_t)a.B * H * a.NP * DH + (size_t)3 * D * D + 3 * D;
-  const unsigned prep_blocks = (unsigned)((prep + kThreads - 1) / kThreads < 2048 ? (prep + kThreads - 1) / kThreads : 2048);
+  // prep: B H ceil(NP / 64) transpose tiles, then blocks zeroing the atomic sums
+  const size_t nzero = (size_t)kRedCopies * (3 * H * DE + DE) + 2 * H + (size_t)2 * H * a.dy + 2 * H +
+                       (size_t)a.B * 2 * H + (size_t)3 * D * D + 3 * D;
+  const size_t zblocks = (nzero + kThreads - 1) / kThreads < 1024 ? (nzero + kThreads - 1) / kThreads : 1024;
+  const unsigned prep_blocks = (unsigned)((size_t)a.B * H * ((a.NP + 63) / 64) + zblocks);  // < 2^31 for n <= 2^20
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
   const int KB = (a.NP + 63) / 64;
   if (g.recompute_a) {  // two-pass context: A recomputed (and stored) by the first pass
