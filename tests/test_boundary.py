@@ -273,3 +273,18 @@ def test_block_rules(lib):
         assert blk(ctx, wsb=wsb - 1) == L.EA_E_WORKSPACE
         assert "block" in lib.ea_kernel_name(L.KERNELS.index("block (node, edge, y kernels)")).decode()
         lib.ea_ctx_destroy(ctx)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built HIP library the binding raises."""
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        L.load_library(str(tmp_path / "libedge_attn.so"))
+
+
+def test_sampling_loop_checks_block_parameters():
+    from edge_aware_graph_amd import workloads as W
+    from edge_aware_graph_amd.sampling import SamplingLoop
+    dims = W.CONFIGS["tiny"].dims
+    with pytest.raises(ValueError, match="one set of block parameters per layer"):
+        SamplingLoop(dims, [{}], device="cpu", block_params=[{}, {}])
