@@ -2,12 +2,14 @@
 the definition, pinned by finite differences of the C oracle).
 
 Tolerances, per tensor, relative to the tensor's largest reference value:
-float32 1e-4 (the layer's float32 tolerance); bfloat16 2e-2. In bfloat16 the
-GPU takes the softmax Jacobian at the stored (rounded) A where the oracle
-takes it at the unrounded softmax, rounds dO . V-side and FiLM-side
-intermediates to bfloat16 as MFMA operands, and stores dX, dE and dy in
-bfloat16: each step is a relative error of about 2^-8, a few of them in a
-chain. Masked pairs' dE and padded rows' dX are +0.0 bit-exactly.
+float32 1e-4 (the layer's float32 tolerance); bfloat16 2e-2. In bfloat16 both
+sides take the softmax Jacobian at the stored (rounded) A (the oracle's
+reading, pinned on the CPU against torch's softmax backward handed that A and
+against finite differences where the rounding is exact); the GPU also rounds
+dO . V-side and FiLM-side intermediates to bfloat16 as MFMA operands and
+stores dX, dE and dy in bfloat16: each step is a relative error of about
+2^-8, a few of them in a chain. Masked pairs' dE and padded rows' dX are +0.0
+bit-exactly.
 """
 import dataclasses
 

@@ -566,3 +566,181 @@ def test_backward_edge_rows_match_full_backward(bf16):
     for gb, rows in ((0, [0, 3, 9]), (1, [2, 5, 7]), (2, [0, 4])):
         got = OB.edge_grad_rows(b, dO, dEp, H=2, bf16=bf16, b=gb, rows=rows)
         np.testing.assert_allclose(got, full[gb, rows], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------- bfloat16 softmax Jacobian of the backward oracle
+
+def _rounded_softmax_grad(u, pm, g):
+    """Gradient of sum(A * g) with respect to u through the oracle's bfloat16
+    softmax, and the stored (rounded) A."""
+    ut = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+    A = OB._RoundedSoftmax.apply(ut, torch.tensor(pm))
+    (gu,) = torch.autograd.grad((A * torch.tensor(g, dtype=torch.float64)).sum(), [ut])
+    return gu.numpy(), A.detach()
+
+
+def test_bf16_softmax_backward_is_library_jacobian_at_stored_output():
+    """The bfloat16-mode softmax backward is the softmax vector-Jacobian
+    product taken at the stored, rounded A: torch's own softmax backward
+    routine, handed that output tensor, gives the same values. Logits are
+    generic (bfloat16 rounding of A is inexact), rows include masked keys and
+    a row with no real key (A = 0, no gradient). The same routine handed the
+    unrounded softmax differs measurably, so the test tells the two readings
+    apart."""
+    rng = np.random.default_rng(71)
+    B, H, n = 2, 3, 9
+    u = rng.standard_normal((B, H, n, n)) * 2.0
+    mask = np.ones((B, n), bool)
+    mask[0, 6:] = False
+    mask[1, [1, 4]] = False
+    pm = mask[:, None, :, None] & mask[:, None, None, :]
+    pm = np.broadcast_to(pm, (B, H, n, n)).copy()
+    pm[1, :, 2, :] = False          # a query row with no real key
+    u = np.where(pm, u, -np.inf)                     # as the layer feeds them: -inf off the mask,
+    u = np.where(pm.any(-1, keepdims=True), u, 0.0)  # rows without a real key all 0
+    g = rng.standard_normal(u.shape)
+    got, A = _rounded_softmax_grad(u, pm, g)
+    lib = torch._softmax_backward_data(torch.tensor(g), A, -1, torch.float64).numpy()
+    np.testing.assert_allclose(got, lib, rtol=0, atol=1e-14)
+    assert np.all(got[~pm] == 0.0)
+    assert np.all(got[1, :, 2, :] == 0.0)
+    exact = torch.where(torch.tensor(pm), torch.softmax(torch.tensor(u), -1), torch.zeros((), dtype=torch.float64))
+    at_exact = torch._softmax_backward_data(torch.tensor(g), exact, -1, torch.float64).numpy()
+    assert np.abs(at_exact - got).max() > 1e-4
+
+
+def _softmax_np(v):
+    e = np.exp(v - v.max())
+    return e / e.sum()
+
+
+@pytest.mark.parametrize("probs", [[0.25, 0.75], [0.125, 0.375, 0.25, 0.25], [0.5, 0.25, 0.125, 0.125],
+                                   [1 / 8.0] * 8, [1.0]])
+def test_bf16_softmax_backward_equals_finite_differences_where_rounding_is_exact(probs):
+    """Where the softmax is dyadic (two keys with logit gap ln 3 give 1/4 and
+    3/4; uniform rows over 2^k keys give 2^-k), bfloat16 rounding of A is
+    exact, so the bfloat16-mode backward must be the true derivative of the
+    softmax: central differences of a plain numpy softmax, one logit at a
+    time. A padded key (masked) gets no gradient."""
+    k = len(probs)
+    n = k + 1
+    u = np.full((1, 1, 1, n), -np.inf)
+    u[0, 0, 0, :k] = np.log(np.asarray(probs)) + 0.37
+    pm = np.zeros((1, 1, 1, n), bool)
+    pm[..., :k] = True
+    rng = np.random.default_rng(72 + k)
+    g = rng.standard_normal(u.shape)
+    got, A = _rounded_softmax_grad(u, pm, g)
+    np.testing.assert_array_equal(A.numpy()[0, 0, 0, :k], np.asarray(probs))  # rounding is exact here
+    h = 1e-6
+    for j in range(k):
+        up, um = u[0, 0, 0, :k].copy(), u[0, 0, 0, :k].copy()
+        up[j] += h
+        um[j] -= h
+        fd = ((_softmax_np(up) - _softmax_np(um)) / (2 * h) * g[0, 0, 0, :k]).sum()
+        assert abs(fd - got[0, 0, 0, j]) <= 1e-8, (j, fd, got[0, 0, 0, j])
+    assert got[0, 0, 0, k] == 0.0
+
+
+def _dyadic_batch():
+    """A tiny batch on which every bfloat16 rounding point of the layer is
+    exact: X, W_q, W_k, W_v and their biases are multiples of 1/4 small
+    enough that Q, K and V are bfloat16 values; gamma_e = 1 and gamma_y = 2;
+    E is chosen so that each real row's logits are logarithms of dyadic
+    probabilities (1/8, 3/8, 1/4, 1/4 and permutations; 1/4 and 3/4 for two
+    keys; uniform), so the softmax rounds to itself. Q and K are not zero, so
+    the score path (dQ, dK, dgamma_e) carries gradient too."""
+    rng = np.random.default_rng(81)
+    B, n, H, dh, de, dy = 2, 5, 2, 2, 3, 2
+    d = H * dh
+    q4 = lambda shape, lo, hi: (rng.integers(lo, hi + 1, size=shape) / 4.0).astype(np.float64)
+    b = {"mask": np.zeros((B, n), np.uint8)}
+    b["mask"][0, :4] = 1
+    b["mask"][1, :2] = 1
+    X = rng.integers(-1, 2, size=(B, n, d)).astype(np.float64)
+    X[b["mask"] == 0] = 0.0
+    for w in ("q", "k", "v"):
+        b["w_" + w] = q4((d, d), -4, 4)
+        b["b_" + w] = q4((d,), -2, 2)
+    b["w_emul"] = np.zeros((H, de))
+    b["b_emul"] = np.zeros(H)
+    b["w_eadd"] = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0]])
+    b["b_eadd"] = np.array([0.25, -0.5])
+    b["y"] = np.ones((B, dy))
+    b["w_ymul"] = np.array([[0.5, -0.5], [0.25, -0.25]])   # y . w_ymul = 0
+    b["b_ymul"] = np.ones(H)                                  # gamma_y = 2
+    b["w_yadd"] = q4((H, dy), -2, 2)
+    b["b_yadd"] = q4((H,), -2, 2)
+    b["w_e"] = q4((de, H), -4, 4)
+    b["b_e"] = q4((de,), -2, 2)
+    # scores s = q_i . k_j / sqrt(dh) of the real pairs (float64)
+    m = b["mask"].astype(bool)
+    Q = np.where(m[..., None], X @ b["w_q"].T + b["b_q"], 0.0).reshape(B, n, H, dh)
+    K = np.where(m[..., None], X @ b["w_k"].T + b["b_k"], 0.0).reshape(B, n, H, dh)
+    V = np.where(m[..., None], X @ b["w_v"].T + b["b_v"], 0.0)
+    for T in (Q, K, V):
+        assert np.array_equal(W.bf16_round_array(T.astype(np.float32)), T)  # bfloat16 values
+    s = np.einsum("bihd,bjhd->bhij", Q, K) / math.sqrt(dh)
+    rows4 = [np.log([1, 3, 2, 2]), np.log([4, 2, 1, 1]), np.log([2, 2, 3, 1]), np.zeros(4)]
+    rows2 = [np.log([1, 3]), np.log([3, 1])]
+    E = rng.standard_normal((B, n, n, de)) * 0.5
+    gam_y = 2.0
+    for g_, nr, rows in ((0, 4, rows4), (1, 2, rows2)):
+        for i in range(nr):
+            for h in range(H):
+                t = rows[(i + h) % len(rows)] + 0.3 * h   # target logits u (any row shift)
+                # u = (s + beta_e) gamma_y + beta_y: beta_e = E[h] + b_eadd[h]
+                E[g_, i, :nr, h] = t / gam_y - s[g_, h, i, :nr] - b["b_eadd"][h]
+    pair = m[:, :, None] & m[:, None, :]
+    E[~pair] = 0.0
+    b["X"], b["E"] = X, E
+    for k in list(b):
+        if k != "mask":
+            b[k] = b[k].astype(np.float32)
+    b["n_real"] = b["mask"].sum(1)
+    return b, H
+
+
+def test_bf16_backward_equals_true_derivative_where_rounding_is_exact():
+    """On a batch where every bfloat16 rounding point is exact (A dyadic, Q, K,
+    V bfloat16 values), the bfloat16-mode backward oracle (straight-through
+    rounding, softmax Jacobian at the stored A) must be the true derivative of
+    the layer: central differences of the C oracle, a separate code base, for
+    a few coordinates of every input and weight. A sign flip or a dropped
+    -sum(A g) term in the bfloat16 softmax backward fails here."""
+    b, H = _dyadic_batch()
+    ref = O.forward(b, H=H, bf16=True)
+    pm = real_pairs(b["mask"])
+    Ar = ref["A"][np.broadcast_to(pm[:, None], ref["A"].shape)]
+    assert np.all(np.isin(Ar, [0.125, 0.375, 0.25, 0.5, 0.75, 1.0])), "A must be dyadic here"
+    rng = np.random.default_rng(82)
+    dO = rng.standard_normal(b["X"].shape)
+    dEp = rng.standard_normal(b["E"].shape)
+    g16 = OB.backward(b, dO, dEp, H=H, bf16=True)
+    g32 = OB.backward(b, dO, dEp, H=H, bf16=False)
+
+    def loss(bb):
+        r = O.forward(bb, H=H)
+        return float((r["O"] * dO).sum() + (r["Ep"] * dEp).sum())
+
+    hstep = 2.0 ** -14
+    checked = 0
+    for k in OB.INPUTS + OB.WEIGHTS:
+        g = g16[k]
+        scale = max(1.0, float(np.abs(g32[k]).max()))
+        # float64 reference backward agrees up to the 1e-7 logit offsets of float32 E
+        assert np.abs(g - g32[k]).max() <= 1e-5 * scale, k
+        nz = np.flatnonzero(np.abs(g32[k]) > 1e-3)
+        pick = rng.choice(nz, size=min(3, nz.size), replace=False) if nz.size else []
+        for idx in pick:
+            pos = np.unravel_index(idx, g.shape)
+            bp, bm = dict(b), dict(b)
+            bp[k] = b[k].copy(); bp[k][pos] += np.float32(hstep)
+            bm[k] = b[k].copy(); bm[k][pos] -= np.float32(hstep)
+            fd = (loss(bp) - loss(bm)) / (2 * hstep)
+            assert abs(fd - g[pos]) <= 1e-5 * max(1.0, abs(fd)), (k, pos, fd, g[pos])
+            checked += 1
+    assert checked >= 30
+    # the score path and the softmax carry gradient on this batch
+    for k in ("w_q", "w_k", "w_emul", "w_eadd", "E", "w_ymul"):
+        assert np.abs(g16[k]).max() > 1e-2, k
