@@ -2,14 +2,23 @@
 one MI355X.
 
 A step is one whole layer call (``edge_attn_layer``: Q/K/V projection, scores
-with head-wise FiLM, masked softmax, A and O, residual edge update) over one
-synthetic batch already resident in HBM. Steps rotate over enough distinct
-input/output buffer sets that the working set exceeds the 256 MB Infinity
-Cache, so every step streams from HBM.
+with head-wise FiLM, masked softmax, A and O, residual edge update; large
+graphs take both passes of the two-pass scheme) over one synthetic batch
+already resident in HBM. Where a batch is small, steps rotate over enough
+distinct input/output buffer sets that the working set exceeds the 256 MB
+Infinity Cache, so every step streams from HBM.
 
-Prints one JSON line: graphs/s (value), edge-tokens/s, the dominant kernel's
+With no workload named, the JSON line is the large-graph configuration (B=4,
+n=1024, two-pass: the largest that the layer is quoted on) and carries the
+other four configurations (tiny, planar, tree, SBM) as sub-records in
+``configs``, each with its own GPU time, roofline fraction and CPU oracle
+legs. ``--workload NAME`` prints that configuration alone.
+
+Every line carries graphs/s (value), edge-tokens/s, the dominant kernel's
 roofline record (algorithmic bytes over its HIP-event-timed average
-duration), and the CPU oracle timed on the host as a reported baseline.
+duration), the layer's own algorithmic bytes per step and their rate, and the
+CPU oracle timed on the host as a reported baseline (all cores and one
+thread, median of three runs where a run is short).
 """
 from __future__ import annotations
 
@@ -37,10 +46,13 @@ VARIANT_FLAGS = {"none": 0, "light_edge": 0x2, "no_score_mod": 0x4, "unnormalize
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="planar", choices=["planar", "tree", "sbm", "large", "tiny"])
+    ap.add_argument("--workload", default="all", choices=["all", "planar", "tree", "sbm", "large", "tiny"],
+                    help="all (default): the large configuration as the line, the others as sub-records")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sub-steps", type=int, default=200,
+                    help="timed steps of each sub-record configuration (--workload all)")
     ap.add_argument("--hot", action="store_true", help="also time back-to-back calls on one buffer set")
     ap.add_argument("--variant", default="none", choices=sorted(VARIANT_FLAGS),
                     help="ablation variant of the layer (the default is the full layer)")
@@ -309,23 +321,208 @@ def traffic_from_profiles(kernel: str, workload: str, profiles_dir: str = None):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(batch, dims, budget_s: float = 12.0, oracle_variant: int = 0):
-    """The oracle (as it stands) on whole graphs of the same batch, host cores."""
+def layer_algorithmic_bytes(dims, n_real: np.ndarray, two_pass: bool) -> float:
+    """Bytes one layer call must move, whatever its kernels keep in between.
+
+    Per edge token (b, i, j): E read on real pairs (twice in two-pass mode:
+    the scheme reads it in both passes), E' written over the whole padded
+    layout, A written (single pass only). Per node row: X read (real rows),
+    O written (all rows). Per graph: y read; two-pass adds the softmax
+    statistics (float32, H per row). Plus the weights, read once. At the
+    planar shape this is (2 de + H) 2 B = 272 B per edge token and 2 d 2 B =
+    1024 B per node, 75.9 MB in all."""
+    s = 2 if dims.dtype == "bf16" else 4
+    B, n, d, de, dy, H = dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H
+    nr = n_real.astype(np.float64)
+    tokens, real_tokens = B * n * n, float(np.sum(nr ** 2))
+    e_read = real_tokens * de * s * (2 if two_pass else 1)
+    e_write = tokens * de * s
+    a_write = 0 if two_pass else tokens * H * s
+    lse = B * H * n * 4 if two_pass else 0
+    x_read, o_write = float(np.sum(nr)) * d * s, B * n * d * s
+    weights = (3 * d * d + 2 * H * de + 2 * H * dy + de * H) * s + B * dy * s
+    return e_read + e_write + a_write + lse + x_read + o_write + weights
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sub_batch(batch, graphs: int):
+    return {k: (v[:graphs] if k in ("X", "E", "y", "mask", "adj", "n_real") else v) for k, v in batch.items()}
+
+
+def cpu_legs(batch, dims, budget_s: float = 4.0, oracle_variant: int = 0, runs: int = 3):
+    """The oracle (as it stands) timed on the host: all cores (OpenMP over
+    query rows) and one thread. Each leg runs the oracle on a sample of the
+    batch sized to about `budget_s` (whole graphs when one fits, else the
+    first query rows of graph 0: the oracle's cost per row does not depend
+    on the row), `runs` times, and reports the median as graphs/s of the
+    batch's shape (rows/s divided by the n rows of a graph)."""
     from oracle import oracle as OR
-    threads = OR.num_threads()
-    # a first graph to size the sample
+    bf = dims.dtype == "bf16"
+    all_threads = OR.num_threads()
+    out = {}
+    for leg, threads in (("all_cores", all_threads), ("single_thread", 1)):
+        prev = OR.set_num_threads(threads)
+        try:
+            t0 = time.perf_counter()
+            OR.forward(_sub_batch(batch, 1), dims.H, bf16=bf, rows=[(0, i) for i in range(min(dims.n, 16))],
+                       variant=oracle_variant)
+            per_row = max((time.perf_counter() - t0) / min(dims.n, 16), 1e-6)
+            rows_fit = budget_s / per_row
+            if rows_fit >= dims.n:  # whole graphs
+                g = int(max(1, min(dims.B, rows_fit // dims.n)))
+                sub, rows, what = _sub_batch(batch, g), None, "the first %d of the %d graphs" % (g, dims.B)
+                units = float(g)
+            else:
+                r = int(max(8, min(dims.n, rows_fit)))
+                sub, rows = _sub_batch(batch, 1), [(0, i) for i in range(r)]
+                what = "the first %d of the %d query rows of graph 0" % (r, dims.n)
+                units = r / float(dims.n)
+            times = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                OR.forward(sub, dims.H, bf16=bf, rows=rows, variant=oracle_variant)
+                times.append(time.perf_counter() - t0)
+            med = float(np.median(times))
+            out[leg] = {"value": units / med, "unit": "graphs/s", "threads": threads, "runs": runs,
+                        "median_s": med, "sample": what}
+        finally:
+            OR.set_num_threads(prev)
+    return out
+
+
+def cpu_baseline(batch, dims, budget_s: float = 4.0, oracle_variant: int = 0, runs: int = 3):
+    """cpu_baseline record: the all-core leg as the value, the one-thread leg beside it."""
+    legs = cpu_legs(batch, dims, budget_s, oracle_variant, runs)
+    a = legs["all_cores"]
+    return {"value": a["value"], "unit": "graphs/s", "cores": a["threads"], "kind": "oracle",
+            "sample": "%s, every output of those rows (float64 C loops, OpenMP over query rows), "
+                      "median of %d runs; graphs/s of this configuration's shape" % (a["sample"], runs),
+            "single_thread": legs["single_thread"], "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def event_pair_overhead_us(reps: int = 200) -> float:
+    """Median elapsed time of two HIP events recorded back to back on the
+    current stream: what a per-launch event pair adds to a kernel's time."""
+    import torch
+    st = torch.cuda.current_stream()
+    vals = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        e1.record(st)
+        e1.synchronize()
+        vals.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(vals))
+
+
+def time_layer(name: str, steps: int, warmup: int, variant: str = "none", hot: bool = False):
+    """GPU record of one configuration: wall time per layer call over `steps`
+    calls (after `warmup`), per-kernel HIP-event durations over the same
+    sequence, the dominant kernel's roofline and the layer's algorithmic rate."""
+    import torch
+    from edge_aware_graph_amd import workloads as W
+    from edge_aware_graph_amd.layer import EdgeAttention
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[name]
+    dims = cfg.dims
+    print("[bench] workload %s: %s" % (cfg.name, cfg.description), file=sys.stderr, flush=True)
+    batch = W.make_batch(cfg.name, bias_scale=0.0)
+    n_real = batch["n_real"]
+    dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+    vflag = VARIANT_FLAGS[variant]
+    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype, variant=vflag)
+    two_pass = layer.two_pass
+    recompute = layer.recomputes_update
+    # biases are all zero in the timed configuration: passed as NULL
+    weights = {k: torch.from_numpy(batch[k]).to(dev, dt) for k in batch if k.startswith("w_")}
+    X0 = torch.from_numpy(batch["X"]).to(dev, dt)
+    E0 = torch.from_numpy(batch["E"]).to(dev, dt)
+    y0 = torch.from_numpy(batch["y"]).to(dev, dt)
+    m0 = torch.from_numpy(batch["mask"]).to(dev)
+    B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
+    es = 2 if dims.dtype == "bf16" else 4
+    set_bytes = (2 * B * n * n * de + B * n * d * 2 + (0 if two_pass else B * H * n * n)) * es + layer.workspace_bytes
+    nsets = int(max(1, min(16, -(-2 * INFINITY_CACHE_BYTES // set_bytes))))
+    sets = []
+    for k in range(nsets):
+        sets.append(dict(
+            X=X0 if k == 0 else X0.clone(), E=E0 if k == 0 else E0.clone(), y=y0.clone(), mask=m0.clone(),
+            O=torch.empty(B, n, d, dtype=dt, device=dev),
+            A=None if two_pass else torch.empty(B, H, n, n, dtype=dt, device=dev),
+            Eo=torch.empty(B, n, n, de, dtype=dt, device=dev),
+            ws=torch.empty(layer.workspace_bytes, dtype=torch.uint8, device=dev)))
+    print("[bench] %d buffer sets of %.1f MiB (two_pass=%s)" % (nsets, set_bytes / 2**20, two_pass),
+          file=sys.stderr, flush=True)
+    calls = [layer.bind_layer(weights, st["X"], st["E"], st["y"], st["mask"], st["O"], st["A"], st["Eo"], st["ws"])
+             for st in sets]
+    for k in range(warmup):
+        calls[k % nsets]()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` layer calls
     t0 = time.perf_counter()
-    OR.forward({k: (v[:1] if k in ("X", "E", "y", "mask", "adj", "n_real") else v) for k, v in batch.items()},
-               dims.H, bf16=(dims.dtype == "bf16"))
-    per_graph = max(time.perf_counter() - t0, 1e-4)
-    g = int(max(1, min(dims.B, budget_s / per_graph)))
-    sub = {k: (v[:g] if k in ("X", "E", "y", "mask", "adj", "n_real") else v) for k, v in batch.items()}
-    t0 = time.perf_counter()
-    OR.forward(sub, dims.H, bf16=(dims.dtype == "bf16"), variant=oracle_variant)
-    dt = time.perf_counter() - t0
-    return {"value": g / dt, "unit": "graphs/s", "cores": threads, "kind": "oracle",
-            "sample": "the first %d of the %d graphs of the timed batch, every query row, all outputs "
-                      "(float64 C loops, OpenMP over rows); graphs/s scales directly" % (g, dims.B)}
+    for k in range(steps):
+        calls[k % nsets]()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    print("[bench] %s: timed %d steps, %.4f ms/step" % (name, steps, ms_per_step), file=sys.stderr, flush=True)
+    # per-kernel durations from HIP events on the launch stream, same step sequence
+    layer.profile_begin()
+    for k in range(steps):
+        calls[k % nsets]()
+    prof = layer.profile_end()
+    kernels = {kn: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for kn, (ms, cnt) in prof.items() if cnt}
+    for kn in kernels:
+        b = algorithmic_bytes(kn, dims, n_real, two_pass, recompute)
+        kernels[kn]["alg_bytes"] = b
+        kernels[kn]["alg_GBps"] = b / (kernels[kn]["avg_us"] * 1e-6) / 1e9
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    alg = kernels[dominant]["alg_bytes"]
+    achieved = kernels[dominant]["alg_GBps"]
+    layer_bytes = layer_algorithmic_bytes(dims, n_real, two_pass)
+    rec = {
+        "graphs_per_s": B / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step,
+        "edge_tokens_per_s": B * n * n / (ms_per_step * 1e-3),
+        "real_edge_tokens_per_s": float(np.sum(n_real.astype(np.float64) ** 2)) / (ms_per_step * 1e-3),
+        "layer_alg_bytes": layer_bytes,
+        "layer_alg_GBps": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "layer_frac_of_hbm": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "dy": dims.dy, "H": H,
+                   "dh": dims.dh, "structure": cfg.structure, "two_pass": two_pass, "variant": variant,
+                   "edge_tokens_per_step": B * n * n, "real_edge_tokens_per_step": int(np.sum(n_real ** 2)),
+                   "buffer_sets": nsets},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles(dominant, cfg.name) if variant == "none" else None,
+                     "alg_bytes_per_launch": alg, "avg_launch_us": kernels[dominant]["avg_us"]},
+        "kernels": kernels,
+        "data": "synthetic (seeded %s graphs, random Xavier weights)" % cfg.structure,
+        "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
+    }
+    if hot:
+        for _ in range(warmup):
+            calls[0]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            calls[0]()
+        torch.cuda.synchronize()
+        rec["hot_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
+    del calls, sets, X0, E0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, batch, dims
 
 
 def main():
@@ -338,140 +535,81 @@ def main():
 
     import torch
     from edge_aware_graph_amd import workloads as W
-    from edge_aware_graph_amd.layer import EdgeAttention
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    cfg = W.CONFIGS[args.workload]
-    dims = cfg.dims
-    print("[bench] workload %s: %s" % (cfg.name, cfg.description), file=sys.stderr, flush=True)
-    batch = W.make_batch(cfg.name, bias_scale=0.0)
-    n_real = batch["n_real"]
-    if args.sampling_layers > 0:
-        print(json.dumps(sampling_bench(args, cfg, dims, batch)), flush=True)
+    special = args.sampling_layers > 0 or args.backward or args.block
+    if special:
+        name = "planar" if args.workload == "all" else args.workload
+        cfg = W.CONFIGS[name]
+        print("[bench] workload %s: %s" % (cfg.name, cfg.description), file=sys.stderr, flush=True)
+        batch = W.make_batch(cfg.name, bias_scale=0.0)
+        if args.sampling_layers > 0:
+            print(json.dumps(sampling_bench(args, cfg, cfg.dims, batch)), flush=True)
+        elif args.backward:
+            print(json.dumps(backward_bench(args, cfg, cfg.dims, batch)), flush=True)
+        else:
+            print(json.dumps(block_bench(args, cfg, cfg.dims, batch)), flush=True)
         return
-    if args.backward:
-        print(json.dumps(backward_bench(args, cfg, dims, batch)), flush=True)
-        return
-    if args.block:
-        print(json.dumps(block_bench(args, cfg, dims, batch)), flush=True)
-        return
-    dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
 
-    variant = VARIANT_FLAGS[args.variant]
-    layer = EdgeAttention(dims.B, dims.n, dims.d, dims.de, dims.dy, dims.H, dims.dh, dims.dtype,
-                          variant=variant)
-    two_pass = layer.two_pass
-    recompute = layer.recomputes_update
-    weights = {k: torch.from_numpy(batch[k]).to(dev, dt) for k in batch if k.startswith(("w_", "b_"))}
-    # biases are all zero in the timed configuration: pass NULL
-    for k in list(weights):
-        if k.startswith("b_"):
-            weights.pop(k)
-
-    X0 = torch.from_numpy(batch["X"]).to(dev, dt)
-    E0 = torch.from_numpy(batch["E"]).to(dev, dt)
-    y0 = torch.from_numpy(batch["y"]).to(dev, dt)
-    m0 = torch.from_numpy(batch["mask"]).to(dev)
-    B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
-    es = 2 if dims.dtype == "bf16" else 4
-    set_bytes = (2 * B * n * n * de + B * n * d * 2 + (0 if two_pass else B * H * n * n)) * es + layer.workspace_bytes
-    nsets = int(max(1, min(16, -(-2 * INFINITY_CACHE_BYTES // set_bytes))))
-    sets = []
-    for _ in range(nsets):
-        sets.append(dict(
-            X=X0.clone(), E=E0.clone(), y=y0.clone(), mask=m0.clone(),
-            O=torch.empty(B, n, d, dtype=dt, device=dev),
-            A=None if two_pass else torch.empty(B, H, n, n, dtype=dt, device=dev),
-            Eo=torch.empty(B, n, n, de, dtype=dt, device=dev),
-            ws=torch.empty(layer.workspace_bytes, dtype=torch.uint8, device=dev)))
-    print("[bench] %d buffer sets of %.1f MiB (two_pass=%s)" % (nsets, set_bytes / 2**20, two_pass),
-          file=sys.stderr, flush=True)
-
-    calls = [layer.bind_layer(weights, s["X"], s["E"], s["y"], s["mask"], s["O"], s["A"], s["Eo"], s["ws"])
-             for s in sets]
-
-    def step(k):
-        calls[k % nsets]()
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
-
-    # timed region: exactly K steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    graphs_per_s = B / (ms_per_step * 1e-3)
-    print("[bench] timed %d steps: %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
-
-    # per-kernel durations from HIP events on the launch stream, same step sequence
-    layer.profile_begin()
-    for k in range(args.steps):
-        step(k)
-    prof = layer.profile_end()
-    kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
-    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    avg_s = kernels[dominant]["avg_us"] * 1e-6
-    alg = algorithmic_bytes(dominant, dims, n_real, two_pass, recompute)
-    achieved = alg / avg_s / 1e9
-    for name in kernels:
-        b = algorithmic_bytes(name, dims, n_real, two_pass, recompute)
-        kernels[name]["alg_bytes"] = b
-        kernels[name]["alg_GBps"] = b / (kernels[name]["avg_us"] * 1e-6) / 1e9
-    traffic = traffic_from_profiles(dominant, cfg.name) if not variant else None
-
+    oracle_variant = {"none": 0, "light_edge": 1, "no_score_mod": 2, "unnormalized": 4}[args.variant]
+    head = "large" if args.workload == "all" else args.workload
+    rec, batch, dims = time_layer(head, args.steps, args.warmup, args.variant, args.hot)
     out = {
         "metric": "graphs/s per fused layer forward (edge-aware attention + residual edge update)",
-        "value": graphs_per_s,
+        "value": rec["graphs_per_s"],
         "unit": "graphs/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
-        "data": "synthetic (seeded %s graphs, random Xavier weights)" % cfg.structure,
-        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "dy": dims.dy, "H": H,
-                   "dh": dims.dh, "structure": cfg.structure, "two_pass": two_pass, "variant": args.variant,
-                   "edge_tokens_per_step": B * n * n, "real_edge_tokens_per_step": int(np.sum(n_real ** 2)),
-                   "buffer_sets": nsets},
-        "edge_tokens_per_s": B * n * n / (ms_per_step * 1e-3),
-        "layer_alg_GBps": sum(algorithmic_bytes(k, dims, n_real, two_pass, recompute) for k in kernels) / (ms_per_step * 1e-3) / 1e9,
-        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": alg, "avg_launch_us": kernels[dominant]["avg_us"]},
-        "kernels": kernels,
+        "dtype": rec["dtype"],
+        "data": rec["data"],
+        "config": rec["config"],
+        "edge_tokens_per_s": rec["edge_tokens_per_s"],
+        "real_edge_tokens_per_s": rec["real_edge_tokens_per_s"],
+        "layer_alg_bytes": rec["layer_alg_bytes"],
+        "layer_alg_GBps": rec["layer_alg_GBps"],
+        "layer_frac_of_hbm": rec["layer_frac_of_hbm"],
+        "roofline": rec["roofline"],
+        "kernels": rec["kernels"],
+        "event_pair_overhead_us": event_pair_overhead_us(),
     }
-
-    if args.hot:
-        for _ in range(args.warmup):
-            calls[0]()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            calls[0]()
-        torch.cuda.synchronize()
-        out["hot_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / args.steps
-
+    if "hot_ms_per_step" in rec:
+        out["hot_ms_per_step"] = rec["hot_ms_per_step"]
     # plain copy of known size (for scaling rocprofv3 byte counters)
-    cp_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cp_src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
     cp_dst = torch.empty_like(cp_src)
     cp_dst.copy_(cp_src)
     torch.cuda.synchronize()
+    del cp_src, cp_dst
     out["copy_calibration_bytes"] = 256 << 20
-
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(batch, dims, oracle_variant={"none": 0, "light_edge": 1, "no_score_mod": 2,
-                                                                        "unnormalized": 4}[args.variant])
+        print("[bench] timing the CPU oracle (%s)" % head, file=sys.stderr, flush=True)
+        runs = 1 if dims.n > 256 else 3
+        out["cpu_baseline"] = cpu_baseline(batch, dims, budget_s=6.0, oracle_variant=oracle_variant, runs=runs)
+        out["gpu_over_oracle_all_cores"] = rec["graphs_per_s"] / out["cpu_baseline"]["value"]
+    del batch
+    if args.workload == "all":
+        configs = {}
+        for name in ("tiny", "planar", "tree", "sbm"):
+            sub, sbatch, sdims = time_layer(name, args.sub_steps, args.warmup, args.variant)
+            if not args.no_cpu_baseline:
+                print("[bench] timing the CPU oracle (%s)" % name, file=sys.stderr, flush=True)
+                legs = cpu_legs(sbatch, sdims, budget_s=3.0, oracle_variant=oracle_variant, runs=3)
+                sub["cpu_oracle"] = legs
+                sub["gpu_over_oracle_all_cores"] = sub["graphs_per_s"] / legs["all_cores"]["value"]
+                sub["gpu_over_oracle_single_thread"] = sub["graphs_per_s"] / legs["single_thread"]["value"]
+            del sbatch
+            configs[name] = sub
+        configs["large"] = {k: rec[k] for k in ("graphs_per_s", "ms_per_step", "edge_tokens_per_s",
+                                                "real_edge_tokens_per_s", "layer_alg_bytes", "layer_alg_GBps",
+                                                "layer_frac_of_hbm", "roofline")}
+        out["configs"] = configs
+        # structure changes values, not work: planar and tree should time the same
+        out["tree_over_planar_time"] = configs["tree"]["ms_per_step"] / configs["planar"]["ms_per_step"]
     print(json.dumps(out), flush=True)
 
 

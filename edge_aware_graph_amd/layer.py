@@ -140,15 +140,54 @@ def _check(lib, status: int):
         raise EaError(status, "%s: %s" % (lib.ea_status_str(status).decode(), lib.ea_last_error().decode()))
 
 
-def _ptr(t) -> Optional[int]:
-    """Device pointer of a tensor (None -> NULL). Plain ints pass through."""
+def _check_tensor(t, name: str, shape, dtype, what: str = ""):
+    """Reject a tensor the C ABI cannot check itself: the library sees only a
+    pointer, so a wrong element type or a short buffer would make its kernels
+    read or write out of bounds. Checks a torch tensor, contiguous, element
+    type and exact shape; None passes (NULL)."""
     if t is None:
-        return None
-    if isinstance(t, int):
-        return t
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor (got %s)" % (name, type(t).__name__))
     if not t.is_contiguous():
-        raise ValueError("tensors passed to the layer must be contiguous")
-    return t.data_ptr()
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s%s" % (name, t.dtype, dtype, what))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+class _Args:
+    """The tensor arguments of one call. `add` checks each tensor's type,
+    contiguity, element type and shape as it comes; `ptrs` then checks that
+    every one lives on the current CUDA device (a host tensor would be read
+    through a host address) and returns the pointers in order."""
+
+    def __init__(self, ea: "EdgeAttention"):
+        self.ea = ea
+        self.items = []
+
+    def add(self, name: str, t, kind: str = "layer", key: Optional[str] = None):
+        import torch
+        shape = None if kind == "bytes" else self.ea._shapes[key or name]
+        if kind == "layer":
+            _check_tensor(t, name, shape, self.ea._tdtype(), " (the context's dtype is %s)" % self.ea.dtype)
+        else:
+            _check_tensor(t, name, shape, {"u8": torch.uint8, "f32": torch.float32, "bytes": None}[kind])
+        self.items.append((name, t))
+
+    def ptrs(self):
+        import torch
+        out = []
+        for name, t in self.items:
+            if t is None:
+                out.append(None)
+                continue
+            if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+                raise ValueError("%s is on %s, expected the current CUDA device" % (name, t.device))
+            out.append(t.data_ptr())
+        return out
 
 
 def _stream(stream) -> Optional[int]:
@@ -170,6 +209,7 @@ class EdgeAttention:
         _check(self.lib, self.lib.ea_ctx_create(ctypes.byref(self.desc), ctypes.byref(ctx)))
         self.ctx = ctx
         self.dtype = dtype
+        self._shapes = self._arg_shapes()
 
     def __del__(self):
         ctx = getattr(self, "ctx", None)
@@ -185,19 +225,62 @@ class EdgeAttention:
     def two_pass(self) -> bool:
         return bool(self.lib.ea_is_two_pass(self.ctx))
 
-    @staticmethod
-    def attn_params(w: Dict) -> AttnParams:
-        return AttnParams(*[_ptr(w.get(k)) for k in ATTN_PARAM_NAMES])
+    def _arg_shapes(self) -> Dict[str, tuple]:
+        """Shape of every tensor argument, by name, from the context's desc."""
+        dsc = self.desc
+        B, n, d, de, dy, H = dsc.B, dsc.n, dsc.d, dsc.de, dsc.dy, dsc.H
+        sh = {"X": (B, n, d), "E": (B, n, n, de), "y": (B, dy), "mask": (B, n), "O": (B, n, d),
+              "A": (B, H, n, n), "E_out": (B, n, n, de), "U": (B, H, n, n),
+              "dO": (B, n, d), "dE_out": (B, n, n, de), "dX": (B, n, d), "dE": (B, n, n, de), "dy": (B, dy),
+              "X_out": (B, n, d), "y_out": (B, dy),
+              "w_q": (d, d), "w_k": (d, d), "w_v": (d, d), "b_q": (d,), "b_k": (d,), "b_v": (d,),
+              "w_emul": (H, de), "w_eadd": (H, de), "b_emul": (H,), "b_eadd": (H,),
+              "w_ymul": (H, dy), "w_yadd": (H, dy), "b_ymul": (H,), "b_yadd": (H,),
+              "w_e": (de, H), "b_e": (de,)}
+        blk = {"w_o": (d, d), "b_o": (d,), "ln_x1_g": (d,), "ln_x1_b": (d,), "w_x1": (d, d), "b_x1": (d,),
+               "w_x2": (d, d), "b_x2": (d,), "ln_x2_g": (d,), "ln_x2_b": (d,),
+               "ln_e1_g": (de,), "ln_e1_b": (de,), "w_e1": (2 * de, de), "b_e1": (2 * de,),
+               "w_e2": (de, 2 * de), "b_e2": (de,), "ln_e2_g": (de,), "ln_e2_b": (de,),
+               "w_yy": (dy, dy), "w_yx": (dy, d), "w_ye": (dy, de), "b_yo": (dy,), "ln_y1_g": (dy,),
+               "ln_y1_b": (dy,), "w_y1": (dy, dy), "b_y1": (dy,), "w_y2": (dy, dy), "b_y2": (dy,),
+               "ln_y2_g": (dy,), "ln_y2_b": (dy,)}
+        sh.update({"block." + k: v for k, v in blk.items()})
+        return sh
+
+    def _tdtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def _args(self, w: Optional[Dict] = None, attn: bool = False, update: bool = False) -> _Args:
+        """A checked argument list, starting with the attention and/or update
+        parameters of `w` (absent names are NULL)."""
+        a = _Args(self)
+        for k in (ATTN_PARAM_NAMES if attn else ()) + (UPDATE_PARAM_NAMES if update else ()):
+            a.add(k, w.get(k))
+        return a
+
+    def attn_params(self, w: Dict) -> AttnParams:
+        return AttnParams(*self._args(w, attn=True).ptrs())
+
+    def update_params(self, w: Dict) -> UpdateParams:
+        return UpdateParams(*self._args(w, update=True).ptrs())
 
     @staticmethod
-    def update_params(w: Dict) -> UpdateParams:
-        return UpdateParams(*[_ptr(w.get(k)) for k in UPDATE_PARAM_NAMES])
+    def _split(ptrs, k: int):
+        return ptrs[:k], ptrs[k:]
 
     def forward(self, w, X, E, y, mask, O, A, ws, stream=None):
-        p = self.attn_params(w)
-        _check(self.lib, self.lib.edge_attn_forward(
-            self.ctx, ctypes.byref(p), _ptr(X), _ptr(E), _ptr(y), _ptr(mask), _ptr(O), _ptr(A),
-            _ptr(ws), self._ws_len(ws), _stream(stream)))
+        a = self._args(w, attn=True)
+        for name, t in (("X", X), ("E", E), ("y", y)):
+            a.add(name, t)
+        a.add("mask", mask, "u8")
+        a.add("O", O)
+        a.add("A", A)
+        a.add("ws", ws, "bytes")
+        pp, rest = self._split(a.ptrs(), len(ATTN_PARAM_NAMES))
+        p = AttnParams(*pp)
+        _check(self.lib, self.lib.edge_attn_forward(self.ctx, ctypes.byref(p), *rest, self._ws_len(ws),
+                                                    _stream(stream)))
 
     @property
     def recomputes_update(self) -> bool:
@@ -205,26 +288,44 @@ class EdgeAttention:
         return self.two_pass or bool(self.desc.flags & EA_VARIANT_UNNORMALIZED)
 
     def update(self, w, E, y, mask, A, E_out, ws, stream=None):
-        p = self.attn_params(w) if w.get("w_q") is not None else None
-        u = self.update_params(w)
+        with_p = w.get("w_q") is not None
+        a = self._args(w, attn=with_p, update=True)
+        a.add("E", E)
+        a.add("y", y)
+        a.add("mask", mask, "u8")
+        a.add("A", A)
+        a.add("E_out", E_out)
+        a.add("ws", ws, "bytes")
+        ptrs = a.ptrs()
+        npar = len(ATTN_PARAM_NAMES) if with_p else 0
+        p = AttnParams(*ptrs[:npar]) if with_p else None
+        u = UpdateParams(*ptrs[npar:npar + len(UPDATE_PARAM_NAMES)])
+        rest = ptrs[npar + len(UPDATE_PARAM_NAMES):]
         _check(self.lib, self.lib.edge_update(
-            self.ctx, ctypes.byref(p) if p is not None else None, ctypes.byref(u), _ptr(E), _ptr(y),
-            _ptr(mask), _ptr(A), _ptr(E_out), _ptr(ws), self._ws_len(ws), _stream(stream)))
+            self.ctx, ctypes.byref(p) if p is not None else None, ctypes.byref(u), *rest, self._ws_len(ws),
+            _stream(stream)))
+
+    def _layer_args(self, w, X, E, y, mask, O, A, E_out, ws, stream):
+        a = self._args(w, attn=True, update=True)
+        for name, t in (("X", X), ("E", E), ("y", y)):
+            a.add(name, t)
+        a.add("mask", mask, "u8")
+        for name, t in (("O", O), ("A", A), ("E_out", E_out)):
+            a.add(name, t)
+        a.add("ws", ws, "bytes")
+        ptrs = a.ptrs()
+        na, nu = len(ATTN_PARAM_NAMES), len(UPDATE_PARAM_NAMES)
+        p, u = AttnParams(*ptrs[:na]), UpdateParams(*ptrs[na:na + nu])
+        return p, u, (self.ctx, ctypes.byref(p), ctypes.byref(u), *ptrs[na + nu:], self._ws_len(ws), _stream(stream))
 
     def layer(self, w, X, E, y, mask, O, A, E_out, ws, stream=None):
-        p = self.attn_params(w)
-        u = self.update_params(w)
-        _check(self.lib, self.lib.edge_attn_layer(
-            self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask),
-            _ptr(O), _ptr(A), _ptr(E_out), _ptr(ws), self._ws_len(ws), _stream(stream)))
+        p, u, args = self._layer_args(w, X, E, y, mask, O, A, E_out, ws, stream)
+        _check(self.lib, self.lib.edge_attn_layer(*args))
 
     def bind_layer(self, w, X, E, y, mask, O, A, E_out, ws, stream=None):
         """Marshal the arguments of one layer call once; returns a callable
         that launches it (on `stream`, else the current stream at bind time)."""
-        p = self.attn_params(w)
-        u = self.update_params(w)
-        args = (self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask),
-                _ptr(O), _ptr(A), _ptr(E_out), _ptr(ws), self._ws_len(ws), _stream(stream))
+        p, u, args = self._layer_args(w, X, E, y, mask, O, A, E_out, ws, stream)
         fn, lib = self.lib.edge_attn_layer, self.lib
         keep = (p, u, w, X, E, y, mask, O, A, E_out, ws)  # keep the tensors alive
 
@@ -241,13 +342,26 @@ class EdgeAttention:
 
     def backward(self, w, X, E, y, mask, A, dO, dEp, dX, dE, dy, grads: Dict, ws, bws, stream=None):
         """Gradients of the layer after a forward on this context (grads: float32 tensors by name)."""
-        p = self.attn_params(w)
-        u = self.update_params(w)
-        g = Grads(*[_ptr(grads[name]) for name, _ in Grads._fields_])
+        a = self._args(w, attn=True, update=True)
+        for name, t in (("X", X), ("E", E), ("y", y)):
+            a.add(name, t)
+        a.add("mask", mask, "u8")
+        for name, t in (("A", A), ("dO", dO), ("dE_out", dEp), ("dX", dX), ("dE", dE), ("dy", dy)):
+            a.add(name, t)
+        gnames = [name for name, _ in Grads._fields_]
+        for name in gnames:
+            a.add("grad " + name, grads[name], "f32", key=name)
+        a.add("ws", ws, "bytes")
+        a.add("bws", bws, "bytes")
+        ptrs = a.ptrs()
+        na, nu = len(ATTN_PARAM_NAMES), len(UPDATE_PARAM_NAMES)
+        p, u = AttnParams(*ptrs[:na]), UpdateParams(*ptrs[na:na + nu])
+        io = ptrs[na + nu:na + nu + 10]
+        g = Grads(*ptrs[na + nu + 10:na + nu + 10 + len(gnames)])
+        pws, pbws = ptrs[-2], ptrs[-1]
         _check(self.lib, self.lib.edge_attn_backward(
-            self.ctx, ctypes.byref(p), ctypes.byref(u), _ptr(X), _ptr(E), _ptr(y), _ptr(mask), _ptr(A),
-            _ptr(dO), _ptr(dEp), _ptr(dX), _ptr(dE), _ptr(dy), ctypes.byref(g),
-            _ptr(ws), self._ws_len(ws), _ptr(bws), self._ws_len(bws), _stream(stream)))
+            self.ctx, ctypes.byref(p), ctypes.byref(u), *io, ctypes.byref(g),
+            pws, self._ws_len(ws), pbws, self._ws_len(bws), _stream(stream)))
 
     @property
     def block_workspace_bytes(self) -> int:
@@ -256,11 +370,21 @@ class EdgeAttention:
     def bind_block(self, w, bp: Dict, X, E, y, mask, X_out, E_out, y_out, ws, stream=None):
         """Marshal the arguments of one block call (layer weights w, block
         parameters bp by name) once; returns a callable that launches it."""
-        p = self.attn_params(w)
-        u = self.update_params(w)
-        b = BlockParams(*[_ptr(bp[name]) for name in BLOCK_PARAM_NAMES])
-        args = (self.ctx, ctypes.byref(p), ctypes.byref(u), ctypes.byref(b), _ptr(X), _ptr(E), _ptr(y), _ptr(mask),
-                _ptr(X_out), _ptr(E_out), _ptr(y_out), _ptr(ws), self._ws_len(ws), _stream(stream))
+        a = self._args(w, attn=True, update=True)
+        for name in BLOCK_PARAM_NAMES:
+            a.add("block." + name, bp[name])
+        for name, t in (("X", X), ("E", E), ("y", y)):
+            a.add(name, t)
+        a.add("mask", mask, "u8")
+        for name, t in (("X_out", X_out), ("E_out", E_out), ("y_out", y_out)):
+            a.add(name, t)
+        a.add("ws", ws, "bytes")
+        ptrs = a.ptrs()
+        na, nu, nb = len(ATTN_PARAM_NAMES), len(UPDATE_PARAM_NAMES), len(BLOCK_PARAM_NAMES)
+        p, u = AttnParams(*ptrs[:na]), UpdateParams(*ptrs[na:na + nu])
+        b = BlockParams(*ptrs[na + nu:na + nu + nb])
+        args = (self.ctx, ctypes.byref(p), ctypes.byref(u), ctypes.byref(b), *ptrs[na + nu + nb:],
+                self._ws_len(ws), _stream(stream))
         fn, lib = self.lib.edge_attn_block, self.lib
         keep = (p, u, b, w, bp, X, E, y, mask, X_out, E_out, y_out, ws)
 
@@ -276,10 +400,16 @@ class EdgeAttention:
         self.bind_block(w, bp, X, E, y, mask, X_out, E_out, y_out, ws, stream)()
 
     def debug_logits(self, w, X, E, y, mask, U, ws, stream=None):
-        p = self.attn_params(w)
-        _check(self.lib, self.lib.ea_debug_logits(
-            self.ctx, ctypes.byref(p), _ptr(X), _ptr(E), _ptr(y), _ptr(mask), _ptr(U),
-            _ptr(ws), self._ws_len(ws), _stream(stream)))
+        a = self._args(w, attn=True)
+        for name, t in (("X", X), ("E", E), ("y", y)):
+            a.add(name, t)
+        a.add("mask", mask, "u8")
+        a.add("U", U, "f32")
+        a.add("ws", ws, "bytes")
+        pp, rest = self._split(a.ptrs(), len(ATTN_PARAM_NAMES))
+        p = AttnParams(*pp)
+        _check(self.lib, self.lib.ea_debug_logits(self.ctx, ctypes.byref(p), *rest, self._ws_len(ws),
+                                                  _stream(stream)))
 
     def profile_begin(self):
         _check(self.lib, self.lib.ea_profile_begin(self.ctx))
@@ -290,9 +420,6 @@ class EdgeAttention:
         _check(self.lib, self.lib.ea_profile_end(self.ctx, ms, cnt))
         return {KERNELS[k]: (ms[k], cnt[k]) for k in range(len(KERNELS))}
 
-    def _ws_len(self, ws) -> int:
-        if ws is None:
-            return 0
-        if isinstance(ws, int):
-            return self.workspace_bytes
-        return ws.numel() * ws.element_size()
+    @staticmethod
+    def _ws_len(ws) -> int:
+        return 0 if ws is None else ws.numel() * ws.element_size()

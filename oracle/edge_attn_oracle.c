@@ -306,3 +306,16 @@ int eao_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads the row loop uses from now on (timing legs: 1 thread, all cores);
+   returns the previous count. No effect without OpenMP. */
+int eao_set_num_threads(int t) {
+#ifdef _OPENMP
+  const int prev = omp_get_max_threads();
+  if (t >= 1) omp_set_num_threads(t);
+  return prev;
+#else
+  (void)t;
+  return 1;
+#endif
+}

@@ -73,6 +73,8 @@ def _load():
         lib.eao_vi_product.argtypes = [ctypes.POINTER(_Dims), _f64p, _f64p, _f64p]
         lib.eao_num_threads.restype = ctypes.c_int
         lib.eao_num_threads.argtypes = []
+        lib.eao_set_num_threads.restype = ctypes.c_int
+        lib.eao_set_num_threads.argtypes = [ctypes.c_int]
         lib.eao_bf16_round.restype = ctypes.c_double
         lib.eao_bf16_round.argtypes = [ctypes.c_double]
         _lib = lib
@@ -187,3 +189,8 @@ def bf16_round(x: float) -> float:
 def num_threads() -> int:
     """Threads the oracle's row loop runs on."""
     return int(_load().eao_num_threads())
+
+
+def set_num_threads(t: int) -> int:
+    """Threads of the row loop from now on; returns the previous count."""
+    return int(_load().eao_set_num_threads(int(t)))

@@ -66,3 +66,40 @@ def test_traffic_gate(tmp_path):
     os.remove(src)
     assert bench.traffic_from_profiles("demo", "planar", str(tmp_path)) is None  # source gone
 
+
+
+def test_layer_bytes_at_the_configurations():
+    """The layer's algorithmic bytes per call: (2 de + H) 2 B = 272 B per edge
+    token and 2 d 2 B = 1024 B per node at planar, 75.9 MB with the weights;
+    two-pass reads E in both passes (384 B per token), 1.615 GB at the large
+    shape; SBM reads E and X on real pairs and rows only, 238 MB."""
+    planar = W.CONFIGS["planar"].dims
+    full = np.full(planar.B, planar.n)
+    b = bench.layer_algorithmic_bytes(planar, full, False)
+    assert abs(b - 75.9e6) < 0.05e6
+    tokens, rows = planar.B * planar.n ** 2, planar.B * planar.n
+    weights = (3 * 256 * 256 + 2 * 8 * 64 * 2 + 64 * 8) * 2 + planar.B * 64 * 2
+    assert b == tokens * 272 + rows * 1024 + weights
+    large = W.CONFIGS["large"].dims
+    bl = bench.layer_algorithmic_bytes(large, np.full(large.B, large.n), True)
+    assert abs(bl - 1.615e9) < 0.001e9
+    assert bl - large.B * large.n ** 2 * 384 < 5e6
+    sbm = W.CONFIGS["sbm"]
+    n_real = W.make_batch("sbm")["n_real"]
+    assert abs(bench.layer_algorithmic_bytes(sbm.dims, n_real, False) - 238e6) < 1e6
+
+
+def test_cpu_legs_report_medians_and_both_thread_counts():
+    """The oracle's timing legs on a small batch: all cores and one thread,
+    graphs/s of the batch's shape, the thread count restored afterwards."""
+    from oracle import oracle as OR
+    dims = W.CONFIGS["tiny"].dims
+    batch = W.make_batch("tiny")
+    before = OR.num_threads()
+    legs = bench.cpu_legs(batch, dims, budget_s=0.05, runs=3)
+    assert OR.num_threads() == before
+    assert legs["single_thread"]["threads"] == 1 and legs["all_cores"]["threads"] == before
+    for leg in legs.values():
+        assert leg["value"] > 0 and leg["runs"] == 3 and leg["unit"] == "graphs/s"
+    rec = bench.cpu_baseline(batch, dims, budget_s=0.05)
+    assert rec["kind"] == "oracle" and rec["cores"] == before and rec["cpu_model"]
