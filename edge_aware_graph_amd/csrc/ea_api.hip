@@ -19,6 +19,7 @@ struct ea_ctx {
   ea_desc d;
   int NP;          // n rounded up to a multiple of 16
   int two_pass;
+  int generic;     // the shape has no tuned kernels: the generic path runs
   int forward_done;
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
@@ -116,6 +117,7 @@ ea::LayerArgs make_args(const ea_ctx* c, const ea_attn_params* p, const ea_updat
   a.lse = reinterpret_cast<float*>(base + c->off_lse);
   a.gy = reinterpret_cast<float*>(base + c->off_gy);
   a.B = c->d.B; a.n = c->d.n; a.NP = c->NP; a.dy = c->d.dy;
+  a.H = c->d.H; a.dh = c->d.dh; a.de = c->d.de; a.d = c->d.d;
   a.scale = (float)(1.0 / sqrt((double)c->d.dh));
   a.variant = (int)(c->d.flags & kVariants);
   return a;
@@ -140,7 +142,13 @@ ea_status timed(ea_ctx* c, int kernel, hipStream_t s, F&& launch) {
 }
 
 ea_status run_qkv(ea_ctx* c, const ea::LayerArgs& a, hipStream_t s) {
+  if (c->generic) return timed(c, EA_K_QKV, s, [&] { return ea::launch_gen_qkv(a, c->d.dtype, s); });
   return timed(c, EA_K_QKV, s, [&] { return ea::launch_qkv(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, s); });
+}
+
+// The generic path's row kernel (every shape the boundary accepts).
+ea_status run_gen(ea_ctx* c, const ea::LayerArgs& a, int kernel, int mode, hipStream_t s) {
+  return timed(c, kernel, s, [&] { return ea::launch_gen_row(a, c->d.dtype, mode, c->two_pass, s); });
 }
 
 ea_status check_io(const ea_ctx* c, const void* X, const void* E, const void* y,
@@ -199,14 +207,18 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
     return fail(EA_E_SHAPE, "B * n (padded to 16) must stay below 2^31");
   if (d.dtype != EA_FP32 && d.dtype != EA_BF16) return fail(EA_E_UNSUPPORTED, "dtype %d", d.dtype);
   if (d.flags & ~(EA_FORCE_TWO_PASS | kVariants)) return fail(EA_E_UNSUPPORTED, "unknown flags 0x%x", d.flags);
-  if (!ea::shape_supported(d.dtype, d.H, d.dh, d.de))
-    return fail(EA_E_UNSUPPORTED, "(H, dh, de) = (%d, %d, %d) is not built; supported: (4,16,16), (8,32,64)",
-                d.H, d.dh, d.de);
+  if (d.dh != 16 && d.dh != 32 && d.dh != 64)
+    return fail(EA_E_UNSUPPORTED, "dh = %d: the head width must be 16, 32 or 64", d.dh);
+  if (d.de % 16 != 0) return fail(EA_E_UNSUPPORTED, "de = %d: the edge width must be a multiple of 16", d.de);
+  if (2 * d.H > 32) return fail(EA_E_UNSUPPORTED, "H = %d: at most 16 heads (2H <= 32)", d.H);
+  if ((long long)d.B * d.n * d.n * d.de >= (1ll << 46))
+    return fail(EA_E_SHAPE, "the edge tensor B n^2 de must stay below 2^46 elements");
   ea_ctx* c = new (std::nothrow) ea_ctx();
   if (!c) return fail(EA_E_SHAPE, "out of host memory");
   c->d = d;
   c->NP = (d.n + 15) / 16 * 16;
   c->two_pass = (d.flags & EA_FORCE_TWO_PASS) || d.n > EA_SINGLE_PASS_MAX_N;
+  c->generic = !ea::shape_supported(d.dtype, d.H, d.dh, d.de);
   c->forward_done = 0;
   c->esz = d.dtype == EA_BF16 ? 2 : 4;
   const size_t qkv = round256((size_t)d.B * d.H * c->NP * d.dh * c->esz);
@@ -274,6 +286,11 @@ ea_status edge_attn_forward(ea_ctx* c, const ea_attn_params* p, const void* X, c
   a.A = A;
   c->forward_done = 0;
   EA_TRY(run_qkv(c, a, s));
+  if (c->generic) {
+    EA_TRY(run_gen(c, a, EA_K_ATTN, ea::kGenForward, s));
+    c->forward_done = 1;
+    return EA_OK;
+  }
   const int mode = c->two_pass ? ea::kOnline : ea::kSingle;
   EA_TRY(timed(c, EA_K_ATTN, s, [&] { return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, mode, s); }));
   c->forward_done = 1;
@@ -302,6 +319,7 @@ ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params
                   c->two_pass ? "two-pass" : "unnormalized-variant");
     ea::LayerArgs a = make_args(c, p, u, nullptr, E, y, mask, ws);
     a.E_out = E_out;
+    if (c->generic) return run_gen(c, a, EA_K_UPDATE, ea::kGenUpdate, s);
     const int mode = unnormalized(c) ? ea::kRecomputeU : ea::kRecompute;
     return timed(c, EA_K_UPDATE, s, [&] {
       return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, mode, s);
@@ -311,6 +329,7 @@ ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params
   ea::LayerArgs a = make_args(c, nullptr, u, nullptr, E, y, mask, ws ? ws : E_out);
   a.A = const_cast<void*>(A);
   a.E_out = E_out;
+  if (c->generic) return run_gen(c, a, EA_K_UPDATE, ea::kGenUpdate, s);
   return timed(c, EA_K_UPDATE, s, [&] {
     return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kReadA, s);
   });
@@ -322,6 +341,26 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
   g_err[0] = 0;
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
   if (c->two_pass || unnormalized(c)) {
+    if (c->generic) {  // one row kernel: both passes and the update
+      if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
+      EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
+      EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
+      EA_TRY(check_ptr(E_out, "E_out", 16, true));
+      EA_TRY(check_attn_params(c, p));
+      EA_TRY(check_io(c, X, E, y, mask, true));
+      EA_TRY(check_ptr(O, "O", 16, true));
+      if (c->two_pass && A) return fail(EA_E_UNSUPPORTED, "A is not produced in two-pass mode; pass NULL");
+      if (!c->two_pass) EA_TRY(check_ptr(A, "A", 16, true));
+      EA_TRY(check_ws(c, ws, ws_bytes));
+      hipStream_t s = static_cast<hipStream_t>(stream);
+      ea::LayerArgs a = make_args(c, p, u, X, E, y, mask, ws);
+      a.O = O; a.A = A; a.E_out = E_out;
+      c->forward_done = 0;
+      EA_TRY(run_qkv(c, a, s));
+      EA_TRY(run_gen(c, a, EA_K_FUSED, ea::kGenLayer, s));
+      c->forward_done = 1;
+      return EA_OK;
+    }
     // Validate everything before the first launch.
     if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
     EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
@@ -346,6 +385,11 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
   a.E_out = E_out;
   c->forward_done = 0;
   EA_TRY(run_qkv(c, a, s));
+  if (c->generic) {
+    EA_TRY(run_gen(c, a, EA_K_FUSED, ea::kGenLayer, s));
+    c->forward_done = 1;
+    return EA_OK;
+  }
   EA_TRY(timed(c, EA_K_FUSED, s, [&] {
     return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kFused, s);
   }));
@@ -362,14 +406,27 @@ ea_status ea_debug_logits(ea_ctx* c, const ea_attn_params* p, const void* X, con
   EA_TRY(check_io(c, X, E, y, mask, true));
   EA_TRY(check_ptr(U, "U", 16, true));
   EA_TRY(check_ws(c, ws, ws_bytes));
-  if (c->NP > 4 * 64) return fail(EA_E_UNSUPPORTED, "logit export is limited to n <= 256");
+  if (!c->generic && c->NP > 4 * 64)
+    return fail(EA_E_UNSUPPORTED, "the tuned logit export is limited to n <= 256");
   hipStream_t s = static_cast<hipStream_t>(stream);
   ea::LayerArgs a = make_args(c, p, nullptr, X, E, y, mask, ws);
   a.U = U;
   EA_TRY(run_qkv(c, a, s));
+  if (c->generic) return run_gen(c, a, EA_K_ATTN, ea::kGenLogits, s);
   return timed(c, EA_K_ATTN, s, [&] {
     return ea::launch_attn(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kLogits, s);
   });
+}
+
+ea_status ea_debug_softmax(ea_ctx* c, const float* U, void* A, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  EA_TRY(check_ptr(U, "U", 16, true));
+  EA_TRY(check_ptr(A, "A", 16, true));
+  const long rows = (long)c->d.B * c->d.H * c->d.n;
+  if (rows >= (1l << 31)) return fail(EA_E_SHAPE, "B H n must stay below 2^31");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, EA_K_ATTN, s, [&] { return ea::launch_gen_softmax(U, A, rows, c->d.n, c->d.dtype, s); });
 }
 
 size_t ea_block_workspace_bytes(const ea_ctx* c) { return c ? c->blk_bytes : 0; }
@@ -431,6 +488,8 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   if ((uint64_t)c->d.B * c->NP * c->NP >= (1ull << 31))
     return fail(EA_E_UNSUPPORTED, "the backward indexes pairs in 32 bits: B n_p^2 must stay below 2^31");
   if (c->d.flags & kVariants) return fail(EA_E_UNSUPPORTED, "the backward is built for the full layer (no variant flag)");
+  if (c->generic)
+    return fail(EA_E_UNSUPPORTED, "the backward is built for (H, dh, de) = (4, 16, 16) and (8, 32, 64)");
   if (c->d.dtype == EA_FP32 && c->d.de != 16)
     return fail(EA_E_UNSUPPORTED, "the float32 backward is built for (H, dh, de) = (4, 16, 16)");
   EA_TRY(check_attn_params(c, p));

@@ -50,6 +50,7 @@ struct LayerArgs {
   float* U;      // logits (kLogits)
   // sizes
   int B, n, NP, dy;
+  int H, dh, de, d;  // runtime copies (the tuned kernels take them as template parameters)
   float scale;   // 1/sqrt(dh)
   int variant;   // Variant bits
 };
@@ -118,5 +119,18 @@ hipError_t launch_backward(const LayerArgs& a, const BwdArgs& g, int dtype, int 
                            hipStream_t s);
 // Whether (dtype, H, dh, de) is instantiated.
 bool shape_supported(int dtype, int H, int dh, int de);
+
+// Generic path: any shape the boundary accepts (dh in {16, 32, 64}, de a
+// multiple of 16, 2H <= 32), one block per query row, runtime sizes.
+enum GenMode : int {
+  kGenForward = 0,  // O, and A (single pass) or lse (two-pass)
+  kGenLayer = 1,    // O, A (single pass) and E'
+  kGenUpdate = 2,   // E' from A (single pass) or from A recomputed with lse (two-pass)
+  kGenLogits = 3,   // the masked logits u
+};
+hipError_t launch_gen_qkv(const LayerArgs& a, int dtype, hipStream_t s);
+hipError_t launch_gen_row(const LayerArgs& a, int dtype, int mode, int two_pass, hipStream_t s);
+// Row softmax of float32 logits U [rows, n] into A [rows, n] (layer dtype).
+hipError_t launch_gen_softmax(const float* U, void* A, long rows, int n, int dtype, hipStream_t s);
 
 }  // namespace ea

@@ -34,7 +34,7 @@ EXPORTS = ("ea_ctx_create", "ea_ctx_destroy", "ea_workspace_bytes", "ea_is_two_p
            "ea_last_error", "ea_debug_logits", "ea_profile_begin", "ea_profile_end",
            "ea_backward_workspace_bytes", "edge_attn_backward",
            "ea_block_workspace_bytes", "edge_attn_block",
-           "ea_kernel_name")
+           "ea_kernel_name", "ea_debug_softmax")
 
 # Parameters of the graph-transformer block, in the order of ea_block_params.
 BLOCK_PARAM_NAMES = ("w_o", "b_o", "ln_x1_g", "ln_x1_b", "w_x1", "b_x1", "w_x2", "b_x2", "ln_x2_g", "ln_x2_b",
@@ -112,6 +112,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edge_attn_layer.argtypes = [vp, ap, up, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ea_debug_logits.restype = ctypes.c_int
     lib.ea_debug_logits.argtypes = [vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ea_debug_softmax.restype = ctypes.c_int
+    lib.ea_debug_softmax.argtypes = [vp, vp, vp, vp]
     lib.ea_status_str.restype = ctypes.c_char_p
     lib.ea_status_str.argtypes = [ctypes.c_int]
     lib.ea_last_error.restype = ctypes.c_char_p
@@ -410,6 +412,14 @@ class EdgeAttention:
         p = AttnParams(*pp)
         _check(self.lib, self.lib.ea_debug_logits(self.ctx, ctypes.byref(p), *rest, self._ws_len(ws),
                                                   _stream(stream)))
+
+    def debug_softmax(self, U, A, stream=None):
+        """Softmax stage alone: A = softmax over keys of float32 logits U [B, H, n, n]."""
+        a = _Args(self)
+        a.add("U", U, "f32")
+        a.add("A", A)
+        pU, pA = a.ptrs()
+        _check(self.lib, self.lib.ea_debug_softmax(self.ctx, pU, pA, _stream(stream)))
 
     def profile_begin(self):
         _check(self.lib, self.lib.ea_profile_begin(self.ctx))

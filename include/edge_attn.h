@@ -104,7 +104,17 @@ typedef struct {
   uint32_t flags;
 } ea_desc;
 
-/* Supported shapes: (H, dh, de) in {(4, 16, 16), (8, 32, 64)}; any B, n, dy. */
+/*
+ * Supported shapes: dh in {16, 32, 64}, de a positive multiple of 16,
+ * 1 <= H <= 16 (2H <= 32), d = H dh; any B, n, dy (B <= 65535, n <= 2^20,
+ * B n^2 de < 2^46); otherwise EA_E_UNSUPPORTED or EA_E_SHAPE.
+ * (H, dh, de) = (4, 16, 16) and (8, 32, 64) run tuned kernels (MFMA, E held
+ * on chip from the scores to the edge update); every other shape runs the
+ * generic path (one block per query row, runtime sizes, VALU arithmetic,
+ * E read twice per row), with the same results up to float32 rounding.
+ * The backward is built for the two tuned shapes only; the block for
+ * (d, de, dy) = (64, 16, 16) and, in bfloat16, (256, 64, 64).
+ */
 
 typedef struct {
   const void *w_q, *w_k, *w_v;            /* [d, d]                       */
@@ -218,12 +228,22 @@ const char* ea_last_error(void);
 
 /*
  * Stage export for parity tests: the masked logits u [B, H, n, n] (float32,
- * -inf at masked pairs), computed by the same score stage as the layer.
+ * -inf at masked pairs), computed by the same score stage as the layer
+ * (tuned shapes: n <= 256, else EA_E_UNSUPPORTED; generic shapes: any n).
  */
 ea_status ea_debug_logits(ea_ctx* ctx, const ea_attn_params* p,
                           const void* X, const void* E, const void* y,
                           const uint8_t* node_mask, float* U,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage export for parity tests: the softmax stage alone. U [B, H, n, n]
+ * float32 logits (-inf at masked pairs), A [B, H, n, n] in the context's
+ * dtype: A = softmax over the last axis, a row without a finite logit gives
+ * 0, masked entries +0.0, rounded to the storage type (bfloat16: nearest
+ * even). The same row softmax as the generic path's. No workspace.
+ */
+ea_status ea_debug_softmax(ea_ctx* ctx, const float* U, void* A, void* stream);
 
 /*
  * Graph-transformer block around the layer. The method's page ("Efficient

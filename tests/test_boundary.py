@@ -51,8 +51,15 @@ def create(lib, desc):
     (dict(B=0), L.EA_E_SHAPE), (dict(n=0), L.EA_E_SHAPE), (dict(dy=0), L.EA_E_SHAPE),
     (dict(d=60), L.EA_E_SHAPE), (dict(B=70000), L.EA_E_SHAPE),
     (dict(dtype=7), L.EA_E_UNSUPPORTED), (dict(flags=0x10), L.EA_E_UNSUPPORTED),
-    (dict(H=2, dh=32), L.EA_E_UNSUPPORTED), (dict(de=32), L.EA_E_UNSUPPORTED),
+    (dict(d=96, H=2, dh=48), L.EA_E_UNSUPPORTED), (dict(d=32, H=4, dh=8), L.EA_E_UNSUPPORTED),
+    (dict(de=24), L.EA_E_UNSUPPORTED), (dict(de=8), L.EA_E_UNSUPPORTED),
+    (dict(d=17 * 16, H=17, dh=16), L.EA_E_UNSUPPORTED),
     (dict(), L.EA_OK), (dict(d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_BF16), L.EA_OK),
+    # shapes without tuned kernels take the generic path
+    (dict(d=512, de=64, dy=64, H=8, dh=64, dtype=L.EA_BF16), L.EA_OK),
+    (dict(d=128, de=32, H=4, dh=32), L.EA_OK), (dict(d=64, H=2, dh=32), L.EA_OK),
+    (dict(d=256, de=16, H=16, dh=16), L.EA_OK), (dict(d=1024, de=128, H=16, dh=64), L.EA_OK),
+    (dict(d=64, de=48, H=1, dh=64, dtype=L.EA_BF16), L.EA_OK),
 ])
 def test_ctx_create_validation(lib, kw, status):
     st, ctx = create(lib, make_desc(**kw))
@@ -219,7 +226,8 @@ def test_backward_rules(lib):
                                       FAKE, FAKE, FAKE, FAKE, FAKE, k.get("g", ctypes.byref(g)), FAKE, 1 << 40,
                                       k.get("bws", FAKE), k.get("bwsb", 1 << 40), None)
     for kw in (dict(flags=L.EA_VARIANT_LIGHT_EDGE),
-               dict(d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_FP32)):
+               dict(d=256, de=64, dy=64, H=8, dh=32, dtype=L.EA_FP32),
+               dict(d=128, de=32, H=4, dh=32), dict(d=512, de=64, dy=64, H=8, dh=64, dtype=L.EA_BF16)):
         st, ctx = create(lib, make_desc(**kw))
         assert st == L.EA_OK
         assert bwd(ctx) == L.EA_E_UNSUPPORTED, kw
@@ -288,3 +296,27 @@ def test_sampling_loop_checks_block_parameters():
     dims = W.CONFIGS["tiny"].dims
     with pytest.raises(ValueError, match="one set of block parameters per layer"):
         SamplingLoop(dims, [{}], device="cpu", block_params=[{}, {}])
+
+
+def test_softmax_stage_export_rules(lib):
+    """ea_debug_softmax checks its pointers before launching anything."""
+    st, ctx = create(lib, make_desc())
+    assert st == L.EA_OK
+    assert lib.ea_debug_softmax(ctx, None, FAKE, None) == L.EA_E_NULLPTR
+    assert lib.ea_debug_softmax(ctx, FAKE, None, None) == L.EA_E_NULLPTR
+    assert lib.ea_debug_softmax(ctx, MISALIGNED, FAKE, None) == L.EA_E_ALIGN
+    assert lib.ea_debug_softmax(None, FAKE, FAKE, None) == L.EA_E_NULLPTR
+    lib.ea_ctx_destroy(ctx)
+
+
+def test_generic_logit_export_has_no_row_limit(lib):
+    """The tuned logit export stops at n = 256 (checked after the workspace);
+    a generic shape has no such rule and fails here only on its workspace."""
+    p = attn_params()
+    for kw, ws, status in ((dict(n=300), 1 << 40, L.EA_E_UNSUPPORTED),
+                           (dict(n=300, d=128, de=32, H=4, dh=32), 16, L.EA_E_WORKSPACE)):
+        st, ctx = create(lib, make_desc(**kw))
+        assert st == L.EA_OK
+        st = lib.ea_debug_logits(ctx, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+        assert st == status, (kw, lib.ea_last_error())
+        lib.ea_ctx_destroy(ctx)
