@@ -10,6 +10,7 @@
 
 #include <new>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "edge_attn.h"
@@ -157,6 +158,35 @@ ea_status check_io(const ea_ctx* c, const void* X, const void* E, const void* y,
   EA_TRY(check_ptr(E, "E", 16, true));
   EA_TRY(check_ptr(y, "y", 4, global_film_on(c)));
   if (!mask) return fail(EA_E_NULLPTR, "node_mask is NULL");
+  return EA_OK;
+}
+
+// Workspace of edge_attn_layer_noalloc: a file-scope device array, so that
+// the call allocates nothing. Each GPU the library runs on holds its own
+// copy until the process ends. In host code the array's name is not a device
+// address; the address of this device's copy comes from hipGetSymbolAddress
+// (once per device, with that device current) and only that address is used.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ea_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EA_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(EA_E_HIP, "device %d is beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(EA_E_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return EA_OK;
 }
 
@@ -395,6 +425,25 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
   }));
   c->forward_done = 1;
   return EA_OK;
+}
+
+size_t ea_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+ea_status edge_attn_layer_noalloc(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                                  const void* X, const void* E, const void* y, const uint8_t* mask,
+                                  void* O, void* A, void* E_out, void* stream) {
+  g_err[0] = 0;
+  if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
+  if (c->ws_bytes > kScratchBytes)
+    return fail(EA_E_WORKSPACE, "the layer needs %zu bytes of workspace; edge_attn_layer_noalloc holds at most %zu",
+                c->ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  EA_TRY(scratch_address(&ws));
+  const ea_status st = edge_attn_layer(c, p, u, X, E, y, mask, O, A, E_out, ws, kScratchBytes, stream);
+  // the workspace is internal and shared by later calls: no backward or
+  // two-pass edge_update may rely on what this call left in it
+  c->forward_done = 0;
+  return st;
 }
 
 ea_status ea_debug_logits(ea_ctx* c, const ea_attn_params* p, const void* X, const void* E,

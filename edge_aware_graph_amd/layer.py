@@ -34,7 +34,7 @@ EXPORTS = ("ea_ctx_create", "ea_ctx_destroy", "ea_workspace_bytes", "ea_is_two_p
            "ea_last_error", "ea_debug_logits", "ea_profile_begin", "ea_profile_end",
            "ea_backward_workspace_bytes", "edge_attn_backward",
            "ea_block_workspace_bytes", "edge_attn_block",
-           "ea_kernel_name", "ea_debug_softmax")
+           "ea_kernel_name", "ea_debug_softmax", "ea_noalloc_max_workspace_bytes", "edge_attn_layer_noalloc")
 
 # Parameters of the graph-transformer block, in the order of ea_block_params.
 BLOCK_PARAM_NAMES = ("w_o", "b_o", "ln_x1_g", "ln_x1_b", "w_x1", "b_x1", "w_x2", "b_x2", "ln_x2_g", "ln_x2_b",
@@ -114,6 +114,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ea_debug_logits.argtypes = [vp, ap, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ea_debug_softmax.restype = ctypes.c_int
     lib.ea_debug_softmax.argtypes = [vp, vp, vp, vp]
+    lib.ea_noalloc_max_workspace_bytes.restype = sz
+    lib.ea_noalloc_max_workspace_bytes.argtypes = []
+    lib.edge_attn_layer_noalloc.restype = ctypes.c_int
+    lib.edge_attn_layer_noalloc.argtypes = [vp, ap, up, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ea_status_str.restype = ctypes.c_char_p
     lib.ea_status_str.argtypes = [ctypes.c_int]
     lib.ea_last_error.restype = ctypes.c_char_p
@@ -323,6 +327,20 @@ class EdgeAttention:
     def layer(self, w, X, E, y, mask, O, A, E_out, ws, stream=None):
         p, u, args = self._layer_args(w, X, E, y, mask, O, A, E_out, ws, stream)
         _check(self.lib, self.lib.edge_attn_layer(*args))
+
+    def layer_noalloc(self, w, X, E, y, mask, O, A, E_out, stream=None):
+        """edge_attn_layer without a workspace argument (the library's own device array)."""
+        a = self._args(w, attn=True, update=True)
+        for name, t in (("X", X), ("E", E), ("y", y)):
+            a.add(name, t)
+        a.add("mask", mask, "u8")
+        for name, t in (("O", O), ("A", A), ("E_out", E_out)):
+            a.add(name, t)
+        ptrs = a.ptrs()
+        na, nu = len(ATTN_PARAM_NAMES), len(UPDATE_PARAM_NAMES)
+        p, u = AttnParams(*ptrs[:na]), UpdateParams(*ptrs[na:na + nu])
+        _check(self.lib, self.lib.edge_attn_layer_noalloc(self.ctx, ctypes.byref(p), ctypes.byref(u),
+                                                          *ptrs[na + nu:], _stream(stream)))
 
     def bind_layer(self, w, X, E, y, mask, O, A, E_out, ws, stream=None):
         """Marshal the arguments of one layer call once; returns a callable

@@ -179,6 +179,25 @@ ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same call as edge_attn_layer for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): it takes no workspace and allocates nothing; the
+ * workspace is a device array inside the library, one copy per GPU, held
+ * until the process ends. The caller still passes inputs and outputs, with
+ * the same rules as edge_attn_layer. A context whose workspace
+ * (ea_workspace_bytes) exceeds ea_noalloc_max_workspace_bytes() (16 MiB)
+ * gets EA_E_WORKSPACE and nothing is enqueued. Every call on one GPU uses
+ * the same array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller. Nothing may rely on what
+ * a call leaves in that array: the backward and a two-pass edge_update
+ * cannot follow this call (they get EA_E_STATE).
+ */
+size_t ea_noalloc_max_workspace_bytes(void);
+ea_status edge_attn_layer_noalloc(ea_ctx* ctx, const ea_attn_params* p, const ea_update_params* u,
+                                  const void* X, const void* E, const void* y,
+                                  const uint8_t* node_mask, void* O, void* A, void* E_out, void* stream);
+
+/*
  * Backward of the layer (forward plus residual edge update): the gradients
  * of a loss L with respect to the inputs and every weight, given dL/dO and
  * dL/dE'. The derivative of the definition ("Efficient Edge-aware Attention
