@@ -35,6 +35,17 @@ def scratch_users(remarks: str):
     return users
 
 
+def missing_stubs(lib_path: str):
+    """Kernel launch stubs the library references but does not define (the
+    host pass can drop a kernel's stub without an error when a device builtin
+    in its body does not type-check for the host); such a library fails to
+    load with an undefined symbol."""
+    res = subprocess.run(["nm", "-u", lib_path], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("nm failed on %s: %s" % (lib_path, res.stderr))
+    return [line.split()[-1] for line in res.stdout.splitlines() if "__device_stub__" in line]
+
+
 def build(verbose: bool = False, extra=()) -> str:
     """Compile every HIP source into the shared library (always rebuilds).
 
@@ -54,6 +65,10 @@ def build(verbose: bool = False, extra=()) -> str:
     if spills:
         os.remove(tmp)
         raise RuntimeError("kernels use scratch memory: %s" % ", ".join("%s (%d B/lane)" % s for s in spills))
+    stubs = missing_stubs(tmp)
+    if stubs:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the library: %s" % ", ".join(stubs))
     os.replace(tmp, LIB)
     return LIB
 

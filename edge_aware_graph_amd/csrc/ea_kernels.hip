@@ -1217,6 +1217,169 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
     up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak, [] {});
 }
 
+// Wait until at most N vector memory operations of this wave are in flight
+// (s_waitcnt with vmcnt N and the other counters at their maximum). The
+// counter retires operations in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
+
+// One wave's E tile (16 queries x 16 keys x DE, bfloat16) into LDS with
+// global-to-LDS loads of 16 bytes per lane: piece q of key jj of lane l lands
+// at dst[(jj * DE / 32 + q) * 64 + l], the lane order of the register
+// fragments. Pairs outside the n x n layout read the nearest one inside it.
+// (The source goes to the builtin as const void*: another pointer type makes
+// the host pass drop the kernel's launch stub without an error.)
+template <typename T, int DE>
+__device__ __forceinline__ void e_tile_to_lds(const T* E, int b, int n, int i, int j0, int lg, u32x4* dst) {
+  constexpr int LPK = DE / 32;
+  const T* row = E + ((size_t)b * n + (i < n ? i : n - 1)) * n * DE + lg * (DE / 4);
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = j0 + jj;
+    const T* src = row + (size_t)(j < n ? j : n - 1) * DE;
+#pragma unroll
+    for (int q = 0; q < LPK; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 8 * q),
+                                       (__attribute__((address_space(3))) void*)(dst + (jj * LPK + q) * 64), 16, 0, 0);
+  }
+}
+
+// Two-pass pass 2 (and the unnormalized update) in bfloat16, as a persistent
+// pipeline. Work items are (graph, 16-query block, group of 4 key tiles), key
+// group fastest, so the blocks running at one time cover whole rows of E.
+// Every block walks items blockIdx.x, blockIdx.x + gridDim.x, ...; wave w of
+// an item owns key tile 4 * group + w. While a wave computes one item from
+// registers, its next item's E tile streams into the wave's own LDS region
+// through global-to-LDS loads (16 bytes per lane, in the lane order of the
+// register fragments), so the E reads of the next item overlap the score
+// stage, the update and the E' stores of this one. The global-to-LDS loads
+// are not tracked by the compiler's waits: the kernel waits explicitly (all
+// vector memory operations but this item's E' stores before reading the
+// tile, and its own LDS reads before the next tile may overwrite it).
+// Every pair of a tile is read (masked values are discarded by the selects).
+template <typename T, int H, int DH, int DE, int MODE>
+__global__ __launch_bounds__(kThreads) void update_pipe_kernel(LayerArgs a, int items) {
+  static_assert(sizeof(T) == 2 && DE % 32 == 0, "bfloat16, 16-byte pieces");
+  constexpr int LPK = DE / 32;   // 16-byte pieces per lane and key
+  constexpr int NL = 16 * LPK;   // per tile
+  constexpr int kStores = 16 * LPK;  // E' store instructions of a whole tile
+  static_assert(kStores < 64, "vmcnt range");
+  __shared__ u32x4 ebuf[kWaves][NL][64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int n = a.n, NP = a.NP, JT = NP / 16, QB = NP / 16, KG = (JT + kWaves - 1) / kWaves;
+  const int G = gridDim.x;
+  int it = blockIdx.x;
+  if (it >= items) return;  // uniform
+  struct Item {
+    int b, i0, jt;
+  };
+  auto decode = [&](int x) {
+    Item r;
+    const int rest = x / KG;
+    r.jt = (x - rest * KG) * kWaves + w;
+    r.i0 = (rest % QB) * 16;
+    r.b = rest / QB;
+    return r;
+  };
+  Scorer<T, H, DH, DE> sc;
+  Frag<T, DH / 4> kf[H];
+  float L[H];
+  // raw mask bytes and whether their node exists: the select happens at the
+  // use (the next iteration), so nothing waits on these loads early
+  uint32_t mq, mk;
+  bool q_in, k_in;
+  auto issue_small = [&](const Item& m) {
+    sc.setup(a, m.b, m.i0);
+    const int i = m.i0 + li, j = 16 * m.jt + li;
+    q_in = i < n;
+    k_in = j < n;
+    mq = sc.mask_b[q_in ? i : n - 1];
+    mk = sc.mask_b[k_in ? j : n - 1];
+    sc.load_queries(a);
+    sc.load_k(m.jt, kf);
+    if constexpr (MODE == kRecompute) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) L[h] = a.lse[((size_t)m.b * H + h) * NP + sc.i];
+    }
+  };
+  const T* Eg = static_cast<const T*>(a.E);
+  Item cur = decode(it);
+  e_tile_to_lds<T, DE>(Eg, cur.b, n, cur.i0 + li, 16 * cur.jt, lg, &ebuf[w][0][0]);
+  issue_small(cur);  // sets the scorer's lane indices, which load_film uses
+  sc.load_film(a);
+  Updater<T, H, DE> up;
+  up.init(a, li, lg);
+  up.finish();
+  bool prev_full = false;  // the previous item stored a whole tile (kStores stores)
+  for (;;) {
+    const int nx = it + G;
+    const bool more = nx < items;  // uniform
+    __builtin_amdgcn_sched_barrier(0);
+    // this item's E tile (and small loads) have landed: all but the previous
+    // item's E' stores, which are the newest operations
+    if (prev_full) wait_vmcnt<kStores>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    ETile<T, DE> et;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+      for (int q = 0; q < LPK; ++q) {
+        const u32x4 v = ebuf[w][jj * LPK + q][l];
+        et.f[jj].w[4 * q] = v.x; et.f[jj].w[4 * q + 1] = v.y; et.f[jj].w[4 * q + 2] = v.z; et.f[jj].w[4 * q + 3] = v.w;
+      }
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    const Item nxt = decode(more ? nx : it);
+    if (more) e_tile_to_lds<T, DE>(Eg, nxt.b, n, nxt.i0 + li, 16 * nxt.jt, lg, &ebuf[w][0][0]);
+    __builtin_amdgcn_sched_barrier(0);  // the tile's loads are issued before this item's work
+    // this item: logits, A, then the next item's small loads, then the update
+    const int i = cur.i0 + li, j0 = 16 * cur.jt;
+    const bool mi = q_in && mq != 0u;
+    const uint32_t bits = key_bits(k_in ? mk : 0u);
+    const bool live = (__ballot(mi) & 0xffffull) != 0ull && bits != 0u && cur.jt < JT;  // uniform
+    sc.mi = mi;
+    float A[H][4];
+    {
+      f32x4 S[H];
+      sc.qk(kf, S);
+      const f32x4 fc = sc.film_start();
+      float R[4][16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) sc.film(et.f[jj], fc, R, jj);
+      float u[H][4];
+      sc.scores_from(R, S, bits, u);
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (MODE == kRecomputeU)
+            A[h][r] = u[h][r] == kNegInf ? 0.f : u[h][r];
+          else
+            A[h][r] = (u[h][r] == kNegInf || L[h] == kNegInf) ? 0.f : __expf(u[h][r] - L[h]);
+        }
+    }
+    const bool full = tile_full(mi, bits);
+    const int b = cur.b, jt = cur.jt;
+    if (more) issue_small(nxt);
+    if (live) {
+      Frag<T, 4> ak[H];
+#pragma unroll
+      for (int h = 0; h < H; ++h) ak[h].set(A[h]);
+      up.template tile<true>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, mi, j0, lg, bits, full, ak, [] {});
+    } else if (jt < JT) {
+      zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, j0, lg);
+    }
+    prev_full = live && full;
+    if (!more) break;
+    it = nx;
+    cur = nxt;
+  }
+}
+
 // ------------------------------------------------------------------ backward
 
 // Gradients of one layer (forward and residual edge update), single-pass
@@ -2240,6 +2403,20 @@ __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArg
 
 // ------------------------------------------------------------------ dispatch
 
+// Compute units of the current device (queried once per device).
+int num_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+
 template <typename T, int H, int DH, int DE, int MODE>
 hipError_t attn_maxt(const LayerArgs& a, int maxt, dim3 grid, hipStream_t s) {
   switch (maxt) {
@@ -2272,6 +2449,18 @@ template <typename T, int H, int DH, int DE>
 hipError_t update_shape(const LayerArgs& a, int mode, hipStream_t s) {
   const int JT = a.NP / 16;
   const dim3 grid((unsigned)JT * ((JT + kWaves - 1) / kWaves), a.B);  // < 2^31 for n <= 2^20
+  if constexpr (sizeof(T) == 2 && DE % 32 == 0) {
+    if (mode == kRecompute || mode == kRecomputeU) {
+      // persistent pipeline: one block per compute unit, items = grid of the plain kernel
+      const int items = (int)grid.x * (int)grid.y;  // B NP/16 ceil(NP/64) < 2^31 for n <= 2^20
+      const int blocks = items < num_cus() ? items : num_cus();
+      if (mode == kRecompute)
+        hipLaunchKernelGGL((update_pipe_kernel<T, H, DH, DE, kRecompute>), dim3(blocks), dim3(kThreads), 0, s, a, items);
+      else
+        hipLaunchKernelGGL((update_pipe_kernel<T, H, DH, DE, kRecomputeU>), dim3(blocks), dim3(kThreads), 0, s, a, items);
+      return hipGetLastError();
+    }
+  }
   if (mode == kReadA)
     hipLaunchKernelGGL((update_kernel<T, H, DH, DE, kReadA>), grid, dim3(kThreads), 0, s, a);
   else if (mode == kRecompute)

@@ -17,3 +17,13 @@ def test_scratch_users_found():
 
 def test_no_scratch_users():
     assert B.scratch_users(REMARKS.replace(": 52 ", ": 0 ")) == []
+
+
+def test_built_library_defines_every_kernel_stub():
+    """Every kernel the host code launches has its launch stub in the library
+    (an undefined stub makes the library fail to load)."""
+    import os
+    import pytest
+    if not os.path.exists(B.LIB):
+        pytest.skip("library not built")
+    assert B.missing_stubs(B.LIB) == []
