@@ -588,8 +588,7 @@ def main():
     out["copy_calibration_bytes"] = 256 << 20
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle (%s)" % head, file=sys.stderr, flush=True)
-        runs = 1 if dims.n > 256 else 3
-        out["cpu_baseline"] = cpu_baseline(batch, dims, budget_s=6.0, oracle_variant=oracle_variant, runs=runs)
+        out["cpu_baseline"] = cpu_baseline(batch, dims, budget_s=3.0, oracle_variant=oracle_variant, runs=3)
         out["gpu_over_oracle_all_cores"] = rec["graphs_per_s"] / out["cpu_baseline"]["value"]
     del batch
     if args.workload == "all":

@@ -763,6 +763,16 @@ __device__ __forceinline__ bool tile_full(bool mi, uint32_t bits) {
   return bits == 0xffffu && (__ballot(mi) & 0xffffull) == 0xffffull;
 }
 
+// Wait until at most N vector memory operations of this wave are in flight
+// (s_waitcnt with vmcnt N and the other counters at their maximum). The
+// counter retires operations in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
+
 // ------------------------------------------------------------------ attention
 
 // Single-pass tail shared by kSingle and kFused: masked softmax over the full
@@ -909,7 +919,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
   constexpr int D = H * DH;
   constexpr bool kKeepE = MODE == kFused && MAXT == 1 && sizeof(T) == 2;
   static_assert(D <= 256 && 2 * H <= 16, "shape");
-  __shared__ __align__(16) float os_s[kWaves * 16 * kOPitch<D>];  // O partials of each wave
+  // Two-pass pass 1 in bfloat16 with de = 64 streams E through LDS (see the
+  // kOnline branch); the O partials of the epilogue reuse that space once
+  // every wave has left its key loop.
+  constexpr bool kPipe = MODE == kOnline && sizeof(T) == 2 && DE == 64;
+  constexpr int kRowPitch = 8 * DE * 2 + 16;            // bytes: 8 keys of one query row, padded
+  constexpr int kHalfBytes = 16 * kRowPitch;            // 16 query rows
+  constexpr int kOBytes = kWaves * 16 * kOPitch<D> * 4;
+  constexpr int kEBytes = kPipe ? kWaves * 2 * kHalfBytes : 0;
+  __shared__ __align__(16) unsigned char smem_raw[kOBytes > kEBytes ? kOBytes : kEBytes];
+  float* os_s = reinterpret_cast<float*>(smem_raw);  // O partials of each wave
   __shared__ float red_s[2][kWaves][H][16];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
@@ -922,7 +941,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
 
   if constexpr (MODE == kOnline) {
     const uint32_t mq = sc.query_mask_byte();
-    uint32_t mk = sc.key_mask_byte(w);
+    uint32_t mk = kPipe ? 0u : sc.key_mask_byte(w);
     sc.load_weights(a);
     sc.mi = mq != 0u;
     sc.mi_any = (__ballot(sc.mi) & 0xffffull) != 0ull;
@@ -958,31 +977,129 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
         }
       }
     };
-    for (int jt = w; jt < JT; jt += kWaves) {
-      const uint32_t bits = key_bits(mk);
-      if (bits == 0u || !sc.mi_any) {  // tile without real pairs: the running statistics do not change
-        mk = sc.key_mask_byte(jt + kWaves);
-        continue;
+    if constexpr (kPipe) {
+      // E through LDS in half tiles (8 keys). Each half tile of the wave's
+      // next key tile is fetched by 16 global-to-LDS loads, one per query
+      // row, each moving that row's 8 keys (1 KB, contiguous in E) into a
+      // padded LDS row; the FiLM products read each key's fragment straight
+      // from LDS (two 16-byte reads per lane, no bank conflicts), so the E
+      // tile never sits in registers. A half is refetched as soon as this
+      // tile's FiLM products have read it, so the next tile streams in while
+      // this one's second half, scores, softmax and A V run. Per tile the
+      // wave issues, in this order: half 0 (16 loads), half 1 (16), the key
+      // mask byte (1), K (H), V (H DH / 16); every load is unconditional
+      // (after the last tile they read the zero table or a clamped tile), so
+      // the waits below count exactly. Every pair is read (masked values are
+      // discarded by the selects of the score stage).
+      constexpr int kV = H * (DH / 16);
+      constexpr int kAfterHalf = 16 + 1 + H + kV;  // loads issued after a tile's half 0
+      static_assert(kAfterHalf < 64, "vmcnt range");
+      unsigned char* ebase = smem_raw + (size_t)w * 2 * kHalfBytes;
+      const T* erow0 = sc.E + ((size_t)b * n) * n * DE;  // graph b
+      auto fetch_half = [&](int jt, int half, bool valid) {
+        const int j = 16 * jt + 8 * half + (l >> 3);  // lane l: key j, 16-byte piece l % 8
+        const int jc = j < n ? j : n - 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ir = i0 + r < n ? i0 + r : n - 1;
+          const T* src = valid ? erow0 + ((size_t)ir * n + jc) * DE + (l & 7) * 8 : zeros<T>() + (l & 15) * 8;
+          __builtin_amdgcn_global_load_lds((const void*)src,
+                                           (__attribute__((address_space(3))) void*)(ebase + half * kHalfBytes + r * kRowPitch),
+                                           16, 0, 0);
+        }
+      };
+      uint32_t mk_raw;
+      bool k_in;
+      auto key_mask_raw = [&](int jt) {  // raw byte; the select happens at the use
+        const int j = 16 * jt + li;
+        k_in = j < n;
+        mk_raw = sc.mask_b[k_in ? j : n - 1];
+      };
+      auto film_half = [&](int half, const f32x4& fc, float (&R)[4][16]) {
+        const unsigned char* rowp = ebase + half * kHalfBytes + li * kRowPitch + lg * (DE / 4) * 2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          Frag<T, DE / 4> e;
+          const u32x4 v0 = *reinterpret_cast<const u32x4*>(rowp + k * DE * 2);
+          const u32x4 v1 = *reinterpret_cast<const u32x4*>(rowp + k * DE * 2 + 16);
+          e.w[0] = v0.x; e.w[1] = v0.y; e.w[2] = v0.z; e.w[3] = v0.w;
+          e.w[4] = v1.x; e.w[5] = v1.y; e.w[6] = v1.z; e.w[7] = v1.w;
+          sc.film(e, fc, R, 8 * half + k);
+        }
+      };
+      if (sc.mi_any && w < JT) {  // uniform per wave
+        Frag<T, DH / 4> kf[H];
+        Frag<T, 4> vf[H][DH / 16];
+        fetch_half(w, 0, true);
+        fetch_half(w, 1, true);
+        key_mask_raw(w);
+        sc.load_k(w, kf);
+        sc.load_v(w, vf);
+        for (int jt = w; jt < JT; jt += kWaves) {
+          const int jn = jt + kWaves;
+          const bool more = jn < JT;  // uniform
+          const f32x4 fc = sc.film_start();
+          float R[4][16];
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vmcnt<kAfterHalf>();  // half 0 of this tile in LDS
+          __builtin_amdgcn_sched_barrier(0);
+          film_half(0, fc, R);
+          wait_lgkmcnt0();  // half 0 read: it may be refetched
+          __builtin_amdgcn_sched_barrier(0);
+          fetch_half(jn, 0, more);
+          // half 1 of this tile, its mask byte, K and V: everything but the
+          // next tile's half 0 just issued (loaded a tile ago, K and V are in
+          // by now; waiting here keeps the compiler from waiting for the
+          // whole prefetch at their uses)
+          wait_vmcnt<16>();
+          __builtin_amdgcn_sched_barrier(0);
+          film_half(1, fc, R);
+          wait_lgkmcnt0();
+          __builtin_amdgcn_sched_barrier(0);
+          fetch_half(jn, 1, more);
+          const uint32_t bits = key_bits(k_in ? mk_raw : 0u);
+          key_mask_raw(jn);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 S[H];
+          sc.qk(kf, S);
+          sc.load_k(jn, kf);
+          float u[H][4];
+          sc.scores_from(R, S, bits, u);
+          online_step(u, vf);
+          sc.load_v(jn, vf);
+        }
+        // the last tile's prefetch (zeros or clamped reads) still lands in
+        // this wave's half tiles, which the O partials reuse after the barrier
+        wait_vmcnt<0>();
       }
-      Frag<T, DH / 4> kf[H];
-      sc.load_k(jt, kf);
-      Frag<T, 4> vf[H][DH / 16];
-      float u[H][4];
-      if constexpr (sizeof(T) == 2) {
-        sc.load_v(jt, vf);
-        ETile<T, DE> et;
-        et.load(sc.E, b, n, i, sc.mi, 16 * jt, lg, bits);
-        mk = sc.key_mask_byte(jt + kWaves);  // next tile's mask, behind this tile's loads
-        sc.logits(et, kf, bits, u);
-      } else {
-        // float32: V after the scores, so that it is not live next to them
-        mk = sc.key_mask_byte(jt + kWaves);
-        sc.logits_streamed(16 * jt, kf, bits, u);
-        sc.load_v(jt, vf);
+    } else {
+      for (int jt = w; jt < JT; jt += kWaves) {
+        const uint32_t bits = key_bits(mk);
+        if (bits == 0u || !sc.mi_any) {  // tile without real pairs: the running statistics do not change
+          mk = sc.key_mask_byte(jt + kWaves);
+          continue;
+        }
+        Frag<T, DH / 4> kf[H];
+        sc.load_k(jt, kf);
+        Frag<T, 4> vf[H][DH / 16];
+        float u[H][4];
+        if constexpr (sizeof(T) == 2) {
+          sc.load_v(jt, vf);
+          ETile<T, DE> et;
+          et.load(sc.E, b, n, i, sc.mi, 16 * jt, lg, bits);
+          mk = sc.key_mask_byte(jt + kWaves);  // next tile's mask, behind this tile's loads
+          sc.logits(et, kf, bits, u);
+        } else {
+          // float32: V after the scores, so that it is not live next to them
+          mk = sc.key_mask_byte(jt + kWaves);
+          sc.logits_streamed(16 * jt, kf, bits, u);
+          sc.load_v(jt, vf);
+        }
+        online_step(u, vf);
       }
-      online_step(u, vf);
     }
-    // combine lane groups, then waves
+    // combine lane groups, then waves (the barrier below also ends every
+    // wave's use of the E half tiles in LDS, which the O partials then reuse)
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const float lsum = lg_sum(l_run[h]);
@@ -1216,16 +1333,6 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   if (jt < JT)
     up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak, [] {});
 }
-
-// Wait until at most N vector memory operations of this wave are in flight
-// (s_waitcnt with vmcnt N and the other counters at their maximum). The
-// counter retires operations in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
 
 // One wave's E tile (16 queries x 16 keys x DE, bfloat16) into LDS with
 // global-to-LDS loads of 16 bytes per lane: piece q of key jj of lane l lands
