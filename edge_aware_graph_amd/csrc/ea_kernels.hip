@@ -640,14 +640,24 @@ struct Updater {
         }
       }
     } else if constexpr (kBF) {
+      // E read again, kPf keys ahead of their use. The loads are
+      // unconditional (pairs outside the n x n map read the zero table), so
+      // they stay in flight across keys; values of masked pairs are
+      // discarded by the step's select.
+      constexpr int kPf = 4;
+      Frag<T, DE / 4> buf[kPf];
+      auto src = [&](int jj) {
+        return (iin && j0 + jj < n) ? E + rowoff + (size_t)(j0 + jj) * DE : zeros<T>();
+      };
+#pragma unroll
+      for (int q = 0; q < kPf; ++q) buf[q].load(src(q));
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         if (jj == 8) mid();
         const size_t off = rowoff + (size_t)(j0 + jj) * DE;
-        const bool real = (okj >> jj) & 1u;
-        Frag<T, DE / 4> ef;
-        if (real) ef.load(E + off); else ef.zero();
-        step<false>(ef, Eout, off, iin & (j0 + jj < n), real, R, jj);
+        const Frag<T, DE / 4> ef = buf[jj % kPf];
+        if (jj + kPf < 16) buf[jj % kPf].load(src(jj + kPf));
+        step<false>(ef, Eout, off, iin & (j0 + jj < n), (okj >> jj) & 1u, R, jj);
       }
     } else {
       // float32: E read in groups of 4 keys, the next group in flight (the

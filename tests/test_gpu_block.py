@@ -89,6 +89,17 @@ def test_block_ragged_random_masks(n, dtype):
     check(got, ref, batch, dims)
 
 
+def test_block_single_pass_aliased_outputs_n40():
+    """bfloat16 single-pass block (n = 40, one graph with a masked tail)
+    with X2, E2 and y2 written over X, E and y."""
+    dims = dims_of("planar", B=3, n=40)
+    batch = W.make_batch("planar", bias_scale=0.1, dims=dims)
+    batch["mask"][1, 29:] = 0
+    bp = W.make_block_params(dims, seed=7)
+    got, ref = run_block(batch, dims, bp, alias=True)
+    check(got, ref, batch, dims)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_block_two_pass_and_aliased_outputs(dtype):
     """Forced two-pass layer inside the block, outputs written over the inputs."""
