@@ -24,7 +24,7 @@ struct ea_ctx {
   int forward_done;
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
-  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_red, boff_dp, boff_ar, bws_bytes;  // backward workspace
+  size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_ps, boff_red, boff_wp, boff_dp, boff_ar, bws_bytes;  // backward workspace
   int blk_nxb, blk_exb;  // block: node and edge blocks per graph
   size_t blk_off_o, blk_off_a, blk_off_px, blk_off_pe, blk_bytes;  // block workspace (after the layer's)
   // kernel timing window
@@ -263,8 +263,10 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_df = c->boff_ds + round256(pairs * d.H * sizeof(float));
   c->boff_dqkv = c->boff_df + round256(pairs * 2 * d.H * c->esz);
   c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
-  c->boff_red = c->boff_dgy + round256((size_t)d.B * 2 * d.H * sizeof(float));
-  c->boff_dp = c->boff_red + round256((size_t)ea::kRedCopies * (3 * d.H * d.de + d.de) * sizeof(float));
+  c->boff_ps = c->boff_dgy + round256((size_t)d.B * 4 * d.H * sizeof(float));
+  c->boff_red = c->boff_ps + round256((size_t)d.B * (c->NP / 16) * ((c->NP + 63) / 64) * 4 * d.H * sizeof(float));
+  c->boff_wp = c->boff_red + round256((size_t)ea::kRedRows * (3 * d.H * d.de + d.de) * sizeof(float));
+  c->boff_dp = c->boff_wp + round256((size_t)ea::kMaxKsplit * (3 * (size_t)d.d * d.d + 3 * d.d) * sizeof(float));
   c->boff_ar = c->boff_dp + round256((size_t)d.B * d.H * c->NP * ((c->NP + 63) / 64) * sizeof(float));
   // two-pass contexts: the backward recomputes A [B, H, n, n] into its workspace
   c->bws_bytes = c->boff_ar + (c->two_pass ? round256((size_t)d.B * d.H * d.n * d.n * c->esz) : 0);
@@ -579,7 +581,9 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   g.DF = bb + c->boff_df;
   g.DQKV = reinterpret_cast<float*>(bb + c->boff_dqkv);
   g.DGY = reinterpret_cast<float*>(bb + c->boff_dgy);
+  g.PS = reinterpret_cast<float*>(bb + c->boff_ps);
   g.RED = reinterpret_cast<float*>(bb + c->boff_red);
+  g.WP = reinterpret_cast<float*>(bb + c->boff_wp);
   g.DP = reinterpret_cast<float*>(bb + c->boff_dp);
   if (c->two_pass) {  // A recomputed from the logits and lse into the workspace
     g.A = bb + c->boff_ar;

@@ -72,16 +72,22 @@ struct BwdArgs {
   float* DS;     // ds [B, H, NP, NP] (float32: the key-bias gradient, a sum of ds over keys, nearly cancels)
   void* DF;      // dgamma_e, dbeta_e [B, 2H, NP, NP], the layer's dtype
   float* DQKV;   // dQ | dK | dV [B, NP, 3, d]
-  float* DGY;    // dgamma_y, dbeta_y [B, 2H]
-  float* RED;    // pair-reduction partial sums [kRedCopies][2 H de + de H + de]
+  float* DGY;    // per graph: dgamma_y, dbeta_y, and the graph's parts of db_emul, db_eadd [B, 4H]
+  float* PS;     // the same four sums per block of the pair kernel [B, NP / 16, ps_kb, 4H]
+  float* RED;    // pair-reduction sums, one row per block of the reduction [red_rows][2 H de + de H + de]
+  float* WP;     // dW GEMM: weight and bias gradients per contraction slice [ksplit][3 d d + 3 d]
   float* DP;     // n > 64: parts of D_i = sum_j A_ij dA_ij per key block [B, H, NP, ceil(NP / 64)]
   int recompute_a;  // two-pass context: A [B, H, n, n] is recomputed into the buffer g.A points to
+  int ps_kb;        // key blocks of the pair-kernel launch that writes PS
+  int red_rows;     // blocks of the pair reduction
+  int ksplit;       // contraction slices of the dW GEMM
 };
 
-// Copies of the pair reduction's outputs: blocks of the reduction add into
-// copy blockIdx % kRedCopies, which keeps the number of atomic adds per
-// address low; a later kernel sums the copies.
-constexpr int kRedCopies = 32;
+// The backward sums nothing with atomics: every block writes its partial
+// sums to a slot of its own and a later kernel adds the slots in a fixed
+// order, so the gradients are the same bits on every run.
+constexpr int kRedRows = 1024;  // most blocks of the pair reduction
+constexpr int kMaxKsplit = 16;  // most contraction slices of the dW GEMM
 
 // Graph-transformer block around the layer: parameters (in this order; the
 // nn.Linear [out, in] layout, all in the layer's dtype) and arguments.

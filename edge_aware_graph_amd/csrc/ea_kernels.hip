@@ -1523,65 +1523,32 @@ __device__ __forceinline__ void store4(T* p, const float* v) {
   }
 }
 
-// bwd_prep: zero the gradients that are accumulated with atomics, and V in
-// row layout [B, H, NP, dh] (the forward keeps V^T).
+// bwd_prep: V in row layout [B, H, NP, dh] (the forward keeps V^T), one
+// (graph, head, 64 keys) tile per block through LDS, 16-byte reads and
+// writes on both sides.
 template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs g) {
   const int NP = a.NP;
-  constexpr int D = H * DH, EPC = 16 / (int)sizeof(T);
-  // The first B H ceil(NP / 64) blocks: V rows from V^T through LDS, one
-  // (graph, head, 64 keys) tile each, 16-byte reads and writes on both sides
-  const int JB = (NP + 63) / 64, nvt = a.B * H * JB;
-  if ((int)blockIdx.x < nvt) {
-    __shared__ __align__(16) T vt_s[DH][64 + EPC];
-    const int bh = blockIdx.x / JB, j0 = (blockIdx.x % JB) * 64;
-    const T* src = static_cast<const T*>(a.Vt) + (size_t)bh * DH * NP;
-    // NP is a multiple of 16: a chunk of EPC keys is wholly inside or outside
-    for (int c = threadIdx.x; c < DH * 64 / EPC; c += kThreads) {
-      const int t = c / (64 / EPC), jj = (c % (64 / EPC)) * EPC;
-      if (j0 + jj < NP)
-        *reinterpret_cast<u32x4*>(&vt_s[t][jj]) = *reinterpret_cast<const u32x4*>(src + (size_t)t * NP + j0 + jj);
-    }
-    __syncthreads();
-    T* dst = static_cast<T*>(g.Vr) + (size_t)bh * NP * DH;
-    for (int c = threadIdx.x; c < 64 * DH / EPC; c += kThreads) {
-      const int jj = c / (DH / EPC), t0 = (c % (DH / EPC)) * EPC;
-      if (j0 + jj < NP) {
-        __align__(16) T v[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) v[e] = vt_s[t0 + e][jj];
-        *reinterpret_cast<u32x4*>(dst + (size_t)(j0 + jj) * DH + t0) = *reinterpret_cast<const u32x4*>(v);
-      }
-    }
-    return;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  const int JB = (NP + 63) / 64;
+  __shared__ T vt_s[DH][64 + EPC];
+  const int bh = blockIdx.x / JB, j0 = (blockIdx.x % JB) * 64;
+  const T* src = static_cast<const T*>(a.Vt) + (size_t)bh * DH * NP;
+  // NP is a multiple of 16: a chunk of EPC keys is wholly inside or outside
+  for (int c = threadIdx.x; c < DH * 64 / EPC; c += kThreads) {
+    const int t = c / (64 / EPC), jj = (c % (64 / EPC)) * EPC;
+    if (j0 + jj < NP)
+      *reinterpret_cast<u32x4*>(&vt_s[t][jj]) = *reinterpret_cast<const u32x4*>(src + (size_t)t * NP + j0 + jj);
   }
-  // The other blocks zero what is summed atomically: the pair reduction's
-  // copies, the FiLM-bias gradients (b_emul, b_eadd), the global FiLM's
-  // weight and bias gradients, and the projection weight and bias gradients
-  const size_t nred = (size_t)kRedCopies * (3 * H * DE + DE), nzy = (size_t)2 * H * a.dy + 2 * H;
-  const size_t nz1 = nred + 2 * H + nzy, nz2 = (size_t)a.B * 2 * H;
-  const size_t nw = (size_t)3 * D * D + 3 * D;
-  const size_t stride = (size_t)(gridDim.x - nvt) * blockDim.x;
-  for (size_t k = (size_t)(blockIdx.x - nvt) * blockDim.x + threadIdx.x; k < nz1 + nz2 + nw; k += stride) {
-    if (k >= nz1 + nz2) {  // projection weight and bias gradients
-      const size_t q = k - nz1 - nz2;
-      if (q < (size_t)3 * D * D) (q < (size_t)D * D ? g.gw_q : q < (size_t)2 * D * D ? g.gw_k : g.gw_v)[q % ((size_t)D * D)] = 0.f;
-      else (q - 3 * D * D < D ? g.gb_q : q - 3 * D * D < 2 * D ? g.gb_k : g.gb_v)[(q - 3 * D * D) % D] = 0.f;
-    } else if (k < nz1) {
-      size_t q = k;
-      if (q < nred) { g.RED[q] = 0.f; continue; }
-      q -= nred;
-      if (q < (size_t)H) { g.gb_em[q] = 0.f; continue; }
-      q -= H;
-      if (q < (size_t)H) { g.gb_ea[q] = 0.f; continue; }
-      q -= H;
-      if (q < (size_t)H * a.dy) { g.gw_ym[q] = 0.f; continue; }
-      q -= (size_t)H * a.dy;
-      if (q < (size_t)H * a.dy) { g.gw_ya[q] = 0.f; continue; }
-      q -= (size_t)H * a.dy;
-      (q < (size_t)H ? g.gb_ym : g.gb_ya)[q % H] = 0.f;
-    } else {
-      g.DGY[k - nz1] = 0.f;
+  __syncthreads();
+  T* dst = static_cast<T*>(g.Vr) + (size_t)bh * NP * DH;
+  for (int c = threadIdx.x; c < 64 * DH / EPC; c += kThreads) {
+    const int jj = c / (DH / EPC), t0 = (c % (DH / EPC)) * EPC;
+    if (j0 + jj < NP) {
+      __align__(16) T v[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) v[e] = vt_s[t0 + e][jj];
+      *reinterpret_cast<u32x4*>(dst + (size_t)(j0 + jj) * DH + t0) = *reinterpret_cast<const u32x4*>(v);
     }
   }
 }
@@ -1874,14 +1841,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
     }
   }
   __syncthreads();
+  // this block's slot of PS: dgamma_y [H], dbeta_y [H], db_emul [H], db_eadd [H]
   if (tid < 4 * H) {
     float x = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) x += sum_s[ww][tid];
     const int h = tid >> 2, q = tid & 3;
-    float* dst = q == 0 ? g.DGY + (size_t)b * 2 * H + h : q == 1 ? g.DGY + (size_t)b * 2 * H + H + h
-               : q == 2 ? g.gb_em + h : g.gb_ea + h;
-    atomicAdd(dst, x);
+    g.PS[(((size_t)b * JT + blockIdx.x) * KB + blockIdx.z) * 4 * H + q * H + h] = x;
   }
 }
 
@@ -2082,15 +2048,15 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
     step(cidx + gridDim.x, r1, r0);
   }
   if (cb < DE) {
-    // copy layout: dW_emul [H][DE], dW_eadd [H][DE], dW_e [DE][H], db_e [DE]
-    float* red = g.RED + (size_t)(blockIdx.x % kRedCopies) * (3 * H * DE + DE);
+    // this block's row of RED: dW_emul [H][DE], dW_eadd [H][DE], dW_e [DE][H], db_e [DE]
+    float* red = g.RED + (size_t)blockIdx.x * (3 * H * DE + DE);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * lg + r;  // accF: FiLM row 4 lg + r, channel cb + li
-      if (row < 2 * H) atomicAdd(red + (size_t)row * DE + cb + li, accF[r]);
+      if (row < 2 * H) red[(size_t)row * DE + cb + li] = accF[r];
       const int ch = cb + 4 * lg + r;  // accE: channel cb + 4 lg + r, head li (or the sum)
-      if (li < H) atomicAdd(red + 2 * H * DE + (size_t)ch * H + li, accE[r]);
-      else if (li == H) atomicAdd(red + 3 * H * DE + ch, accE[r]);
+      if (li < H) red[2 * H * DE + (size_t)ch * H + li] = accE[r];
+      else if (li == H) red[3 * H * DE + ch] = accE[r];
     }
   }
 }
@@ -2115,7 +2081,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
   const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
   const int NP = a.NP, n = a.n;
   const int M = MODE == kDX ? a.B * NP : 3 * D, K = MODE == kDX ? 3 * D : a.B * NP;
-  // blockIdx.z takes a slice of the contraction (kDW: the partial sums are added atomically)
+  // blockIdx.z takes a slice of the contraction (kDW: each slice writes its own partial sums)
   const int kslice = (K + gridDim.z - 1) / gridDim.z;
   const int kbeg = blockIdx.z * kslice, kend = K < kbeg + kslice ? K : kbeg + kslice;
   const T* X = static_cast<const T*>(a.X);
@@ -2225,8 +2191,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
     const int m = m0 + tid;
     if (tid < 64 && m < M) {
       const float t = as[0][tid] + as[1][tid] + as[2][tid] + as[3][tid];
-      const int wsel = m / D;
-      atomicAdd((wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v) + m % D, t);
+      g.WP[(size_t)blockIdx.z * (3 * D * D + 3 * D) + 3 * D * D + m] = t;  // this slice's db of row m
     }
   }
 #pragma unroll
@@ -2242,9 +2207,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
         const int bq = m / NP, ii = m % NP;
         if (ii < n) Num<T>::st(static_cast<T*>(g.dX) + ((size_t)bq * n + ii) * D + col, v);
       } else {
-        const int wsel = m / D, f = m % D;
-        float* dst = wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v;
-        atomicAdd(dst + (size_t)f * D + col, v);
+        g.WP[(size_t)blockIdx.z * (3 * D * D + 3 * D) + (size_t)m * D + col] = v;  // this slice's dW
       }
     }
   }
@@ -2426,8 +2389,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
       float t = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) t += cs_s[r][tid];
-      const int m = m0 + tid, wsel = m / D;
-      atomicAdd((wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v) + m % D, t);
+      g.WP[(size_t)blockIdx.z * (3 * D * D + 3 * D) + 3 * D * D + m0 + tid] = t;  // this slice's db
     }
   }
 #pragma unroll
@@ -2440,81 +2402,137 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
       const int bq = m / NP, ii = m % NP;
       if (ii < n) Num<bf16_t>::st(static_cast<bf16_t*>(g.dX) + ((size_t)bq * n + ii) * D + col, v);
     } else {
-      const int wsel = m / D, f = m % D;
-      atomicAdd((wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v) + (size_t)f * D + col, v);
+      g.WP[(size_t)blockIdx.z * (3 * D * D + 3 * D) + (size_t)m * D + col] = v;  // this slice's dW
     }
   }
 }
 
-// bwd_small: the global FiLM's gradients and dy. Block row blockIdx.y takes
-// graphs b0 = 16 blockIdx.y .. b0 + 15; each thread computes one item:
+// bwd_sums: the fixed-order sums of the partial slots (no atomics anywhere
+// in the backward, so every run gives the same bits). Blocks, in order:
+//   B blocks, one per graph: DGY[b] = sum over the pair kernel's blocks of
+//     the graph (PS rows in order): dgamma_y, dbeta_y, and the graph's parts
+//     of db_emul, db_eadd;
+//   ceil(NR / 16) blocks of 16 columns of RED (NR = 3 H de + de): dW_emul,
+//     dW_eadd, dW_e, db_e as sums over the pair reduction's rows;
+//   then one thread per projection gradient (dW_q|k|v, db_q|k|v): the sum
+//     over the dW GEMM's contraction slices.
+// Column sums take a fixed split of the rows over the threads and add the
+// threads' parts in a fixed order.
+template <typename T, int H, int DH, int DE>
+__global__ __launch_bounds__(kThreads) void bwd_sums_kernel(LayerArgs a, BwdArgs g) {
+  constexpr int NR = 3 * H * DE + DE, F = 4 * H, GF = kThreads / F, CB = 16, GC = kThreads / CB, D = H * DH;
+  static_assert(kThreads % F == 0, "whole groups");
+  __shared__ float part_s[kThreads];
+  const int tid = threadIdx.x, B = a.B;
+  const int nrb = (NR + CB - 1) / CB;
+  // column c of `rows` rows (row stride `stride`), rows split over `groups`
+  // threads: rows q, q + groups, ... for the thread of group q
+  auto colsum = [&](const float* base, int rows, size_t stride, int groups, int q) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int r = q;
+    for (; r + 3 * groups < rows; r += 4 * groups) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = base[(size_t)(r + u * groups) * stride];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += v[u];
+    }
+    for (; r < rows; r += groups) acc[0] += base[(size_t)r * stride];
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+  if ((int)blockIdx.x < B) {
+    const int b = blockIdx.x, rows = a.NP / 16 * g.ps_kb;
+    const int c = tid % F, q = tid / F;
+    part_s[tid] = colsum(g.PS + (size_t)b * rows * F + c, rows, F, GF, q);
+    __syncthreads();
+    if (tid < F) {
+      float t = 0.f;
+      for (int k = 0; k < GF; ++k) t += part_s[k * F + tid];
+      g.DGY[(size_t)b * F + tid] = t;
+    }
+  } else if ((int)blockIdx.x < B + nrb) {
+    const int c = ((int)blockIdx.x - B) * CB + tid % CB, q = tid / CB;
+    part_s[tid] = c < NR ? colsum(g.RED + c, g.red_rows, NR, GC, q) : 0.f;
+    __syncthreads();
+    if (tid < CB && c < NR) {
+      float t = 0.f;
+      for (int k = 0; k < GC; ++k) t += part_s[k * CB + tid];
+      if (c < H * DE) g.gw_em[c] = t;
+      else if (c < 2 * H * DE) g.gw_ea[c - H * DE] = t;
+      else if (c < 3 * H * DE) g.gw_e[c - 2 * H * DE] = t;
+      else g.gb_e[c - 3 * H * DE] = t;
+    }
+  } else {
+    const size_t nw = (size_t)3 * D * D + 3 * D;
+    const size_t o = (size_t)((int)blockIdx.x - B - nrb) * kThreads + tid;
+    if (o >= nw) return;
+    float t = 0.f;
+    for (int z = 0; z < g.ksplit; ++z) t += g.WP[(size_t)z * nw + o];
+    if (o < (size_t)3 * D * D) {
+      const int wsel = (int)(o / ((size_t)D * D));
+      (wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v)[o % ((size_t)D * D)] = t;
+    } else {
+      const int m = (int)(o - (size_t)3 * D * D), wsel = m / D;
+      (wsel == 0 ? g.gb_q : wsel == 1 ? g.gb_k : g.gb_v)[m % D] = t;
+    }
+  }
+}
+
+// bwd_small: the global FiLM's gradients and dy, from the per-graph sums
+// DGY [B, 4H] (dgamma_y, dbeta_y, db_emul part, db_eadd part); one thread
+// per item, sums over the graphs in graph order:
 //   dy[b][c]         = sum_h W_ymul[h][c] dgamma_y[b][h] + W_yadd[h][c] dbeta_y[b][h]
-//   dW_y(mul|add)[h][c] += sum_b dgamma_y|dbeta_y[b][h] y[b][c]   (atomic over blocks)
-//   db_y(mul|add)[h]    += sum_b dgamma_y|dbeta_y[b][h]           (atomic over blocks)
-// and (block row 0) the sums of the pair reduction's copies: dW_emul, dW_eadd,
-// dW_e, db_e. All of an item's loads are independent and issued together.
+//   dW_y(mul|add)[h][c] = sum_b dgamma_y|dbeta_y[b][h] y[b][c]
+//   db_y(mul|add)[h]    = sum_b dgamma_y|dbeta_y[b][h]
+//   db_e(mul|add)[h]    = sum_b (the graph's part)
 template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int GB = 16;
-  const int B = a.B, dy = a.dy, b0 = blockIdx.y * GB;
+  constexpr int F = 4 * H;
+  const int B = a.B, dy = a.dy;
   const int item = blockIdx.x * kThreads + threadIdx.x;
-  const int n_dy = GB * dy, n_w = 2 * H * dy, n_b = 2 * H;
+  const int n_dy = B * dy, n_w = 2 * H * dy, n_b = 2 * H;
   const T* y = static_cast<const T*>(a.y);
   const T* Wm = static_cast<const T*>(a.w_ymul);
   const T* Wa = static_cast<const T*>(a.w_yadd);
+  // sum over the graphs of DGY[b][o] times f(b), four graphs per step
+  auto over_graphs = [&](int o, auto f) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int b = 0;
+    for (; b + 3 < B; b += 4) {
+      float v[4], w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = g.DGY[(size_t)(b + u) * F + o];
+        w[u] = f(b + u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += v[u] * w[u];
+    }
+    for (; b < B; ++b) acc[0] += g.DGY[(size_t)b * F + o] * f(b);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
   if (item < n_dy) {
-    const int bb = item / dy, c = item % dy, b = b0 + bb, bc = b < B ? b : 0;
+    const int b = item / dy, c = item % dy;
     float dg[2 * H], wv[2 * H];
 #pragma unroll
     for (int o = 0; o < 2 * H; ++o) {
-      dg[o] = g.DGY[(size_t)bc * 2 * H + o];
+      dg[o] = g.DGY[(size_t)b * F + o];
       wv[o] = Num<T>::ld((o < H ? Wm : Wa) + (size_t)(o % H) * dy + c);
     }
     float s = 0.f;
 #pragma unroll
     for (int o = 0; o < 2 * H; ++o) s += wv[o] * dg[o];
-    if (b < B) Num<T>::st(static_cast<T*>(g.dy) + (size_t)b * dy + c, s);
+    Num<T>::st(static_cast<T*>(g.dy) + (size_t)b * dy + c, s);
   } else if (item < n_dy + n_w) {
     const int o = (item - n_dy) / dy, c = (item - n_dy) % dy;
-    float dg[GB], yv[GB];
-#pragma unroll
-    for (int bb = 0; bb < GB; ++bb) {
-      const int b = b0 + bb, bc = b < B ? b : 0;
-      const float x = g.DGY[(size_t)bc * 2 * H + o], v = Num<T>::ld(y + (size_t)bc * dy + c);
-      dg[bb] = b < B ? x : 0.f;
-      yv[bb] = v;
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < GB; ++bb) s += dg[bb] * yv[bb];
-    atomicAdd((o < H ? g.gw_ym : g.gw_ya) + (size_t)(o % H) * dy + c, s);
-  } else if (item >= n_dy + n_w + n_b) {
-    constexpr int NR = 3 * H * DE + DE;
-    const int o = item - n_dy - n_w - n_b;
-    if (blockIdx.y != 0 || o >= NR) return;
-    float v[kRedCopies];
-#pragma unroll
-    for (int k = 0; k < kRedCopies; ++k) v[k] = g.RED[(size_t)k * NR + o];
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < kRedCopies; ++k) s += v[k];
-    if (o < H * DE) g.gw_em[o] = s;
-    else if (o < 2 * H * DE) g.gw_ea[o - H * DE] = s;
-    else if (o < 3 * H * DE) g.gw_e[o - 2 * H * DE] = s;
-    else g.gb_e[o - 3 * H * DE] = s;
-  } else {
+    const float s = over_graphs(o, [&](int b) { return Num<T>::ld(y + (size_t)b * dy + c); });
+    (o < H ? g.gw_ym : g.gw_ya)[(size_t)(o % H) * dy + c] = s;
+  } else if (item < n_dy + n_w + n_b) {
     const int o = item - n_dy - n_w;
-    float dg[GB];
-#pragma unroll
-    for (int bb = 0; bb < GB; ++bb) {
-      const int b = b0 + bb, bc = b < B ? b : 0;
-      const float x = g.DGY[(size_t)bc * 2 * H + o];
-      dg[bb] = b < B ? x : 0.f;
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < GB; ++bb) s += dg[bb];
-    atomicAdd((o < H ? g.gb_ym : g.gb_ya) + o % H, s);
+    (o < H ? g.gb_ym : g.gb_ya)[o % H] = over_graphs(o, [](int) { return 1.f; });
+  } else if (item < n_dy + n_w + 2 * n_b) {
+    const int o = item - n_dy - n_w - n_b;  // 0 .. 2H - 1: db_emul, then db_eadd
+    (o < H ? g.gb_em : g.gb_ea)[o % H] = over_graphs(2 * H + o, [](int) { return 1.f; });
   }
 }
 
@@ -2599,14 +2617,18 @@ hipError_t qkv_shape(const LayerArgs& a, hipStream_t s) {
 }
 
 template <typename T, int H, int DH, int DE>
-hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
+hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g0, hipStream_t s) {
   constexpr int D = H * DH;
   const int JT = a.NP / 16;
-  // prep: B H ceil(NP / 64) transpose tiles, then blocks zeroing the atomic sums
-  const size_t nzero = (size_t)kRedCopies * (3 * H * DE + DE) + 2 * H + (size_t)2 * H * a.dy + 2 * H +
-                       (size_t)a.B * 2 * H + (size_t)3 * D * D + 3 * D;
-  const size_t zblocks = (nzero + kThreads - 1) / kThreads < 1024 ? (nzero + kThreads - 1) / kThreads : 1024;
-  const unsigned prep_blocks = (unsigned)((size_t)a.B * H * ((a.NP + 63) / 64) + zblocks);  // < 2^31 for n <= 2^20
+  BwdArgs g = g0;
+  const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
+  // the pair reduction: 1024 blocks, four per CU (the LDS fits four), all resident
+  g.red_rows = (int)(chunks < (size_t)kRedRows ? chunks : (size_t)kRedRows);
+  // dW: the rows (contraction) split in slices of at least 256
+  const int rows = a.B * a.NP;
+  g.ksplit = rows / 256 < 1 ? 1 : (rows / 256 > kMaxKsplit ? kMaxKsplit : rows / 256);
+  g.ps_kb = (g.recompute_a || a.NP > 64) ? (a.NP + 63) / 64 : 1;
+  const unsigned prep_blocks = (unsigned)((size_t)a.B * H * ((a.NP + 63) / 64));  // < 2^31 for n <= 2^20
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
   const int KB = (a.NP + 63) / 64;
   if (g.recompute_a) {  // two-pass context: A recomputed (and stored) by the first pass
@@ -2619,14 +2641,8 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
   }
   hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B, (a.NP + 63) / 64), dim3(kThreads), 0, s, a, g);
-  const size_t chunks = ((size_t)a.B * a.NP * a.NP + 63) / 64;
-  // 1024 blocks: four per CU (the LDS fits four), all resident; each output
-  // takes one atomic add per block, spread over the 32 copies
-  const unsigned red_blocks = (unsigned)(chunks < 1024 ? chunks : 1024);
-  hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(red_blocks), dim3(kThreads), 0, s, a, g);
-  // dW: the rows (contraction) split in slices of at least 256
-  const int rows = a.B * a.NP, ksplit = rows / 256 < 1 ? 1 : (rows / 256 > 16 ? 16 : rows / 256);
-  const dim3 gdx((a.B * a.NP + 63) / 64, D / 64, 1), gdw(3 * D / 64, D / 64, ksplit);
+  hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(g.red_rows), dim3(kThreads), 0, s, a, g);
+  const dim3 gdx((a.B * a.NP + 63) / 64, D / 64, 1), gdw(3 * D / 64, D / 64, g.ksplit);
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH, kDX>), gdx, dim3(kThreads), 0, s, a, g);
     hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH, kDW>), gdw, dim3(kThreads), 0, s, a, g);
@@ -2634,8 +2650,11 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 64>), gdx, dim3(kThreads), 0, s, a, g);
     hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW, 64>), gdw, dim3(kThreads), 0, s, a, g);
   }
-  const int small_items = 16 * a.dy + 2 * H * a.dy + 2 * H + 3 * H * DE + DE;
-  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH, DE>), dim3((small_items + kThreads - 1) / kThreads, (a.B + 15) / 16),
+  constexpr int NR = 3 * H * DE + DE;
+  const size_t sums_blocks = (size_t)a.B + (NR + 15) / 16 + ((size_t)3 * D * D + 3 * D + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((bwd_sums_kernel<T, H, DH, DE>), dim3((unsigned)sums_blocks), dim3(kThreads), 0, s, a, g);
+  const size_t small_items = (size_t)a.B * a.dy + 2 * H * a.dy + 4 * H;
+  hipLaunchKernelGGL((bwd_small_kernel<T, H, DH, DE>), dim3((unsigned)((small_items + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, a, g);
   return hipGetLastError();
 }

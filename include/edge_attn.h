@@ -219,10 +219,9 @@ ea_status edge_attn_layer_noalloc(ea_ctx* ctx, const ea_attn_params* p, const ea
  * in the parameters' layouts, overwritten (not accumulated). bws is the
  * backward's own workspace (ea_backward_workspace_bytes, 256-byte aligned).
  * Masked pairs get dE = +0.0; padded rows of dX are +0.0.
- * Repeatability: dX and dE come from sums in a fixed order and repeat
- * bitwise; dy and the weight gradients are sums over many blocks added with
- * float32 atomics, whose order varies between calls, so two identical calls
- * agree to the float32 rounding of those sums but not always bitwise.
+ * Repeatability: every output is a sum in a fixed order (no atomics: blocks
+ * write partial sums to slots of their own, which a later kernel adds in
+ * order), so identical calls give the same bits.
  */
 typedef struct {
   float *w_q, *w_k, *w_v;       /* [d, d] */

@@ -214,18 +214,16 @@ def test_backward_large_full_size_sampled_rows():
         assert err <= 2e-2 * scale, "graph %d rows %s: max err %.3e > 2e-2 * %.3e" % (b, rows, err, scale)
 
 
-def test_backward_repeatable_within_float32_summation_order():
-    """Two identical backward calls. dE and dX come from fixed-order sums and
-    must agree bitwise; the weight gradients are sums over many blocks added
-    with float32 atomics, whose order varies from run to run, so they agree
-    to float32 rounding of those sums (1e-5 of each tensor's scale), not
-    necessarily bitwise."""
-    dims = dims_of("planar", B=4)
-    batch = W.make_batch("planar", bias_scale=0.1, dims=dims)
-    g1, _ = run_backward(batch, dims, seed=3)
-    g2, _ = run_backward(batch, dims, seed=3)
-    for k in ("X", "E"):
-        assert np.array_equal(g1[k], g2[k]), k
-    for k in g1:
-        scale = max(float(np.abs(g1[k]).max()), 1e-6)
-        assert np.abs(g1[k].astype(np.float64) - g2[k]).max() <= 1e-5 * scale, k
+@pytest.mark.parametrize("name,over,two_pass", [("planar", {"B": 4}, False), ("tiny", {"dtype": "fp32"}, False),
+                                               ("sbm", {"B": 2}, False), ("planar", {"B": 2}, True)],
+                         ids=["planar-bf16", "tiny-fp32", "sbm-bf16", "planar-two-pass"])
+def test_backward_bitwise_repeatable(name, over, two_pass):
+    """Three identical backward calls give the same bits in every gradient:
+    nothing is summed with atomics (each block writes its partial sums to a
+    slot of its own, and the slots are added in a fixed order)."""
+    dims = dims_of(name, **over)
+    batch = W.make_batch(name, bias_scale=0.1, dims=dims)
+    runs = [run_backward(batch, dims, seed=3, force_two_pass=two_pass)[0] for _ in range(3)]
+    for k in runs[0]:
+        for r in runs[1:]:
+            assert np.array_equal(runs[0][k], r[k], equal_nan=False), k
