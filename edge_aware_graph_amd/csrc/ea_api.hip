@@ -23,7 +23,7 @@ struct ea_ctx {
   int generic;     // the shape has no tuned kernels: the generic path runs
   int forward_done;
   size_t esz;      // element size of desc.dtype
-  size_t off_q, off_k, off_v, off_lse, off_gy, ws_bytes;
+  size_t off_q, off_k, off_v, off_lse, off_gy, off_order, ws_bytes;
   size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_ps, boff_red, boff_wp, boff_dp, boff_ar, bws_bytes;  // backward workspace
   int blk_nxb, blk_exb;  // block: node and edge blocks per graph
   size_t blk_off_o, blk_off_a, blk_off_px, blk_off_pe, blk_bytes;  // block workspace (after the layer's)
@@ -257,7 +257,8 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->off_v = 2 * qkv;
   c->off_lse = 3 * qkv;
   c->off_gy = c->off_lse + round256((size_t)d.B * d.H * c->NP * sizeof(float));
-  c->ws_bytes = c->off_gy + round256((size_t)d.B * 2 * d.H * sizeof(float));
+  c->off_order = c->off_gy + round256((size_t)d.B * 2 * d.H * sizeof(float));
+  c->ws_bytes = c->off_order + round256((size_t)d.B * (c->NP / 16) * sizeof(int));
   const size_t pairs = (size_t)d.B * c->NP * c->NP;
   c->boff_ds = qkv;  // V rows first
   c->boff_df = c->boff_ds + round256(pairs * d.H * sizeof(float));
@@ -415,6 +416,8 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
   a.O = O;
   a.A = A;
   a.E_out = E_out;
+  if (!c->generic && !c->two_pass && ea::wants_order(c->d.dtype, c->d.H, c->d.dh, c->d.de, c->d.B, c->NP))
+    a.order = reinterpret_cast<int*>(static_cast<char*>(ws) + c->off_order);
   c->forward_done = 0;
   EA_TRY(run_qkv(c, a, s));
   if (c->generic) {

@@ -43,6 +43,7 @@ struct LayerArgs {
   void* Vt;    // [B, H, dh, NP]
   float* lse;  // [B, H, NP]
   float* gy;   // [B, 2H]: gamma_y (1 + ...) then beta_y per graph
+  int* order;  // [B NP/16]: work order of the layer's attention kernel, or NULL (see wants_order)
   // outputs
   void* O;
   void* A;       // attention map (kSingle/kFused) or the map to read (kReadA)
@@ -125,6 +126,9 @@ hipError_t launch_backward(const LayerArgs& a, const BwdArgs& g, int dtype, int 
                            hipStream_t s);
 // Whether (dtype, H, dh, de) is instantiated.
 bool shape_supported(int dtype, int H, int dh, int de);
+// Whether the layer's attention kernel (kFused) for this shape takes a work
+// order (LayerArgs::order), which qkv_kernel then writes.
+bool wants_order(int dtype, int H, int dh, int de, int B, int NP);
 
 // Generic path: any shape the boundary accepts (dh in {16, 32, 64}, de a
 // multiple of 16, 2H <= 32), one block per query row, runtime sizes.

@@ -124,6 +124,98 @@ __device__ __forceinline__ void global_film(const LayerArgs& a, uint32_t m0, uin
   }
 }
 
+// Most logical blocks the work order sorts (one byte of LDS each); larger
+// batches keep the plain order.
+constexpr int kOrderMax = 16384;
+constexpr int kOrderKeys = 6;  // 0, and 1 + 0..4 live tiles per wave
+
+// Work order of fused_stream_kernel (a.order): its logical blocks (graph,
+// 16-query block) sorted by expected length, longest first, equal lengths in
+// index order.
+// The hardware deals block ids to the 8 XCDs in turn and each XCD starts its
+// blocks in id order, so every XCD gets the same mix of long and short
+// blocks and starts the longest ones first (with a prefix node mask the
+// blocks of a ragged batch range from one key tile to several per wave). A
+// block's length is taken as 1 + the most key tiles with a real key that one
+// of its waves reads (wave w reads tiles w, w + kWaves, ...), and 0 without a
+// real query. One block of threads; smem: kOrderMax + 128 bytes.
+__device__ __forceinline__ void work_order(const LayerArgs& a, unsigned char* smem) {
+  const int n = a.n, JT = a.NP / 16, NB = a.B * JT;
+  uint8_t* real_s = smem;  // per (graph, 16-node group): some real node
+  int* cnt_s = reinterpret_cast<int*>(smem + kOrderMax);
+  int* wcnt_s = cnt_s + kOrderKeys;  // [kWaves][kOrderKeys]
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  // a 16-node group is a query block and a key tile at once
+  for (int p = tid; p < NB; p += kThreads) {
+    const int b = p / JT, t = p % JT;
+    uint32_t m[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 16 * t + r;
+      m[r] = a.mask[(size_t)b * n + (j < n ? j : n - 1)];
+    }
+    uint32_t any = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) any |= (16 * t + r < n) ? m[r] : 0u;
+    real_s[p] = any != 0u;
+  }
+  if (tid < kOrderKeys) cnt_s[tid] = 0;
+  __syncthreads();
+  auto key_of = [&](int L) -> int {
+    if (!real_s[L]) return 0;
+    const uint8_t* g = real_s + (L / JT) * JT;
+    int most = 0;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      int c = 0;
+      for (int jt = ww; jt < JT; jt += kWaves) c += g[jt];
+      most = c > most ? c : most;
+    }
+    return 1 + (most < kOrderKeys - 2 ? most : kOrderKeys - 2);
+  };
+  for (int L = tid; L < NB; L += kThreads) atomicAdd(&cnt_s[key_of(L)], 1);
+  __syncthreads();
+  // next position of each key: longer blocks first (the blocks without a
+  // real query, zero stores only, last: placed right after the longest ones
+  // instead, they shared the first round's bandwidth with them and the
+  // kernel took as long)
+  int start[kOrderKeys];
+  {
+    int acc = 0;
+#pragma unroll
+    for (int k = kOrderKeys - 1; k >= 0; --k) {
+      start[k] = acc;
+      acc += cnt_s[k];
+    }
+  }
+  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));  // lanes under this one
+  for (int c0 = 0; c0 < NB; c0 += kThreads) {
+    const int L = c0 + tid;
+    const int k = L < NB ? key_of(L) : -1;
+    int rank = 0;
+#pragma unroll
+    for (int kk = 0; kk < kOrderKeys; ++kk) {
+      const uint64_t bal = __ballot(k == kk);
+      if (l == 0) wcnt_s[w * kOrderKeys + kk] = __popcll(bal);
+      if (k == kk) rank = __popcll(bal & below);
+    }
+    __syncthreads();
+    if (k >= 0) {
+      int pos = rank;
+#pragma unroll
+      for (int kk = 0; kk < kOrderKeys; ++kk)
+        if (kk == k) {
+          pos += start[kk];
+          for (int ww = 0; ww < w; ++ww) pos += wcnt_s[ww * kOrderKeys + kk];
+        }
+      a.order[pos] = L;
+    }
+#pragma unroll
+    for (int kk = 0; kk < kOrderKeys; ++kk)
+      for (int ww = 0; ww < kWaves; ++ww) start[kk] += wcnt_s[ww * kOrderKeys + kk];
+    __syncthreads();
+  }
+}
+
 // Q | K | V = X W^T + b for rows (b, i) of the padded batch; rows of padded
 // nodes and the slots i in [n, NP) are written as zeros. Q, K: [B, H, NP, DH];
 // V transposed: [B, H, DH, NP]. One block computes a 64-row x 64-feature tile:
@@ -148,7 +240,15 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(LayerArgs a) {
   const uint32_t NP = a.NP, n = a.n;
   const uint32_t rows = (uint32_t)a.B * NP;  // < 2^31 (checked at context creation)
   const uint32_t m0 = blockIdx.x * 64u;
-  const int f0 = blockIdx.y * 64;
+  // with a work order to write, column 0 is an extra column whose first
+  // block (the first one dispatched) writes it
+  const int yb = a.order ? (int)blockIdx.y - 1 : (int)blockIdx.y;
+  if (yb < 0) {
+    static_assert(sizeof(lds) >= kOrderMax + 128, "LDS of the work order");
+    if (blockIdx.x == 0) work_order(a, reinterpret_cast<unsigned char*>(lds));
+    return;
+  }
+  const int f0 = yb * 64;
   if (f0 >= 3 * D) {  // extra column of blocks
     global_film<T, H>(a, m0, 64u, rows);
     return;
@@ -511,6 +611,85 @@ struct Scorer {
   }
 };
 
+// E streamed through LDS in half tiles (bfloat16, de = 64): the 8 keys of one
+// half of a 16 x 16 (query, key) tile. LDS row r holds query row i0 + r: its
+// 8 keys, 1 KB contiguous in E, padded by 16 bytes so that the fragment reads
+// below fall on distinct banks.
+template <typename T, int DE>
+struct EHalf {
+  static_assert(sizeof(T) == 2 && DE == 64, "bfloat16, de = 64");
+  static constexpr int kRowPitch = 8 * DE * 2 + 16;  // bytes
+  static constexpr int kBytes = 16 * kRowPitch;      // one half tile
+  // 16 global-to-LDS loads, one per query row, into half `half` of the two
+  // half tiles at ebase: lane l moves the 16-byte piece l % 8 of key
+  // 16 jt + 8 half + l / 8. Rows and keys past n read row and key n - 1
+  // (their values are discarded by the selects of the score stage and of the
+  // edge update); valid = false reads the zero table instead, so that the
+  // count of loads is the same.
+  static __device__ __forceinline__ void fetch(const T* Eb, int n, int i0, int jt, int half, bool valid,
+                                               unsigned char* ebase, int l) {
+    const int j = 16 * jt + 8 * half + (l >> 3);
+    const int jc = j < n ? j : n - 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ir = i0 + r < n ? i0 + r : n - 1;
+      const T* src = valid ? Eb + ((size_t)ir * n + jc) * DE + (l & 7) * 8 : zeros<T>() + (l & 15) * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)(ebase + half * kBytes + r * kRowPitch),
+                                       16, 0, 0);
+    }
+  }
+  // This lane's E fragments (query row li, channel quarter lg) of all 8 keys
+  // of the half, read in one asm block that also waits for the reads. The
+  // compiler cannot tell which LDS bytes a global-to-LDS transfer writes, so
+  // before any LDS read it sees, it waits for every transfer in flight; reads
+  // it does not see leave the next half tile in flight (the kernels wait for
+  // the half tile they read explicitly).
+  static __device__ __forceinline__ void frags8(const unsigned char* half, int li, int lg, Frag<T, DE / 4> (&e)[8]) {
+    const uint32_t a = (uint32_t)(size_t)(__attribute__((address_space(3))) const unsigned char*)(
+        half + li * kRowPitch + lg * (DE / 4) * 2);
+    u32x4 v[16];
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:16\n\t"
+        "ds_read_b128 %2, %16 offset:128\n\t"
+        "ds_read_b128 %3, %16 offset:144\n\t"
+        "ds_read_b128 %4, %16 offset:256\n\t"
+        "ds_read_b128 %5, %16 offset:272\n\t"
+        "ds_read_b128 %6, %16 offset:384\n\t"
+        "ds_read_b128 %7, %16 offset:400\n\t"
+        "ds_read_b128 %8, %16 offset:512\n\t"
+        "ds_read_b128 %9, %16 offset:528\n\t"
+        "ds_read_b128 %10, %16 offset:640\n\t"
+        "ds_read_b128 %11, %16 offset:656\n\t"
+        "ds_read_b128 %12, %16 offset:768\n\t"
+        "ds_read_b128 %13, %16 offset:784\n\t"
+        "ds_read_b128 %14, %16 offset:896\n\t"
+        "ds_read_b128 %15, %16 offset:912\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7]),
+          "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]), "=v"(v[14]), "=v"(v[15])
+        : "v"(a));
+    static_assert(DE * 2 == 128, "key pitch of the offsets above");
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      e[k].w[0] = v[2 * k].x; e[k].w[1] = v[2 * k].y; e[k].w[2] = v[2 * k].z; e[k].w[3] = v[2 * k].w;
+      e[k].w[4] = v[2 * k + 1].x; e[k].w[5] = v[2 * k + 1].y; e[k].w[6] = v[2 * k + 1].z; e[k].w[7] = v[2 * k + 1].w;
+    }
+  }
+  // This lane's E fragment (query row li, channel quarter lg) of key k of the
+  // half: two 16-byte LDS reads.
+  static __device__ __forceinline__ Frag<T, DE / 4> frag(const unsigned char* half, int li, int lg, int k) {
+    const unsigned char* p = half + li * kRowPitch + lg * (DE / 4) * 2 + k * DE * 2;
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(p + 16);
+    Frag<T, DE / 4> e;
+    e.w[0] = v0.x; e.w[1] = v0.y; e.w[2] = v0.z; e.w[3] = v0.w;
+    e.w[4] = v1.x; e.w[5] = v1.y; e.w[6] = v1.z; e.w[7] = v1.w;
+    return e;
+  }
+};
+
 // +0.0 into the edge outputs of one 16 x 16 tile (pairs inside the n x n layout).
 template <typename T, int DE>
 __device__ __forceinline__ void zero_edge_tile(T* Eout, int b, int n, int i, int j0, int lg) {
@@ -583,11 +762,11 @@ struct Updater {
   // of each head (the layout of the A store and of the A V operand).
   // mid() runs once, after the first 8 keys (every caller's wave must reach
   // it exactly once: it may hold a barrier).
-  template <bool KEEP, typename Mid>
-  __device__ __forceinline__ void tile(const ETile<T, DE>& et, const T* E, T* Eout, int b, int n, int i,
-                                       bool mi, int j0, int lg, uint32_t bits, bool full,
-                                       const Frag<T, 4> (&A)[H], Mid&& mid) const {
-    float R[4][RW];
+  // The head operand of the update's products for one tile, from A as laid
+  // out by the A store (this lane: keys 4*lg .. 4*lg+3 of each head);
+  // afterwards block x of lane group lg holds key 4*x + r', heads
+  // lg*QH .. (lg+1)*QH - 1.
+  __device__ __forceinline__ void head_operand(const Frag<T, 4> (&A)[H], float (&R)[4][RW]) const {
     if constexpr (kBF) {
       // R[x][2*r' + q2]: packed bfloat16 pair (head 4x + 2q2, head 4x + 2q2 + 1)
       // of key 4*lg + r'; slot H holds 1 (against b_e), the rest 0
@@ -615,8 +794,15 @@ struct Updater {
             R[x][rp * QH + q] = h < H ? A[h].get(rp) : 0.f;
           }
     }
-    // now block x of lane group lg: key 4*x + r', heads lg*QH .. (lg+1)*QH - 1
     lane_group_transpose<RW>(R);
+  }
+
+  template <bool KEEP, typename Mid>
+  __device__ __forceinline__ void tile(const ETile<T, DE>& et, const T* E, T* Eout, int b, int n, int i,
+                                       bool mi, int j0, int lg, uint32_t bits, bool full,
+                                       const Frag<T, 4> (&A)[H], Mid&& mid) const {
+    float R[4][RW];
+    head_operand(A, R);
     const size_t rowoff = ((size_t)b * n + i) * n * DE + lg * (DE / 4);
     if (bits == 0u) {  // no real pair in the tile (uniform): zeros only
       zero_edge_tile<T, DE>(Eout, b, n, i, j0, lg);
@@ -687,10 +873,11 @@ struct Updater {
     }
   }
 
-  // One key of the tile: ef holds this lane's E channels of pair (i, j).
+  // The outputs of one key of the tile: ef holds this lane's E channels of
+  // pair (i, j); masked pairs give +0.0 (unless FULL: every pair is real).
   template <bool FULL>
-  __device__ __forceinline__ void step(const Frag<T, DE / 4>& ef, T* Eout, size_t off, bool inb, bool real,
-                                       const float (&R)[4][RW], int jj) const {
+  __device__ __forceinline__ void outputs(const Frag<T, DE / 4>& ef, bool real, const float (&R)[4][RW], int jj,
+                                          float (&out)[DE / 4]) const {
     Frag<T, QH> af;
     if constexpr (kBF) {
       af.w[0] = has_heads ? __float_as_uint(R[jj >> 2][2 * (jj & 3)]) : 0u;
@@ -698,7 +885,6 @@ struct Updater {
     } else {
       if (has_heads) af.set(&R[jj >> 2][(jj & 3) * QH]); else af.zero();
     }
-    float out[DE / 4];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       f32x4 c;
@@ -716,11 +902,29 @@ struct Updater {
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[4 * ch + r] = (FULL || real) ? c[r] : 0.f;
     }
+  }
+  // One key of the tile, stored when the pair lies inside the layout (inb).
+  template <bool FULL>
+  __device__ __forceinline__ void step(const Frag<T, DE / 4>& ef, T* Eout, size_t off, bool inb, bool real,
+                                       const float (&R)[4][RW], int jj) const {
+    float out[DE / 4];
+    outputs<FULL>(ef, real, R, jj, out);
     if (FULL || inb) {
       Frag<T, DE / 4> of;
       of.set(out);
       of.store(Eout + off);
     }
+  }
+  // One key of the tile, stored by every lane to dst (the caller points lanes
+  // whose pair lies outside the layout at a sink).
+  template <bool FULL>
+  __device__ __forceinline__ void step_to(const Frag<T, DE / 4>& ef, T* dst, bool real, const float (&R)[4][RW],
+                                          int jj) const {
+    float out[DE / 4];
+    outputs<FULL>(ef, real, R, jj, out);
+    Frag<T, DE / 4> of;
+    of.set(out);
+    of.store(dst);
   }
 };
 
@@ -782,8 +986,53 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
+// Barrier for data exchanged through LDS only: this wave's LDS operations are
+// complete before s_barrier, and its global memory operations stay in
+// flight (__syncthreads() waits for those as well). The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  wait_lgkmcnt0();
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
 
 // ------------------------------------------------------------------ attention
+
+// A block without a real query: its rows of A, O (and E') are +0.0. Wave w
+// writes the key tiles w, w + kWaves, ... of its rows.
+template <typename T, int H, int DH, int DE, int MAXT, bool EDGE>
+__device__ __forceinline__ void zero_block(const LayerArgs& a, int b, int i0, int i, int w, int lg) {
+  constexpr int D = H * DH;
+  const int n = a.n, JT = a.NP / 16;
+  T* Ag = static_cast<T*>(a.A);
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) {
+    const int jt = w + kWaves * tt, jb = 16 * jt + 4 * lg;
+    if (jt >= JT || i >= n) continue;
+    Frag<T, 4> z;
+    z.zero();
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      T* row = Ag + (((size_t)b * H + h) * n + i) * n;
+      if ((n & 3) == 0) {  // uniform: 4 keys in or out together, one vector store
+        if (jb < n) z.store(row + jb);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (jb + r < n) Num<T>::st(row + jb + r, 0.f);
+      }
+    }
+    if constexpr (EDGE) zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, 16 * jt, lg);
+  }
+  for (int idx = threadIdx.x; idx < 16 * D / 4; idx += kThreads) {
+    const int il = idx / (D / 4), c = (idx % (D / 4)) * 4;
+    if (i0 + il >= n) continue;
+    Frag<T, 4> z;
+    z.zero();
+    z.store(static_cast<T*>(a.O) + ((size_t)b * n + i0 + il) * D + c);
+  }
+}
 
 // Single-pass tail shared by kSingle and kFused: masked softmax over the full
 // row (lane groups by register swaps, waves through LDS), A rounded to the
@@ -1006,6 +1255,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
       static_assert(kAfterHalf < 64, "vmcnt range");
       unsigned char* ebase = smem_raw + (size_t)w * 2 * kHalfBytes;
       const T* erow0 = sc.E + ((size_t)b * n) * n * DE;  // graph b
+      // the transfers of EHalf::fetch, written out: through that helper the
+      // compiler allocates this loop's registers differently (3811 against
+      // 3508 instructions, more accumulator-register copies)
       auto fetch_half = [&](int jt, int half, bool valid) {
         const int j = 16 * jt + 8 * half + (l >> 3);  // lane l: key j, 16-byte piece l % 8
         const int jc = j < n ? j : n - 1;
@@ -1026,16 +1278,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
         mk_raw = sc.mask_b[k_in ? j : n - 1];
       };
       auto film_half = [&](int half, const f32x4& fc, float (&R)[4][16]) {
-        const unsigned char* rowp = ebase + half * kHalfBytes + li * kRowPitch + lg * (DE / 4) * 2;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          Frag<T, DE / 4> e;
-          const u32x4 v0 = *reinterpret_cast<const u32x4*>(rowp + k * DE * 2);
-          const u32x4 v1 = *reinterpret_cast<const u32x4*>(rowp + k * DE * 2 + 16);
-          e.w[0] = v0.x; e.w[1] = v0.y; e.w[2] = v0.z; e.w[3] = v0.w;
-          e.w[4] = v1.x; e.w[5] = v1.y; e.w[6] = v1.z; e.w[7] = v1.w;
-          sc.film(e, fc, R, 8 * half + k);
-        }
+        for (int k = 0; k < 8; ++k) sc.film(EHalf<T, DE>::frag(ebase + half * kHalfBytes, li, lg, k), fc, R, 8 * half + k);
       };
       if (sc.mi_any && w < JT) {  // uniform per wave
         Frag<T, DH / 4> kf[H];
@@ -1171,27 +1415,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
       if constexpr (MODE != kLogits) {
         if ((__ballot(sc.mi) & 0xffffull) == 0ull) {
           // no real query in the block (uniform): A, O and E' rows are all +0.0
-          T* Ag = static_cast<T*>(a.A);
-#pragma unroll
-          for (int tt = 0; tt < MAXT; ++tt) {
-            const int jt = w + kWaves * tt, jb = 16 * jt + 4 * lg;
-            if (jt >= JT || i >= n) continue;
-#pragma unroll
-            for (int h = 0; h < H; ++h) {
-              T* row = Ag + (((size_t)b * H + h) * n + i) * n;
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (jb + r < n) Num<T>::st(row + jb + r, 0.f);
-            }
-            if constexpr (MODE == kFused) zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, 16 * jt, lg);
-          }
-          for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
-            const int il = idx / (D / 4), c = (idx % (D / 4)) * 4;
-            if (i0 + il >= n) continue;
-            Frag<T, 4> z;
-            z.zero();
-            z.store(static_cast<T*>(a.O) + ((size_t)b * n + i0 + il) * D + c);
-          }
+          zero_block<T, H, DH, DE, MAXT, MODE == kFused>(a, b, i0, i, w, lg);
           return;
         }
       }
@@ -1224,6 +1448,305 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
             }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------ fused layer, several key tiles per wave
+
+// Where lanes of fused_stream_kernel whose pair lies outside the n x n layout
+// store their edge outputs (a lane's de / 4 channels of one key; nothing
+// reads it).
+__device__ __align__(16) uint32_t kEdgeSink[8];
+
+// Single-pass layer (scores, softmax, A, O and the residual edge update) for
+// 64 < n <= 64 MAXT in bfloat16 with de = 64. One block per (graph, 16-query
+// block); wave w owns key tiles w, w + kWaves, ... (MAXT of them) and reads
+// only its live ones (some real key, in a block with a real query). The E
+// tiles of a wave (MAXT x 32 KB) do not fit on chip next to the rest, so each
+// live tile crosses from HBM twice, both times through LDS in half tiles
+// with the next half tile in flight: for the scores, and after the softmax
+// over the whole row for the update. The stream does not stop between the
+// two phases: the last score step prefetches the first update tile.
+// The global-to-LDS transfers are not tracked by the compiler's waits, so the
+// kernel issues its memory operations in a fixed order and waits explicitly:
+//   score step:  [half 0 of the next tile] [half 1 of the next tile]
+//   update step: [half 0 of the next tile] [E' stores, keys 0-7]
+//                [half 1 of the next tile] [E' stores, keys 8-15]
+// K and V fragments load outside these loops; A, and the E' zeros of the
+// tiles without a real key, are stored after the update loop.
+template <typename T, int H, int DH, int DE, int MAXT>
+__global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
+  static_assert(sizeof(T) == 2 && DE == 64 && MAXT >= 2, "bfloat16, de = 64, several key tiles");
+  using EH = EHalf<T, DE>;
+  using Up = Updater<T, H, DE>;
+  constexpr int D = H * DH;
+  constexpr int kEBytes = kWaves * 2 * EH::kBytes;
+  static_assert(kWaves * 16 * kOPitch<D> * 4 <= kEBytes, "the O partials reuse the E half tiles");
+  constexpr int kHalfStores = 16;  // E' stores of a half tile: 8 keys, two 16-byte stores each
+  static_assert(3 * kHalfStores < 64, "vmcnt range");
+  __shared__ __align__(16) unsigned char smem_raw[kEBytes];
+  __shared__ float red_s[2][kWaves][H][16];
+  const int tid = threadIdx.x, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the wave's tiles and waits are scalar
+  int ib, b;
+  if (a.order) {  // the work order written by qkv_kernel (uniform)
+    const int L = a.order[blockIdx.y * gridDim.x + blockIdx.x];
+    ib = L % (int)gridDim.x;
+    b = L / (int)gridDim.x;
+  } else {
+    xcd_block(ib, b);
+  }
+  const int i0 = ib * 16;
+  Scorer<T, H, DH, DE> sc;
+  sc.setup(a, b, i0);
+  const int JT = sc.JT, n = a.n, i = sc.i;
+  // mask bytes first: which tiles are live decides what the E stream reads
+  const uint32_t mq = sc.query_mask_byte();
+  uint32_t mk[MAXT];
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) mk[tt] = sc.key_mask_byte(w + kWaves * tt);
+  sc.load_weights(a);
+  Up up;
+  up.init(a, li, lg);
+  sc.mi = mq != 0u;
+  if ((__ballot(sc.mi) & 0xffffull) == 0ull) {  // no real query (uniform): zeros only
+    zero_block<T, H, DH, DE, MAXT, true>(a, b, i0, i, w, lg);
+    return;
+  }
+  // every small load has landed before the stream starts: afterwards the
+  // loops below hold no older load the compiler would have to wait for
+  wait_vmcnt<0>();
+  uint32_t bits[MAXT];
+  uint32_t live = 0u;  // bit tt: tile w + kWaves tt has a real key (uniform)
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) {
+    bits[tt] = key_bits(mk[tt]);  // 0 past the padded size
+    if (bits[tt] != 0u) live |= 1u << tt;
+  }
+  const int first = live ? __builtin_ctz(live) : 0;
+  unsigned char* ebase = smem_raw + (size_t)w * 2 * EH::kBytes;
+  const T* Eb = sc.E + (size_t)b * n * n * DE;
+  auto fetch = [&](int tt, int half) { EH::fetch(Eb, n, i0, w + kWaves * tt, half, true, ebase, l); };
+  // Both loops below walk the live tiles at run time with every memory
+  // operation unconditional (where there is no next tile, this one is read
+  // again, from L2), so that the compiler's own waits never have to merge
+  // paths with different operations in flight.
+
+  // ---- scores: live tiles in order, the next one streaming in
+  float u[MAXT][H][4];
+#pragma unroll
+  for (int q = 0; q < MAXT; ++q) Scorer<T, H, DH, DE>::no_keys(u[q]);
+  // K of every tile of the wave up front (no load into registers crosses a
+  // step of the loop, so leaving it waits for nothing)
+  Frag<T, DH / 4> kall[MAXT][H];
+#pragma unroll
+  for (int q = 0; q < MAXT; ++q) sc.load_k(w + kWaves * q, kall[q]);
+  fetch(first, 0);  // a wave without live tiles reads its first tile and discards it
+  fetch(first, 1);
+#pragma unroll 1
+  for (uint32_t m = live; m != 0u; m &= m - 1u) {
+    const int tt = __builtin_ctz(m);
+    const uint32_t rest = m & (m - 1u);
+    const int nt = rest ? __builtin_ctz(rest) : first;  // after the last score tile: the first update tile
+    uint32_t bt = 0u;
+    Frag<T, DH / 4> kf[H];
+#pragma unroll
+    for (int q = 0; q < MAXT; ++q)
+      if (q == tt) {
+        bt = bits[q];
+#pragma unroll
+        for (int h = 0; h < H; ++h) kf[h] = kall[q][h];
+      }
+    const f32x4 fc = sc.film_start();
+    float R[4][16];
+    Frag<T, DE / 4> ef[8];
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<16>();  // half 0 of this tile (newer: its half 1)
+    EH::frags8(ebase, li, lg, ef);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(nt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sc.film(ef[k], fc, R, k);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<16>();  // half 1 of this tile (newer: the half 0 just issued)
+    EH::frags8(ebase + EH::kBytes, li, lg, ef);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(nt, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sc.film(ef[k], fc, R, 8 + k);
+    f32x4 S[H];
+    sc.qk(kf, S);
+    float ut[H][4];
+    sc.scores_from(R, S, bt, ut);
+#pragma unroll
+    for (int q = 0; q < MAXT; ++q)
+      if (q == tt)
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[q][h][r] = ut[h][r];
+  }
+
+  // ---- softmax over the whole row (lane groups by register swaps, waves
+  // through LDS); the V fragments of the wave's tiles load meanwhile (all of
+  // them, unconditionally: tiles past the padded size read the last one)
+  Frag<T, 4> vf[MAXT][H][DH / 16];
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) sc.load_v(w + kWaves * tt, vf[tt]);
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float m = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, u[tt][h][r]);
+    m = lg_max(m);
+    if (lg == 0) red_s[0][w][h][li] = m;
+  }
+  lds_barrier();  // the update's first tile stays in flight
+  float inv[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_s[0][ww][h][li]);
+    // exp(u - M) as 2^(u log2 e - M log2 e); masked logits give exactly 0
+    const float mb = (M == kNegInf) ? 0.f : M * kLog2e;
+    float s = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < MAXT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(u[tt][h][r], kLog2e, -mb));
+        u[tt][h][r] = p;
+        s += p;
+      }
+    s = lg_sum(s);
+    if (lg == 0) red_s[1][w][h][li] = s;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) L += red_s[1][ww][h][li];
+    inv[h] = (L > 0.f) ? __builtin_amdgcn_rcpf(L) : 0.f;
+  }
+
+  // ---- A in bfloat16 (stored later), O^T += V^T A^T over the live tiles
+  f32x4 oacc[H][DH / 16];
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Frag<T, 4> ak[MAXT][H];
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = u[tt][h][r] * inv[h];
+      ak[tt][h].set(p);
+    }
+    if ((live >> tt) & 1u) {
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int tc = 0; tc < DH / 16; ++tc) oacc[h][tc] = mma(oacc[h][tc], vf[tt][h][tc], ak[tt][h]);
+    }
+  }
+
+  // ---- residual edge update of the live tiles, E streamed through LDS again
+  up.finish();
+  T* Eout = static_cast<T*>(a.E_out);
+  const bool iin = i < n;
+  const size_t rowoff = ((size_t)b * n + (iin ? i : 0)) * n * DE + lg * (DE / 4);
+  // every lane stores each key (pairs outside the n x n layout to the sink),
+  // so that each half tile issues kHalfStores stores and the waits count exactly
+  static_assert(DE / 4 * sizeof(T) <= sizeof(kEdgeSink), "sink size");
+  T* sink = reinterpret_cast<T*>(kEdgeSink);
+  wait_vmcnt<0>();  // the first update tile has landed (and every load before it)
+#pragma unroll 1
+  for (uint32_t m = live; m != 0u; m &= m - 1u) {
+    const int tt = __builtin_ctz(m);
+    const uint32_t rest = m & (m - 1u);
+    const int nt = rest ? __builtin_ctz(rest) : tt;  // after the last tile: this one again
+    const int j0 = 16 * (w + kWaves * tt);
+    Frag<T, 4> akc[H];
+    uint32_t bt = 0u;
+#pragma unroll
+    for (int q = 0; q < MAXT; ++q)
+      if (q == tt) {
+        bt = bits[q];
+#pragma unroll
+        for (int h = 0; h < H; ++h) akc[h] = ak[q][h];
+      }
+    float R[4][Up::RW];
+    up.head_operand(akc, R);
+    const bool full = tile_full(sc.mi, bt);
+    const uint32_t okj = sc.mi ? bt : 0u;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __builtin_amdgcn_sched_barrier(0);
+      // this half tile in LDS: newer are the stores of the two half tiles
+      // before it and the half tile fetched between them (for the first tile
+      // everything has landed already)
+      wait_vmcnt<3 * kHalfStores>();
+      Frag<T, DE / 4> ef[8];
+      EH::frags8(ebase + half * EH::kBytes, li, lg, ef);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(nt, half);
+      __builtin_amdgcn_sched_barrier(0);
+      if (full) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int jj = 8 * half + k;
+          up.template step_to<true>(ef[k], Eout + rowoff + (size_t)(j0 + jj) * DE, true, R, jj);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int jj = 8 * half + k;
+          T* dst = (iin && j0 + jj < n) ? Eout + rowoff + (size_t)(j0 + jj) * DE : sink;
+          up.template step_to<false>(ef[k], dst, (okj >> jj) & 1u, R, jj);
+        }
+      }
+    }
+  }
+  // the last fetches land in LDS before the O partials reuse it (newer: the
+  // last half tile's stores, which stay in flight)
+  if (live) wait_vmcnt<kHalfStores>(); else wait_vmcnt<0>();
+  lds_barrier();
+  const uint32_t qbits = (uint32_t)(__ballot(sc.mi) & 0xffffull);
+  float* os_s = reinterpret_cast<float*>(smem_raw);
+  o_partials_to_lds<H, DH>(os_s, oacc, w, li, lg);
+  lds_barrier();
+  o_reduce_store<T, H, DH>(a, os_s, b, i0, qbits);
+
+  // ---- A of every tile of the wave, and the E' zeros of the dead tiles
+  T* Ag = static_cast<T*>(a.A);
+#pragma unroll
+  for (int tt = 0; tt < MAXT; ++tt) {
+    const int jt = w + kWaves * tt, j0 = 16 * jt, jb = j0 + 4 * lg;
+    if (jt >= JT) continue;  // uniform
+    if ((n & 3) == 0) {  // uniform: 4 keys in or out together, one vector store
+      if (iin && jb < n) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) ak[tt][h].store(Ag + (((size_t)b * H + h) * n + i) * n + jb);
+      }
+    } else if (iin) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        T* row = Ag + (((size_t)b * H + h) * n + i) * n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (jb + r < n) Num<T>::st(row + jb + r, ak[tt][h].get(r));
+      }
+    }
+    if (!((live >> tt) & 1u)) zero_edge_tile<T, DE>(Eout, b, n, i, j0, lg);
   }
 }
 
@@ -2571,7 +3094,18 @@ hipError_t attn_shape(const LayerArgs& a, int mode, hipStream_t s) {
   const int maxt = (JT + kWaves - 1) / kWaves;
   switch (mode) {
     case kSingle: return attn_maxt<T, H, DH, DE, kSingle>(a, maxt, grid, s);
-    case kFused: return attn_maxt<T, H, DH, DE, kFused>(a, maxt, grid, s);
+    case kFused:
+      if constexpr (sizeof(T) == 2 && DE == 64) {
+        // two or three key tiles per wave: E streamed through LDS
+        // (fused_stream_kernel; with four, its K and V fragments would not
+        // fit in registers)
+        switch (maxt) {
+          case 2: hipLaunchKernelGGL((fused_stream_kernel<T, H, DH, DE, 2>), grid, dim3(kThreads), 0, s, a); return hipGetLastError();
+          case 3: hipLaunchKernelGGL((fused_stream_kernel<T, H, DH, DE, 3>), grid, dim3(kThreads), 0, s, a); return hipGetLastError();
+          default: break;
+        }
+      }
+      return attn_maxt<T, H, DH, DE, kFused>(a, maxt, grid, s);
     case kLogits: return attn_maxt<T, H, DH, DE, kLogits>(a, maxt, grid, s);
     case kOnline:
       hipLaunchKernelGGL((attn_kernel<T, H, DH, DE, 1, kOnline>), grid, dim3(kThreads), 0, s, a);
@@ -2611,7 +3145,7 @@ template <typename T, int D, int DH>
 hipError_t qkv_shape(const LayerArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.NP;
   // one extra column of blocks computes the global FiLM coefficients
-  const dim3 grid((unsigned)((rows + 63) / 64), 3 * D / 64 + 1);  // rows < 2^31
+  const dim3 grid((unsigned)((rows + 63) / 64), 3 * D / 64 + 1 + (a.order ? 1 : 0));  // rows < 2^31
   hipLaunchKernelGGL((qkv_kernel<T, D, DH>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -2660,6 +3194,13 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g0, hipStream_t s) 
 }
 
 }  // namespace
+
+bool wants_order(int dtype, int H, int dh, int de, int B, int NP) {
+  // fused_stream_kernel: bfloat16, de = 64, two or three key tiles per wave
+  const int JT = NP / 16, maxt = (JT + kWaves - 1) / kWaves;
+  return dtype == 1 && shape_supported(dtype, H, dh, de) && de == 64 && (maxt == 2 || maxt == 3) &&
+         (long)B * JT <= kOrderMax;
+}
 
 bool shape_supported(int dtype, int H, int dh, int de) {
   if (dtype != 0 && dtype != 1) return false;

@@ -136,7 +136,8 @@ typedef struct ea_ctx ea_ctx; /* opaque, host memory only */
 ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out);
 void ea_ctx_destroy(ea_ctx* ctx);
 
-/* Workspace bytes the context needs (Q, K, V^T per head, softmax statistics). */
+/* Workspace bytes the context needs (Q, K, V^T per head, softmax statistics,
+ * global FiLM coefficients, the attention kernel's work order). */
 size_t ea_workspace_bytes(const ea_ctx* ctx);
 
 /* 1 when the context runs the two-pass scheme, else 0 (-1 for NULL). */

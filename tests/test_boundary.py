@@ -85,7 +85,8 @@ def test_mode_and_workspace_plan(lib):
         qkv = -(-3 * 8 * NP * 32 * 2 // 256) * 256
         lse = -(-3 * 8 * NP * 4 // 256) * 256
         gy = -(-3 * 2 * 8 * 4 // 256) * 256
-        assert lib.ea_workspace_bytes(ctx) == 3 * qkv + lse + gy
+        order = -(-3 * (NP // 16) * 4 // 256) * 256
+        assert lib.ea_workspace_bytes(ctx) == 3 * qkv + lse + gy + order
         lib.ea_ctx_destroy(ctx)
     assert lib.ea_is_two_pass(None) == -1
     assert lib.ea_workspace_bytes(None) == 0
