@@ -2943,9 +2943,9 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
 // threads' parts in a fixed order.
 template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_sums_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int NR = 3 * H * DE + DE, F = 4 * H, GF = kThreads / F, CB = 16, GC = kThreads / CB, D = H * DH;
+  constexpr int NR = 3 * H * DE + DE, F = 4 * H, GF = kThreads / F, CB = 16, D = H * DH;
   static_assert(kThreads % F == 0, "whole groups");
-  __shared__ float part_s[kThreads];
+  __shared__ __align__(16) float part_s[4 * kThreads];
   const int tid = threadIdx.x, B = a.B;
   const int nrb = (NR + CB - 1) / CB;
   // column c of `rows` rows (row stride `stride`), rows split over `groups`
@@ -2974,12 +2974,29 @@ __global__ __launch_bounds__(kThreads) void bwd_sums_kernel(LayerArgs a, BwdArgs
       g.DGY[(size_t)b * F + tid] = t;
     }
   } else if ((int)blockIdx.x < B + nrb) {
-    const int c = ((int)blockIdx.x - B) * CB + tid % CB, q = tid / CB;
-    part_s[tid] = c < NR ? colsum(g.RED + c, g.red_rows, NR, GC, q) : 0.f;
+    // 16 columns as four 16-byte column groups; the rows split over 64 row
+    // groups (rows q, q + 64, ...), each thread's rows loaded 16 at a time
+    static_assert(NR % CB == 0 && CB == 16, "whole 16-byte column groups");
+    constexpr int RG = kThreads / 4, U = 16;
+    const int cg = tid & 3, q = tid >> 2, c0 = ((int)blockIdx.x - B) * CB + 4 * cg;
+    const float* base = g.RED + c0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int rows = g.red_rows;
+    int r = q;
+    for (; r + (U - 1) * RG < rows; r += U * RG) {
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)(r + u * RG) * NR);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc += v[u];
+    }
+    for (; r < rows; r += RG) acc += *reinterpret_cast<const f32x4*>(base + (size_t)r * NR);
+    *reinterpret_cast<f32x4*>(&part_s[4 * tid]) = acc;
     __syncthreads();
-    if (tid < CB && c < NR) {
+    if (tid < CB) {
+      const int c = ((int)blockIdx.x - B) * CB + tid;
       float t = 0.f;
-      for (int k = 0; k < GC; ++k) t += part_s[k * CB + tid];
+      for (int k = 0; k < RG; ++k) t += part_s[16 * k + tid];  // row group k holds columns 4 cg .. of its 4 threads
       if (c < H * DE) g.gw_em[c] = t;
       else if (c < 2 * H * DE) g.gw_ea[c - H * DE] = t;
       else if (c < 3 * H * DE) g.gw_e[c - 2 * H * DE] = t;
