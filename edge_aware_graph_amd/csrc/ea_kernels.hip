@@ -624,16 +624,15 @@ struct EHalf {
   // half tiles at ebase: lane l moves the 16-byte piece l % 8 of key
   // 16 jt + 8 half + l / 8. Rows and keys past n read row and key n - 1
   // (their values are discarded by the selects of the score stage and of the
-  // edge update); valid = false reads the zero table instead, so that the
-  // count of loads is the same.
-  static __device__ __forceinline__ void fetch(const T* Eb, int n, int i0, int jt, int half, bool valid,
-                                               unsigned char* ebase, int l) {
+  // edge update).
+  static __device__ __forceinline__ void fetch(const T* Eb, int n, int i0, int jt, int half, unsigned char* ebase,
+                                               int l) {
     const int j = 16 * jt + 8 * half + (l >> 3);
     const int jc = j < n ? j : n - 1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ir = i0 + r < n ? i0 + r : n - 1;
-      const T* src = valid ? Eb + ((size_t)ir * n + jc) * DE + (l & 7) * 8 : zeros<T>() + (l & 15) * 8;
+      const T* src = Eb + ((size_t)ir * n + jc) * DE + (l & 7) * 8;
       __builtin_amdgcn_global_load_lds((const void*)src,
                                        (__attribute__((address_space(3))) void*)(ebase + half * kBytes + r * kRowPitch),
                                        16, 0, 0);
@@ -1472,8 +1471,11 @@ __device__ __align__(16) uint32_t kEdgeSink[8];
 //   score step:  [half 0 of the next tile] [half 1 of the next tile]
 //   update step: [half 0 of the next tile] [E' stores, keys 0-7]
 //                [half 1 of the next tile] [E' stores, keys 8-15]
-// K and V fragments load outside these loops; A, and the E' zeros of the
-// tiles without a real key, are stored after the update loop.
+// Loads retire in issue order; the kernel does not rely on stores retiring
+// in order with older loads (the compiler does not assume it either), so a
+// wait counts only the loads issued after the one it waits for. K and V
+// fragments load outside these loops; A, and the E' zeros of the tiles
+// without a real key, are stored after the update loop.
 template <typename T, int H, int DH, int DE, int MAXT>
 __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   static_assert(sizeof(T) == 2 && DE == 64 && MAXT >= 2, "bfloat16, de = 64, several key tiles");
@@ -1482,8 +1484,6 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   constexpr int D = H * DH;
   constexpr int kEBytes = kWaves * 2 * EH::kBytes;
   static_assert(kWaves * 16 * kOPitch<D> * 4 <= kEBytes, "the O partials reuse the E half tiles");
-  constexpr int kHalfStores = 16;  // E' stores of a half tile: 8 keys, two 16-byte stores each
-  static_assert(3 * kHalfStores < 64, "vmcnt range");
   __shared__ __align__(16) unsigned char smem_raw[kEBytes];
   __shared__ float red_s[2][kWaves][H][16];
   const int tid = threadIdx.x, l = tid & 63, li = l & 15, lg = l >> 4;
@@ -1526,7 +1526,7 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   const int first = live ? __builtin_ctz(live) : 0;
   unsigned char* ebase = smem_raw + (size_t)w * 2 * EH::kBytes;
   const T* Eb = sc.E + (size_t)b * n * n * DE;
-  auto fetch = [&](int tt, int half) { EH::fetch(Eb, n, i0, w + kWaves * tt, half, true, ebase, l); };
+  auto fetch = [&](int tt, int half) { EH::fetch(Eb, n, i0, w + kWaves * tt, half, ebase, l); };
   // Both loops below walk the live tiles at run time with every memory
   // operation unconditional (where there is no next tile, this one is read
   // again, from L2), so that the compiler's own waits never have to merge
@@ -1665,7 +1665,7 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   const bool iin = i < n;
   const size_t rowoff = ((size_t)b * n + (iin ? i : 0)) * n * DE + lg * (DE / 4);
   // every lane stores each key (pairs outside the n x n layout to the sink),
-  // so that each half tile issues kHalfStores stores and the waits count exactly
+  // so that every half tile issues the same stores
   static_assert(DE / 4 * sizeof(T) <= sizeof(kEdgeSink), "sink size");
   T* sink = reinterpret_cast<T*>(kEdgeSink);
   wait_vmcnt<0>();  // the first update tile has landed (and every load before it)
@@ -1691,10 +1691,11 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       __builtin_amdgcn_sched_barrier(0);
-      // this half tile in LDS: newer are the stores of the two half tiles
-      // before it and the half tile fetched between them (for the first tile
-      // everything has landed already)
-      wait_vmcnt<3 * kHalfStores>();
+      // this half tile in LDS. Newer are the stores of the two half tiles
+      // before it and the half tile fetched between them; only the newer
+      // loads (16) are counted (for the first tile everything has landed
+      // already)
+      wait_vmcnt<16>();
       Frag<T, DE / 4> ef[8];
       EH::frags8(ebase + half * EH::kBytes, li, lg, ef);
       __builtin_amdgcn_sched_barrier(0);
@@ -1716,9 +1717,9 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
       }
     }
   }
-  // the last fetches land in LDS before the O partials reuse it (newer: the
-  // last half tile's stores, which stay in flight)
-  if (live) wait_vmcnt<kHalfStores>(); else wait_vmcnt<0>();
+  // the last fetches land in LDS before the O partials reuse it (only
+  // stores are newer: wait for everything)
+  wait_vmcnt<0>();
   lds_barrier();
   const uint32_t qbits = (uint32_t)(__ballot(sc.mi) & 0xffffull);
   float* os_s = reinterpret_cast<float*>(smem_raw);
@@ -1898,16 +1899,14 @@ __device__ __forceinline__ void e_tile_to_lds(const T* E, int b, int n, int i, i
 // register fragments), so the E reads of the next item overlap the score
 // stage, the update and the E' stores of this one. The global-to-LDS loads
 // are not tracked by the compiler's waits: the kernel waits explicitly (all
-// vector memory operations but this item's E' stores before reading the
-// tile, and its own LDS reads before the next tile may overwrite it).
+// vector memory operations before reading the tile, and its own LDS reads
+// before the next tile may overwrite it).
 // Every pair of a tile is read (masked values are discarded by the selects).
 template <typename T, int H, int DH, int DE, int MODE>
 __global__ __launch_bounds__(kThreads) void update_pipe_kernel(LayerArgs a, int items) {
   static_assert(sizeof(T) == 2 && DE % 32 == 0, "bfloat16, 16-byte pieces");
   constexpr int LPK = DE / 32;   // 16-byte pieces per lane and key
   constexpr int NL = 16 * LPK;   // per tile
-  constexpr int kStores = 16 * LPK;  // E' store instructions of a whole tile
-  static_assert(kStores < 64, "vmcnt range");
   __shared__ u32x4 ebuf[kWaves][NL][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int n = a.n, NP = a.NP, JT = NP / 16, QB = NP / 16, KG = (JT + kWaves - 1) / kWaves;
@@ -1954,14 +1953,14 @@ __global__ __launch_bounds__(kThreads) void update_pipe_kernel(LayerArgs a, int 
   Updater<T, H, DE> up;
   up.init(a, li, lg);
   up.finish();
-  bool prev_full = false;  // the previous item stored a whole tile (kStores stores)
   for (;;) {
     const int nx = it + G;
     const bool more = nx < items;  // uniform
     __builtin_amdgcn_sched_barrier(0);
-    // this item's E tile (and small loads) have landed: all but the previous
-    // item's E' stores, which are the newest operations
-    if (prev_full) wait_vmcnt<kStores>(); else wait_vmcnt<0>();
+    // this item's E tile and small loads have landed (newer are only the
+    // previous item's E' stores, which are not counted on to retire in order
+    // with older loads: wait for everything)
+    wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
     ETile<T, DE> et;
 #pragma unroll
@@ -2013,7 +2012,6 @@ __global__ __launch_bounds__(kThreads) void update_pipe_kernel(LayerArgs a, int 
     } else if (jt < JT) {
       zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, j0, lg);
     }
-    prev_full = live && full;
     if (!more) break;
     it = nx;
     cur = nxt;
