@@ -666,8 +666,10 @@ struct EHalf {
         "ds_read_b128 %14, %16 offset:896\n\t"
         "ds_read_b128 %15, %16 offset:912\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7]),
-          "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]), "=v"(v[14]), "=v"(v[15])
+        // early-clobber outputs: a read may land before a later one has
+        // taken its address from the input register
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
         : "v"(a));
     static_assert(DE * 2 == 128, "key pitch of the offsets above");
 #pragma unroll
@@ -1527,10 +1529,10 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   unsigned char* ebase = smem_raw + (size_t)w * 2 * EH::kBytes;
   const T* Eb = sc.E + (size_t)b * n * n * DE;
   auto fetch = [&](int tt, int half) { EH::fetch(Eb, n, i0, w + kWaves * tt, half, ebase, l); };
-  // Both loops below walk the live tiles at run time with every memory
-  // operation unconditional (where there is no next tile, this one is read
-  // again, from L2), so that the compiler's own waits never have to merge
-  // paths with different operations in flight.
+  // Both loops below walk the live tiles at run time. The score loop issues
+  // the same transfers in every step (after the last score tile it fetches
+  // the first update tile); the update loop fetches only while a next tile
+  // exists.
 
   // ---- scores: live tiles in order, the next one streaming in
   float u[MAXT][H][4];
@@ -1541,8 +1543,10 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   Frag<T, DH / 4> kall[MAXT][H];
 #pragma unroll
   for (int q = 0; q < MAXT; ++q) sc.load_k(w + kWaves * q, kall[q]);
-  fetch(first, 0);  // a wave without live tiles reads its first tile and discards it
-  fetch(first, 1);
+  if (live) {  // uniform
+    fetch(first, 0);
+    fetch(first, 1);
+  }
 #pragma unroll 1
   for (uint32_t m = live; m != 0u; m &= m - 1u) {
     const int tt = __builtin_ctz(m);
@@ -1673,7 +1677,7 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   for (uint32_t m = live; m != 0u; m &= m - 1u) {
     const int tt = __builtin_ctz(m);
     const uint32_t rest = m & (m - 1u);
-    const int nt = rest ? __builtin_ctz(rest) : tt;  // after the last tile: this one again
+    const int nt = rest ? __builtin_ctz(rest) : tt;
     const int j0 = 16 * (w + kWaves * tt);
     Frag<T, 4> akc[H];
     uint32_t bt = 0u;
@@ -1692,14 +1696,14 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
     for (int half = 0; half < 2; ++half) {
       __builtin_amdgcn_sched_barrier(0);
       // this half tile in LDS. Newer are the stores of the two half tiles
-      // before it and the half tile fetched between them; only the newer
-      // loads (16) are counted (for the first tile everything has landed
+      // before it and the half tile fetched between them (if any); only the
+      // newer loads are counted (for the first tile everything has landed
       // already)
-      wait_vmcnt<16>();
+      if (half == 0 || rest) wait_vmcnt<16>(); else wait_vmcnt<0>();
       Frag<T, DE / 4> ef[8];
       EH::frags8(ebase + half * EH::kBytes, li, lg, ef);
       __builtin_amdgcn_sched_barrier(0);
-      fetch(nt, half);
+      if (rest) fetch(nt, half);  // uniform
       __builtin_amdgcn_sched_barrier(0);
       if (full) {
 #pragma unroll
