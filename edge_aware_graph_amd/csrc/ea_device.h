@@ -67,6 +67,11 @@ struct Num<bf16_t> {
 // Nothing writes it.
 __device__ __align__(16) uint32_t kZeros[64] = {};
 
+// Cache-policy operand of the global-to-LDS transfers: the default, or the
+// non-temporal (streaming) policy for data read once.
+constexpr int kCpolDefault = 0;
+constexpr int kCpolStream = 2;
+
 template <typename T>
 __device__ __forceinline__ const T* zeros() { return reinterpret_cast<const T*>(kZeros); }
 
@@ -105,6 +110,22 @@ struct Frag {
       w[0] = v.x; w[1] = v.y;
     } else {
       w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  // The same with the non-temporal (streaming) cache policy: data read once
+  // that should not displace the caches' other contents (used for E, whose
+  // lines would otherwise push the written E' lines out of the Infinity
+  // Cache early).
+  __device__ __forceinline__ void load_nt(const T* p) {
+    if constexpr (ND % 4 == 0) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int s = 0; s < ND / 4; ++s) {
+        const u32x4 v = __builtin_nontemporal_load(q + s);
+        w[4 * s] = v.x; w[4 * s + 1] = v.y; w[4 * s + 2] = v.z; w[4 * s + 3] = v.w;
+      }
+    } else {
+      load(p);
     }
   }
   __device__ __forceinline__ void store(T* p) const {

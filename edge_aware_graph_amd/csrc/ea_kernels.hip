@@ -406,12 +406,17 @@ struct ETile {
   // any load; pairs outside the n x n layout read the nearest pair inside it.
   // Values of pairs that are not real are discarded by the selects of the
   // score stage and of the edge update.
+  // NT: with the non-temporal policy (E read once by the fused layer).
+  template <bool NT = false>
   __device__ __forceinline__ void load_all(const T* E, int b, int n, int i, int j0, int lg) {
     const T* row = E + ((size_t)b * n + (i < n ? i : n - 1)) * n * DE + lg * (DE / 4);
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       const int j = j0 + jj < n ? j0 + jj : n - 1;
-      f[jj].load(row + (size_t)j * DE);
+      if constexpr (NT)
+        f[jj].load_nt(row + (size_t)j * DE);
+      else
+        f[jj].load(row + (size_t)j * DE);
     }
   }
   __device__ __forceinline__ void load(const T* E, int b, int n, int i, bool mi, int j0, int lg, uint32_t bits) {
@@ -625,6 +630,7 @@ struct EHalf {
   // 16 jt + 8 half + l / 8. Rows and keys past n read row and key n - 1
   // (their values are discarded by the selects of the score stage and of the
   // edge update).
+  template <int CPOL = kCpolDefault>
   static __device__ __forceinline__ void fetch(const T* Eb, int n, int i0, int jt, int half, unsigned char* ebase,
                                                int l) {
     const int j = 16 * jt + 8 * half + (l >> 3);
@@ -635,7 +641,7 @@ struct EHalf {
       const T* src = Eb + ((size_t)ir * n + jc) * DE + (l & 7) * 8;
       __builtin_amdgcn_global_load_lds((const void*)src,
                                        (__attribute__((address_space(3))) void*)(ebase + half * kBytes + r * kRowPitch),
-                                       16, 0, 0);
+                                       16, 0, CPOL);
     }
   }
   // This lane's E fragments (query row li, channel quarter lg) of all 8 keys
@@ -1250,7 +1256,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
       // mask byte (1), K (H), V (H DH / 16); every load is unconditional
       // (after the last tile they read the zero table or a clamped tile), so
       // the waits below count exactly. Every pair is read (masked values are
-      // discarded by the selects of the score stage).
+      // discarded by the selects of the score stage). The transfers take the
+      // streaming cache policy, since pass 1 reads E once: over a loop of
+      // layer calls at B = 4, n = 1024 pass 1 went from 141 to 112 us with
+      // it and pass 2, which then finds none of E in the Infinity Cache,
+      // from 206 to 224 us (the layer from 355 to 341 us).
       constexpr int kV = H * (DH / 16);
       constexpr int kAfterHalf = 16 + 1 + H + kV;  // loads issued after a tile's half 0
       static_assert(kAfterHalf < 64, "vmcnt range");
@@ -1268,7 +1278,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
           const T* src = valid ? erow0 + ((size_t)ir * n + jc) * DE + (l & 7) * 8 : zeros<T>() + (l & 15) * 8;
           __builtin_amdgcn_global_load_lds((const void*)src,
                                            (__attribute__((address_space(3))) void*)(ebase + half * kHalfBytes + r * kRowPitch),
-                                           16, 0, 0);
+                                           16, 0, kCpolStream);
         }
       };
       uint32_t mk_raw;
@@ -1402,7 +1412,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(LayerArgs a) {
       // one tile per wave: every in-bounds pair is read, so the loads need
       // no mask bytes (masked values are discarded by the selects)
       ETile<T, DE> et;
-      et.load_all(sc.E, b, n, i, 16 * w, lg);
+      et.template load_all<true>(sc.E, b, n, i, 16 * w, lg);
       __builtin_amdgcn_sched_barrier(0);  // nothing that waits on a load moves above the E stream
       sc.mi = mq != 0u;
       bits[0] = key_bits(mk[0]);
