@@ -426,6 +426,43 @@ def event_pair_overhead_us(reps: int = 200) -> float:
     return float(np.median(vals))
 
 
+def hbm_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """Achievable HBM rate on a plain stream, for context next to the kernels'
+    roofline fractions: the library's probe copy (nbytes read + nbytes
+    written) and probe read over nbytes, each launched `reps` times after
+    three warm-up launches, timed with events on the launch stream (median
+    launch)."""
+    import torch
+    from edge_aware_graph_amd import layer as L
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    acc = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    res = {"bytes": nbytes, "launches": reps}
+    for kind in ("copy", "read"):
+        run = (lambda: L.probe_copy(src, dst, st)) if kind == "copy" else (lambda: L.probe_read(src, acc, st))
+        for _ in range(3):
+            run()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            run()
+            e1.record(st)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(times))
+        moved = 2 * nbytes if kind == "copy" else nbytes
+        res[kind + "_us"] = t * 1e6
+        res[kind + "_GBps"] = moved / t / 1e9
+    if not torch.equal(dst[:4096], src[:4096]):
+        raise RuntimeError("probe copy gave wrong bytes")
+    del src, dst, acc
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_layer(name: str, steps: int, warmup: int, variant: str = "none", hot: bool = False):
     """GPU record of one configuration: wall time per layer call over `steps`
     calls (after `warmup`), per-kernel HIP-event durations over the same
@@ -586,6 +623,10 @@ def main():
     torch.cuda.synchronize()
     del cp_src, cp_dst
     out["copy_calibration_bytes"] = 256 << 20
+    out["hbm_ceiling"] = hbm_ceiling()
+    rl = out["roofline"]
+    rl["achieved_over_measured_ceiling"] = rl["achieved"] / out["hbm_ceiling"][
+        "copy_GBps" if rl["kernel"] in ("update_kernel", "attn_kernel(fused)") else "read_GBps"]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle (%s)" % head, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(batch, dims, budget_s=3.0, oracle_variant=oracle_variant, runs=3)

@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libedge_attn.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ea_kernels.hip", "ea_block.hip", "ea_generic.hip", "ea_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ea_kernels.hip", "ea_block.hip", "ea_generic.hip", "ea_probe.hip", "ea_api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are disabled: only scalar fp32 VALU and MFMA are used.

@@ -483,6 +483,25 @@ ea_status ea_debug_softmax(ea_ctx* c, const float* U, void* A, void* stream) {
   return timed(c, EA_K_ATTN, s, [&] { return ea::launch_gen_softmax(U, A, rows, c->d.n, c->d.dtype, s); });
 }
 
+ea_status ea_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  g_err[0] = 0;
+  if (bytes == 0) return EA_OK;
+  EA_TRY(check_ptr(src, "src", 16, true));
+  EA_TRY(check_ptr(dst, "dst", 16, true));
+  if (bytes % 16) return fail(EA_E_ALIGN, "bytes must be a multiple of 16");
+  const hipError_t e = ea::launch_probe_copy(src, dst, bytes / 16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EA_OK : fail(EA_E_HIP, "probe copy launch failed: %s", hipGetErrorString(e));
+}
+
+ea_status ea_probe_read(const void* src, size_t bytes, uint32_t* xor_out, void* stream) {
+  g_err[0] = 0;
+  EA_TRY(check_ptr(src, "src", 16, bytes > 0));
+  EA_TRY(check_ptr(xor_out, "xor_out", 4, true));
+  if (bytes % 16) return fail(EA_E_ALIGN, "bytes must be a multiple of 16");
+  const hipError_t e = ea::launch_probe_read(src, bytes / 16, xor_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EA_OK : fail(EA_E_HIP, "probe read launch failed: %s", hipGetErrorString(e));
+}
+
 size_t ea_block_workspace_bytes(const ea_ctx* c) { return c ? c->blk_bytes : 0; }
 
 ea_status edge_attn_block(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,

@@ -124,6 +124,10 @@ hipError_t launch_update(const LayerArgs& a, int dtype, int H, int dh, int de, i
 // dX, dW, small sums); returns the first launch error.
 hipError_t launch_backward(const LayerArgs& a, const BwdArgs& g, int dtype, int H, int dh, int de,
                            hipStream_t s);
+// Bandwidth probes (ea_probe.hip): a plain copy of n16 16-byte pieces, and a
+// plain read whose words are XOR-ed into *xor_out.
+hipError_t launch_probe_copy(const void* src, void* dst, size_t n16, hipStream_t s);
+hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* xor_out, hipStream_t s);
 // Whether (dtype, H, dh, de) is instantiated.
 bool shape_supported(int dtype, int H, int dh, int de);
 // Whether the layer's attention kernel (kFused) for this shape takes a work

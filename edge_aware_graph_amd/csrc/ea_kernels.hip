@@ -1539,6 +1539,11 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
   unsigned char* ebase = smem_raw + (size_t)w * 2 * EH::kBytes;
   const T* Eb = sc.E + (size_t)b * n * n * DE;
   auto fetch = [&](int tt, int half) { EH::fetch(Eb, n, i0, w + kWaves * tt, half, ebase, l); };
+  // the update's re-read is the tile's last use: streaming cache policy
+  // (75.0 against 77.2 us at B = 32, n = 192)
+  auto fetch_last = [&](int tt, int half) {
+    EH::template fetch<kCpolStream>(Eb, n, i0, w + kWaves * tt, half, ebase, l);
+  };
   // Both loops below walk the live tiles at run time. The score loop issues
   // the same transfers in every step (after the last score tile it fetches
   // the first update tile); the update loop fetches only while a next tile
@@ -1713,7 +1718,7 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
       Frag<T, DE / 4> ef[8];
       EH::frags8(ebase + half * EH::kBytes, li, lg, ef);
       __builtin_amdgcn_sched_barrier(0);
-      if (rest) fetch(nt, half);  // uniform
+      if (rest) fetch_last(nt, half);  // uniform
       __builtin_amdgcn_sched_barrier(0);
       if (full) {
 #pragma unroll

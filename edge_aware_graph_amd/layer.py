@@ -34,7 +34,8 @@ EXPORTS = ("ea_ctx_create", "ea_ctx_destroy", "ea_workspace_bytes", "ea_is_two_p
            "ea_last_error", "ea_debug_logits", "ea_profile_begin", "ea_profile_end",
            "ea_backward_workspace_bytes", "edge_attn_backward",
            "ea_block_workspace_bytes", "edge_attn_block",
-           "ea_kernel_name", "ea_debug_softmax", "ea_noalloc_max_workspace_bytes", "edge_attn_layer_noalloc")
+           "ea_kernel_name", "ea_debug_softmax", "ea_noalloc_max_workspace_bytes", "edge_attn_layer_noalloc",
+           "ea_probe_copy", "ea_probe_read")
 
 # Parameters of the graph-transformer block, in the order of ea_block_params.
 BLOCK_PARAM_NAMES = ("w_o", "b_o", "ln_x1_g", "ln_x1_b", "w_x1", "b_x1", "w_x2", "b_x2", "ln_x2_g", "ln_x2_b",
@@ -118,6 +119,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ea_noalloc_max_workspace_bytes.argtypes = []
     lib.edge_attn_layer_noalloc.restype = ctypes.c_int
     lib.edge_attn_layer_noalloc.argtypes = [vp, ap, up, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ea_probe_copy.restype = ctypes.c_int
+    lib.ea_probe_copy.argtypes = [vp, vp, sz, vp]
+    lib.ea_probe_read.restype = ctypes.c_int
+    lib.ea_probe_read.argtypes = [vp, sz, vp, vp]
     lib.ea_status_str.restype = ctypes.c_char_p
     lib.ea_status_str.argtypes = [ctypes.c_int]
     lib.ea_last_error.restype = ctypes.c_char_p
@@ -201,6 +206,35 @@ def _stream(stream) -> Optional[int]:
         return stream if isinstance(stream, int) else stream.cuda_stream
     import torch
     return torch.cuda.current_stream().cuda_stream
+
+
+def _probe_tensor(t, name: str):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous torch tensor" % name)
+    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s, expected the current CUDA device" % (name, t.device))
+    return t.numel() * t.element_size()
+
+
+def probe_copy(src, dst, stream=None) -> None:
+    """ea_probe_copy over the whole of src into dst (same byte size)."""
+    nb = _probe_tensor(src, "src")
+    if _probe_tensor(dst, "dst") != nb:
+        raise ValueError("src and dst must hold the same number of bytes")
+    lib = load_library()
+    _check(lib, lib.ea_probe_copy(src.data_ptr(), dst.data_ptr(), nb, _stream(stream)))
+
+
+def probe_read(src, xor_out, stream=None) -> None:
+    """ea_probe_read over the whole of src; xor_out: an int32 tensor of one element."""
+    import torch
+    nb = _probe_tensor(src, "src")
+    _probe_tensor(xor_out, "xor_out")
+    if xor_out.dtype != torch.int32 or xor_out.numel() != 1:
+        raise ValueError("xor_out must be one int32 element")
+    lib = load_library()
+    _check(lib, lib.ea_probe_read(src.data_ptr(), nb, xor_out.data_ptr(), _stream(stream)))
 
 
 class EdgeAttention:

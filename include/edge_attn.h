@@ -316,6 +316,24 @@ ea_status ea_profile_begin(ea_ctx* ctx);
 ea_status ea_profile_end(ea_ctx* ctx, double* total_ms, int64_t* launches);
 const char* ea_kernel_name(int kernel_id);
 
+/*
+ * Bandwidth probes (measurement context, not part of the layer): the HBM rate
+ * this GPU reaches on a plain stream, for a benchmark to report next to the
+ * layer's kernels (the pages give the layer's cost as memory traffic, not
+ * arithmetic: "Efficient Edge-aware Attention Network for Graph Generation",
+ * digest, full-text summary).
+ *
+ * ea_probe_copy copies `bytes` from src to dst (device memory, 16-byte
+ *   aligned, bytes a multiple of 16, the ranges must not overlap); bytes = 0
+ *   does nothing.
+ * ea_probe_read reads `bytes` at src and XORs every 32-bit word into
+ *   *xor_out (device memory, 4-byte aligned; the caller zeroes it first if
+ *   it wants the XOR itself); bytes = 0 only checks the pointers.
+ * Both are asynchronous on `stream`; errors as for every other entry point.
+ */
+ea_status ea_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+ea_status ea_probe_read(const void* src, size_t bytes, uint32_t* xor_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

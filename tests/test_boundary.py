@@ -321,3 +321,16 @@ def test_generic_logit_export_has_no_row_limit(lib):
         st = lib.ea_debug_logits(ctx, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
         assert st == status, (kw, lib.ea_last_error())
         lib.ea_ctx_destroy(ctx)
+
+
+def test_probe_argument_rules(lib):
+    """The bandwidth probes check pointers, alignment and size before launching."""
+    assert lib.ea_probe_copy(None, FAKE, 4096, None) == L.EA_E_NULLPTR
+    assert lib.ea_probe_copy(FAKE, None, 4096, None) == L.EA_E_NULLPTR
+    assert lib.ea_probe_copy(MISALIGNED, FAKE, 4096, None) == L.EA_E_ALIGN
+    assert lib.ea_probe_copy(FAKE, FAKE, 4100, None) == L.EA_E_ALIGN
+    assert lib.ea_probe_copy(None, None, 0, None) == L.EA_OK  # nothing to move
+    assert lib.ea_probe_read(None, 4096, FAKE, None) == L.EA_E_NULLPTR
+    assert lib.ea_probe_read(FAKE, 4096, None, None) == L.EA_E_NULLPTR
+    assert lib.ea_probe_read(FAKE, 4096, FAKE + 2, None) == L.EA_E_ALIGN
+    assert lib.ea_probe_read(FAKE, 4100, FAKE, None) == L.EA_E_ALIGN
