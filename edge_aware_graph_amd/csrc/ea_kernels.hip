@@ -2281,15 +2281,36 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   }
   float ds[H][4], dge[H][4], dbe[H][4];
   float sgy[H], sby[H], sge[H], sbe[H];
+  // D_i per head: the sum of the key blocks' parts in key-block order. The
+  // parts of four key blocks of every head are requested together (clamped
+  // indices, the surplus discarded by a uniform condition), so a row of KB
+  // parts costs ceil(KB / 4) round trips instead of H KB dependent ones.
+  float Dv[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) Dv[h] = 0.f;
+  if constexpr (PM == kPairAll) {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) Dv[h] += red_s[ww][h][li];
+  } else {
+    const float* dp = g.DP + ((size_t)b * H * NP + i) * KB;  // head h at + h NP KB
+    for (int kb0 = 0; kb0 < KB; kb0 += 4) {
+      float x[H][4];
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[h][q] = dp[(size_t)h * NP * KB + (kb0 + q < KB ? kb0 + q : KB - 1)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (kb0 + q < KB)
+#pragma unroll
+          for (int h = 0; h < H; ++h) Dv[h] += x[h][q];
+    }
+  }
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    float Dh = 0.f;
-    if constexpr (PM == kPairAll) {
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) Dh += red_s[ww][h][li];
-    } else {
-      for (int kb = 0; kb < KB; ++kb) Dh += g.DP[(((size_t)b * H + h) * NP + i) * KB + kb];
-    }
+    const float Dh = Dv[h];
     const float gyh = sc.gy[h];
     sgy[h] = sby[h] = sge[h] = sbe[h] = 0.f;
 #pragma unroll
