@@ -2436,42 +2436,69 @@ __global__ __launch_bounds__(kThreads) void bwd_qkv_kernel(LayerArgs a, BwdArgs 
   f32x4 acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int NPP = M * M / kThreads, NPD = M * DH / kThreads;
-  for (int c0 = 0; c0 < NP; c0 += M) {
-    float vr[NPP], vc[NPP], va[NPP], vq[NPD], vk[NPD], vo[NPD];
+  // One contraction chunk in registers: ds rows and columns as 16-byte
+  // pieces (4 per thread each), A as 2-byte values (its rows of n elements
+  // are not 16-byte aligned), Q, K and dO rows as one NPD-element piece.
+  // Chunk c0 + M is requested while chunk c0 is multiplied from LDS, so the
+  // loads of one chunk run under the products of the previous one.
+  constexpr int NPP = M * M / kThreads, NPD = M * DH / kThreads, NP4 = NPP / 4;
+  struct Chunk {
+    f32x4 r[NP4], c[NP4];
+    uint32_t a[NPP];
+    Frag<T, NPD> q, k, o;
+  };
+  const int prr = tid / (DH / NPD), pt0 = (tid % (DH / NPD)) * NPD;  // Q, K, dO row and column of this thread
+  auto load_chunk = [&](int c0, Chunk& x) {
 #pragma unroll
-    for (int k = 0; k < NPP; ++k) {
-      const int idx = tid + k * kThreads, hi = idx / M, lo = idx % M;
-      // dsr: row r0 + hi, column c0 + lo;  dsc and A: row c0 + hi, column r0 + lo
+    for (int k = 0; k < NP4; ++k) {
+      const int idx = tid + k * kThreads, hi = idx / (M / 4), lo = (idx % (M / 4)) * 4;
+      // dsr: row r0 + hi, columns c0 + lo ..;  dsc: row c0 + hi, columns r0 + lo ..
       const bool okr = r0 + hi < NP && c0 + lo < NP, okc = c0 + hi < NP && r0 + lo < NP;
-      const bool oka = c0 + hi < n && r0 + lo < n;
-      vr[k] = g.DS[(bh * NP + (okr ? r0 + hi : 0)) * NP + (okr ? c0 + lo : 0)];
-      vc[k] = g.DS[(bh * NP + (okc ? c0 + hi : 0)) * NP + (okc ? r0 + lo : 0)];
-      va[k] = Num<T>::ld(Ag + bh * n * n + (oka ? (size_t)(c0 + hi) * n + r0 + lo : 0));
-    }
-#pragma unroll
-    for (int k = 0; k < NPD; ++k) {
-      const int idx = tid + k * kThreads, rr = idx / DH, t = idx % DH, c = c0 + rr;
-      const int cp = c < NP ? c : 0, cn = c < n ? c : 0;
-      vq[k] = Num<T>::ld(Qw + (bh * NP + cp) * DH + t);
-      vk[k] = Num<T>::ld(Kw + (bh * NP + cp) * DH + t);
-      vo[k] = Num<T>::ld(dO + ((size_t)b * n + cn) * D + h * DH + t);
+      x.r[k] = *reinterpret_cast<const f32x4*>(g.DS + (bh * NP + (okr ? r0 + hi : 0)) * NP + (okr ? c0 + lo : 0));
+      x.c[k] = *reinterpret_cast<const f32x4*>(g.DS + (bh * NP + (okc ? c0 + hi : 0)) * NP + (okc ? r0 + lo : 0));
     }
 #pragma unroll
     for (int k = 0; k < NPP; ++k) {
       const int idx = tid + k * kThreads, hi = idx / M, lo = idx % M;
-      dsr_s[hi][lo] = r0 + hi < NP && c0 + lo < NP ? vr[k] : 0.f;
-      dsc_s[lo][hi] = c0 + hi < NP && r0 + lo < NP ? vc[k] : 0.f;  // [output row][contraction]
-      a_s[lo][hi] = c0 + hi < n && r0 + lo < n ? va[k] : 0.f;
+      const bool oka = c0 + hi < n && r0 + lo < n;
+      x.a[k] = Num<T>::ldraw(Ag + bh * n * n + (oka ? (size_t)(c0 + hi) * n + r0 + lo : 0));
+    }
+    const int c = c0 + prr, cp = c < NP ? c : 0, cn = c < n ? c : 0;
+    x.q.load(Qw + (bh * NP + cp) * DH + pt0);
+    x.k.load(Kw + (bh * NP + cp) * DH + pt0);
+    x.o.load(dO + ((size_t)b * n + cn) * D + h * DH + pt0);
+  };
+  auto stage_chunk = [&](int c0, const Chunk& x) {
+#pragma unroll
+    for (int k = 0; k < NP4; ++k) {
+      const int idx = tid + k * kThreads, hi = idx / (M / 4), lo = (idx % (M / 4)) * 4;
+      const bool okr = r0 + hi < NP && c0 + lo < NP, okc = c0 + hi < NP && r0 + lo < NP;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsr_s[hi][lo + e] = okr ? x.r[k][e] : 0.f;
+        dsc_s[lo + e][hi] = okc ? x.c[k][e] : 0.f;  // [output row][contraction]
+      }
     }
 #pragma unroll
-    for (int k = 0; k < NPD; ++k) {
-      const int idx = tid + k * kThreads, rr = idx / DH, t = idx % DH, c = c0 + rr;
-      q_s[rr][t] = c < NP ? vq[k] : 0.f;
-      k_s[rr][t] = c < NP ? vk[k] : 0.f;
-      o_s[rr][t] = c < n ? vo[k] : 0.f;
+    for (int k = 0; k < NPP; ++k) {
+      const int idx = tid + k * kThreads, hi = idx / M, lo = idx % M;
+      a_s[lo][hi] = c0 + hi < n && r0 + lo < n ? Num<T>::fromraw(x.a[k]) : 0.f;
     }
+    const int c = c0 + prr;
+#pragma unroll
+    for (int e = 0; e < NPD; ++e) {
+      q_s[prr][pt0 + e] = c < NP ? x.q.get(e) : 0.f;
+      k_s[prr][pt0 + e] = c < NP ? x.k.get(e) : 0.f;
+      o_s[prr][pt0 + e] = c < n ? x.o.get(e) : 0.f;
+    }
+  };
+  Chunk ck;
+  load_chunk(0, ck);
+  for (int c0 = 0; c0 < NP; c0 += M) {
+    stage_chunk(c0, ck);
     __syncthreads();
+    if (c0 + M < NP) load_chunk(c0 + M, ck);  // uniform
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of the products
     const int csteps = (NP - c0 < M ? NP - c0 : M) / 4;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
