@@ -2393,11 +2393,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
     float v[4] = {sgy[h], sby[h], sge[h], sbe[h]};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float x = lg_sum(v[q]);
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
+      // over the lane groups, then the 16 lanes of a row by row moves (the
+      // same pairs, quads, halves and whole row as an exchange by lane index
+      // xor 1, 2, 4, 8, without an LDS round trip per step)
+      const float x = row16_sum(lg_sum(v[q]));
       if (l == 0) sum_s[w][4 * h + q] = x;
     }
   }
