@@ -2125,6 +2125,23 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   const bool tile_ok = jt < JT;  // uniform per wave; waves past JT compute zeros
   const uint32_t mq = sc.query_mask_byte();
   const uint32_t mk = sc.key_mask_byte(jt);
+  // kPairUse with at most kMaxKB key blocks: the key blocks' parts of D for
+  // this lane group's heads are requested before any other load and summed
+  // once the dE' tile is in flight, so their round trip hides under the
+  // tile's instead of following the softmax backward's barrier
+  constexpr int HPG = (H + 3) / 4, kMaxKB = 16;
+  constexpr bool kUse = PM == kPairUse;
+  __shared__ float d_s[kUse ? kWaves : 1][kUse ? H : 1][16];
+  float dpx[kUse ? HPG : 1][kUse ? kMaxKB : 1];
+  if constexpr (kUse) {
+#pragma unroll
+    for (int hh = 0; hh < HPG; ++hh) {
+      const int h = lg * HPG + hh < H ? lg * HPG + hh : H - 1;
+      const float* row = g.DP + (((size_t)b * H + h) * NP + i) * KB;
+#pragma unroll
+      for (int q = 0; q < kMaxKB; ++q) dpx[hh][q] = row[q < KB ? q : KB - 1];
+    }
+  }
   sc.load_weights(a);
   Frag<T, DH / 4> kf[H], vr[H], dof[H];
   sc.load_k(jt, kf);
@@ -2194,6 +2211,18 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   {
     ETile<T, DE> dt;
     dt.load_all(dEp, b, n, i, j0, lg);
+    if constexpr (kUse) {
+      if (KB <= kMaxKB) {  // uniform; the parts in key-block order
+#pragma unroll
+        for (int hh = 0; hh < HPG; ++hh) {
+          float x = 0.f;
+#pragma unroll
+          for (int q = 0; q < kMaxKB; ++q)
+            if (q < KB) x += dpx[hh][q];
+          if (lg * HPG + hh < H) d_s[w][lg * HPG + hh][li] = x;
+        }
+      }
+    }
     if constexpr (kKeepDep) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
@@ -2293,6 +2322,11 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
     for (int h = 0; h < H; ++h)
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) Dv[h] += red_s[ww][h][li];
+  } else if (kUse && KB <= kMaxKB) {  // summed after the tile loads (above)
+    if constexpr (kUse) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) Dv[h] = d_s[w][h][li];
+    }
   } else {
     const float* dp = g.DP + ((size_t)b * H * NP + i) * KB;  // head h at + h NP KB
     for (int kb0 = 0; kb0 < KB; kb0 += 4) {
