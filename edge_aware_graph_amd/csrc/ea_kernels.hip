@@ -2142,6 +2142,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       for (int q = 0; q < kMaxKB; ++q) dpx[hh][q] = row[q < KB ? q : KB - 1];
     }
   }
+  // kPairPartA: the forward's row statistics of this lane's query, requested
+  // with the other small loads rather than where A is recomputed
+  float Lr[PM == kPairPartA ? H : 1];
+  if constexpr (PM == kPairPartA) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) Lr[h] = a.lse[((size_t)b * H + h) * NP + i];
+  }
   sc.load_weights(a);
   Frag<T, DH / 4> kf[H], vr[H], dof[H];
   sc.load_k(jt, kf);
@@ -2270,7 +2277,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
     T* Aw = static_cast<T*>(const_cast<void*>(g.A));
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const float L = a.lse[((size_t)b * H + h) * NP + i];
+      const float L = Lr[h];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gam = R[h >> 2][4 * r + (h & 3)];
@@ -2278,8 +2285,16 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
         const float u = ((S[h][r] * sc.scale) * gam + bet) * sc.gy[h] + sc.gy[H + h];
         const bool ok = ((okb >> r) & 1u) && L != kNegInf;
         Av[h][r] = ok ? Num<T>::rnd(__expf(u - L)) : 0.f;
-        const int j = j0 + 4 * lg + r;
-        if (i < n && j < n) Num<T>::st(Aw + (((size_t)b * H + h) * n + i) * n + j, Av[h][r]);
+      }
+      // the lane's four keys in one store where rows of n keep them aligned
+      const int jb = j0 + 4 * lg;
+      T* dst = Aw + (((size_t)b * H + h) * n + i) * n + jb;
+      if (n % 4 == 0) {  // uniform
+        if (i < n && jb < n) store4<T>(dst, Av[h]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (i < n && jb + r < n) Num<T>::st(dst + r, Av[h][r]);
       }
     }
   }
