@@ -2164,15 +2164,27 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   float Av[H][4];
   if constexpr (PM != kPairPartA) {
     const T* Ag = static_cast<const T*>(g.A);
+    const int jb = j0 + 4 * lg;
+    if (n % 4 == 0) {  // uniform: the lane's four keys in one load
+      const bool ok = i < n && jb < n;
 #pragma unroll
-    for (int h = 0; h < H; ++h)
+      for (int h = 0; h < H; ++h) {
+        Frag<T, 4> f;
+        f.load(Ag + ((size_t)b * H + h) * n * n + (ok ? (size_t)i * n + jb : 0));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * lg + r;
-        const bool ok = i < n && j < n;
-        const float v = Num<T>::ld(Ag + ((size_t)b * H + h) * n * n + (ok ? (size_t)i * n + j : 0));
-        Av[h][r] = ok ? v : 0.f;
+        for (int r = 0; r < 4; ++r) Av[h][r] = ok ? f.get(r) : 0.f;
       }
+    } else {
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = jb + r;
+          const bool ok = i < n && j < n;
+          const float v = Num<T>::ld(Ag + ((size_t)b * H + h) * n * n + (ok ? (size_t)i * n + j : 0));
+          Av[h][r] = ok ? v : 0.f;
+        }
+    }
   }
   // W_e^T row li (head li) over this lane group's channels, for dA through E'
   Frag<T, DE / 4> wet;
