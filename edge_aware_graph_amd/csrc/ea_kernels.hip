@@ -3078,6 +3078,15 @@ __global__ __launch_bounds__(kThreads) void bwd_sums_kernel(LayerArgs a, BwdArgs
   auto colsum = [&](const float* base, int rows, size_t stride, int groups, int q) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int r = q;
+    // sixteen rows' loads per step (row r + u groups into partial sum u % 4,
+    // the same order as four per step), then four, then one
+    for (; r + 15 * groups < rows; r += 16 * groups) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = base[(size_t)(r + u * groups) * stride];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u & 3] += v[u];
+    }
     for (; r + 3 * groups < rows; r += 4 * groups) {
       float v[4];
 #pragma unroll
@@ -3131,8 +3140,15 @@ __global__ __launch_bounds__(kThreads) void bwd_sums_kernel(LayerArgs a, BwdArgs
     const size_t nw = (size_t)3 * D * D + 3 * D;
     const size_t o = (size_t)((int)blockIdx.x - B - nrb) * kThreads + tid;
     if (o >= nw) return;
+    // every slice's value requested at once (clamped slice index, the surplus
+    // discarded by a uniform condition), then added in slice order
+    float v[kMaxKsplit];
+#pragma unroll
+    for (int z = 0; z < kMaxKsplit; ++z) v[z] = g.WP[(size_t)(z < g.ksplit ? z : g.ksplit - 1) * nw + o];
     float t = 0.f;
-    for (int z = 0; z < g.ksplit; ++z) t += g.WP[(size_t)z * nw + o];
+#pragma unroll
+    for (int z = 0; z < kMaxKsplit; ++z)
+      if (z < g.ksplit) t += v[z];
     if (o < (size_t)3 * D * D) {
       const int wsel = (int)(o / ((size_t)D * D));
       (wsel == 0 ? g.gw_q : wsel == 1 ? g.gw_k : g.gw_v)[o % ((size_t)D * D)] = t;
@@ -3159,10 +3175,21 @@ __global__ __launch_bounds__(kThreads) void bwd_small_kernel(LayerArgs a, BwdArg
   const T* y = static_cast<const T*>(a.y);
   const T* Wm = static_cast<const T*>(a.w_ymul);
   const T* Wa = static_cast<const T*>(a.w_yadd);
-  // sum over the graphs of DGY[b][o] times f(b), four graphs per step
+  // sum over the graphs of DGY[b][o] times f(b), graph b into partial sum
+  // b % 4 in graph order; sixteen graphs' loads per step, then four
   auto over_graphs = [&](int o, auto f) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int b = 0;
+    for (; b + 15 < B; b += 16) {
+      float v[16], w[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        v[u] = g.DGY[(size_t)(b + u) * F + o];
+        w[u] = f(b + u);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u & 3] += v[u] * w[u];
+    }
     for (; b + 3 < B; b += 4) {
       float v[4], w[4];
 #pragma unroll
