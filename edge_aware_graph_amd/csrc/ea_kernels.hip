@@ -2874,7 +2874,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(LayerArgs a, BwdArgs
 // columns are contiguous, and writes each column's 4 values as one 8-byte
 // LDS store (a 4 x 4 transpose in registers); kDX's DQKV rows are already
 // contraction-contiguous and are written as they are.
-template <int H, int DH, int MODE>
+template <int H, int DH>
 __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, BwdArgs g) {
   // chunk depth TK divides D: a kDX chunk lies inside one of W_q, W_k, W_v
   constexpr int D = H * DH, TM = 64, TN = 64, TK = D >= 128 ? 128 : 64, LK = TK + 8;
@@ -2885,13 +2885,24 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
   __shared__ float cs_s[16][64];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int wm = w & 1, wn = w >> 1;
-  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
+  // one launch for both products: the kDX tiles (row tile fastest), then
+  // the kDW tiles (output row tile fastest, then column tile, then slice);
+  // they are independent, so every block of both is resident at once
+  const int nx = (a.B * a.NP + TM - 1) / TM, ndx = nx * (D / TN), nwx = 3 * D / TM;
+  const int id = blockIdx.x;
+  const int MODE = id < ndx ? kDX : kDW;  // uniform per block
+  const int rw = id - ndx;
+  const int bx = MODE == kDX ? id % nx : rw % nwx;
+  const int by = MODE == kDX ? id / nx : (rw / nwx) % (D / TN);
+  const int bz = MODE == kDX ? 0 : rw / (nwx * (D / TN));
+  const int gz = MODE == kDX ? 1 : g.ksplit;
+  const int m0 = bx * TM, n0 = by * TN;
   const int NP = a.NP, n = a.n;
   const int M = MODE == kDX ? a.B * NP : 3 * D, K = MODE == kDX ? 3 * D : a.B * NP;
   // slices of whole chunks, so that a row quad (4 rows from a multiple of 4)
   // never straddles a slice or a graph (NP is a multiple of 16)
-  const int kslice = ((K + gridDim.z - 1) / gridDim.z + TK - 1) / TK * TK;
-  const int kbeg = blockIdx.z * kslice, kend = K < kbeg + kslice ? K : kbeg + kslice;
+  const int kslice = ((K + gz - 1) / gz + TK - 1) / TK * TK;
+  const int kbeg = bz * kslice, kend = K < kbeg + kslice ? K : kbeg + kslice;
   const bf16_t* X = static_cast<const bf16_t*>(a.X);
   // per thread and chunk: 2 groups of (4 contraction rows x 4 columns); the
   // group's column quad cq = idx % 16 and row quad kq = idx / 16, idx = tid + 256 e
@@ -3028,7 +3039,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
     }
     __syncthreads();
   }
-  if (MODE == kDW && blockIdx.y == 0) {
+  if (MODE == kDW && by == 0) {
     // bias sums: the 16 threads of a column quad (tid % 16) reduce through LDS
 #pragma unroll
     for (int q = 0; q < 4; ++q) cs_s[tid / 16][4 * (tid % 16) + q] = csum[q];
@@ -3037,7 +3048,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
       float t = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) t += cs_s[r][tid];
-      g.WP[(size_t)blockIdx.z * (3 * D * D + 3 * D) + 3 * D * D + m0 + tid] = t;  // this slice's db
+      g.WP[(size_t)bz * (3 * D * D + 3 * D) + 3 * D * D + m0 + tid] = t;  // this slice's db
     }
   }
 #pragma unroll
@@ -3050,7 +3061,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
       const int bq = m / NP, ii = m % NP;
       if (ii < n) Num<bf16_t>::st(static_cast<bf16_t*>(g.dX) + ((size_t)bq * n + ii) * D + col, v);
     } else {
-      g.WP[(size_t)blockIdx.z * (3 * D * D + 3 * D) + (size_t)m * D + col] = v;  // this slice's dW
+      g.WP[(size_t)bz * (3 * D * D + 3 * D) + (size_t)m * D + col] = v;  // this slice's dW
     }
   }
 }
@@ -3347,8 +3358,9 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g0, hipStream_t s) 
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(g.red_rows), dim3(kThreads), 0, s, a, g);
   const dim3 gdx((a.B * a.NP + 63) / 64, D / 64, 1), gdw(3 * D / 64, D / 64, g.ksplit);
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH, kDX>), gdx, dim3(kThreads), 0, s, a, g);
-    hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH, kDW>), gdw, dim3(kThreads), 0, s, a, g);
+    // both products in one launch: the kDX tiles, then the kDW tiles
+    const unsigned nboth = gdx.x * gdx.y + gdw.x * gdw.y * gdw.z;
+    hipLaunchKernelGGL((bwd_gemm_bf16_kernel<H, DH>), dim3(nboth), dim3(kThreads), 0, s, a, g);
   } else {
     hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDX, 64>), gdx, dim3(kThreads), 0, s, a, g);
     hipLaunchKernelGGL((bwd_gemm_kernel<T, H, DH, kDW, 64>), gdw, dim3(kThreads), 0, s, a, g);
