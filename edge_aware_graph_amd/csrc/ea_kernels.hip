@@ -2676,14 +2676,40 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_reduce_kernel(LayerArgs a, 
     if (cidx + gridDim.x < nchunks) load_chunk(cidx + gridDim.x, nxt);
     __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's MFMAs
     if (cb < DE) {
-      // MFMA 16x16x4: lane (li, lg) supplies A[li][k = lg] and B[k = lg][li]
+      if constexpr (sizeof(T) == 2) {
+        // bfloat16: every staged value is a bfloat16 value held as a float,
+        // so packing it back is exact and MFMA 16x16x16 bf16 (lane (li, lg):
+        // A[li][k = 4 lg .. 4 lg + 3], B[k][li]) forms the same products as
+        // the float32 form, a quarter of the MFMA issue time
 #pragma unroll
-      for (int ks = 0; ks < P / 4; ++ks) {
-        const int pk = 4 * ks + lg;
-        const float fa = li < 2 * H ? f_s[li < 2 * H ? li : 0][pk] : 0.f;  // FiLM row li
-        accF = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, e_s[pk][cb + li], accF, 0, 0, 0);
-        const float ab = li < H ? a_s[li < H ? li : 0][pk] : (li == H ? 1.f : 0.f);  // head li, or ones
-        accE = __builtin_amdgcn_mfma_f32_16x16x4f32(d_s[pk][cb + li], ab, accE, 0, 0, 0);
+        for (int k16 = 0; k16 < P / 16; ++k16) {
+          const int p0 = 16 * k16 + 4 * lg;
+          float fa4[4], eb4[4], da4[4], ab4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            fa4[r] = li < 2 * H ? f_s[li < 2 * H ? li : 0][p0 + r] : 0.f;  // FiLM row li
+            eb4[r] = e_s[p0 + r][cb + li];
+            da4[r] = d_s[p0 + r][cb + li];
+            ab4[r] = li < H ? a_s[li < H ? li : 0][p0 + r] : (li == H ? 1.f : 0.f);  // head li, or ones
+          }
+          Frag<bf16_t, 4> fa, eb, da, ab;
+          fa.set(fa4);
+          eb.set(eb4);
+          da.set(da4);
+          ab.set(ab4);
+          accF = mma(accF, fa, eb);
+          accE = mma(accE, da, ab);
+        }
+      } else {
+        // MFMA 16x16x4: lane (li, lg) supplies A[li][k = lg] and B[k = lg][li]
+#pragma unroll
+        for (int ks = 0; ks < P / 4; ++ks) {
+          const int pk = 4 * ks + lg;
+          const float fa = li < 2 * H ? f_s[li < 2 * H ? li : 0][pk] : 0.f;  // FiLM row li
+          accF = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, e_s[pk][cb + li], accF, 0, 0, 0);
+          const float ab = li < H ? a_s[li < H ? li : 0][pk] : (li == H ? 1.f : 0.f);  // head li, or ones
+          accE = __builtin_amdgcn_mfma_f32_16x16x4f32(d_s[pk][cb + li], ab, accE, 0, 0, 0);
+        }
       }
     }
     __syncthreads();
