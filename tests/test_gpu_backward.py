@@ -147,11 +147,14 @@ def test_backward_prefix_masks_padded_tiles(n, dtype, n_real, two_pass):
     check(got, ref, batch, dims)
 
 
-@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"dtype": "bf16"}), ("planar", {"B": 2, "n": 100})],
-                         ids=["tiny-fp32", "tiny-bf16", "n100-bf16"])
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"dtype": "bf16"}), ("planar", {"B": 2, "n": 100}),
+                                       ("planar", {"B": 2, "n": 37})],
+                         ids=["tiny-fp32", "tiny-bf16", "n100-bf16", "n37-bf16"])
 def test_backward_forced_two_pass(name, over):
     """Two-pass contexts keep no A: the backward recomputes it as exp(u - lse)
-    from the forward's row statistics (forced two-pass at small n)."""
+    from the forward's row statistics (forced two-pass at small n). With n =
+    37 the rows of the n x n map are not multiples of four keys, so A is
+    stored and read back one key at a time."""
     dims = dims_of(name, **over)
     batch = W.make_batch(name, bias_scale=0.1, dims=dims)
     if "n" in over:
@@ -182,6 +185,23 @@ def test_backward_large_full_size_sampled_rows():
     gradient finite."""
     dims = dims_of("large")
     batch = W.make_batch("large", bias_scale=0.1)
+    sampled_rows_check(batch, dims)
+
+
+def test_backward_more_than_16_key_blocks_sampled_rows():
+    """n = 1040 (17 key blocks of 64): the second pair pass sums the key
+    blocks' parts of D in its loop form rather than from the parts requested
+    ahead of the tiles (at most 16); checked like the large configuration on
+    sampled rows of one graph with a ragged mask."""
+    dims = dims_of("large", B=1, n=1040)
+    batch = W.make_batch("large", bias_scale=0.1, dims=dims)
+    rng = np.random.default_rng(1040)
+    batch["mask"] = (rng.random((1, 1040)) < 0.9).astype(np.uint8)
+    batch["mask"][0, [0, 1039]] = 1
+    sampled_rows_check(batch, dims)
+
+
+def sampled_rows_check(batch, dims):
     run = HX.Run(batch, dims)
     assert run.layer.two_pass
     run.fused()
