@@ -2938,9 +2938,12 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
     uint8_t mk[NB][4];  // kDW: mask bytes of the X rows
     bool ok[NB][4];     // kDW: the X row exists (below kend, node below n)
   };
-  // kDX's A: NA float4 per thread, rows mm = idx / (TK / 4), columns 4 (idx % (TK / 4))
-  u32x4 xa[NA];
+  // kDX's A: NA float4 per thread, rows mm = idx / (TK / 4), columns 4 (idx %
+  // (TK / 4)), held in the registers of kDW's float32 source (one launch runs
+  // both products, so the two share their staging registers)
+  static_assert(NA == 4 * NB, "kDX's A pieces fill kDW's float32 staging");
   Stage st;
+  u32x4* xa = &st.fa[0][0];
   auto load = [&](int k0) {
     if (MODE == kDX) {
       // a chunk lies wholly inside the contraction or wholly past it (the
