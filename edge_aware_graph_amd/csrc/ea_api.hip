@@ -265,7 +265,7 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->boff_dqkv = c->boff_df + round256(pairs * 2 * d.H * c->esz);
   c->boff_dgy = c->boff_dqkv + round256((size_t)d.B * c->NP * 3 * d.d * sizeof(float));
   c->boff_ps = c->boff_dgy + round256((size_t)d.B * 4 * d.H * sizeof(float));
-  c->boff_red = c->boff_ps + round256((size_t)d.B * (c->NP / 16) * ((c->NP + 63) / 64) * 4 * d.H * sizeof(float));
+  c->boff_red = c->boff_ps + round256((size_t)d.B * (c->NP / 16) * (ea::kUseSplit * ((c->NP + 63) / 64)) * 4 * d.H * sizeof(float));
   c->boff_wp = c->boff_red + round256((size_t)ea::kRedRows * (3 * d.H * d.de + d.de) * sizeof(float));
   c->boff_dp = c->boff_wp + round256((size_t)ea::kMaxKsplit * (3 * (size_t)d.d * d.d + 3 * d.d) * sizeof(float));
   c->boff_ar = c->boff_dp + round256((size_t)d.B * d.H * c->NP * ((c->NP + 63) / 64) * sizeof(float));

@@ -89,6 +89,10 @@ struct BwdArgs {
 // order, so the gradients are the same bits on every run.
 constexpr int kRedRows = 1024;  // most blocks of the pair reduction
 constexpr int kMaxKsplit = 16;  // most contraction slices of the dW GEMM
+// blocks per 64 keys in the backward's second pair pass (n > 64 or two-pass
+// contexts): blocks of two waves (32 keys), two to a CU, so that their phases
+// need not coincide; each block writes its own slot of the per-block sums
+constexpr int kUseSplit = 2;
 
 // Graph-transformer block around the layer: parameters (in this order; the
 // nn.Linear [out, in] layout, all in the layer's dtype) and arguments.

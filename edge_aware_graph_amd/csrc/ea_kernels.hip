@@ -2103,25 +2103,27 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
 //     A = exp(u - lse_i) rounded to T (the operand the forward's update used),
 //     and written to g.A for the kernels that follow.
 enum PairMode : int { kPairAll = 0, kPairPart = 1, kPairUse = 2, kPairPartA = 3 };
-template <typename T, int H, int DH, int DE, int PM>
-__global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs g) {
+template <typename T, int H, int DH, int DE, int PM, int WV = kWaves>
+__global__ __launch_bounds__(WV * 64) void bwd_pair_kernel(LayerArgs a, BwdArgs g) {
   constexpr int D = H * DH, NCH = DE / 16;
   // Modes that write dE keep the dE' tile of step (1) in LDS for step (5)
   // (each lane reads back its own words), so dE' crosses HBM once
   constexpr bool kKeepDep = PM == kPairAll || PM == kPairUse;
   constexpr int NDW = Frag<T, DE / 4>::ND;  // words of one lane's fragment
   constexpr int NDC = NDW % 4 == 0 ? 4 : NDW;  // words per LDS access
-  __shared__ float red_s[kWaves][H][16];
-  __shared__ float sum_s[kWaves][4 * H];
-  __shared__ __align__(16) uint32_t dep_s[kKeepDep ? kWaves * 16 * NDW * 64 : 1];
+  static_assert(WV == kWaves || PM == kPairUse, "the row sums of D over a block's waves need all four key tiles");
+  __shared__ float red_s[WV][H][16];
+  __shared__ float sum_s[WV][4 * H];
+  __shared__ __align__(16) uint32_t dep_s[kKeepDep ? WV * 16 * NDW * 64 : 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int b = blockIdx.y, i0 = blockIdx.x * 16;
   // word group c of key jj of this lane: 16-byte pieces of consecutive lanes side by side
   auto dep_at = [&](int jj, int c) { return dep_s + (((w * 16 + jj) * (NDW / NDC) + c) * 64 + l) * NDC; };
   Scorer<T, H, DH, DE> sc;
   sc.setup(a, b, i0);
-  const int n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, jt = kWaves * blockIdx.z + w, j0 = 16 * jt;
-  const int KB = gridDim.z;  // key blocks of the row
+  const int n = a.n, NP = a.NP, JT = sc.JT, i = sc.i, jt = WV * blockIdx.z + w, j0 = 16 * jt;
+  const int KB = (NP + 63) / 64;  // 64-key blocks of the row (the parts of D)
+  const int KBZ = gridDim.z;      // key blocks of this launch (the slots of PS)
   const bool tile_ok = jt < JT;  // uniform per wave; waves past JT compute zeros
   const uint32_t mq = sc.query_mask_byte();
   const uint32_t mk = sc.key_mask_byte(jt);
@@ -2131,7 +2133,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   // tile's instead of following the softmax backward's barrier
   constexpr int HPG = (H + 3) / 4, kMaxKB = 16;
   constexpr bool kUse = PM == kPairUse;
-  __shared__ float d_s[kUse ? kWaves : 1][kUse ? H : 1][16];
+  __shared__ float d_s[kUse ? WV : 1][kUse ? H : 1][16];
   float dpx[kUse ? HPG : 1][kUse ? kMaxKB : 1];
   if constexpr (kUse) {
 #pragma unroll
@@ -2330,7 +2332,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
       const int h = tid >> 4, q = tid & 15, iq = i - li + q;
       float x = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) x += red_s[ww][h][q];
+      for (int ww = 0; ww < WV; ++ww) x += red_s[ww][h][q];
       g.DP[(((size_t)b * H + h) * NP + iq) * KB + blockIdx.z] = x;
     }
     return;
@@ -2348,7 +2350,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) Dv[h] += red_s[ww][h][li];
+      for (int ww = 0; ww < WV; ++ww) Dv[h] += red_s[ww][h][li];
   } else if (kUse && KB <= kMaxKB) {  // summed after the tile loads (above)
     if constexpr (kUse) {
 #pragma unroll
@@ -2466,9 +2468,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pair_kernel(LayerArgs a, BwdArgs
   if (tid < 4 * H) {
     float x = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) x += sum_s[ww][tid];
+    for (int ww = 0; ww < WV; ++ww) x += sum_s[ww][tid];
     const int h = tid >> 2, q = tid & 3;
-    g.PS[(((size_t)b * JT + blockIdx.x) * KB + blockIdx.z) * 4 * H + q * H + h] = x;
+    g.PS[(((size_t)b * JT + blockIdx.x) * KBZ + blockIdx.z) * 4 * H + q * H + h] = x;
   }
 }
 
@@ -3370,18 +3372,22 @@ hipError_t backward_shape(const LayerArgs& a, const BwdArgs& g0, hipStream_t s) 
   // dW: the rows (contraction) split in slices of at least 256
   const int rows = a.B * a.NP;
   g.ksplit = rows / 256 < 1 ? 1 : (rows / 256 > kMaxKsplit ? kMaxKsplit : rows / 256);
-  g.ps_kb = (g.recompute_a || a.NP > 64) ? (a.NP + 63) / 64 : 1;
+  // n > 64 and two-pass: the second pair pass runs kUseSplit blocks per 64
+  // keys, each with its own slot of the per-block sums
+  constexpr int kUseWaves = kWaves / kUseSplit;
+  static_assert(kUseWaves * kUseSplit == kWaves, "whole key tiles per block");
+  g.ps_kb = (g.recompute_a || a.NP > 64) ? kUseSplit * ((a.NP + 63) / 64) : 1;
   const unsigned prep_blocks = (unsigned)((size_t)a.B * H * ((a.NP + 63) / 64));  // < 2^31 for n <= 2^20
   hipLaunchKernelGGL((bwd_prep_kernel<T, H, DH, DE>), dim3(prep_blocks), dim3(kThreads), 0, s, a, g);
   const int KB = (a.NP + 63) / 64;
   if (g.recompute_a) {  // two-pass context: A recomputed (and stored) by the first pass
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairPartA>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
-    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse, kUseWaves>), dim3(JT, a.B, kUseSplit * KB), dim3(64 * kUseWaves), 0, s, a, g);
   } else if (a.NP <= 64) {
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairAll>), dim3(JT, a.B, 1), dim3(kThreads), 0, s, a, g);
   } else {  // key blocks of 64: the row sums of D first, then the rest
     hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairPart>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
-    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse>), dim3(JT, a.B, KB), dim3(kThreads), 0, s, a, g);
+    hipLaunchKernelGGL((bwd_pair_kernel<T, H, DH, DE, kPairUse, kUseWaves>), dim3(JT, a.B, kUseSplit * KB), dim3(64 * kUseWaves), 0, s, a, g);
   }
   hipLaunchKernelGGL((bwd_qkv_kernel<T, H, DH>), dim3(H, a.B, (a.NP + 63) / 64), dim3(kThreads), 0, s, a, g);
   hipLaunchKernelGGL((bwd_pair_reduce_kernel<T, H, DE>), dim3(g.red_rows), dim3(kThreads), 0, s, a, g);
