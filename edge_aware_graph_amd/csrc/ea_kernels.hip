@@ -2568,12 +2568,41 @@ __global__ __launch_bounds__(kThreads) void bwd_qkv_kernel(LayerArgs a, BwdArgs 
       if (mt >= mtn) continue;  // uniform per wave
       const int row = 16 * mt + li, col = 16 * nt + li;
       f32x4 c = acc[t];
+      if constexpr (sizeof(T) == 2) {
+        // bfloat16 MFMA 16x16x16 (lane (li, lg): k = 4 lg .. 4 lg + 3 of 16):
+        // K, Q, A and dO are bfloat16 values, so their packing is exact;
+        // the float32 ds enters as its bfloat16 rounding plus the rounded
+        // remainder, a second product (2^-18 of ds per term)
+#pragma unroll 2
+        for (int s16 = 0; s16 < csteps / 4; ++s16) {
+          const int k0 = 16 * s16 + 4 * lg;
+          float av[4], bv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            av[r] = which == 0 ? dsr_s[row][k0 + r] : which == 1 ? dsc_s[row][k0 + r] : a_s[row][k0 + r];
+            bv[r] = which == 0 ? k_s[k0 + r][col] : which == 1 ? q_s[k0 + r][col] : o_s[k0 + r][col];
+          }
+          Frag<bf16_t, 4> ah, bq;
+          ah.set(av);
+          bq.set(bv);
+          c = mma(c, ah, bq);
+          if (which < 2) {  // uniform per wave
+            float lo[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lo[r] = av[r] - ah.get(r);
+            Frag<bf16_t, 4> al;
+            al.set(lo);
+            c = mma(c, al, bq);
+          }
+        }
+      } else {
 #pragma unroll 4
-      for (int s4 = 0; s4 < csteps; ++s4) {
-        const int kk = 4 * s4 + lg;
-        const float av = which == 0 ? dsr_s[row][kk] : which == 1 ? dsc_s[row][kk] : a_s[row][kk];
-        const float bv = which == 0 ? k_s[kk][col] : which == 1 ? q_s[kk][col] : o_s[kk][col];
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+        for (int s4 = 0; s4 < csteps; ++s4) {
+          const int kk = 4 * s4 + lg;
+          const float av = which == 0 ? dsr_s[row][kk] : which == 1 ? dsc_s[row][kk] : a_s[row][kk];
+          const float bv = which == 0 ? k_s[kk][col] : which == 1 ? q_s[kk][col] : o_s[kk][col];
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+        }
       }
       acc[t] = c;
     }
