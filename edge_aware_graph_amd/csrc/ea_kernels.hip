@@ -3139,43 +3139,34 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_bf16_kernel(LayerArgs a, Bw
 // threads' parts in a fixed order.
 template <typename T, int H, int DH, int DE>
 __global__ __launch_bounds__(kThreads) void bwd_sums_kernel(LayerArgs a, BwdArgs g) {
-  constexpr int NR = 3 * H * DE + DE, F = 4 * H, GF = kThreads / F, CB = 16, D = H * DH;
-  static_assert(kThreads % F == 0, "whole groups");
+  constexpr int NR = 3 * H * DE + DE, F = 4 * H, CB = 16, D = H * DH;
   __shared__ __align__(16) float part_s[4 * kThreads];
   const int tid = threadIdx.x, B = a.B;
   const int nrb = (NR + CB - 1) / CB;
-  // column c of `rows` rows (row stride `stride`), rows split over `groups`
-  // threads: rows q, q + groups, ... for the thread of group q
-  auto colsum = [&](const float* base, int rows, size_t stride, int groups, int q) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int r = q;
-    // sixteen rows' loads per step (row r + u groups into partial sum u % 4,
-    // the same order as four per step), then four, then one
-    for (; r + 15 * groups < rows; r += 16 * groups) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = base[(size_t)(r + u * groups) * stride];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) acc[u & 3] += v[u];
-    }
-    for (; r + 3 * groups < rows; r += 4 * groups) {
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = base[(size_t)(r + u * groups) * stride];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += v[u];
-    }
-    for (; r < rows; r += groups) acc[0] += base[(size_t)r * stride];
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  };
   if ((int)blockIdx.x < B) {
+    // the graph's PS rows: F columns as F / 4 16-byte column groups, the
+    // rows split over kThreads / (F / 4) row groups (rows q, q + RG2, ...),
+    // each thread's rows loaded 16 at a time, the row groups added in order
+    constexpr int CG = F / 4, RG2 = kThreads / CG, U = 16;
+    static_assert(F % 4 == 0 && kThreads % CG == 0 && RG2 * F <= 4 * kThreads, "column groups");
     const int b = blockIdx.x, rows = a.NP / 16 * g.ps_kb;
-    const int c = tid % F, q = tid / F;
-    part_s[tid] = colsum(g.PS + (size_t)b * rows * F + c, rows, F, GF, q);
+    const int cg = tid % CG, q = tid / CG;
+    const float* base = g.PS + (size_t)b * rows * F + 4 * cg;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int r = q;
+    for (; r + (U - 1) * RG2 < rows; r += U * RG2) {
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)(r + u * RG2) * F);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc += v[u];
+    }
+    for (; r < rows; r += RG2) acc += *reinterpret_cast<const f32x4*>(base + (size_t)r * F);
+    *reinterpret_cast<f32x4*>(&part_s[q * F + 4 * cg]) = acc;
     __syncthreads();
     if (tid < F) {
       float t = 0.f;
-      for (int k = 0; k < GF; ++k) t += part_s[k * F + tid];
+      for (int k = 0; k < RG2; ++k) t += part_s[k * F + tid];
       g.DGY[(size_t)b * F + tid] = t;
     }
   } else if ((int)blockIdx.x < B + nrb) {
