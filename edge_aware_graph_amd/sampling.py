@@ -66,15 +66,23 @@ class SamplingLoop:
         self.X[0].copy_(X0)
         self.E[0].copy_(E0)
         self.y[0].copy_(y)
-        cur = 0
-        for _ in range(steps):
-            for k, w in enumerate(self.weights):
+        # every (layer, buffer parity) call is checked and marshalled once per
+        # run, so the loop itself only launches
+        calls = []
+        for k, w in enumerate(self.weights):
+            per = []
+            for cur in (0, 1):
                 nxt = 1 - cur
                 if self.blocks:
-                    self.layer.block(w, self.block_params[k], self.X[cur], self.E[cur], self.y[cur], mask,
-                                     self.X[nxt], self.E[nxt], self.y[nxt], self.ws)
+                    per.append(self.layer.bind_block(w, self.block_params[k], self.X[cur], self.E[cur], self.y[cur],
+                                                     mask, self.X[nxt], self.E[nxt], self.y[nxt], self.ws))
                 else:
-                    self.layer.layer(w, self.X[cur], self.E[cur], self.y[0], mask, self.X[nxt], self.A,
-                                     self.E[nxt], self.ws)
-                cur = nxt
+                    per.append(self.layer.bind_layer(w, self.X[cur], self.E[cur], self.y[0], mask, self.X[nxt],
+                                                     self.A, self.E[nxt], self.ws))
+            calls.append(per)
+        cur = 0
+        for _ in range(steps):
+            for per in calls:
+                per[cur]()
+                cur = 1 - cur
         return self.X[cur], self.E[cur], (self.y[cur] if self.blocks else self.y[0])
