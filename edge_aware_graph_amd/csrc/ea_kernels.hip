@@ -2093,8 +2093,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(LayerArgs a, BwdArgs
   }
 }
 
-// bwd_pair: one block per (16 queries, graph, 64 keys), wave w = key tile
-// 4 blockIdx.z + w. The row sums D_i = sum_j A_ij dA_ij span every key:
+// bwd_pair: one block per (16 queries, graph, 16 WV keys), wave w = key tile
+// WV blockIdx.z + w (WV = 4 waves, 64 keys, except kPairUse, which runs
+// kWaves / kUseSplit). The row sums D_i = sum_j A_ij dA_ij span every key:
 //   kPairAll  (n <= 64, one key block): D from the block's four waves;
 //   kPairPart (64 < n): only dA, and the block's part of D into DP;
 //   kPairUse  (64 < n): D as the sum of the key blocks' parts, then the rest;
