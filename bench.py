@@ -58,6 +58,8 @@ def parse():
                     help="ablation variant of the layer (the default is the full layer)")
     ap.add_argument("--backward", action="store_true",
                     help="time training steps instead: the layer forward plus its backward")
+    ap.add_argument("--recompute-a", action="store_true",
+                    help="with --backward on two-pass shapes: pass no A (the backward recomputes it)")
     ap.add_argument("--block", action="store_true",
                     help="time the graph-transformer block around the layer (layer + node, edge and y paths)")
     ap.add_argument("--sampling-layers", type=int, default=0,
@@ -69,8 +71,9 @@ def parse():
 def backward_bench(args, cfg, dims, batch):
     """Training step of the layer: edge_attn_layer then edge_attn_backward, on
     buffer sets rotated so that every step reads from HBM (two buffer sets:
-    at the large shape one set holds several GB). Two-pass shapes store no A;
-    the backward recomputes it."""
+    at the large shape one set holds several GB). Two-pass shapes pass an A
+    buffer, which the layer's second pass fills and the backward reads
+    (--recompute-a: no A, the backward recomputes it)."""
     import torch
     from edge_aware_graph_amd.layer import EdgeAttention
     dev = torch.device("cuda:0")
@@ -85,7 +88,7 @@ def backward_bench(args, cfg, dims, batch):
             X=torch.from_numpy(batch["X"]).to(dev, dt), E=torch.from_numpy(batch["E"]).to(dev, dt),
             y=torch.from_numpy(batch["y"]).to(dev, dt), m=torch.from_numpy(batch["mask"]).to(dev),
             O=torch.empty(B, n, d, dtype=dt, device=dev),
-            A=None if layer.two_pass else torch.empty(B, H, n, n, dtype=dt, device=dev),
+            A=None if (layer.two_pass and args.recompute_a) else torch.empty(B, H, n, n, dtype=dt, device=dev),
             Eo=torch.empty(B, n, n, de, dtype=dt, device=dev),
             dO=torch.from_numpy(rng.standard_normal((B, n, d)).astype(np.float32)).to(dev, dt),
             dEp=torch.from_numpy(rng.standard_normal((B, n, n, de)).astype(np.float32)).to(dev, dt),
@@ -116,7 +119,7 @@ def backward_bench(args, cfg, dims, batch):
     prof = layer.profile_end()
     kernels = {name: {"avg_us": 1e3 * ms / cnt, "launches": cnt} for name, (ms, cnt) in prof.items() if cnt}
     bwd_name = [k for k in kernels if k.startswith("backward")][0]
-    alg = algorithmic_bytes("backward", dims, batch["n_real"], layer.two_pass)
+    alg = algorithmic_bytes("backward", dims, batch["n_real"], layer.two_pass and args.recompute_a)
     bwd_us = kernels[bwd_name]["avg_us"]
     return {
         "metric": "graphs/s per training step of the layer (forward + backward)",
@@ -125,7 +128,8 @@ def backward_bench(args, cfg, dims, batch):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if dims.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded %s graphs, random Xavier weights, random output gradients)" % cfg.structure,
-        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "H": H, "buffer_sets": len(sets)},
+        "config": {"workload": cfg.name, "B": B, "n": n, "d": d, "de": de, "H": H, "buffer_sets": len(sets),
+                   "two_pass": layer.two_pass, "a_stored": sets[0]["A"] is not None},
         # the backward's launches taken together (HIP events around the call)
         "roofline": {"kernel": bwd_name, "bound": "hbm", "achieved": alg / (bwd_us * 1e3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": alg / (bwd_us * 1e3) / HBM_PEAK_GBS,

@@ -22,6 +22,7 @@ struct ea_ctx {
   int two_pass;
   int generic;     // the shape has no tuned kernels: the generic path runs
   int forward_done;
+  const void* a_written;  // two-pass: the A buffer the last edge_attn_layer call filled (else NULL)
   size_t esz;      // element size of desc.dtype
   size_t off_q, off_k, off_v, off_lse, off_gy, off_order, ws_bytes;
   size_t boff_ds, boff_df, boff_dqkv, boff_dgy, boff_ps, boff_red, boff_wp, boff_dp, boff_ar, bws_bytes;  // backward workspace
@@ -250,6 +251,7 @@ ea_status ea_ctx_create(const ea_desc* desc, ea_ctx** out) {
   c->two_pass = (d.flags & EA_FORCE_TWO_PASS) || d.n > EA_SINGLE_PASS_MAX_N;
   c->generic = !ea::shape_supported(d.dtype, d.H, d.dh, d.de);
   c->forward_done = 0;
+  c->a_written = nullptr;
   c->esz = d.dtype == EA_BF16 ? 2 : 4;
   const size_t qkv = round256((size_t)d.B * d.H * c->NP * d.dh * c->esz);
   c->off_q = 0;
@@ -318,6 +320,7 @@ ea_status edge_attn_forward(ea_ctx* c, const ea_attn_params* p, const void* X, c
   a.O = O;
   a.A = A;
   c->forward_done = 0;
+  c->a_written = nullptr;
   EA_TRY(run_qkv(c, a, s));
   if (c->generic) {
     EA_TRY(run_gen(c, a, EA_K_ATTN, ea::kGenForward, s));
@@ -330,10 +333,11 @@ ea_status edge_attn_forward(ea_ctx* c, const ea_attn_params* p, const void* X, c
   return EA_OK;
 }
 
-ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
-                      const void* E, const void* y, const uint8_t* mask, const void* A,
-                      void* E_out, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
+// The edge update; A_out (two-pass, no variant flag): the second pass also
+// writes the attention map it recomputes.
+static ea_status update_impl(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                             const void* E, const void* y, const uint8_t* mask, const void* A,
+                             void* A_out, void* E_out, void* ws, size_t ws_bytes, void* stream) {
   if (!c) return fail(EA_E_NULLPTR, "ctx is NULL");
   if (!u) return fail(EA_E_NULLPTR, "update parameters are NULL");
   EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
@@ -352,6 +356,7 @@ ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params
                   c->two_pass ? "two-pass" : "unnormalized-variant");
     ea::LayerArgs a = make_args(c, p, u, nullptr, E, y, mask, ws);
     a.E_out = E_out;
+    a.A = A_out;
     if (c->generic) return run_gen(c, a, EA_K_UPDATE, ea::kGenUpdate, s);
     const int mode = unnormalized(c) ? ea::kRecomputeU : ea::kRecompute;
     return timed(c, EA_K_UPDATE, s, [&] {
@@ -366,6 +371,13 @@ ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params
   return timed(c, EA_K_UPDATE, s, [&] {
     return ea::launch_update(a, c->d.dtype, c->d.H, c->d.dh, c->d.de, ea::kReadA, s);
   });
+}
+
+ea_status edge_update(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
+                      const void* E, const void* y, const uint8_t* mask, const void* A,
+                      void* E_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return update_impl(c, p, u, E, y, mask, A, nullptr, E_out, ws, ws_bytes, stream);
 }
 
 ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_params* u,
@@ -389,6 +401,7 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
       ea::LayerArgs a = make_args(c, p, u, X, E, y, mask, ws);
       a.O = O; a.A = A; a.E_out = E_out;
       c->forward_done = 0;
+      c->a_written = nullptr;
       EA_TRY(run_qkv(c, a, s));
       EA_TRY(run_gen(c, a, EA_K_FUSED, ea::kGenLayer, s));
       c->forward_done = 1;
@@ -399,8 +412,18 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
     EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
     EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
     EA_TRY(check_ptr(E_out, "E_out", 16, true));
-    EA_TRY(edge_attn_forward(c, p, X, E, y, mask, O, A, ws, ws_bytes, stream));
-    return edge_update(c, p, u, E, y, mask, nullptr, E_out, ws, ws_bytes, stream);
+    if (!c->two_pass) {  // unnormalized variant, one pass: A from the forward, the update recomputes
+      EA_TRY(edge_attn_forward(c, p, X, E, y, mask, O, A, ws, ws_bytes, stream));
+      return update_impl(c, p, u, E, y, mask, nullptr, nullptr, E_out, ws, ws_bytes, stream);
+    }
+    // two-pass: A, if given, is written by the second pass
+    if (A && unnormalized(c))
+      return fail(EA_E_UNSUPPORTED, "A is not produced by the two-pass scheme with the unnormalized variant");
+    EA_TRY(check_ptr(A, "A", 16, false));
+    EA_TRY(edge_attn_forward(c, p, X, E, y, mask, O, nullptr, ws, ws_bytes, stream));
+    EA_TRY(update_impl(c, p, u, E, y, mask, nullptr, A, E_out, ws, ws_bytes, stream));
+    c->a_written = A;
+    return EA_OK;
   }
   EA_TRY(check_attn_params(c, p));
   EA_TRY(check_io(c, X, E, y, mask, true));
@@ -419,6 +442,7 @@ ea_status edge_attn_layer(ea_ctx* c, const ea_attn_params* p, const ea_update_pa
   if (!c->generic && !c->two_pass && ea::wants_order(c->d.dtype, c->d.H, c->d.dh, c->d.de, c->d.B, c->NP))
     a.order = reinterpret_cast<int*>(static_cast<char*>(ws) + c->off_order);
   c->forward_done = 0;
+  c->a_written = nullptr;
   EA_TRY(run_qkv(c, a, s));
   if (c->generic) {
     EA_TRY(run_gen(c, a, EA_K_FUSED, ea::kGenLayer, s));
@@ -448,6 +472,7 @@ ea_status edge_attn_layer_noalloc(ea_ctx* c, const ea_attn_params* p, const ea_u
   // the workspace is internal and shared by later calls: no backward or
   // two-pass edge_update may rely on what this call left in it
   c->forward_done = 0;
+  c->a_written = nullptr;
   return st;
 }
 
@@ -571,7 +596,7 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   EA_TRY(check_ptr(u->w_e, "w_e", 16, true));
   EA_TRY(check_ptr(u->b_e, "b_e", 4, false));
   EA_TRY(check_io(c, X, E, y, mask, true));
-  EA_TRY(check_ptr(A, "A", 16, !c->two_pass));  // two-pass: not produced by the forward, ignored
+  EA_TRY(check_ptr(A, "A", 16, !c->two_pass));  // two-pass: used only if the preceding layer call wrote it
   EA_TRY(check_ptr(dO, "dO", 16, true));
   EA_TRY(check_ptr(dEp, "dE_out", 16, true));
   EA_TRY(check_ptr(dX, "dX", 16, true));
@@ -607,7 +632,7 @@ ea_status edge_attn_backward(ea_ctx* c, const ea_attn_params* p, const ea_update
   g.RED = reinterpret_cast<float*>(bb + c->boff_red);
   g.WP = reinterpret_cast<float*>(bb + c->boff_wp);
   g.DP = reinterpret_cast<float*>(bb + c->boff_dp);
-  if (c->two_pass) {  // A recomputed from the logits and lse into the workspace
+  if (c->two_pass && !(A && A == c->a_written)) {  // A recomputed from the logits and lse into the workspace
     g.A = bb + c->boff_ar;
     g.recompute_a = 1;
   }

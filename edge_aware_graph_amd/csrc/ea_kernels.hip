@@ -1779,6 +1779,28 @@ __global__ __launch_bounds__(kThreads) void fused_stream_kernel(LayerArgs a) {
 // score stage and takes A = exp(u - lse) from pass 1's statistics;
 // kRecomputeU (unnormalized variant) re-runs it and takes the logit u itself.
 // The E fragments of the tile are read once (bfloat16) and serve both stages.
+// Two-pass pass 2 with an A buffer: this lane's four keys jb .. jb + 3 of
+// query i, every head, into A [B, H, n, n] (the bfloat16 operand the update
+// uses, 0 at masked pairs); keys or queries outside the n x n map are not
+// written.
+template <typename T, int H>
+__device__ __forceinline__ void store_a_keys(T* Ag, int b, int n, int i, int jb, const Frag<T, 4> (&ak)[H]) {
+  if ((n & 3) == 0) {  // uniform: 4 keys in or out together, one vector store
+    if (i < n && jb < n) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) ak[h].store(Ag + (((size_t)b * H + h) * n + i) * n + jb);
+    }
+  } else if (i < n) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      T* row = Ag + (((size_t)b * H + h) * n + i) * n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (jb + r < n) Num<T>::st(row + jb + r, ak[h].get(r));
+    }
+  }
+}
+
 template <typename T, int H, int DH, int DE, int MODE>
 __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
@@ -1840,6 +1862,14 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   const uint32_t bits = key_bits(mk);
   if ((__ballot(sc.mi) & 0xffffull) == 0ull || bits == 0u) {  // no real pair in the tile (uniform): zeros only
     if (jt < JT) zero_edge_tile<T, DE>(static_cast<T*>(a.E_out), b, n, i, j0, lg);
+    if constexpr (MODE == kRecompute) {
+      if (a.A != nullptr && jt < JT) {  // uniform: the map is asked for
+        Frag<T, 4> z[H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) z[h].zero();
+        store_a_keys<T, H>(static_cast<T*>(a.A), b, n, i, j0 + 4 * lg, z);
+      }
+    }
     return;
   }
   ETile<T, DE> et;
@@ -1883,6 +1913,9 @@ __global__ __launch_bounds__(kThreads) void update_kernel(LayerArgs a) {
   Frag<T, 4> ak[H];
 #pragma unroll
   for (int h = 0; h < H; ++h) ak[h].set(A[h]);
+  if constexpr (MODE == kRecompute) {
+    if (a.A != nullptr && jt < JT) store_a_keys<T, H>(static_cast<T*>(a.A), b, n, i, j0 + 4 * lg, ak);
+  }
   if (jt < JT)
     up.template tile<kKeepE>(et, sc.E, static_cast<T*>(a.E_out), b, n, i, sc.mi, j0, lg, bits, full, ak, [] {});
 }
@@ -2023,6 +2056,14 @@ __global__ __launch_bounds__(kThreads) void update_pipe_kernel(LayerArgs a, int 
     const bool full = tile_full(mi, bits);
     const int b = cur.b, jt = cur.jt;
     if (more) issue_small(nxt);
+    if constexpr (MODE == kRecompute) {
+      if (a.A != nullptr && jt < JT) {  // uniform: the map is asked for (0 at masked pairs)
+        Frag<T, 4> aq[H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) aq[h].set(A[h]);
+        store_a_keys<T, H>(static_cast<T*>(a.A), b, n, i, j0 + 4 * lg, aq);
+      }
+    }
     if (live) {
       Frag<T, 4> ak[H];
 #pragma unroll

@@ -171,8 +171,11 @@ ea_status edge_update(ea_ctx* ctx, const ea_attn_params* p, const ea_update_para
 /*
  * The whole layer in one call: the same outputs as edge_attn_forward followed
  * by edge_update. Single-pass mode runs attention and the edge update in one
- * fused kernel; two-pass mode runs both passes. A as in edge_attn_forward.
- * E_out may alias E.
+ * fused kernel; two-pass mode runs both passes. A as in edge_attn_forward,
+ * except that in two-pass mode A may also be given (no variant flag, a tuned
+ * shape, else EA_E_UNSUPPORTED): the second pass then writes the attention
+ * map too, +0.0 at masked pairs (the values its edge update used), and
+ * edge_attn_backward may read it instead of recomputing it. E_out may alias E.
  */
 ea_status edge_attn_layer(ea_ctx* ctx, const ea_attn_params* p, const ea_update_params* u,
                           const void* X, const void* E, const void* y,
@@ -207,9 +210,10 @@ ea_status edge_attn_layer_noalloc(ea_ctx* ctx, const ea_attn_params* p, const ea
  * b_e), with the forward's stored A (bfloat16 mode: its rounding points pass
  * gradients through unchanged). Supported: B n_p^2 < 2^31 (n_p = n rounded
  * up to 16), no variant flag, bfloat16 for both built shapes and float32 for
- * (4, 16, 16) (else EA_E_UNSUPPORTED). Two-pass contexts store no A: the
- * backward recomputes it, exp(u - lse) from the forward's row statistics, in
- * its own workspace, and the A argument is ignored (may be NULL).
+ * (4, 16, 16) (else EA_E_UNSUPPORTED). Two-pass contexts: when A is the
+ * buffer the preceding edge_attn_layer call on this context wrote, the
+ * backward reads it; otherwise (NULL, or any other buffer) it recomputes A,
+ * exp(u - lse) from the forward's row statistics, in its own workspace.
  *
  * Needs a preceding edge_attn_layer or edge_attn_forward on this context with
  * the same inputs, parameters, ws and stream (its Q, K, V, global FiLM and,

@@ -40,7 +40,7 @@ class Run:
     """Device buffers and one layer context for a batch."""
 
     def __init__(self, batch, dims: W.LayerDims, force_two_pass=False, device="cuda", variant=0,
-                 drop=()):
+                 drop=(), keep_a=False):
         self.dims = dims
         self.dev = upload(batch, dims.dtype, device)
         for k in drop:  # parameters the variant does not read are passed as NULL
@@ -51,7 +51,9 @@ class Run:
         B, n, d, de, H = dims.B, dims.n, dims.d, dims.de, dims.H
         self.ws = torch.empty(self.layer.workspace_bytes, dtype=torch.uint8, device=device)
         self.O = torch.full((B, n, d), float("nan"), dtype=dt, device=device)
-        self.A = None if self.layer.two_pass else torch.full((B, H, n, n), float("nan"), dtype=dt, device=device)
+        # two-pass contexts write A only when given a buffer (keep_a)
+        self.A = None if (self.layer.two_pass and not keep_a) else \
+            torch.full((B, H, n, n), float("nan"), dtype=dt, device=device)
         self.Eo = torch.full((B, n, n, de), float("nan"), dtype=dt, device=device)
 
     def fused(self):

@@ -31,9 +31,9 @@ def dims_of(name, **over):
     return dataclasses.replace(W.CONFIGS[name].dims, **over)
 
 
-def run_backward(batch, dims, seed=0, force_two_pass=False):
+def run_backward(batch, dims, seed=0, force_two_pass=False, keep_a=False):
     dt = HX.tdtype(dims.dtype)
-    run = HX.Run(batch, dims, force_two_pass=force_two_pass)
+    run = HX.Run(batch, dims, force_two_pass=force_two_pass, keep_a=keep_a)
     run.fused()
     B, n, d, de, H, dy = dims.B, dims.n, dims.d, dims.de, dims.H, dims.dy
     rng = np.random.default_rng(seed)
@@ -163,6 +163,23 @@ def test_backward_forced_two_pass(name, over):
         mask[0] = 1
         batch["mask"] = mask
     got, ref = run_backward(batch, dims, force_two_pass=True)
+    check(got, ref, batch, dims)
+
+
+@pytest.mark.parametrize("name,over,force", [("tiny", {}, True), ("planar", {"B": 2, "n": 100}, True),
+                                             ("planar", {"B": 2, "n": 37}, True), ("planar", {"B": 1, "n": 300}, False)],
+                         ids=["tiny-fp32", "n100-bf16", "n37-bf16", "n300-bf16"])
+def test_backward_two_pass_with_stored_a(name, over, force):
+    """Two-pass contexts given an A buffer: the layer's second pass writes A,
+    and the backward, handed that buffer, uses it instead of recomputing it."""
+    dims = dims_of(name, **over)
+    batch = W.make_batch(name, bias_scale=0.1, dims=dims)
+    if "n" in over:
+        rng = np.random.default_rng(over["n"])
+        mask = (rng.random((dims.B, dims.n)) < 0.8).astype(np.uint8)
+        mask[0] = 1
+        batch["mask"] = mask
+    got, ref = run_backward(batch, dims, seed=5, force_two_pass=force, keep_a=True)
     check(got, ref, batch, dims)
 
 

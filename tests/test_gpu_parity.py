@@ -236,3 +236,26 @@ def test_permutation_equivariance():
     assert np.abs(p["O"] - a["O"][:, perm]).max() <= HX.BF16_ABS_TOL
     assert np.abs(p["A"] - a["A"][:, :, perm][:, :, :, perm]).max() <= HX.BF16_ABS_TOL
     assert np.abs(p["Ep"] - a["Ep"][:, perm][:, :, perm]).max() <= HX.BF16_ABS_TOL
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,force", [("tiny", {}, True), ("planar", {"B": 2, "n": 100}, True),
+                                             ("planar", {"B": 2, "n": 37}, True), ("planar", {"B": 1, "n": 300}, False)],
+                         ids=["tiny-fp32", "n100-bf16", "n37-bf16", "n300-bf16"])
+def test_two_pass_layer_writes_a(name, over, force):
+    """A two-pass layer call given an A buffer returns the attention map too
+    (written by the second pass, +0.0 at masked pairs), with O and E' as
+    without it."""
+    dims = dataclasses.replace(W.CONFIGS[name].dims, **over)
+    batch = W.make_batch(name, bias_scale=0.1, dims=dims)
+    if "n" in over:
+        rng = np.random.default_rng(over["n"] + 1)
+        mask = (rng.random((dims.B, dims.n)) < 0.8).astype(np.uint8)
+        mask[0] = 1
+        batch["mask"] = mask
+    run = HX.Run(batch, dims, force_two_pass=force, keep_a=True)
+    assert run.layer.two_pass
+    res = run.fused().results()
+    assert "A" in res
+    ref = OR.forward(batch, dims.H, bf16=(dims.dtype == "bf16"))
+    HX.compare(res, ref, batch["mask"], dims)
